@@ -1,0 +1,316 @@
+"""Pool model of the oracle: physical blocks, refcounts, block tables, COW.
+
+Test infrastructure only (see the package docstring).
+
+The model follows two pages:
+
+* abhik.ai "examples/pagedattention.py", class ``KVPool``: a fixed pool of
+  physical blocks, an authored ``allocation_order`` (a full permutation of the
+  block ids), refcounts, per-sequence block tables and lengths; a new block is
+  the first free id in that order (region physical_pool and ``_allocate``);
+  a token position maps to ``(table[p // block_size], p % block_size)``
+  (region logical_address); appending into a shared, partially filled tail
+  first copies that whole block to a fresh one (region copy_on_write); fork
+  copies the parent's table and bumps every refcount (region fork_prefix);
+  release drops refcounts and frees blocks that reach zero (region
+  release_sequence).
+* vladkulikov.com notebook "Модуль 10", class ``PagedKVPool``: multi-token
+  append with a preflight block count (one extra block when the tail is
+  partial and shared, plus whole blocks for what does not fit in the tail),
+  checked before anything changes; ``share_prefix`` giving the target the
+  first ``ceil(prefix / block_size)`` blocks; the fill / payload / waste /
+  savings accounting; and the ``validate`` invariants.
+
+Where the two pages differ, the readings are:
+
+* next free block: the smallest rank in ``allocation_order`` (the first
+  page's rule); the second page's free list is a LIFO stack, which gives the
+  same ids on every trace either page prints, since none allocates after a
+  release;
+* a copy-on-write copies the whole block (first page); only live slots are
+  ever read;
+* ``fork(src, dst)`` is ``share(src, dst, len(src))``; the first page's
+  context tuple is not modelled (one pool per model and layer).
+
+Storage: ``K`` and ``V`` are float64 arrays ``[num_blocks, block_size,
+num_kv_heads, head_dim]`` -- block, slot, head, dim -- the first page's
+``keys[num_blocks, block_size, dim]`` with a KV-head axis added in the
+``[kv_len, num_kv_heads, head_dim]`` token order of ferrum-kv's
+``paged_attention``.  The oracle copies a block at the moment of the COW; it
+also records the ``(src, dst)`` pair so a test can compare the list of copies
+a device implementation must perform.
+"""
+
+from __future__ import annotations
+
+import heapq
+import math
+
+import numpy as np
+
+
+class OutOfBlocks(MemoryError):
+    """The preflight found fewer free blocks than the operation needs."""
+
+
+class UnknownSequence(KeyError):
+    """The sequence id is not live (never created, or already released)."""
+
+
+class SequenceExists(ValueError):
+    """The sequence id is already live."""
+
+
+def _positive_int(value, name):
+    if isinstance(value, bool) or not isinstance(value, (int, np.integer)) or value <= 0:
+        raise ValueError(f"{name} must be a positive integer")
+    return int(value)
+
+
+def _non_negative_int(value, name):
+    if isinstance(value, bool) or not isinstance(value, (int, np.integer)) or value < 0:
+        raise ValueError(f"{name} must be a non-negative integer")
+    return int(value)
+
+
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+class Pool:
+    """Fixed pool of physical KV blocks shared by refcounted block tables."""
+
+    def __init__(self, num_blocks, block_size, num_kv_heads=1, head_dim=1,
+                 allocation_order=None, store_values=True):
+        self.num_blocks = _positive_int(num_blocks, "num_blocks")
+        self.block_size = _positive_int(block_size, "block_size")
+        self.num_kv_heads = _positive_int(num_kv_heads, "num_kv_heads")
+        self.head_dim = _positive_int(head_dim, "head_dim")
+        if allocation_order is None:
+            order = list(range(self.num_blocks))
+        else:
+            order = [int(x) for x in allocation_order]
+        if sorted(order) != list(range(self.num_blocks)):
+            raise ValueError("allocation_order must be a full permutation")
+        self.order = tuple(order)
+        # rank[b] = position of block b in the authored order.
+        self.rank = [0] * self.num_blocks
+        for position, block in enumerate(self.order):
+            self.rank[block] = position
+        self.refs = np.zeros(self.num_blocks, dtype=np.int64)
+        self.free = set(range(self.num_blocks))
+        # Free blocks keyed by rank; heap pop = first free id in the order.
+        self._free_heap = [(self.rank[b], b) for b in range(self.num_blocks)]
+        heapq.heapify(self._free_heap)
+        self.tables: dict[int, list[int]] = {}
+        self.lengths: dict[int, int] = {}
+        self.copies: list[tuple[int, int]] = []
+        self.store_values = bool(store_values)
+        if self.store_values:
+            shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+            self.K = np.zeros(shape, dtype=np.float64)
+            self.V = np.zeros(shape, dtype=np.float64)
+
+    # ------------------------------------------------------------ lookups
+    def _existing(self, seq):
+        if seq not in self.tables:
+            raise UnknownSequence(seq)
+        return seq
+
+    def _new(self, seq):
+        if seq in self.tables:
+            raise SequenceExists(seq)
+        return seq
+
+    def sequence_length(self, seq):
+        return self.lengths[self._existing(seq)]
+
+    def page_table(self, seq):
+        return tuple(self.tables[self._existing(seq)])
+
+    # ------------------------------------------------------------ allocation
+    def _allocate(self):
+        """First free block in the authored allocation order; refcount 1."""
+        if not self.free:
+            raise OutOfBlocks("physical KV pool exhausted")
+        while True:
+            _, block = heapq.heappop(self._free_heap)
+            if block in self.free:
+                break
+        self.free.remove(block)
+        self.refs[block] = 1
+        return block
+
+    def _drop_ref(self, block):
+        self.refs[block] -= 1
+        if self.refs[block] == 0:
+            self.free.add(block)
+            heapq.heappush(self._free_heap, (self.rank[block], block))
+
+    # ------------------------------------------------------------ operations
+    def create(self, seq):
+        """Empty table, length 0; nothing is reserved up front."""
+        self._new(seq)
+        self.tables[seq] = []
+        self.lengths[seq] = 0
+
+    def blocks_needed(self, seq, n):
+        """Preflight count for appending ``n`` tokens to ``seq``."""
+        length = self.lengths[self._existing(seq)]
+        if n == 0:
+            return 0
+        need = 0
+        remainder = length % self.block_size
+        room = 0
+        if remainder:
+            if self.refs[self.tables[seq][-1]] > 1:
+                need += 1  # copy-on-write replacement of the shared tail
+            room = self.block_size - remainder
+        need += _ceil_div(max(0, n - room), self.block_size)
+        return need
+
+    def append(self, seq, n):
+        """Append ``n`` logical tokens; return the slot of each new position.
+
+        Preflight first: if the pool cannot supply every block the append
+        needs, raise :class:`OutOfBlocks` and change nothing.  Then a shared
+        partial tail is replaced by a private copy, the tail is filled and
+        whole new blocks are taken in allocation order.
+        """
+        n = _non_negative_int(n, "n_tokens")
+        self._existing(seq)
+        need = self.blocks_needed(seq, n)
+        if need > len(self.free):
+            raise OutOfBlocks(f"need {need} free blocks, {len(self.free)} remain")
+        table = self.tables[seq]
+        length = self.lengths[seq]
+        if n and length % self.block_size:
+            old = table[-1]
+            if self.refs[old] > 1:
+                new = self._allocate()
+                if self.store_values:
+                    self.K[new] = self.K[old]
+                    self.V[new] = self.V[old]
+                self.copies.append((old, new))
+                table[-1] = new
+                self._drop_ref(old)
+        first = length
+        for _ in range(_ceil_div(length + n, self.block_size) - len(table)):
+            table.append(self._allocate())
+        self.lengths[seq] = length + n
+        return [self.slot(seq, p) for p in range(first, first + n)]
+
+    def share(self, src, dst, prefix):
+        """New sequence ``dst`` holding the blocks covering ``src[:prefix]``."""
+        self._existing(src)
+        prefix = _non_negative_int(prefix, "prefix_tokens")
+        if prefix > self.lengths[src]:
+            raise ValueError("prefix_tokens exceeds source length")
+        self._new(dst)
+        table = self.tables[src][:_ceil_div(prefix, self.block_size)]
+        for block in table:
+            self.refs[block] += 1
+        self.tables[dst] = list(table)
+        self.lengths[dst] = prefix
+
+    def fork(self, src, dst):
+        """Child with the parent's whole table (every refcount + 1)."""
+        self._existing(src)
+        self.share(src, dst, self.lengths[src])
+
+    def release(self, seq):
+        """Drop one reference per block; blocks at zero become free."""
+        self._existing(seq)
+        for block in self.tables[seq]:
+            self._drop_ref(block)
+        del self.tables[seq]
+        del self.lengths[seq]
+
+    # ------------------------------------------------------------ addressing
+    def address(self, seq, p):
+        """(physical block, offset) of live token position ``p``."""
+        self._existing(seq)
+        if not 0 <= p < self.lengths[seq]:
+            raise ValueError("token index must address a live token")
+        logical, offset = divmod(p, self.block_size)
+        return self.tables[seq][logical], offset
+
+    def slot(self, seq, p):
+        block, offset = self.address(seq, p)
+        return block * self.block_size + offset
+
+    def write(self, slots, k, v):
+        """Store rows ``k[i], v[i]`` (each ``[num_kv_heads, head_dim]``) at slots."""
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        for i, slot in enumerate(slots):
+            block, offset = divmod(int(slot), self.block_size)
+            self.K[block, offset] = k[i]
+            self.V[block, offset] = v[i]
+
+    def gather(self, seq):
+        """Live K/V rows in logical order: two arrays ``[len, Hkv, D]``."""
+        length = self.lengths[self._existing(seq)]
+        keys = np.empty((length, self.num_kv_heads, self.head_dim))
+        values = np.empty((length, self.num_kv_heads, self.head_dim))
+        for p in range(length):
+            block, offset = self.address(seq, p)
+            keys[p] = self.K[block, offset]
+            values[p] = self.V[block, offset]
+        return keys, values
+
+    # ------------------------------------------------------------ accounting
+    def fills(self):
+        """Per block: the largest number of live slots any owner uses."""
+        fill = [0] * self.num_blocks
+        for seq, table in self.tables.items():
+            length = self.lengths[seq]
+            for j, block in enumerate(table):
+                fill[block] = max(fill[block], min(self.block_size, length - j * self.block_size))
+        return fill
+
+    def stats(self):
+        allocated = self.num_blocks - len(self.free)
+        capacity = allocated * self.block_size
+        payload = sum(f for b, f in enumerate(self.fills()) if self.refs[b])
+        logical = sum(self.lengths.values())
+        return {
+            "allocated_blocks": allocated,
+            "free_blocks": len(self.free),
+            "physical_capacity_tokens": capacity,
+            "physical_payload_tokens": payload,
+            "logical_tokens": logical,
+            "internal_waste_tokens": capacity - payload,
+            "sharing_savings_tokens": logical - payload,
+        }
+
+    def snapshot(self, names=None):
+        """Stats plus ``{name: {"blocks", "length"}}`` for every live sequence."""
+        out = dict(self.stats())
+        out["sequences"] = {
+            (names[s] if names else str(s)): {"blocks": list(t), "length": self.lengths[s]}
+            for s, t in sorted(self.tables.items(), key=lambda item: repr(item[0]))
+        }
+        return out
+
+    def validate(self):
+        """Invariants of the second page's ``validate``; AssertionError if broken."""
+        expected = [0] * self.num_blocks
+        for seq, table in self.tables.items():
+            length = self.lengths[seq]
+            assert length >= 0, "negative length"
+            assert len(table) == _ceil_div(length, self.block_size), "table length"
+            assert len(set(table)) == len(table), "block twice in one table"
+            for block in table:
+                assert 0 <= block < self.num_blocks, "block id out of range"
+                expected[block] += 1
+        fill = self.fills()
+        for block in range(self.num_blocks):
+            assert self.refs[block] == expected[block], "refcount != table references"
+            if self.refs[block] == 0:
+                assert block in self.free and fill[block] == 0, "unreferenced block not free"
+            else:
+                assert block not in self.free, "referenced block is free"
+                assert 1 <= fill[block] <= self.block_size, "fill out of range"
+        stats = self.stats()
+        assert stats["logical_tokens"] >= stats["physical_payload_tokens"], "payload > logical"
