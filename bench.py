@@ -1,0 +1,301 @@
+"""Paged-attention benchmark on one MI355X.
+
+One step is one decode step of one attention layer over the whole batch,
+through the C ABI: append one token to every sequence (host bookkeeping and
+slot mapping), write the new K/V rows into their slots (reshape_and_cache),
+then decode attention (plan upload, split-K partial kernel, log-sum-exp
+merge).  Workload: 32 sequences with lengths uniform in [1, 8192], 32 query /
+8 KV heads, head_dim 128, bf16 K/V, block_size 16, a 32768-block pool with
+shuffled block tables, Q/K/V ~ N(0, 1) (seeded, synthetic).
+
+Printed: one JSON line.  ``value`` = decode KV GB/s over whole steps
+(algorithmic bytes: every cached K and V row once, plus Q, O and the block
+tables; decimal GB).  ``roofline`` covers the decode partial kernel alone,
+timed with HIP events recorded on the stream it is launched on.
+``prefill`` measures the chunked causal prefill of 16 sequences x 512 rows on
+a shared 4096-token prefix (TFLOP/s on causal FLOPs).  ``cpu_baseline`` times
+the float64 oracle on a bounded sample of the same decode workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, decimal GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def to_device(arr, dtype):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def build_pool(wl):
+    from paged_kv_cache_block_amd import DevicePool
+    from synth import append_stream
+    pool = DevicePool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, dtype=wl.dtype,
+                      allocation_order=wl.allocation_order)
+    for op in append_stream(wl):
+        if op[0] == "create":
+            pool.create(op[1])
+        elif op[0] == "share":
+            pool.share(*op[1:])
+        else:
+            _, s, n, k, v = op
+            pool.write(pool.append(s, n), to_device(k, wl.dtype), to_device(v, wl.dtype))
+    return pool
+
+
+def decode_alg_bytes(lengths, wl):
+    """K and V rows once each, plus Q, O and the block tables."""
+    elt = wl.elt_bytes
+    kv = sum(lengths) * wl.num_kv_heads * wl.head_dim * 2 * elt
+    qo = 2 * len(lengths) * wl.num_heads * wl.head_dim * elt
+    tables = sum(-(-n // wl.block_size) for n in lengths) * 4
+    return kv + qo + tables
+
+
+def causal_flops(wl):
+    """4 * Hq * D per visible query-key pair (QK and PV, 2 FLOP per MAC)."""
+    lengths = wl.final_lengths()
+    total = 0
+    for s, q_len in wl.prefill:
+        prefix = lengths[s] - q_len
+        total += 4 * wl.num_heads * wl.head_dim * (q_len * prefix + q_len * (q_len + 1) // 2)
+    return total
+
+
+def run_decode(args):
+    import torch
+    from paged_kv_cache_block_amd import abi
+    from synth import decode_queries, gqa_decode
+
+    wl = gqa_decode()
+    log("building the decode workload (32 x U[1,8192], 32/8 heads, d 128, bf16, bs 16)")
+    pool = build_pool(wl)
+    seqs = list(wl.decode_seqs)
+    B = len(seqs)
+    q = to_device(decode_queries(wl), wl.dtype)
+    out = torch.empty_like(q)
+    total_steps = args.warmup + args.steps
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    new_k = torch.randn((total_steps, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    new_v = torch.randn((total_steps, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    lengths = np.array([pool.seq_len(s) for s in seqs], dtype=np.int64)
+    # Workspace for the longest batch this run reaches (lengths grow by 1 a step).
+    ws_need = abi.pa_decode_workspace_bytes(pool.handle, seqs, wl.num_heads)
+    ws = torch.empty(2 * ws_need + (1 << 20), dtype=torch.uint8, device="cuda")
+    # Pinned slot buffers (one per step, so no copy is overwritten in flight).
+    ones = np.ones(B, dtype=np.int32)
+    slot_host = torch.empty((total_steps, B), dtype=torch.int64).pin_memory()
+    slot_dev = torch.empty((total_steps, B), dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    handle = pool.handle
+    alg = []
+
+    def step(i):
+        abi.pa_append_batch(handle, seqs, ones, slot_host[i].numpy())
+        slot_dev[i].copy_(slot_host[i], non_blocking=True)
+        abi.pa_reshape_and_cache(handle, new_k[i], new_v[i], slot_dev[i], B, stream.cuda_stream)
+        abi.pa_decode(handle, seqs, wl.num_heads, q, out, ws, ws.numel(), stream.cuda_stream)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+        lengths += 1
+    torch.cuda.synchronize()
+    abi.pa_timing_reset()
+    abi.pa_timing_enable(True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        step(i)
+        lengths += 1
+        alg.append(decode_alg_bytes(lengths, wl))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    abi.pa_timing_enable(False)
+    dec_ms, dec_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
+    mrg_ms, mrg_n = abi.pa_timing_read(abi.PA_KERNEL_MERGE)
+    cache_ms, cache_n = abi.pa_timing_read(abi.PA_KERNEL_CACHE)
+    pool.validate()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    alg_per_step = float(np.mean(alg))
+    kernel_ms = dec_ms / max(dec_n, 1)
+    merge_ms = mrg_ms / max(mrg_n, 1)
+    result = {
+        "ms_per_step": ms_per_step,
+        "value": alg_per_step / (ms_per_step * 1e-3) / 1e9,
+        "tokens_per_s": B / (ms_per_step * 1e-3),
+        "alg_bytes_per_step": alg_per_step,
+        "decode_kernel_us": kernel_ms * 1e3,
+        "merge_kernel_us": merge_ms * 1e3,
+        "cache_kernel_us": cache_ms / max(cache_n, 1) * 1e3,
+        "kernel_launches": {"decode": dec_n, "merge": mrg_n, "cache": cache_n},
+        "sum_len": int(lengths.sum()),
+    }
+    achieved = alg_per_step / (kernel_ms * 1e-3) / 1e9
+    result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                          "kernel": "decode_gqa_mfma<128,16>",
+                          "decode_plus_merge_GBs": round(alg_per_step / ((kernel_ms + merge_ms) * 1e-3) / 1e9, 1)}
+    pool.close()
+    return wl, result
+
+
+def run_prefill(args):
+    import torch
+    from paged_kv_cache_block_amd import abi
+    from synth import prefill_queries, prefix_prefill
+
+    wl = prefix_prefill()
+    log("building the prefill workload (16 x 512 rows on a shared 4096 prefix)")
+    pool = build_pool(wl)
+    seqs = [s for s, _ in wl.prefill]
+    q_lens = [n for _, n in wl.prefill]
+    q = to_device(prefill_queries(wl), wl.dtype)
+    out = torch.empty_like(q)
+    need = abi.pa_prefill_workspace_bytes(pool.handle, seqs, q_lens, wl.num_heads)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(max(1, args.prefill_warmup)):
+        abi.pa_prefill_chunk(pool.handle, seqs, q_lens, wl.num_heads, q, out, ws, ws.numel(), stream)
+    torch.cuda.synchronize()
+    abi.pa_timing_reset()
+    abi.pa_timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.prefill_iters):
+        abi.pa_prefill_chunk(pool.handle, seqs, q_lens, wl.num_heads, q, out, ws, ws.numel(), stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    abi.pa_timing_enable(False)
+    k_ms, k_n = abi.pa_timing_read(abi.PA_KERNEL_PREFILL)
+    flops = causal_flops(wl)
+    kernel_ms = k_ms / max(k_n, 1)
+    call_ms = (t1 - t0) * 1e3 / args.prefill_iters
+    tflops = flops / (kernel_ms * 1e-3) / 1e12
+    pool.close()
+    return {
+        "workload": "prefix_prefill: 16 seqs share 4096 prefix + 512 own rows, 32/8 heads, d 128, bf16, bs 16",
+        "causal_flops": flops,
+        "ms_per_call": call_ms,
+        "kernel_ms": kernel_ms,
+        "tflops": round(tflops, 2),
+        "tokens_per_s": round(sum(q_lens) / (call_ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
+    }
+
+
+def run_cpu_baseline(wl, seconds):
+    """The float64 oracle (gather through its pool, then attention) on the
+    first sequences of the same decode workload, repeated for ~``seconds``."""
+    import oracle
+    from synth import append_stream, decode_queries
+    from synth.workloads import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    sample = [0, 1, 2, 3]
+    lengths = wl.final_lengths()
+    blocks = sum(-(-lengths[s] // wl.block_size) for s in sample)
+    pool = oracle.Pool(blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    for op in append_stream(wl, only=set(sample)):
+        if op[0] == "append" and op[1] in sample:
+            pool.create(op[1])
+            pool.write(pool.append(op[1], op[2]), to_f64(op[3], wl.dtype), to_f64(op[4], wl.dtype))
+    q = to_f64(decode_queries(wl, sample), wl.dtype)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for i, s in enumerate(sample):
+            oracle.paged_attention(pool, s, q[i:i + 1])
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    sample_lengths = [lengths[s] for s in sample]
+    alg = decode_alg_bytes(sample_lengths, wl) * reps
+    return {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 oracle paged decode of sequences {sample} of the same workload "
+                      f"(lengths {sample_lengths}, all 32 heads), {reps} repetitions in {dt:.1f} s",
+            "tokens_per_s": round(len(sample) * reps / dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-iters", type=int, default=10)
+    ap.add_argument("--prefill-warmup", type=int, default=2)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the paged-attention path "
+              "here is single-GPU.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    from paged_kv_cache_block_amd import abi
+    abi.load()
+
+    wl, dec = run_decode(args)
+    line = {
+        "metric": "paged-attn decode KV GB/s (% of HBM peak) + tokens/s; prefill TFLOP/s",
+        "value": round(dec["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gqa_decode: 32 seqs, lengths U[1,8192] (seed 1), 32 query / 8 KV heads, "
+                               "head_dim 128, bf16 K/V, block_size 16, 32768-block pool, one layer; "
+                               "step = append 1 token/seq + reshape_and_cache + decode",
+                   "global_batch": 32, "seq_len": "U[1,8192]", "parallelism": "single GPU"},
+        "tokens_per_s": round(dec["tokens_per_s"], 1),
+        "hbm_frac_step": round(dec["value"] / HBM_PEAK_GBS, 4),
+        "decode": {k: dec[k] for k in ("decode_kernel_us", "merge_kernel_us", "cache_kernel_us",
+                                        "alg_bytes_per_step", "kernel_launches", "sum_len")},
+        "roofline": dec["roofline"],
+    }
+    if not args.no_prefill:
+        line["prefill"] = run_prefill(args)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        line["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

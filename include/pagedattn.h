@@ -1,0 +1,280 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: paged attention over a refcounted
+ * pool of KV blocks, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources this interface follows (cited by page title and section):
+ *   [KVPool]    abhik.ai "examples/pagedattention.py", class KVPool and its
+ *               regions physical_pool, logical_address, append_or_allocate,
+ *               fork_prefix, copy_on_write, paged_attention, release_sequence.
+ *   [PagedPool] vladkulikov.com notebook "Модуль 10. KV-кэши и эффективный
+ *               инференс", class PagedKVPool (preflighted append, share_prefix,
+ *               release, fill accounting, validate) and its negative tests.
+ *   [ferrum]    docs.rs ferrum-kv 0.4.0 src/attention.rs, paged_attention
+ *               (GQA grouping, 1/sqrt(head_dim) scale, causal mask) and
+ *               PagedKvCacheManager::write_kv as its caller uses it.
+ *   [lecture19] CMU 11-667 lecture 19 infer_world.py, section 3 (online
+ *               softmax statistics, tiled attention).
+ *
+ * Conventions for every call
+ *   - Sequence ids are arbitrary int64 values chosen by the caller.
+ *   - "host" pointers are ordinary CPU memory read or written before the call
+ *     returns; "device" pointers are GPU memory owned by the caller (e.g.
+ *     torch tensors).  The library never frees caller memory.  A pool object
+ *     owns only host metadata plus a few pinned host staging buffers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Device work is enqueued on it and the call returns without waiting,
+ *     except where stated.  All device calls on one pool must use one stream
+ *     (or be ordered by the caller): pending copy-on-write copies are
+ *     flushed onto whichever stream the next device call names.
+ *   - Every call validates all arguments first and, where it allocates
+ *     blocks, preflights the block count; on any error the pool is unchanged
+ *     (strong guarantee, [KVPool] append/_private_tail, [PagedPool] append and
+ *     its "OOM leaves the snapshot unchanged" negative test).  The message of
+ *     the last error on the calling thread is returned by pa_last_error().
+ *   - A pool is not thread-safe.
+ *
+ * Device layouts (row-major, element size 4 for PA_DTYPE_F32, 2 for BF16):
+ *   K pool  [num_blocks][num_kv_heads][block_size][head_dim]
+ *   V pool  [num_blocks][num_kv_heads][head_dim][block_size]
+ *   (one (block, KV head) page of K is block_size rows of head_dim values;
+ *    the same page of V is stored transposed, head_dim rows of block_size
+ *    tokens, so that the P.V contraction over tokens reads contiguous memory.)
+ *   Both pools must be 16-byte aligned.  The layout is a physical choice:
+ *   the logical K/V row of token p of a sequence is the slot
+ *   table[p / block_size] * block_size + p % block_size ([KVPool]
+ *   logical_address), whatever the layout.
+ *   q / out for decode   [B][num_heads][head_dim]
+ *   q / out for prefill  [sum(q_lens)][num_heads][head_dim] (sequence-major,
+ *                        [ferrum] "[q_tokens, num_heads, head_dim]")
+ *   k_new / v_new        [n][num_kv_heads][head_dim]
+ *   q, out, k_new and v_new use the pool dtype; accumulation is fp32.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_pool pa_pool; /* opaque; owns host metadata only */
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,   /* bad size, pointer, prefix, q_len, workspace, ... */
+  PA_ERR_UNKNOWN_SEQ = -2,   /* id not live: never created or already released */
+  PA_ERR_SEQ_EXISTS = -3,    /* id already live */
+  PA_ERR_OUT_OF_BLOCKS = -4, /* preflight: the pool cannot supply the blocks */
+  PA_ERR_DEVICE = -5         /* a HIP call failed (message in pa_last_error) */
+} pa_status;
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+
+typedef struct {
+  int32_t num_blocks;   /* physical blocks in the pool, > 0 */
+  int32_t block_size;   /* token slots per block, > 0 */
+  int32_t num_kv_heads; /* KV heads stored per token, > 0 */
+  int32_t head_dim;     /* values per head, 1..512 */
+  int32_t dtype;        /* pa_dtype of K, V, q and out */
+} pa_pool_desc;
+
+/* Accounting of [PagedPool] (allocated_blocks ... sharing_savings_tokens).
+ * A block's fill is the largest number of live slots any sequence holding it
+ * uses; payload sums fills over referenced blocks; capacity is
+ * allocated * block_size; waste = capacity - payload; logical sums sequence
+ * lengths; savings = logical - payload. */
+typedef struct {
+  int64_t allocated_blocks, free_blocks, physical_capacity_tokens,
+      physical_payload_tokens, logical_tokens, internal_waste_tokens,
+      sharing_savings_tokens;
+} pa_pool_stats;
+
+/* ---------------------------------------------------------------- pool --- */
+
+/* Bytes of ONE of the K / V pools for `desc`:
+ * num_blocks * num_kv_heads * block_size * head_dim * element size.
+ * Returns 0 for an invalid descriptor. */
+size_t pa_pool_bytes(const pa_pool_desc* desc);
+
+/* Create a pool over caller-allocated device pools ([KVPool] physical_pool).
+ * allocation_order: host [num_blocks], a full permutation of 0..num_blocks-1
+ *   giving the order in which free blocks are handed out (the free block of
+ *   lowest rank is taken next, [KVPool] _allocate), or NULL for 0,1,2,...
+ * k_pool, v_pool: device, pa_pool_bytes(desc) bytes each, laid out as in the
+ *   header comment; both NULL gives a metadata-only pool (every device call
+ *   on it fails with PA_ERR_INVALID_ARG).  The caller keeps ownership and
+ *   must keep them alive until pa_pool_destroy.
+ * out: receives the new pool.
+ * Errors: PA_ERR_INVALID_ARG for a bad descriptor, a non-permutation order,
+ *   exactly one NULL pool pointer, misaligned pools or a NULL `out`. */
+pa_status pa_pool_create(const pa_pool_desc* desc, const int32_t* allocation_order,
+                         void* k_pool, void* v_pool, pa_pool** out);
+
+/* Free the pool's host metadata and staging buffers (waits for the pool's
+ * own pending uploads).  NULL is ignored. */
+void pa_pool_destroy(pa_pool* pool);
+
+/* New empty sequence, length 0; no block is reserved ([KVPool] create,
+ * [PagedPool] create).  Errors: PA_ERR_SEQ_EXISTS. */
+pa_status pa_seq_create(pa_pool* pool, int64_t seq);
+
+/* Append n_tokens >= 0 logical tokens to `seq` ([PagedPool] append; [KVPool]
+ * append_or_allocate and copy_on_write).
+ * Preflight: needs = (1 if the tail block is partially filled and shared)
+ *   + ceil(max(0, n_tokens - room_in_tail) / block_size); if needs exceeds
+ *   the free blocks, PA_ERR_OUT_OF_BLOCKS and nothing changes.
+ * Then a shared partial tail is replaced by a fresh block and a whole-block
+ *   copy old -> new is recorded as pending (executed on the device by the
+ *   next device call on this pool, or pa_flush_copies), the tail is filled
+ *   and whole new blocks are taken in allocation order.
+ * slots_out: host [n_tokens] (may be NULL when n_tokens == 0); receives the
+ *   slot of each new position p = old_len .. old_len+n_tokens-1, i.e.
+ *   table[p / block_size] * block_size + p % block_size.  Pass them (on the
+ *   device) to pa_reshape_and_cache.
+ * This call is host-only: it launches nothing.
+ * Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG (n_tokens < 0, NULL
+ *   slots_out with n_tokens > 0), PA_ERR_OUT_OF_BLOCKS. */
+pa_status pa_append(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slots_out);
+
+/* pa_append(pool, seqs[i], n_tokens[i], ...) for i = 0 .. count-1, in order
+ * (a decode step appends one token to every sequence of the batch), with the
+ * slots of all appends concatenated in slots_out (host [sum n_tokens]).
+ * All or nothing: if any append fails, the earlier appends of the batch are
+ * undone (tables, lengths, refcounts, free blocks and pending copies are as
+ * before the call) and that append's status is returned.  Host-only.
+ * Errors: as pa_append; PA_ERR_INVALID_ARG for count < 0 or NULL arrays. */
+pa_status pa_append_batch(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
+                          int32_t count, int64_t* slots_out);
+
+/* New sequence `dst` holding the first ceil(prefix_tokens / block_size)
+ * blocks of `src` with every refcount + 1 and length prefix_tokens
+ * ([PagedPool] share_prefix).  Host-only.
+ * Errors: PA_ERR_UNKNOWN_SEQ (src), PA_ERR_SEQ_EXISTS (dst),
+ *   PA_ERR_INVALID_ARG (prefix_tokens < 0 or > length of src). */
+pa_status pa_share(pa_pool* pool, int64_t src, int64_t dst, int32_t prefix_tokens);
+
+/* pa_share(pool, src, dst, length of src): the child holds the parent's whole
+ * table ([KVPool] fork_prefix).  Host-only.  Errors as pa_share. */
+pa_status pa_fork(pa_pool* pool, int64_t src, int64_t dst);
+
+/* Drop one reference to each block of `seq` and forget it; blocks whose
+ * refcount reaches 0 become free ([KVPool] release_sequence, [PagedPool]
+ * release).  A second release of the same id is PA_ERR_UNKNOWN_SEQ.
+ * Host-only; device contents are left as they are. */
+pa_status pa_release(pa_pool* pool, int64_t seq);
+
+/* Pending copy-on-write copies, oldest first, as (src, dst) block pairs.
+ * pairs_out: host [2 * cap]; *n receives the number pending (may exceed cap;
+ * then only the first cap are written).  Errors: PA_ERR_INVALID_ARG. */
+pa_status pa_pending_copies(const pa_pool* pool, int32_t* pairs_out, int32_t cap, int32_t* n);
+
+/* Enqueue the pending whole-block copies (K and V, every head) on `stream`
+ * in recording order, then clear the list.  Called implicitly at the start
+ * of pa_reshape_and_cache, pa_decode and pa_prefill_chunk.
+ * Errors: PA_ERR_INVALID_ARG (metadata-only pool), PA_ERR_DEVICE. */
+pa_status pa_flush_copies(pa_pool* pool, void* stream);
+
+/* Write new K/V rows into their slots ([KVPool] append stores the row at
+ * (table[p / block_size], p % block_size); ferrum's write_kv):
+ *   Kpool[slot / bs][h][slot % bs][:] = k_new[i][h][:]
+ *   Vpool[slot / bs][h][:][slot % bs] = v_new[i][h][:]   for i < n, every h.
+ * k_new, v_new: device [n][num_kv_heads][head_dim]; slots: device int64 [n].
+ * A slot outside [0, num_blocks * block_size) is skipped.  Two rows naming
+ * one slot race.  Pending copies are flushed first on `stream`.
+ * Errors: PA_ERR_INVALID_ARG (NULL pointers with n > 0, n < 0,
+ *   metadata-only pool), PA_ERR_DEVICE. */
+pa_status pa_reshape_and_cache(pa_pool* pool, const void* k_new, const void* v_new,
+                               const int64_t* slots, int32_t n, void* stream);
+
+/* ------------------------------------------------------------ attention --- */
+
+/* Workspace bytes pa_decode needs for this batch (a device buffer the caller
+ * allocates; it holds the uploaded block tables, the work list and split-K
+ * partial results).  0 if the arguments are invalid. */
+size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32_t B,
+                                 int32_t num_heads);
+
+/* Decode attention: one query row per sequence attends over every cached
+ * token of that sequence ([KVPool] paged_attention: the next position sees
+ * the whole cache; [ferrum] paged_attention with q_tokens = 1):
+ *   for b < B, h < num_heads, with L = length(seqs[b]), G = num_heads /
+ *   num_kv_heads, g = h / G, K_j / V_j = the rows of token j gathered
+ *   through the block table:
+ *     s_j = (q[b][h] . K_j[g]) / sqrt(head_dim),  j < L
+ *     out[b][h] = sum_j softmax(s)_j V_j[g]
+ * Long sequences are split into page ranges whose partial (max, sum, acc)
+ * are merged by log-sum-exp ([lecture19] online_softmax_stats applied
+ * across ranges).
+ * seqs: host [B] live ids (duplicates allowed); q, out: device
+ *   [B][num_heads][head_dim] in the pool dtype; ws: device, at least
+ *   pa_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by the
+ *   caller and overwritten by this call (do not reuse it for another call
+ *   until this one has finished on `stream`).
+ * Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG (B <= 0, num_heads not a
+ *   positive multiple of num_kv_heads, a sequence of length 0 ([ferrum]
+ *   "kv_len must be positive"), small or misaligned ws, NULL pointers,
+ *   metadata-only pool), PA_ERR_DEVICE. */
+pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
+                    const void* q, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes pa_prefill_chunk needs.  0 if the arguments are invalid. */
+size_t pa_prefill_workspace_bytes(const pa_pool* pool, const int64_t* seqs,
+                                  const int32_t* q_lens, int32_t B, int32_t num_heads);
+
+/* Chunked causal prefill ([ferrum] paged_attention with q_tokens > 1): the
+ * q_lens[b] query rows of sequence b are its LAST q_lens[b] positions, whose
+ * K/V must already be appended and cached.  With L = length(seqs[b]), row t
+ * (0 <= t < q_lens[b]) sees keys j <= L - q_lens[b] + t (bottom-right causal
+ * mask, the same rule as [lecture19] CachedDecoder):
+ *     out[r][h] = sum_{j visible} softmax(s)_j V_j[g],  r = row offset of b + t
+ * seqs, q_lens: host [B]; q, out: device [sum q_lens][num_heads][head_dim];
+ * ws: as for pa_decode.
+ * Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG (q_lens[b] < 1 or > L,
+ *   head mismatch, small ws, NULL pointers), PA_ERR_DEVICE. */
+pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,
+                           int32_t B, int32_t num_heads, const void* q, void* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------- inspection --- */
+/* Synchronous host reads of the metadata ([PagedPool] sequence_length,
+ * page_table, the per-block ref_count, the accounting properties and
+ * validate).  They never touch the device. */
+pa_status pa_seq_len(const pa_pool* pool, int64_t seq, int32_t* len);
+/* out: host [cap]; *n receives the table length (only min(n, cap) written). */
+pa_status pa_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap, int32_t* n);
+pa_status pa_refcount(const pa_pool* pool, int32_t block, int32_t* rc);
+pa_status pa_stats(const pa_pool* pool, pa_pool_stats* stats);
+/* [PagedPool] validate: refcount == table references, free <=> refcount 0,
+ * table length == ceil(len / block_size), no block twice in one table, fill
+ * of a referenced block in [1, block_size], logical >= payload.
+ * Returns PA_ERR_INVALID_ARG with the broken invariant in pa_last_error. */
+pa_status pa_validate(const pa_pool* pool);
+/* Number of live sequences; ids_out (host [cap], may be NULL) receives them
+ * in ascending order. */
+pa_status pa_sequences(const pa_pool* pool, int64_t* ids_out, int32_t cap, int32_t* n);
+/* Message of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* ---------------------------------------------------------------- timing --- */
+/* Kernel timing with HIP events recorded on the stream each kernel is
+ * launched on.  Off by default.  pa_timing_read synchronizes on the recorded
+ * events and returns the summed duration and launch count of one kernel
+ * family since the last reset. */
+typedef enum {
+  PA_KERNEL_DECODE = 0,   /* decode partial (split-K) kernel */
+  PA_KERNEL_MERGE = 1,    /* log-sum-exp merge */
+  PA_KERNEL_PREFILL = 2,  /* chunked prefill */
+  PA_KERNEL_CACHE = 3,    /* reshape_and_cache */
+  PA_KERNEL_COPY = 4,     /* copy-on-write block copies */
+  PA_KERNEL_COUNT = 5
+} pa_kernel;
+pa_status pa_timing_enable(int on);
+pa_status pa_timing_reset(void);
+pa_status pa_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDATTN_H */

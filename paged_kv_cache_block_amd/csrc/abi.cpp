@@ -1,0 +1,519 @@
+// C ABI of libpagedattn.so (declared in include/pagedattn.h).
+//
+// Host metadata lives in pa::BlockPool (pool.cpp); work plans in plan.cpp;
+// kernels in cache.hip / decode.hip / prefill.hip.  This file validates
+// arguments, moves plans into the caller's workspace through pinned staging
+// buffers, orders pending copy-on-write copies before any other device work
+// on the pool, and records optional per-kernel timing events.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "pagedattn.h"
+#include "plan.hpp"
+#include "pool.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+pa_status fail(int status, const std::string& msg) {
+  g_err = msg;
+  return static_cast<pa_status>(status);
+}
+
+pa_status ok() { return PA_OK; }
+
+pa_status from(pa::Status s, const std::string& msg) {
+  return s == pa::kOk ? ok() : fail(s, msg);
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define PA_HIP(call)                                  \
+  do {                                                \
+    hipError_t e_ = (call);                           \
+    if (e_ != hipSuccess) return hip_fail(e_, #call); \
+  } while (0)
+
+// ------------------------------------------------------------------ timing
+struct TimingRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRecord> g_records;
+double g_total_ms[PA_KERNEL_COUNT] = {};
+int64_t g_launches[PA_KERNEL_COUNT] = {};
+
+struct TimedLaunch {
+  int kernel;
+  hipStream_t stream;
+  hipEvent_t start = nullptr, stop = nullptr;
+  TimedLaunch(int k, hipStream_t s) : kernel(k), stream(s) {
+    std::lock_guard<std::mutex> lock(g_tmu);
+    if (!g_timing) return;
+    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess ||
+        hipEventRecord(start, stream) != hipSuccess) {
+      start = stop = nullptr;
+    }
+  }
+  void done() {
+    if (!start) return;
+    (void)hipEventRecord(stop, stream);
+    std::lock_guard<std::mutex> lock(g_tmu);
+    g_records.push_back({kernel, start, stop});
+  }
+};
+
+void drain_timing_locked() {
+  for (auto& r : g_records) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      g_total_ms[r.kernel] += ms;
+      g_launches[r.kernel] += 1;
+    }
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_records.clear();
+}
+
+}  // namespace
+
+// -------------------------------------------------------------------- pool
+struct pa_pool {
+  pa::BlockPool meta;
+  pa::PoolGeom geom{};
+  void* k = nullptr;
+  void* v = nullptr;
+  struct Staging {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+  static constexpr int kRing = 4;
+  Staging ring[kRing];
+  int next = 0;
+
+  bool has_device() const { return k != nullptr; }
+
+  // Copy `bytes` of host data to device `dst` on `stream` through a pinned
+  // buffer; the buffer is reused only after its previous copy has finished.
+  pa_status upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+    Staging& st = ring[next];
+    next = (next + 1) % kRing;
+    if (st.pending) {
+      PA_HIP(hipEventSynchronize(st.ev));
+      st.pending = false;
+    }
+    if (!st.ev) PA_HIP(hipEventCreateWithFlags(&st.ev, hipEventDisableTiming));
+    if (st.cap < bytes) {
+      if (st.host) PA_HIP(hipHostFree(st.host));
+      st.host = nullptr;
+      st.cap = 0;
+      size_t cap = std::max<size_t>(bytes + bytes / 2, 1 << 16);
+      PA_HIP(hipHostMalloc(&st.host, cap, hipHostMallocDefault));
+      st.cap = cap;
+    }
+    std::memcpy(st.host, src, bytes);
+    PA_HIP(hipMemcpyAsync(dst, st.host, bytes, hipMemcpyHostToDevice, stream));
+    PA_HIP(hipEventRecord(st.ev, stream));
+    st.pending = true;
+    return ok();
+  }
+
+  pa_status flush(hipStream_t stream) {
+    auto copies = meta.take_pending_copies();
+    if (!has_device() || copies.empty()) return ok();
+    // Copies that touch a block an earlier copy of the same launch writes
+    // (or reads) go to a later launch, so recording order is kept.
+    size_t i = 0;
+    while (i < copies.size()) {
+      std::vector<int32_t> src, dst;
+      while (i < copies.size() && static_cast<int>(src.size()) < pa::kMaxCopiesPerLaunch) {
+        const int32_t s = copies[i].first, d = copies[i].second;
+        bool clash = false;
+        for (size_t j = 0; j < src.size() && !clash; ++j)
+          clash = s == dst[j] || d == dst[j] || d == src[j];
+        if (clash) break;
+        src.push_back(s);
+        dst.push_back(d);
+        ++i;
+      }
+      TimedLaunch t(PA_KERNEL_COPY, stream);
+      hipError_t e = pa::launch_copy_blocks(geom, k, v, src.data(), dst.data(),
+                                            static_cast<int>(src.size()), stream);
+      t.done();
+      if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+    }
+    return ok();
+  }
+
+  ~pa_pool() {
+    for (auto& st : ring) {
+      if (st.pending) (void)hipEventSynchronize(st.ev);
+      if (st.ev) (void)hipEventDestroy(st.ev);
+      if (st.host) (void)hipHostFree(st.host);
+    }
+  }
+};
+
+namespace {
+
+bool desc_ok(const pa_pool_desc* d, std::string* msg) {
+  if (!d) {
+    *msg = "NULL descriptor";
+    return false;
+  }
+  if (d->num_blocks <= 0 || d->block_size <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0) {
+    *msg = "num_blocks, block_size, num_kv_heads and head_dim must be positive";
+    return false;
+  }
+  if (d->head_dim > 512) {
+    *msg = "head_dim must be at most 512";
+    return false;
+  }
+  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16) {
+    *msg = "dtype must be PA_DTYPE_F32 or PA_DTYPE_BF16";
+    return false;
+  }
+  return true;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+float scale_log2_for(int32_t head_dim) {
+  return static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_pool_bytes(const pa_pool_desc* desc) {
+  std::string msg;
+  if (!desc_ok(desc, &msg)) return 0;
+  return static_cast<size_t>(desc->num_blocks) * desc->num_kv_heads * desc->block_size *
+         desc->head_dim * (desc->dtype == PA_DTYPE_BF16 ? 2 : 4);
+}
+
+pa_status pa_pool_create(const pa_pool_desc* desc, const int32_t* allocation_order, void* k_pool,
+                         void* v_pool, pa_pool** out) {
+  std::string msg;
+  if (!out) return fail(PA_ERR_INVALID_ARG, "NULL out pointer");
+  if (!desc_ok(desc, &msg)) return fail(PA_ERR_INVALID_ARG, msg);
+  if ((k_pool == nullptr) != (v_pool == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "k_pool and v_pool must both be NULL or both be set");
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) % 16)
+    return fail(PA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  pa::BlockPool meta;
+  pa::Status s = pa::BlockPool::make(desc->num_blocks, desc->block_size, allocation_order, &meta, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  pa_pool* p = new pa_pool();
+  p->meta = std::move(meta);
+  p->geom = {desc->num_blocks, desc->block_size, desc->num_kv_heads, desc->head_dim, desc->dtype};
+  p->k = k_pool;
+  p->v = v_pool;
+  *out = p;
+  return ok();
+}
+
+void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+pa_status pa_seq_create(pa_pool* pool, int64_t seq) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.create(seq, &msg), msg);
+}
+
+pa_status pa_append(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slots_out) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.append(seq, n_tokens, slots_out, &msg), msg);
+}
+
+pa_status pa_append_batch(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
+                          int32_t count, int64_t* slots_out) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.append_batch(seqs, n_tokens, count, slots_out, &msg), msg);
+}
+
+pa_status pa_share(pa_pool* pool, int64_t src, int64_t dst, int32_t prefix_tokens) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.share(src, dst, prefix_tokens, &msg), msg);
+}
+
+pa_status pa_fork(pa_pool* pool, int64_t src, int64_t dst) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.fork(src, dst, &msg), msg);
+}
+
+pa_status pa_release(pa_pool* pool, int64_t seq) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.release(seq, &msg), msg);
+}
+
+pa_status pa_pending_copies(const pa_pool* pool, int32_t* pairs_out, int32_t cap, int32_t* n) {
+  if (!pool || !n || cap < 0 || (cap > 0 && !pairs_out)) return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  const auto& pending = pool->meta.pending_copies();
+  *n = static_cast<int32_t>(pending.size());
+  for (int32_t i = 0; i < cap && i < *n; ++i) {
+    pairs_out[2 * i] = pending[i].first;
+    pairs_out[2 * i + 1] = pending[i].second;
+  }
+  return ok();
+}
+
+pa_status pa_flush_copies(pa_pool* pool, void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  return pool->flush(as_stream(stream));
+}
+
+pa_status pa_reshape_and_cache(pa_pool* pool, const void* k_new, const void* v_new,
+                               const int64_t* slots, int32_t n, void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  if (!pool->has_device()) return fail(PA_ERR_INVALID_ARG, "metadata-only pool has no device memory");
+  if (n < 0 || (n > 0 && (!k_new || !v_new || !slots)))
+    return fail(PA_ERR_INVALID_ARG, "n must be >= 0 with non-NULL k_new, v_new, slots");
+  hipStream_t s = as_stream(stream);
+  pa_status st = pool->flush(s);
+  if (st != PA_OK) return st;
+  TimedLaunch t(PA_KERNEL_CACHE, s);
+  hipError_t e = pa::launch_reshape_and_cache(pool->geom, pool->k, pool->v, k_new, v_new, slots, n, s);
+  t.done();
+  if (e != hipSuccess) return hip_fail(e, "reshape_and_cache launch");
+  return ok();
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads) {
+  if (!pool) return 0;
+  pa::DecodePlan plan;
+  std::string msg;
+  if (pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                            pool->geom.head_dim, 0, &plan, &msg) != pa::kOk)
+    return 0;
+  return plan.total_bytes;
+}
+
+pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads, const void* q,
+                    void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  if (!pool->has_device()) return fail(PA_ERR_INVALID_ARG, "metadata-only pool has no device memory");
+  if (!q || !out || !ws) return fail(PA_ERR_INVALID_ARG, "q, out and ws must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % pa::kWsAlign)
+    return fail(PA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  if (num_heads <= 0 || num_heads % pool->geom.num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_heads must be a positive multiple of num_kv_heads");
+  if (pool->geom.dtype == PA_DTYPE_BF16 &&
+      (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) % 16)
+    return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  pa::DecodePlan plan;
+  std::string msg;
+  pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                                       pool->geom.head_dim, 0, &plan, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  if (ws_bytes < plan.total_bytes)
+    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
+                                        " bytes, got " + std::to_string(ws_bytes));
+  hipStream_t st = as_stream(stream);
+  pa_status r = pool->flush(st);
+  if (r != PA_OK) return r;
+  r = pool->upload(plan.meta.data(), plan.meta.size() * sizeof(int32_t), ws, st);
+  if (r != PA_OK) return r;
+  char* w = static_cast<char*>(ws);
+  pa::DecodeArgs a{};
+  a.k_pool = pool->k;
+  a.v_pool = pool->v;
+  a.q = q;
+  a.out = out;
+  a.ctx_len = reinterpret_cast<const int32_t*>(w + plan.ctx_off);
+  a.tbl_off = reinterpret_cast<const int32_t*>(w + plan.tbl_off_off);
+  a.tables = reinterpret_cast<const int32_t*>(w + plan.tables_off);
+  a.work = reinterpret_cast<const int32_t*>(w + plan.work_off);
+  a.part_base = reinterpret_cast<const int32_t*>(w + plan.base_off);
+  a.part_m = reinterpret_cast<float*>(w + plan.part_m_off);
+  a.part_l = reinterpret_cast<float*>(w + plan.part_l_off);
+  a.part_acc = reinterpret_cast<float*>(w + plan.part_acc_off);
+  a.merge_seq = reinterpret_cast<const int32_t*>(w + plan.merge_off);
+  a.n_parts_of = reinterpret_cast<const int32_t*>(w + plan.nparts_off);
+  a.batch = B;
+  a.num_heads = num_heads;
+  a.num_kv_heads = pool->geom.num_kv_heads;
+  a.group = num_heads / pool->geom.num_kv_heads;
+  a.pages_per_part = plan.pages_per_part;
+  a.n_work = plan.n_work;
+  a.n_merge = plan.n_merge;
+  a.scale_log2 = scale_log2_for(pool->geom.head_dim);
+  {
+    TimedLaunch t(PA_KERNEL_DECODE, st);
+    hipError_t e = pa::launch_decode_partial(pool->geom, a, st);
+    t.done();
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  if (a.n_merge > 0 && pa::pick_decode_kernel(pool->geom, a.group) != pa::DecodeKernel::kGeneric) {
+    TimedLaunch t(PA_KERNEL_MERGE, st);
+    hipError_t e = pa::launch_decode_merge(pool->geom, a, st);
+    t.done();
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return ok();
+}
+
+size_t pa_prefill_workspace_bytes(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,
+                                  int32_t B, int32_t num_heads) {
+  if (!pool || num_heads <= 0 || num_heads % pool->geom.num_kv_heads) return 0;
+  pa::PrefillPlan plan;
+  std::string msg;
+  const int32_t group = num_heads / pool->geom.num_kv_heads;
+  if (pa::build_prefill_plan(pool->meta, seqs, q_lens, B, num_heads, pool->geom.num_kv_heads,
+                             pa::prefill_rows_per_tile(pool->geom, group), &plan, &msg) != pa::kOk)
+    return 0;
+  return plan.total_bytes;
+}
+
+pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_lens, int32_t B,
+                           int32_t num_heads, const void* q, void* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  if (!pool->has_device()) return fail(PA_ERR_INVALID_ARG, "metadata-only pool has no device memory");
+  if (!q || !out || !ws) return fail(PA_ERR_INVALID_ARG, "q, out and ws must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % pa::kWsAlign)
+    return fail(PA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  if (num_heads <= 0 || num_heads % pool->geom.num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_heads must be a positive multiple of num_kv_heads");
+  if (pool->geom.dtype == PA_DTYPE_BF16 &&
+      (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) % 16)
+    return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  const int32_t group = num_heads / pool->geom.num_kv_heads;
+  pa::PrefillPlan plan;
+  std::string msg;
+  pa::Status s = pa::build_prefill_plan(pool->meta, seqs, q_lens, B, num_heads, pool->geom.num_kv_heads,
+                                        pa::prefill_rows_per_tile(pool->geom, group), &plan, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  if (ws_bytes < plan.total_bytes)
+    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
+                                        " bytes, got " + std::to_string(ws_bytes));
+  hipStream_t st = as_stream(stream);
+  pa_status r = pool->flush(st);
+  if (r != PA_OK) return r;
+  r = pool->upload(plan.meta.data(), plan.meta.size() * sizeof(int32_t), ws, st);
+  if (r != PA_OK) return r;
+  char* w = static_cast<char*>(ws);
+  pa::PrefillArgs a{};
+  a.k_pool = pool->k;
+  a.v_pool = pool->v;
+  a.q = q;
+  a.out = out;
+  a.ctx_len = reinterpret_cast<const int32_t*>(w + plan.ctx_off);
+  a.tbl_off = reinterpret_cast<const int32_t*>(w + plan.tbl_off_off);
+  a.tables = reinterpret_cast<const int32_t*>(w + plan.tables_off);
+  a.q_start = reinterpret_cast<const int32_t*>(w + plan.qstart_off);
+  a.tiles = reinterpret_cast<const int32_t*>(w + plan.tiles_off);
+  a.row_seq = reinterpret_cast<const int32_t*>(w + plan.rowseq_off);
+  a.num_heads = num_heads;
+  a.num_kv_heads = pool->geom.num_kv_heads;
+  a.group = group;
+  a.n_tiles = plan.n_tiles;
+  a.n_rows = plan.n_rows;
+  a.scale_log2 = scale_log2_for(pool->geom.head_dim);
+  TimedLaunch t(PA_KERNEL_PREFILL, st);
+  hipError_t e = pa::launch_prefill(pool->geom, a, st);
+  t.done();
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+pa_status pa_seq_len(const pa_pool* pool, int64_t seq, int32_t* len) {
+  if (!pool || !len) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+  const pa::Sequence* s = pool->meta.find(seq);
+  if (!s) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence: " + std::to_string(seq));
+  *len = static_cast<int32_t>(s->length);
+  return ok();
+}
+
+pa_status pa_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap, int32_t* n) {
+  if (!pool || !n || cap < 0 || (cap > 0 && !out)) return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  const pa::Sequence* s = pool->meta.find(seq);
+  if (!s) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence: " + std::to_string(seq));
+  *n = static_cast<int32_t>(s->table.size());
+  for (int32_t i = 0; i < cap && i < *n; ++i) out[i] = s->table[i];
+  return ok();
+}
+
+pa_status pa_refcount(const pa_pool* pool, int32_t block, int32_t* rc) {
+  if (!pool || !rc || block < 0 || block >= pool->meta.num_blocks())
+    return fail(PA_ERR_INVALID_ARG, "bad block id or NULL argument");
+  *rc = pool->meta.refcount(block);
+  return ok();
+}
+
+pa_status pa_stats(const pa_pool* pool, pa_pool_stats* stats) {
+  if (!pool || !stats) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+  pa::PoolStats s = pool->meta.stats();
+  stats->allocated_blocks = s.allocated_blocks;
+  stats->free_blocks = s.free_blocks;
+  stats->physical_capacity_tokens = s.physical_capacity_tokens;
+  stats->physical_payload_tokens = s.physical_payload_tokens;
+  stats->logical_tokens = s.logical_tokens;
+  stats->internal_waste_tokens = s.internal_waste_tokens;
+  stats->sharing_savings_tokens = s.sharing_savings_tokens;
+  return ok();
+}
+
+pa_status pa_validate(const pa_pool* pool) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.validate(&msg), msg);
+}
+
+pa_status pa_sequences(const pa_pool* pool, int64_t* ids_out, int32_t cap, int32_t* n) {
+  if (!pool || !n || cap < 0 || (cap > 0 && !ids_out)) return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  std::vector<int64_t> ids = pool->meta.sequence_ids();
+  *n = static_cast<int32_t>(ids.size());
+  for (int32_t i = 0; i < cap && i < *n; ++i) ids_out[i] = ids[i];
+  return ok();
+}
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+pa_status pa_timing_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_tmu);
+  g_timing = on != 0;
+  return ok();
+}
+
+pa_status pa_timing_reset(void) {
+  std::lock_guard<std::mutex> lock(g_tmu);
+  drain_timing_locked();
+  for (int k = 0; k < PA_KERNEL_COUNT; ++k) {
+    g_total_ms[k] = 0.0;
+    g_launches[k] = 0;
+  }
+  return ok();
+}
+
+pa_status pa_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= PA_KERNEL_COUNT || !total_ms || !launches)
+    return fail(PA_ERR_INVALID_ARG, "bad kernel id or NULL argument");
+  std::lock_guard<std::mutex> lock(g_tmu);
+  drain_timing_locked();
+  *total_ms = g_total_ms[kernel];
+  *launches = g_launches[kernel];
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,409 @@
+// Paged decode attention for gfx950.
+//
+// What is computed (docs.rs ferrum-kv 0.4.0 src/attention.rs,
+// paged_attention with q_tokens = 1; abhik.ai "examples/pagedattention.py",
+// region paged_attention): for sequence b, query head h, KV head
+// g = h / G, scores s_j = q . K_j / sqrt(D) over every cached token j, softmax,
+// output sum_j p_j V_j, with K_j / V_j found through the block table.
+//
+// Kernels
+//   decode_gqa_mfma  bf16, D in {64, 128}, block_size in {16, 32}, G <= 16.
+//       One workgroup = (work item = (sequence, page range), KV head); its 4
+//       waves stride over the pages of the range.  The G query heads of the
+//       KV head form the N dimension of two MFMA contractions per page:
+//         S^T[16 tok x 16 heads]  = K_page[16 x D]   . Q^T[D x 16]  (16x16x32)
+//         O^T[16 d   x 16 heads] += V^T_page[16 x 16] . P^T[16 x 16] (16x16x16)
+//       The C layout of the first (lane holds 4 tokens of one head) is
+//       exactly the B layout of the second, so P never leaves registers, and
+//       the transposed V page makes every V operand an 8-byte contiguous load.
+//       Online softmax per page (running max / sum in registers, exp2 with
+//       log2(e) folded into the scale); the 4 waves merge in LDS; a range
+//       that is the whole sequence writes bf16 output, otherwise fp32
+//       partials (m, l, acc) for the merge kernel.
+//   decode_merge     log-sum-exp combination of the partials of one
+//       (sequence, head): M = max m_c, o = sum e^(m_c-M) acc_c / sum e^(m_c-M) l_c
+//       (CMU 11-667 lecture 19 section 3, online_softmax_stats, applied
+//       across page ranges).
+//   attn_generic     any dtype / head_dim <= 512 / block_size / group; one
+//       wave per (query row, head), 64 keys per step, online softmax.  Used
+//       for fp32 pools and shapes the MFMA kernel does not cover; it also
+//       serves prefill rows (bottom-right causal mask).
+#include <cmath>
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace pa {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// --------------------------------------------------------------- generic ---
+struct GenericArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const void* q;
+  void* out;
+  const int32_t* ctx_len;
+  const int32_t* tbl_off;
+  const int32_t* tables;
+  const int32_t* q_start;  // nullptr: decode, row r is sequence r with q_len 1
+  const int32_t* row_seq;
+  int32_t num_heads, num_kv_heads, group, head_dim, block_size;
+  float scale_log2;
+};
+
+template <typename T>
+__global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
+  extern __shared__ float smem[];
+  float* qs = smem;                                            // [D]
+  float* ps = smem + a.head_dim;                               // [64]
+  int* blks = reinterpret_cast<int*>(ps + 64);                 // [64]
+  int* offs = blks + 64;                                       // [64]
+  const int lane = threadIdx.x;
+  const int r = blockIdx.x / a.num_heads, h = blockIdx.x - r * a.num_heads;
+  int b, t, q_len;
+  if (a.q_start) {
+    b = a.row_seq[r];
+    t = r - a.q_start[b];
+    q_len = a.q_start[b + 1] - a.q_start[b];
+  } else {
+    b = r;
+    t = 0;
+    q_len = 1;
+  }
+  const int L = a.ctx_len[b];
+  const int visible = L - q_len + t + 1;  // keys 0 .. visible-1
+  const int g = h / a.group;
+  const int D = a.head_dim, BS = a.block_size, Hkv = a.num_kv_heads;
+  const int32_t* table = a.tables + a.tbl_off[b];
+  const T* K = static_cast<const T*>(a.k_pool);
+  const T* V = static_cast<const T*>(a.v_pool);
+  const T* q = static_cast<const T*>(a.q) + (static_cast<size_t>(r) * a.num_heads + h) * D;
+  for (int d = lane; d < D; d += 64) qs[d] = Elt<T>::load(q + d);
+  __syncthreads();
+  float m = -INFINITY, l = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  for (int c0 = 0; c0 < visible; c0 += 64) {
+    const int j = c0 + lane;
+    float s = -INFINITY;
+    int blk = 0, off = 0;
+    if (j < visible) {
+      blk = table[j / BS];
+      off = j - (j / BS) * BS;
+      const T* kr = K + ((static_cast<size_t>(blk) * Hkv + g) * BS + off) * D;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot += qs[d] * Elt<T>::load(kr + d);
+      s = dot * a.scale_log2;
+    }
+    const float m_new = fmaxf(m, wave_max(s));  // finite: key c0 is visible
+    const float alpha = exp2f(m - m_new);
+    const float p = j < visible ? exp2f(s - m_new) : 0.f;
+    l = l * alpha + wave_sum(p);
+    ps[lane] = p;
+    blks[lane] = blk;
+    offs[lane] = off;
+    __syncthreads();
+    const int nj = min(64, visible - c0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int d = lane + 64 * k;
+      float x = acc[k] * alpha;
+      if (d < D)
+        for (int jj = 0; jj < nj; ++jj)
+          x += ps[jj] * Elt<T>::load(V + ((static_cast<size_t>(blks[jj]) * Hkv + g) * D + d) * BS + offs[jj]);
+      acc[k] = x;
+    }
+    m = m_new;
+    __syncthreads();
+  }
+  T* o = static_cast<T*>(a.out) + (static_cast<size_t>(r) * a.num_heads + h) * D;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) Elt<T>::store(o + d, acc[k] * inv);
+  }
+}
+
+// ------------------------------------------------------------ GQA / MFMA ---
+template <int D, int BS>
+__global__ __launch_bounds__(256) void decode_gqa_mfma(DecodeArgs a) {
+  constexpr int KS = D / 32;  // k-steps of the 16x16x32 QK contraction
+  constexpr int TT = BS / 16; // 16-token tiles per page
+  constexpr int DT = D / 16;  // 16-wide d tiles of the P.V contraction
+  constexpr int W = kDecodeWaves;
+  __shared__ float s_m[W][16];
+  __shared__ float s_l[W][16];
+  __shared__ float s_acc[W][16][D + 4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n = lane & 15, grp = lane >> 4;
+  const int Hkv = a.num_kv_heads, Hq = a.num_heads, G = a.group;
+  const int wid = blockIdx.x / Hkv, g = blockIdx.x - wid * Hkv;
+  const int b = a.work[2 * wid], c = a.work[2 * wid + 1];
+  const int L = a.ctx_len[b];
+  const int nblk = (L + BS - 1) / BS;
+  const int p0 = c * a.pages_per_part;
+  const int p1 = min(nblk, p0 + a.pages_per_part);
+  const int32_t* table = a.tables + a.tbl_off[b];
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+  const size_t page = static_cast<size_t>(BS) * D;
+
+  // Q^T operand: lane (n, grp) holds q[head g*G+n][32j + 8grp .. +8].
+  bf16x8 qv[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<size_t>(b) * Hq + g * G + n) * D + 8 * grp;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      if (n < G)
+        qv[j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j);
+      else
+        qv[j] = bf16x8{};
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_page = [&](int pg, bf16x8 (&kr)[TT][KS], s16x4 (&vr)[DT][TT]) {
+    const int blk = uniform(table[pg]);
+    const uint16_t* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * page;
+    const uint16_t* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * page;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        kr[tt][j] = *reinterpret_cast<const bf16x8*>(kp + (16 * tt + n) * D + 32 * j + 8 * grp);
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        vr[nt][tt] = *reinterpret_cast<const s16x4*>(vp + (16 * nt + n) * BS + 16 * tt + 4 * grp);
+  };
+
+  auto process = [&](int pg, const bf16x8 (&kr)[TT][KS], const s16x4 (&vr)[DT][TT]) {
+    f32x4 s[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[tt][j], qv[j], s[tt], 0, 0, 0);
+    }
+    // s[tt][i] = score of token pg*BS + 16tt + 4grp + i for head n.
+    const bool tail = pg == nblk - 1;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[tt][i] * a.scale_log2;
+        if (tail && pg * BS + 16 * tt + 4 * grp + i >= L) x = -INFINITY;
+        s[tt][i] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    s16x4 pb[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 e = static_cast<__bf16>(exp2f(s[tt][i] - m_new));
+        psum += static_cast<float>(e);  // l from the same rounded weights as P.V
+        pb[tt][i] = __builtin_bit_cast(short, e);
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) {
+      acc[nt] *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt][tt], pb[tt], acc[nt], 0, 0, 0);
+    }
+  };
+
+  {
+    bf16x8 ka[TT][KS], kb[TT][KS];
+    s16x4 va[DT][TT], vb[DT][TT];
+    int p = p0 + wave;
+    if (p < p1) load_page(p, ka, va);
+    while (p < p1) {
+      if (p + W < p1) load_page(p + W, kb, vb);
+      process(p, ka, va);
+      p += W;
+      if (p >= p1) break;
+      if (p + W < p1) load_page(p + W, ka, va);
+      process(p, kb, vb);
+      p += W;
+    }
+  }
+
+  // Per-head totals over the 4 lane groups, then merge the 4 waves.
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (grp == 0) {
+    s_m[wave][n] = m_run;
+    s_l[wave][n] = l_tot;
+  }
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_acc[wave][n][16 * nt + 4 * grp + i] = acc[nt][i];
+  __syncthreads();
+
+  const int base = a.part_base[b];
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int hn = idx / D, d = idx - hn * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][hn]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float e = exp2f(s_m[w][hn] - M);  // a wave without pages has m = -inf
+      num += e * s_acc[w][hn][d];
+      den += e * s_l[w][hn];
+    }
+    const int h = g * G + hn;
+    if (base < 0) {
+      static_cast<uint16_t*>(a.out)[(static_cast<size_t>(b) * Hq + h) * D + d] = f32_to_bf16(num / den);
+    } else {
+      const size_t row = static_cast<size_t>(base + c) * Hq + h;
+      a.part_acc[row * D + d] = num;
+      if (d == 0) {
+        a.part_m[row] = M;
+        a.part_l[row] = den;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- merge ---
+template <int D, typename T>
+__global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  constexpr int V4 = D / 4;      // float4 lanes per partial row
+  constexpr int R = 256 / V4;    // partial rows in flight
+  __shared__ float s_red[4];
+  __shared__ f32x4 s_num[R][V4];
+  __shared__ float s_den[R];
+  const int tid = threadIdx.x;
+  const int Hq = a.num_heads;
+  const int mi = blockIdx.x / Hq, h = blockIdx.x - mi * Hq;
+  const int b = a.merge_seq[mi];
+  const int base = a.part_base[b], np = a.n_parts_of[b];
+
+  float M = -INFINITY;
+  for (int c = tid; c < np; c += 256) M = fmaxf(M, a.part_m[static_cast<size_t>(base + c) * Hq + h]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+  const int r = tid / V4, v = tid - r * V4;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int c = r; c < np; c += R) {
+    const size_t row = static_cast<size_t>(base + c) * Hq + h;
+    const float w = exp2f(a.part_m[row] - M);
+    num += w * reinterpret_cast<const f32x4*>(a.part_acc + row * D)[v];
+    den += w * a.part_l[row];
+  }
+  s_num[r][v] = num;
+  if (v == 0) s_den[r] = den;
+  __syncthreads();
+  if (tid < V4) {
+    f32x4 tot = s_num[0][tid];
+    float dtot = s_den[0];
+#pragma unroll
+    for (int k = 1; k < R; ++k) {
+      tot += s_num[k][tid];
+      dtot += s_den[k];
+    }
+    const float inv = 1.f / dtot;
+    T* o = static_cast<T*>(a.out) + (static_cast<size_t>(b) * Hq + h) * D + 4 * tid;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Elt<T>::store(o + i, tot[i] * inv);
+  }
+}
+
+template <int D, int BS>
+void launch_gqa(const DecodeArgs& a, int groups, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_gqa_mfma<D, BS>), dim3(groups), dim3(256), 0, stream, a);
+}
+
+}  // namespace
+
+DecodeKernel pick_decode_kernel(const PoolGeom& geom, int32_t group) {
+  const bool d_ok = geom.head_dim == 64 || geom.head_dim == 128;
+  const bool bs_ok = geom.block_size == 16 || geom.block_size == 32;
+  if (geom.dtype == 1 && d_ok && bs_ok && group <= 16) return DecodeKernel::kGqaMfma;
+  return DecodeKernel::kGeneric;
+}
+
+hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream) {
+  switch (pick_decode_kernel(geom, a.group)) {
+    case DecodeKernel::kGqaMfma: {
+      const int groups = a.n_work * a.num_kv_heads;
+      const int D = geom.head_dim, BS = geom.block_size;
+      if (D == 128 && BS == 16) launch_gqa<128, 16>(a, groups, stream);
+      else if (D == 128 && BS == 32) launch_gqa<128, 32>(a, groups, stream);
+      else if (D == 64 && BS == 16) launch_gqa<64, 16>(a, groups, stream);
+      else launch_gqa<64, 32>(a, groups, stream);
+      break;
+    }
+    default: {
+      GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, nullptr, nullptr,
+                    a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,
+                    a.scale_log2};
+      const size_t shmem = (geom.head_dim + 64) * sizeof(float) + 128 * sizeof(int);
+      const dim3 grid(a.batch * a.num_heads);
+      if (geom.dtype == 1)
+        hipLaunchKernelGGL(attn_generic<uint16_t>, grid, dim3(64), shmem, stream, g);
+      else
+        hipLaunchKernelGGL(attn_generic<float>, grid, dim3(64), shmem, stream, g);
+      break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream) {
+  if (a.n_merge == 0 || pick_decode_kernel(geom, a.group) == DecodeKernel::kGeneric)
+    return hipSuccess;
+  const dim3 grid(a.n_merge * a.num_heads);
+  if (geom.head_dim == 128)
+    hipLaunchKernelGGL((decode_merge<128, uint16_t>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_merge<64, uint16_t>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Prefill through the generic kernel (query rows with their causal limits).
+hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream) {
+  GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, a.q_start,
+                a.row_seq, a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,
+                a.scale_log2};
+  const size_t shmem = (geom.head_dim + 64) * sizeof(float) + 128 * sizeof(int);
+  const dim3 grid(a.n_rows * a.num_heads);
+  if (geom.dtype == 1)
+    hipLaunchKernelGGL(attn_generic<uint16_t>, grid, dim3(64), shmem, stream, g);
+  else
+    hipLaunchKernelGGL(attn_generic<float>, grid, dim3(64), shmem, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace pa

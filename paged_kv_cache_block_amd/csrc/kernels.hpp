@@ -1,0 +1,35 @@
+// Host launchers of the gfx950 kernels (defined in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "plan.hpp"
+
+namespace pa {
+
+constexpr int kMaxCopiesPerLaunch = 64;
+
+// Whole-block copies src[i] -> dst[i] (K and V, all heads), i < n <= 64, in
+// one launch.  The caller splits dependent copies into separate launches.
+hipError_t launch_copy_blocks(const PoolGeom& geom, void* k_pool, void* v_pool,
+                              const int32_t* src, const int32_t* dst, int n, hipStream_t stream);
+
+// Kpool[slot/bs][h][slot%bs][:] = k_new[i][h][:], Vpool[slot/bs][h][:][slot%bs] = v_new[i][h][:].
+hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_pool,
+                                    const void* k_new, const void* v_new, const int64_t* slots,
+                                    int32_t n, hipStream_t stream);
+
+// Which decode kernel serves a geometry (for timing labels and tests).
+enum class DecodeKernel { kGqaMfma, kMhaValu, kGeneric };
+DecodeKernel pick_decode_kernel(const PoolGeom& geom, int32_t group);
+
+// Decode: partial kernel, then (if any sequence was split) the merge.
+hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& args, hipStream_t stream);
+hipError_t launch_decode_merge(const PoolGeom& geom, const DecodeArgs& args, hipStream_t stream);
+
+// Prefill (chunked, causal).
+hipError_t launch_prefill(const PoolGeom& geom, const PrefillArgs& args, hipStream_t stream);
+bool prefill_uses_mfma(const PoolGeom& geom, int32_t group);
+int32_t prefill_rows_per_tile(const PoolGeom& geom, int32_t group);
+
+}  // namespace pa

@@ -1,0 +1,229 @@
+// Decode / prefill work plans.  See plan.hpp.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <numeric>
+
+namespace pa {
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Append `n` zero words to `meta`, 4-word aligned, and return the byte offset.
+size_t reserve(std::vector<int32_t>& meta, size_t n) {
+  size_t at = align_up(meta.size(), 4);
+  meta.resize(at + n, 0);
+  return at * sizeof(int32_t);
+}
+
+int32_t* at_bytes(std::vector<int32_t>& meta, size_t byte_off) {
+  return meta.data() + byte_off / sizeof(int32_t);
+}
+
+// Enough workgroups to keep every CU busy with several resident groups:
+// 256 CUs x 8 groups.
+constexpr int64_t kTargetGroups = 2048;
+
+}  // namespace
+
+Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t tokens_per_part,
+                         DecodePlan* plan, std::string* msg) {
+  if (B <= 0 || !seqs) {
+    *msg = "batch must be positive with a non-NULL seqs array";
+    return kInvalidArg;
+  }
+  if (num_heads <= 0 || num_heads % num_kv_heads) {
+    *msg = "num_heads must be a positive multiple of num_kv_heads";
+    return kInvalidArg;
+  }
+  const int32_t bs = pool.block_size();
+  std::vector<const Sequence*> rows(B);
+  int64_t total_pages = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    rows[b] = pool.find(seqs[b]);
+    if (!rows[b]) {
+      *msg = "unknown sequence: " + std::to_string(seqs[b]);
+      return kUnknownSeq;
+    }
+    if (rows[b]->length == 0) {
+      *msg = "kv_len must be positive (sequence " + std::to_string(seqs[b]) + " is empty)";
+      return kInvalidArg;
+    }
+    total_pages += static_cast<int64_t>(rows[b]->table.size());
+  }
+
+  // Pages per partition: the largest candidate that still yields enough
+  // workgroups; each partition is split over kDecodeWaves waves.
+  auto pages_for = [&](int64_t tokens) {
+    int64_t p = std::max<int64_t>(1, tokens / bs);
+    return static_cast<int32_t>(align_up(static_cast<size_t>(p), kDecodeWaves));
+  };
+  auto groups_for = [&](int32_t ppp) {
+    int64_t g = 0;
+    for (int32_t b = 0; b < B; ++b) g += ceil_div(static_cast<int64_t>(rows[b]->table.size()), ppp);
+    return g * num_kv_heads;
+  };
+  int32_t ppp;
+  if (tokens_per_part > 0) {
+    ppp = pages_for(tokens_per_part);
+  } else {
+    static const int64_t kCandidates[] = {4096, 2048, 1024, 512, 256, 128};
+    ppp = pages_for(128);
+    for (int64_t tok : kCandidates) {
+      int32_t p = pages_for(tok);
+      if (groups_for(p) >= kTargetGroups) {
+        ppp = p;
+        break;
+      }
+    }
+  }
+
+  std::vector<int32_t> n_parts_of(B);
+  struct Item { int32_t b, c, pages; };
+  std::vector<Item> items;
+  std::vector<int32_t> part_base(B, -1), merge;
+  int32_t n_parts = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t nblk = static_cast<int32_t>(rows[b]->table.size());
+    int32_t np = static_cast<int32_t>(ceil_div(nblk, ppp));
+    n_parts_of[b] = np;
+    for (int32_t c = 0; c < np; ++c) items.push_back({b, c, std::min(ppp, nblk - c * ppp)});
+    if (np > 1) {
+      part_base[b] = n_parts;
+      n_parts += np;
+      merge.push_back(b);
+    }
+  }
+  // Longest page ranges first so short tails fill in at the end.
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& x, const Item& y) { return x.pages > y.pages; });
+
+  DecodePlan p;
+  p.batch = B;
+  p.pages_per_part = ppp;
+  p.n_work = static_cast<int32_t>(items.size());
+  p.n_merge = static_cast<int32_t>(merge.size());
+  p.n_parts = n_parts;
+  p.total_pages = total_pages;
+  std::vector<int32_t>& meta = p.meta;
+  p.ctx_off = reserve(meta, B);
+  p.tbl_off_off = reserve(meta, B);
+  p.base_off = reserve(meta, B);
+  p.nparts_off = reserve(meta, B);
+  p.work_off = reserve(meta, 2 * items.size());
+  p.merge_off = reserve(meta, std::max<size_t>(1, merge.size()));
+  p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
+  int32_t* ctx = at_bytes(meta, p.ctx_off);
+  int32_t* toff = at_bytes(meta, p.tbl_off_off);
+  int32_t* base = at_bytes(meta, p.base_off);
+  int32_t* npo = at_bytes(meta, p.nparts_off);
+  int32_t* work = at_bytes(meta, p.work_off);
+  int32_t* mrg = at_bytes(meta, p.merge_off);
+  int32_t* tables = at_bytes(meta, p.tables_off);
+  int64_t cursor = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    ctx[b] = static_cast<int32_t>(rows[b]->length);
+    toff[b] = static_cast<int32_t>(cursor);
+    base[b] = part_base[b];
+    npo[b] = n_parts_of[b];
+    std::copy(rows[b]->table.begin(), rows[b]->table.end(), tables + cursor);
+    cursor += static_cast<int64_t>(rows[b]->table.size());
+  }
+  for (size_t i = 0; i < items.size(); ++i) {
+    work[2 * i] = items[i].b;
+    work[2 * i + 1] = items[i].c;
+  }
+  std::copy(merge.begin(), merge.end(), mrg);
+
+  p.meta_bytes = align_up(meta.size() * sizeof(int32_t), kWsAlign);
+  size_t rows_hq = static_cast<size_t>(n_parts) * num_heads;
+  p.part_m_off = p.meta_bytes;
+  p.part_l_off = p.part_m_off + align_up(rows_hq * sizeof(float), kWsAlign);
+  p.part_acc_off = p.part_l_off + align_up(rows_hq * sizeof(float), kWsAlign);
+  p.total_bytes = p.part_acc_off + align_up(rows_hq * head_dim * sizeof(float), kWsAlign);
+  *plan = std::move(p);
+  return kOk;
+}
+
+Status build_prefill_plan(const BlockPool& pool, const int64_t* seqs, const int32_t* q_lens,
+                          int32_t B, int32_t num_heads, int32_t num_kv_heads, int32_t rows_per_tile,
+                          PrefillPlan* plan, std::string* msg) {
+  if (B <= 0 || !seqs || !q_lens) {
+    *msg = "batch must be positive with non-NULL seqs and q_lens";
+    return kInvalidArg;
+  }
+  if (num_heads <= 0 || num_heads % num_kv_heads) {
+    *msg = "num_heads must be a positive multiple of num_kv_heads";
+    return kInvalidArg;
+  }
+  std::vector<const Sequence*> rows(B);
+  int64_t total_pages = 0, total_rows = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    rows[b] = pool.find(seqs[b]);
+    if (!rows[b]) {
+      *msg = "unknown sequence: " + std::to_string(seqs[b]);
+      return kUnknownSeq;
+    }
+    if (q_lens[b] < 1 || q_lens[b] > rows[b]->length) {
+      *msg = "q_lens[b] must be in 1..length(seq) (the rows are the last positions)";
+      return kInvalidArg;
+    }
+    total_pages += static_cast<int64_t>(rows[b]->table.size());
+    total_rows += q_lens[b];
+  }
+  if (total_rows > INT32_MAX / 2) {
+    *msg = "too many query rows";
+    return kInvalidArg;
+  }
+  struct Tile { int32_t b, t0; int64_t keys; };
+  std::vector<Tile> tiles;
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t t0 = 0; t0 < q_lens[b]; t0 += rows_per_tile) {
+      int32_t last = std::min(q_lens[b], t0 + rows_per_tile) - 1;
+      tiles.push_back({b, t0, rows[b]->length - q_lens[b] + last + 1});
+    }
+  // Tiles that see the most keys first.
+  std::stable_sort(tiles.begin(), tiles.end(),
+                   [](const Tile& x, const Tile& y) { return x.keys > y.keys; });
+
+  PrefillPlan p;
+  p.batch = B;
+  p.n_tiles = static_cast<int32_t>(tiles.size());
+  p.n_rows = static_cast<int32_t>(total_rows);
+  std::vector<int32_t>& meta = p.meta;
+  p.ctx_off = reserve(meta, B);
+  p.tbl_off_off = reserve(meta, B);
+  p.qstart_off = reserve(meta, B + 1);
+  p.tiles_off = reserve(meta, 2 * tiles.size());
+  p.rowseq_off = reserve(meta, static_cast<size_t>(total_rows));
+  p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
+  int32_t* ctx = at_bytes(meta, p.ctx_off);
+  int32_t* toff = at_bytes(meta, p.tbl_off_off);
+  int32_t* qs = at_bytes(meta, p.qstart_off);
+  int32_t* tl = at_bytes(meta, p.tiles_off);
+  int32_t* rs = at_bytes(meta, p.rowseq_off);
+  int32_t* tables = at_bytes(meta, p.tables_off);
+  int64_t cursor = 0, row = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    ctx[b] = static_cast<int32_t>(rows[b]->length);
+    toff[b] = static_cast<int32_t>(cursor);
+    qs[b] = static_cast<int32_t>(row);
+    for (int32_t t = 0; t < q_lens[b]; ++t) rs[row + t] = b;
+    row += q_lens[b];
+    std::copy(rows[b]->table.begin(), rows[b]->table.end(), tables + cursor);
+    cursor += static_cast<int64_t>(rows[b]->table.size());
+  }
+  qs[B] = static_cast<int32_t>(row);
+  for (size_t i = 0; i < tiles.size(); ++i) {
+    tl[2 * i] = tiles[i].b;
+    tl[2 * i + 1] = tiles[i].t0;
+  }
+  p.meta_bytes = align_up(meta.size() * sizeof(int32_t), kWsAlign);
+  p.total_bytes = p.meta_bytes;
+  *plan = std::move(p);
+  return kOk;
+}
+
+}  // namespace pa

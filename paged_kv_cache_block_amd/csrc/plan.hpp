@@ -1,0 +1,103 @@
+// Device work plans for decode and prefill: which (sequence, KV head, page
+// range) each workgroup handles, where the block tables and split-K partial
+// results live inside the caller's workspace, and the kernel argument blocks.
+//
+// Host-only (no HIP types) so it builds and is checked on a CPU machine.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pool.hpp"
+
+namespace pa {
+
+constexpr size_t kWsAlign = 256;
+constexpr int kDecodeWaves = 4;  // waves per decode workgroup
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Geometry of a pool (dtype: 0 = fp32, 1 = bf16).
+struct PoolGeom {
+  int32_t num_blocks, block_size, num_kv_heads, head_dim, dtype;  // dtype: 0 f32, 1 bf16
+  int32_t elt() const { return dtype == 1 ? 2 : 4; }
+  size_t page_elems() const { return static_cast<size_t>(block_size) * head_dim; }
+  size_t block_bytes() const {
+    return static_cast<size_t>(num_kv_heads) * page_elems() * elt();
+  }
+};
+
+
+// Kernel arguments of the decode partial kernels.  Every pointer is device
+// memory inside the workspace, except q / out / pools.
+struct DecodeArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const void* q;            // [B][Hq][D]
+  void* out;                // [B][Hq][D]
+  const int32_t* ctx_len;   // [B] tokens per sequence
+  const int32_t* tbl_off;   // [B] offset of the sequence's table in `tables`
+  const int32_t* tables;    // concatenated block tables
+  const int32_t* work;      // [n_work][2] = (b, partition index)
+  const int32_t* part_base; // [B] first partial row of b, or -1 = single partition
+  float* part_m;            // [n_parts][Hq]
+  float* part_l;            // [n_parts][Hq]
+  float* part_acc;          // [n_parts][Hq][D]
+  const int32_t* merge_seq; // [n_merge] sequences with more than one partition
+  const int32_t* n_parts_of;// [B] partitions of b
+  int32_t batch, num_heads, num_kv_heads, group;
+  int32_t pages_per_part;
+  int32_t n_work, n_merge;
+  float scale_log2;         // log2(e) / sqrt(head_dim)
+};
+
+struct DecodePlan {
+  std::vector<int32_t> meta;  // host image of the metadata region
+  size_t meta_bytes = 0;      // aligned
+  size_t part_m_off = 0, part_l_off = 0, part_acc_off = 0, total_bytes = 0;
+  size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, work_off = 0, base_off = 0,
+         merge_off = 0, nparts_off = 0;  // byte offsets in the workspace
+  int32_t n_work = 0, n_merge = 0, n_parts = 0, pages_per_part = 0, batch = 0;
+  int64_t total_pages = 0;
+};
+
+// Build the decode plan for `seqs`.  Validates the batch (known sequences,
+// non-empty contexts); returns kUnknownSeq / kInvalidArg with msg.
+// `tokens_per_part` = 0 chooses the partition size automatically.
+Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t tokens_per_part,
+                         DecodePlan* plan, std::string* msg);
+
+// Kernel arguments of the prefill kernels.
+struct PrefillArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const void* q;            // [R][Hq][D], R = sum q_lens
+  void* out;                // [R][Hq][D]
+  const int32_t* ctx_len;   // [B]
+  const int32_t* tbl_off;   // [B]
+  const int32_t* tables;
+  const int32_t* q_start;   // [B+1] first row of b
+  const int32_t* tiles;     // [n_tiles][2] = (b, first query row of the tile within b)
+  const int32_t* row_seq;   // [R] sequence of each row (generic kernel)
+  int32_t num_heads, num_kv_heads, group;
+  int32_t n_tiles, n_rows;
+  float scale_log2;
+};
+
+struct PrefillPlan {
+  std::vector<int32_t> meta;
+  size_t meta_bytes = 0, total_bytes = 0;
+  size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, qstart_off = 0, tiles_off = 0,
+         rowseq_off = 0;
+  int32_t n_tiles = 0, n_rows = 0, batch = 0;
+};
+
+// `rows_per_tile` query rows (of one sequence) per prefill workgroup.
+Status build_prefill_plan(const BlockPool& pool, const int64_t* seqs, const int32_t* q_lens,
+                          int32_t B, int32_t num_heads, int32_t num_kv_heads, int32_t rows_per_tile,
+                          PrefillPlan* plan, std::string* msg);
+
+}  // namespace pa

@@ -1,0 +1,304 @@
+// Host bookkeeping of the paged KV pool.  See pool.hpp for the sources.
+#include "pool.hpp"
+
+#include <algorithm>
+#include <string>
+
+namespace pa {
+
+namespace {
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+Status BlockPool::make(int32_t num_blocks, int32_t block_size, const int32_t* order,
+                       BlockPool* out, std::string* msg) {
+  if (num_blocks <= 0 || block_size <= 0) {
+    *msg = "num_blocks and block_size must be positive";
+    return kInvalidArg;
+  }
+  BlockPool p;
+  p.num_blocks_ = num_blocks;
+  p.block_size_ = block_size;
+  p.order_.resize(num_blocks);
+  p.rank_.assign(num_blocks, -1);
+  for (int32_t r = 0; r < num_blocks; ++r) {
+    int32_t b = order ? order[r] : r;
+    if (b < 0 || b >= num_blocks || p.rank_[b] != -1) {
+      *msg = "allocation_order must be a full permutation of 0..num_blocks-1";
+      return kInvalidArg;
+    }
+    p.order_[r] = b;
+    p.rank_[b] = r;
+  }
+  p.refs_.assign(num_blocks, 0);
+  std::vector<int32_t> ranks(num_blocks);
+  for (int32_t r = 0; r < num_blocks; ++r) ranks[r] = r;
+  p.free_heap_ = decltype(p.free_heap_)(std::greater<int32_t>(), std::move(ranks));
+  *out = std::move(p);
+  return kOk;
+}
+
+const Sequence* BlockPool::find(int64_t seq) const {
+  auto it = seqs_.find(seq);
+  return it == seqs_.end() ? nullptr : &it->second;
+}
+
+int32_t BlockPool::allocate() {
+  // Caller has preflighted; the heap is non-empty.
+  int32_t block = order_[free_heap_.top()];
+  free_heap_.pop();
+  refs_[block] = 1;
+  if (undo_) undo_->taken.push_back(block);
+  return block;
+}
+
+void BlockPool::drop_ref(int32_t block) {
+  if (--refs_[block] == 0) free_heap_.push(rank_[block]);
+}
+
+Status BlockPool::create(int64_t seq, std::string* msg) {
+  if (seqs_.count(seq)) {
+    *msg = "sequence already exists: " + std::to_string(seq);
+    return kSeqExists;
+  }
+  seqs_.emplace(seq, Sequence{});
+  ++version_;
+  return kOk;
+}
+
+int64_t BlockPool::blocks_needed(const Sequence& s, int64_t n) const {
+  if (n == 0) return 0;
+  int64_t need = 0, room = 0;
+  int64_t remainder = s.length % block_size_;
+  if (remainder) {
+    if (refs_[s.table.back()] > 1) need += 1;  // copy of the shared partial tail
+    room = block_size_ - remainder;
+  }
+  need += ceil_div(std::max<int64_t>(0, n - room), block_size_);
+  return need;
+}
+
+Status BlockPool::append(int64_t seq, int32_t n, int64_t* slots_out, std::string* msg) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end()) {
+    *msg = "unknown sequence: " + std::to_string(seq);
+    return kUnknownSeq;
+  }
+  if (n < 0 || (n > 0 && !slots_out)) {
+    *msg = "n_tokens must be >= 0 and slots_out non-NULL when n_tokens > 0";
+    return kInvalidArg;
+  }
+  Sequence& s = it->second;
+  int64_t need = blocks_needed(s, n);
+  if (need > free_count()) {
+    *msg = "need " + std::to_string(need) + " free blocks, " + std::to_string(free_count()) +
+           " remain";
+    return kOutOfBlocks;
+  }
+  if (n == 0) return kOk;
+  if (s.length % block_size_) {
+    int32_t old = s.table.back();
+    if (refs_[old] > 1) {
+      int32_t fresh = allocate();
+      pending_.emplace_back(old, fresh);
+      s.table.back() = fresh;
+      drop_ref(old);  // old stays referenced by another sequence
+      if (undo_) undo_->dropped.push_back(old);
+    }
+  }
+  int64_t first = s.length;
+  int64_t total = s.length + n;
+  while (static_cast<int64_t>(s.table.size()) < ceil_div(total, block_size_))
+    s.table.push_back(allocate());
+  s.length = total;
+  for (int64_t p = first; p < total; ++p)
+    slots_out[p - first] =
+        static_cast<int64_t>(s.table[p / block_size_]) * block_size_ + p % block_size_;
+  ++version_;
+  return kOk;
+}
+
+Status BlockPool::append_batch(const int64_t* seqs, const int32_t* n, int32_t count,
+                               int64_t* slots_out, std::string* msg) {
+  if (count < 0 || (count > 0 && (!seqs || !n))) {
+    *msg = "count must be >= 0 with non-NULL seqs and n_tokens";
+    return kInvalidArg;
+  }
+  // Undo log: the first-seen state of every touched sequence, the blocks the
+  // batch took from the free heap, the shared tails whose refcount a
+  // copy-on-write dropped, and the pending-copy list length.  Blocks taken
+  // by the batch are private tails or new blocks, so none of them is freed
+  // again inside the batch; restoring the heap's rank set restores the
+  // allocation order exactly.
+  std::unordered_map<int64_t, Sequence> saved;
+  UndoLog log;
+  const size_t pending_before = pending_.size();
+  const uint64_t version_before = version_;
+  undo_ = &log;
+  int64_t offset = 0;
+  Status s = kOk;
+  int32_t i = 0;
+  for (; i < count; ++i) {
+    if (n[i] > 0 && !slots_out) {
+      *msg = "slots_out must be non-NULL when tokens are appended";
+      s = kInvalidArg;
+      break;
+    }
+    auto it = seqs_.find(seqs[i]);
+    if (it != seqs_.end() && !saved.count(seqs[i])) saved.emplace(seqs[i], it->second);
+    s = append(seqs[i], n[i], slots_out ? slots_out + offset : nullptr, msg);
+    if (s != kOk) break;
+    offset += n[i];
+  }
+  undo_ = nullptr;
+  if (s == kOk) return kOk;
+  for (auto& kv : saved) seqs_[kv.first] = std::move(kv.second);
+  for (int32_t b : log.taken) {
+    refs_[b] = 0;
+    free_heap_.push(rank_[b]);
+  }
+  for (int32_t b : log.dropped) ++refs_[b];
+  pending_.resize(pending_before);
+  version_ = version_before;
+  *msg = "append_batch entry " + std::to_string(i) + ": " + *msg;
+  return s;
+}
+
+Status BlockPool::share(int64_t src, int64_t dst, int32_t prefix, std::string* msg) {
+  auto it = seqs_.find(src);
+  if (it == seqs_.end()) {
+    *msg = "unknown sequence: " + std::to_string(src);
+    return kUnknownSeq;
+  }
+  if (prefix < 0 || prefix > it->second.length) {
+    *msg = "prefix_tokens must be in 0..length(src)";
+    return kInvalidArg;
+  }
+  if (seqs_.count(dst)) {
+    *msg = "sequence already exists: " + std::to_string(dst);
+    return kSeqExists;
+  }
+  Sequence child;
+  child.length = prefix;
+  child.table.assign(it->second.table.begin(),
+                     it->second.table.begin() + ceil_div(prefix, block_size_));
+  for (int32_t b : child.table) ++refs_[b];
+  seqs_.emplace(dst, std::move(child));
+  ++version_;
+  return kOk;
+}
+
+Status BlockPool::fork(int64_t src, int64_t dst, std::string* msg) {
+  const Sequence* s = find(src);
+  if (!s) {
+    *msg = "unknown sequence: " + std::to_string(src);
+    return kUnknownSeq;
+  }
+  return share(src, dst, static_cast<int32_t>(s->length), msg);
+}
+
+Status BlockPool::release(int64_t seq, std::string* msg) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end()) {
+    *msg = "unknown or released sequence: " + std::to_string(seq);
+    return kUnknownSeq;
+  }
+  for (int32_t b : it->second.table) drop_ref(b);
+  seqs_.erase(it);
+  ++version_;
+  return kOk;
+}
+
+std::vector<std::pair<int32_t, int32_t>> BlockPool::take_pending_copies() {
+  std::vector<std::pair<int32_t, int32_t>> out;
+  out.swap(pending_);
+  return out;
+}
+
+std::vector<int32_t> BlockPool::fills() const {
+  std::vector<int32_t> fill(num_blocks_, 0);
+  for (const auto& kv : seqs_) {
+    const Sequence& s = kv.second;
+    for (size_t j = 0; j < s.table.size(); ++j) {
+      int64_t used = std::min<int64_t>(block_size_, s.length - static_cast<int64_t>(j) * block_size_);
+      fill[s.table[j]] = std::max<int32_t>(fill[s.table[j]], static_cast<int32_t>(used));
+    }
+  }
+  return fill;
+}
+
+PoolStats BlockPool::stats() const {
+  PoolStats st{};
+  st.free_blocks = free_count();
+  st.allocated_blocks = num_blocks_ - st.free_blocks;
+  st.physical_capacity_tokens = st.allocated_blocks * block_size_;
+  std::vector<int32_t> fill = fills();
+  int64_t payload = 0;
+  for (int32_t b = 0; b < num_blocks_; ++b)
+    if (refs_[b]) payload += fill[b];
+  int64_t logical = 0;
+  for (const auto& kv : seqs_) logical += kv.second.length;
+  st.physical_payload_tokens = payload;
+  st.logical_tokens = logical;
+  st.internal_waste_tokens = st.physical_capacity_tokens - payload;
+  st.sharing_savings_tokens = logical - payload;
+  return st;
+}
+
+Status BlockPool::validate(std::string* msg) const {
+  std::vector<int32_t> expected(num_blocks_, 0);
+  for (const auto& kv : seqs_) {
+    const Sequence& s = kv.second;
+    if (s.length < 0) { *msg = "negative sequence length"; return kInvalidArg; }
+    if (static_cast<int64_t>(s.table.size()) != ceil_div(s.length, block_size_)) {
+      *msg = "page-table length does not match sequence length";
+      return kInvalidArg;
+    }
+    std::vector<int32_t> sorted = s.table;
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) {
+      *msg = "one sequence references a physical block twice";
+      return kInvalidArg;
+    }
+    for (int32_t b : s.table) {
+      if (b < 0 || b >= num_blocks_) { *msg = "page table contains an invalid block id"; return kInvalidArg; }
+      ++expected[b];
+    }
+  }
+  // Free set = blocks whose rank sits in the heap.
+  std::vector<char> is_free(num_blocks_, 0);
+  auto heap = free_heap_;
+  while (!heap.empty()) {
+    int32_t r = heap.top();
+    heap.pop();
+    if (r < 0 || r >= num_blocks_) { *msg = "free list contains an invalid block id"; return kInvalidArg; }
+    if (is_free[order_[r]]) { *msg = "free list contains duplicates"; return kInvalidArg; }
+    is_free[order_[r]] = 1;
+  }
+  std::vector<int32_t> fill = fills();
+  for (int32_t b = 0; b < num_blocks_; ++b) {
+    if (refs_[b] != expected[b]) { *msg = "physical ref_count does not match page tables"; return kInvalidArg; }
+    if (refs_[b] == 0) {
+      if (!is_free[b] || fill[b] != 0) { *msg = "unreferenced block is not clean and free"; return kInvalidArg; }
+    } else {
+      if (is_free[b]) { *msg = "referenced block appears in free list"; return kInvalidArg; }
+      if (fill[b] < 1 || fill[b] > block_size_) { *msg = "referenced block has invalid fill"; return kInvalidArg; }
+    }
+  }
+  PoolStats st = stats();
+  if (st.logical_tokens < st.physical_payload_tokens) {
+    *msg = "physical payload exceeds logical payload";
+    return kInvalidArg;
+  }
+  return kOk;
+}
+
+std::vector<int64_t> BlockPool::sequence_ids() const {
+  std::vector<int64_t> ids;
+  ids.reserve(seqs_.size());
+  for (const auto& kv : seqs_) ids.push_back(kv.first);
+  std::sort(ids.begin(), ids.end());
+  return ids;
+}
+
+}  // namespace pa

@@ -1,0 +1,101 @@
+// Host-side bookkeeping of the paged KV pool: allocation order, refcounts,
+// per-sequence block tables and lengths, preflighted append with
+// copy-on-write, share / fork / release, accounting and invariants.
+//
+// Semantics follow abhik.ai "examples/pagedattention.py" (class KVPool:
+// first free block in the authored allocation order, whole-block copy of a
+// shared partial tail, fork, release) and the "Модуль 10" notebook's
+// PagedKVPool (multi-token append preflight, share_prefix, fill / payload /
+// waste / savings accounting, validate).  This translation unit has no HIP
+// dependency so that it builds and is exercised on a CPU-only machine.
+#pragma once
+
+#include <cstdint>
+#include <functional>
+#include <queue>
+#include <string>
+#include <unordered_map>
+#include <utility>
+#include <vector>
+
+namespace pa {
+
+enum Status : int {
+  kOk = 0,
+  kInvalidArg = -1,
+  kUnknownSeq = -2,
+  kSeqExists = -3,
+  kOutOfBlocks = -4,
+  kDevice = -5,
+};
+
+struct Sequence {
+  int64_t length = 0;
+  std::vector<int32_t> table;
+};
+
+struct PoolStats {
+  int64_t allocated_blocks, free_blocks, physical_capacity_tokens, physical_payload_tokens,
+      logical_tokens, internal_waste_tokens, sharing_savings_tokens;
+};
+
+class BlockPool {
+ public:
+  // `order` empty = identity.  Returns kInvalidArg (with msg) on bad input.
+  static Status make(int32_t num_blocks, int32_t block_size, const int32_t* order,
+                     BlockPool* out, std::string* msg);
+
+  Status create(int64_t seq, std::string* msg);
+  Status append(int64_t seq, int32_t n, int64_t* slots_out, std::string* msg);
+  // append(seqs[i], n[i]) for i = 0..count-1 in order, slots concatenated in
+  // slots_out.  All or nothing: on any failure every earlier append of the
+  // batch is undone and the pool is exactly as before the call.
+  Status append_batch(const int64_t* seqs, const int32_t* n, int32_t count, int64_t* slots_out,
+                      std::string* msg);
+  Status share(int64_t src, int64_t dst, int32_t prefix, std::string* msg);
+  Status fork(int64_t src, int64_t dst, std::string* msg);
+  Status release(int64_t seq, std::string* msg);
+
+  const Sequence* find(int64_t seq) const;
+  int32_t refcount(int32_t block) const { return refs_[block]; }
+  int32_t num_blocks() const { return num_blocks_; }
+  int32_t block_size() const { return block_size_; }
+  int64_t free_count() const { return static_cast<int64_t>(free_heap_.size()); }
+  PoolStats stats() const;
+  Status validate(std::string* msg) const;
+  std::vector<int64_t> sequence_ids() const;
+
+  // Blocks needed to append n tokens to `s` (the preflight count).
+  int64_t blocks_needed(const Sequence& s, int64_t n) const;
+
+  // Copy-on-write copies recorded since the last take_pending_copies().
+  const std::vector<std::pair<int32_t, int32_t>>& pending_copies() const { return pending_; }
+  std::vector<std::pair<int32_t, int32_t>> take_pending_copies();
+
+  // Incremented by every mutation; lets callers cache derived device state.
+  uint64_t version() const { return version_; }
+
+ private:
+  struct UndoLog {
+    std::vector<int32_t> taken;    // blocks allocated
+    std::vector<int32_t> dropped;  // shared tails whose refcount a COW decremented
+  };
+
+  int32_t allocate();
+  void drop_ref(int32_t block);
+  std::vector<int32_t> fills() const;
+
+  int32_t num_blocks_ = 0;
+  int32_t block_size_ = 0;
+  std::vector<int32_t> order_;  // rank -> block
+  std::vector<int32_t> rank_;   // block -> rank
+  std::vector<int32_t> refs_;
+  // Free blocks by rank: the top is the first free block of the order.
+  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_heap_;
+  std::unordered_map<int64_t, Sequence> seqs_;
+  std::vector<std::pair<int32_t, int32_t>> pending_;
+  uint64_t version_ = 0;
+  UndoLog* undo_ = nullptr;  // set while append_batch runs
+};
+
+}  // namespace pa

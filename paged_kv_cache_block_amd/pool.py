@@ -1,0 +1,154 @@
+"""DevicePool: a paged KV pool whose K/V memory is a pair of torch tensors.
+
+Convenience layer over :mod:`paged_kv_cache_block_amd.abi`: torch allocates
+the pools, the decode / prefill workspaces and the device copy of the slot
+mapping; everything else (bookkeeping, cache writes, attention) is a call
+into libpagedattn.so on the current torch stream.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import abi
+
+_DTYPES = {"f32": abi.PA_DTYPE_F32, "bf16": abi.PA_DTYPE_BF16}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class DevicePool:
+    """One pool of ``num_blocks`` blocks; K and V live on ``device``.
+
+    With ``metadata_only=True`` no device memory is allocated and only the
+    bookkeeping calls work (usable on a machine without a GPU).
+    """
+
+    def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, dtype="bf16",
+                 allocation_order=None, device="cuda", metadata_only=False):
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.dtype = dtype
+        self.desc = abi.make_desc(num_blocks, block_size, num_kv_heads, head_dim, _DTYPES[dtype])
+        self.k = self.v = None
+        self._ws = None
+        self.handle = None
+        if not metadata_only:
+            torch = _torch()
+            tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+            shape_k = (num_blocks, num_kv_heads, block_size, head_dim)
+            shape_v = (num_blocks, num_kv_heads, head_dim, block_size)
+            self.k = torch.zeros(shape_k, dtype=tdt, device=device)
+            self.v = torch.zeros(shape_v, dtype=tdt, device=device)
+            assert self.k.numel() * self.k.element_size() == abi.pa_pool_bytes(self.desc)
+        self.handle = abi.pa_pool_create(self.desc, allocation_order, self.k, self.v)
+
+    # ------------------------------------------------------------ lifetime
+    def close(self):
+        if self.handle is not None:
+            abi.pa_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ metadata
+    def create(self, seq):
+        abi.pa_seq_create(self.handle, seq)
+
+    def append(self, seq, n_tokens):
+        return abi.pa_append(self.handle, seq, n_tokens)
+
+    def append_batch(self, seqs, n_tokens, slots_out=None):
+        return abi.pa_append_batch(self.handle, seqs, n_tokens, slots_out)
+
+    def share(self, src, dst, prefix_tokens):
+        abi.pa_share(self.handle, src, dst, prefix_tokens)
+
+    def fork(self, src, dst):
+        abi.pa_fork(self.handle, src, dst)
+
+    def release(self, seq):
+        abi.pa_release(self.handle, seq)
+
+    def pending_copies(self):
+        return abi.pa_pending_copies(self.handle)
+
+    def seq_len(self, seq):
+        return abi.pa_seq_len(self.handle, seq)
+
+    def block_table(self, seq):
+        return abi.pa_block_table(self.handle, seq)
+
+    def refcount(self, block):
+        return abi.pa_refcount(self.handle, block)
+
+    def stats(self):
+        return abi.pa_stats(self.handle)
+
+    def validate(self):
+        abi.pa_validate(self.handle)
+
+    def sequences(self):
+        return abi.pa_sequences(self.handle)
+
+    # ------------------------------------------------------------ device work
+    @staticmethod
+    def _stream(stream):
+        if stream is not None:
+            return stream
+        return _torch().cuda.current_stream().cuda_stream
+
+    def flush(self, stream=None):
+        abi.pa_flush_copies(self.handle, self._stream(stream))
+
+    def write(self, slots, k_new, v_new, stream=None):
+        """Store rows ``k_new[i], v_new[i]`` ([n, Hkv, D] device tensors) at ``slots``."""
+        torch = _torch()
+        if not torch.is_tensor(slots) or slots.device.type != "cuda":
+            slots = torch.as_tensor(np.asarray(slots, dtype=np.int64)).to(self.k.device, non_blocking=False)
+        n = int(slots.numel())
+        assert k_new.shape == (n, self.num_kv_heads, self.head_dim) and k_new.dtype == self.k.dtype
+        assert v_new.shape == k_new.shape and v_new.dtype == k_new.dtype
+        assert k_new.is_contiguous() and v_new.is_contiguous() and slots.dtype == torch.int64
+        abi.pa_reshape_and_cache(self.handle, k_new, v_new, slots, n, self._stream(stream))
+        return slots
+
+    def workspace(self, nbytes):
+        torch = _torch()
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.k.device)
+            assert self._ws.data_ptr() % 256 == 0
+        return self._ws
+
+    def decode(self, seqs, q, out=None, stream=None, ws=None):
+        """One query row per sequence: ``q`` [B, Hq, D] -> ``out`` [B, Hq, D]."""
+        num_heads = q.shape[1]
+        if out is None:
+            out = _torch().empty_like(q)
+        need = abi.pa_decode_workspace_bytes(self.handle, seqs, num_heads)
+        if need == 0:
+            # Invalid batch: let the call itself report why.
+            need = 256
+        if ws is None:
+            ws = self.workspace(need)
+        abi.pa_decode(self.handle, seqs, num_heads, q, out, ws, ws.numel(), self._stream(stream))
+        return out
+
+    def prefill(self, seqs, q_lens, q, out=None, stream=None, ws=None):
+        """Last ``q_lens[b]`` positions of each sequence: ``q`` [sum q_lens, Hq, D]."""
+        num_heads = q.shape[1]
+        if out is None:
+            out = _torch().empty_like(q)
+        need = abi.pa_prefill_workspace_bytes(self.handle, seqs, q_lens, num_heads) or 256
+        if ws is None:
+            ws = self.workspace(need)
+        abi.pa_prefill_chunk(self.handle, seqs, q_lens, num_heads, q, out, ws, ws.numel(),
+                             self._stream(stream))
+        return out

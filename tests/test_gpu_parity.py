@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bar: block tables, slots and refcounts bit-exact; attention outputs within
+|gpu - oracle| <= atol + rtol |oracle| elementwise, (2e-3, 1e-2) for bf16
+K/V with fp32 accumulation and bf16 output, (1e-5, 1e-5) for fp32.
+Small instances of every workload are compared element by element; the
+full-size workloads are compared on every output they have (decode at
+32 x 8192) or on sampled sequences / query rows the oracle computes one by
+one (131072-token and heavy-tailed decode, 4096-prefix prefill).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import (append_stream, decode_queries, gqa_decode, heavy_tail, logical_kv,
+                   long_decode, prefill_queries, prefix_prefill, tiny_fp32)
+from synth.workloads import Workload, to_f64
+
+from gpu_support import (BF16_TOL, F32_TOL, assert_close, build_device_pool, expected_decode, log,
+                         to_device, to_host_f64, tol)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_block_amd import abi
+    abi.load()   # fail loudly if the library is missing
+
+
+def _gather_pool_rows(pool, seq, length):
+    """Live K/V rows of ``seq`` read back from the device pools through the
+    documented layout (K [N][Hkv][bs][D], V [N][Hkv][D][bs])."""
+    table = pool.block_table(seq)
+    k = pool.k.float().cpu().numpy()
+    v = pool.v.float().cpu().numpy()
+    bs = pool.block_size
+    K = np.stack([k[table[p // bs], :, p % bs, :] for p in range(length)])
+    V = np.stack([v[table[p // bs], :, :, p % bs] for p in range(length)])
+    return K, V
+
+
+def _decode(pool, wl, seqs):
+    q_bits = decode_queries(wl, seqs)
+    q = to_device(q_bits, wl.dtype)
+    out = pool.decode(seqs, q)
+    torch.cuda.synchronize()
+    return q_bits, to_host_f64(out)
+
+
+# ------------------------------------------------------------ workload 1
+def test_tiny_fp32_workload():
+    wl = tiny_fp32()
+    log("tiny_fp32: build")
+    pool, ref = build_device_pool(wl, check_against_oracle_pool=True)
+    assert pool.block_table(0).tolist() == [2, 4] and pool.block_table(1).tolist() == [2, 3, 6]
+    assert [pool.refcount(b) for b in range(8)] == ref.refs.tolist()
+    assert pool.stats() == ref.stats()
+    # The copy-on-write copy ran on the device before B's rows were written.
+    rows = logical_kv(wl, [0, 1])
+    for s, n in ((0, 6), (1, 9)):
+        K, V = _gather_pool_rows(pool, s, n)
+        np.testing.assert_array_equal(K, rows[s][0])
+        np.testing.assert_array_equal(V, rows[s][1])
+    log("tiny_fp32: decode")
+    q_bits, got = _decode(pool, wl, [0, 1])
+    want = expected_decode(wl, [0, 1], q_bits)
+    for i in range(2):
+        assert_close(got[i], want[i], *F32_TOL, what=f"decode seq {i}")
+    log("tiny_fp32: prefill")
+    qp = prefill_queries(wl)
+    out = to_host_f64(pool.prefill([1], [3], to_device(qp, wl.dtype)))
+    K, V = (to_f64(x, wl.dtype) for x in rows[1])
+    exp = oracle.attention(to_f64(qp, wl.dtype), K, V)
+    assert_close(out, exp, *F32_TOL, what="prefill")
+    np.testing.assert_allclose(exp, oracle.brute_force_attention(to_f64(qp, wl.dtype), K, V), atol=1e-13)
+
+
+# ------------------------------------------------------------ closed forms
+def _f32_pool(keys, values, block_size, num_blocks, order=None):
+    from paged_kv_cache_block_amd import DevicePool
+    keys = np.asarray(keys, np.float32)
+    n, hkv, d = keys.shape
+    pool = DevicePool(num_blocks, block_size, hkv, d, dtype="f32", allocation_order=order)
+    pool.create(0)
+    slots = pool.append(0, n)
+    pool.write(slots, torch.tensor(keys).cuda(), torch.tensor(np.asarray(values, np.float32)).cuda())
+    return pool
+
+
+def test_ferrum_closed_forms_on_gpu():
+    import math
+    heads, dim = 2, 4
+    pool = _f32_pool(np.ones((3, heads, dim)),
+                     np.stack([np.full((heads, dim), p + 1.0) for p in range(3)]), 16, 4)
+    out = pool.decode([0], torch.ones(1, heads, dim).cuda()).cpu().numpy()
+    np.testing.assert_allclose(out, 2.0, atol=1e-5)
+    rows = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])[:, None, :]
+    pool = _f32_pool(rows, rows, 16, 2)
+    out = pool.prefill([0], [3], torch.tensor(rows, dtype=torch.float32).cuda()).cpu().numpy()[:, 0]
+    w1 = 1.0 / (1.0 + math.exp(-1.0 / math.sqrt(2.0)))
+    e = math.exp(1.0 / math.sqrt(2.0))
+    np.testing.assert_allclose(out, [[1, 0], [1 - w1, w1], [(1 + e) / (2 + e)] * 2], atol=1e-5)
+    keys = np.stack([np.full((1, 2), p + 1.0) for p in range(4)])
+    pool = _f32_pool(keys, 10 * keys, 2, 4, order=[3, 1, 0, 2])
+    out = pool.decode([0], torch.ones(1, 1, 2).cuda()).cpu().numpy()[0, 0]
+    w = np.exp(np.sqrt(2.0) * np.arange(1, 5))
+    np.testing.assert_allclose(out, [10 * (np.arange(1, 5) * w).sum() / w.sum()] * 2, rtol=1e-5)
+
+
+# ------------------------------------------------------------ decode shapes
+def _decode_case(lengths, hq, hkv, d, bs, dtype="bf16", seed=5, num_blocks=None, outliers=False):
+    nb = num_blocks or int(sum(-(-n // bs) for n in lengths) + 7)
+    order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    ops = []
+    for i, n in enumerate(lengths):
+        ops += [("create", i), ("append", i, int(n))]
+    return Workload("case", seed, dtype, nb, bs, hq, hkv, d, order, ops,
+                    decode_seqs=list(range(len(lengths))), outliers=outliers)
+
+
+DECODE_CASES = [
+    # lengths, Hq, Hkv, D, bs
+    ([1, 2, 15, 16, 17, 33, 200, 700], 32, 8, 128, 16),      # GQA 4, ragged tails
+    ([1, 64, 129, 1000, 4100], 64, 8, 128, 16),              # GQA 8, split-K
+    ([5, 31, 32, 33, 517, 2049], 16, 16, 64, 32),             # MHA, D 64, bs 32
+    ([3, 100, 1500], 16, 1, 128, 16),                         # GQA 16
+    ([7, 77, 777], 8, 4, 64, 16),                             # GQA 2, D 64
+    ([9, 300, 3000], 16, 2, 128, 32),                         # GQA 8, bs 32
+    ([2, 90, 1200], 6, 2, 32, 8),                             # generic kernel (D 32, bs 8)
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"L{max(c[0])}-G{c[1]//c[2]}-D{c[3]}-bs{c[4]}")
+def test_decode_shapes(case):
+    lengths, hq, hkv, d, bs = case
+    wl = _decode_case(lengths, hq, hkv, d, bs)
+    log(f"decode case {case}: build")
+    pool, ref = build_device_pool(wl, check_against_oracle_pool=True)
+    seqs = list(range(len(lengths)))
+    q_bits, got = _decode(pool, wl, seqs)
+    want = expected_decode(wl, seqs, q_bits)
+    for i in seqs:
+        assert_close(got[i], want[i], *BF16_TOL, what=f"seq {i} (L={lengths[i]})")
+
+
+def test_decode_fp32_generic():
+    wl = _decode_case([1, 5, 40, 333], 4, 2, 16, 4, dtype="f32")
+    pool, _ = build_device_pool(wl)
+    q_bits, got = _decode(pool, wl, [0, 1, 2, 3])
+    want = expected_decode(wl, [0, 1, 2, 3], q_bits)
+    for i in range(4):
+        assert_close(got[i], want[i], *F32_TOL, what=f"seq {i}")
+
+
+def test_decode_batch_with_duplicates_and_shared_prefix():
+    wl = prefix_prefill(batch=3, prefix=50, chunk=9, num_blocks=64, num_heads=32, num_kv_heads=8,
+                        head_dim=128, block_size=16)
+    pool, ref = build_device_pool(wl, check_against_oracle_pool=True)
+    seqs = [2, 0, 2, 1]
+    q_bits, got = _decode(pool, wl, seqs)
+    want = expected_decode(wl, seqs, q_bits)
+    for i in range(4):
+        assert_close(got[i], want[i], *BF16_TOL, what=f"row {i}")
+    assert (got[0] == got[2]).all()
+
+
+def test_copy_on_write_on_device():
+    from paged_kv_cache_block_amd import DevicePool
+    rng = np.random.default_rng(3)
+    pool = DevicePool(16, 16, 2, 64, dtype="bf16", allocation_order=rng.permutation(16))
+    k = torch.randn(21, 2, 64, dtype=torch.bfloat16, device="cuda")
+    v = torch.randn(21, 2, 64, dtype=torch.bfloat16, device="cuda")
+    pool.create(0)
+    pool.write(pool.append(0, 21), k, v)
+    pool.fork(0, 1)
+    pool.fork(0, 2)
+    s1 = pool.append(1, 1)             # COW of the shared partial tail
+    s2 = pool.append(2, 2)             # another COW of the same source block
+    assert len(pool.pending_copies()) == 2
+    k1 = torch.randn(1, 2, 64, dtype=torch.bfloat16, device="cuda")
+    k2 = torch.randn(2, 2, 64, dtype=torch.bfloat16, device="cuda")
+    pool.write(s1, k1, k1)
+    pool.write(s2, k2, k2)
+    torch.cuda.synchronize()
+    assert pool.pending_copies() == []
+    K0, V0 = _gather_pool_rows(pool, 0, 21)
+    K1, V1 = _gather_pool_rows(pool, 1, 22)
+    K2, V2 = _gather_pool_rows(pool, 2, 23)
+    np.testing.assert_array_equal(K1[:21], K0)
+    np.testing.assert_array_equal(V2[:21], V0)
+    np.testing.assert_array_equal(K1[21], k1[0].float().cpu().numpy())
+    np.testing.assert_array_equal(K2[21:], k2.float().cpu().numpy())
+    np.testing.assert_array_equal(K0, k.float().cpu().numpy())
+
+
+# ------------------------------------------------------------ prefill
+def test_prefix_prefill_small_full_compare():
+    wl = prefix_prefill(batch=4, prefix=300, chunk=70, num_blocks=128, num_heads=32, num_kv_heads=8,
+                        head_dim=128, block_size=16)
+    log("prefill small: build")
+    pool, ref = build_device_pool(wl, check_against_oracle_pool=True)
+    assert pool.refcount(pool.block_table(0)[0]) == 4
+    qp = prefill_queries(wl)
+    seqs = [s for s, _ in wl.prefill]
+    q_lens = [n for _, n in wl.prefill]
+    out = to_host_f64(pool.prefill(seqs, q_lens, to_device(qp, wl.dtype)))
+    rows = logical_kv(wl, seqs)
+    r0 = 0
+    for s, n in wl.prefill:
+        K, V = (to_f64(x, wl.dtype) for x in rows[s])
+        exp = oracle.attention(to_f64(qp[r0:r0 + n], wl.dtype), K, V)
+        assert_close(out[r0:r0 + n], exp, *BF16_TOL, what=f"seq {s}")
+        r0 += n
+
+
+# ------------------------------------------------------------ full size
+def test_gqa_decode_full_size():
+    wl = gqa_decode()
+    log("gqa_decode full: build")
+    pool, _ = build_device_pool(wl)
+    st = pool.stats()
+    assert st["allocated_blocks"] == 8183 and st["logical_tokens"] == 130736
+    seqs = wl.decode_seqs
+    log("gqa_decode full: decode")
+    q_bits, got = _decode(pool, wl, seqs)
+    log("gqa_decode full: oracle")
+    want = expected_decode(wl, seqs, q_bits)
+    for i in seqs:
+        assert_close(got[i], want[i], *BF16_TOL, what=f"seq {i}")
+
+
+def test_long_decode_full_size_sampled():
+    wl = long_decode()
+    log("long_decode full: build")
+    pool, _ = build_device_pool(wl)
+    assert pool.stats()["free_blocks"] == 0
+    seqs = wl.decode_seqs
+    q_bits, got = _decode(pool, wl, seqs)
+    log("long_decode full: oracle on sequences 0 and 3")
+    sample = [0, 3]
+    want = expected_decode(wl, sample, q_bits[sample])
+    for j, i in enumerate(sample):
+        assert_close(got[i], want[j], *BF16_TOL, what=f"seq {i}")
+
+
+def test_heavy_tail_full_size_sampled():
+    wl = heavy_tail()
+    log("heavy_tail full: build")
+    pool, _ = build_device_pool(wl)
+    st = pool.stats()
+    assert st["allocated_blocks"] == 42982 and st["logical_tokens"] == 1371446
+    seqs = wl.decode_seqs
+    q_bits, got = _decode(pool, wl, seqs)
+    lengths = wl.final_lengths()
+    order = sorted(seqs, key=lambda s: lengths[s])
+    sample = sorted(set(order[:6] + order[-6:] + list(np.random.default_rng(0).choice(seqs, 12, replace=False))))
+    log(f"heavy_tail full: oracle on {len(sample)} sequences")
+    want = expected_decode(wl, sample, q_bits[sample])
+    for j, i in enumerate(sample):
+        assert_close(got[i], want[j], *BF16_TOL, what=f"seq {i} (L={lengths[i]})")
+
+
+def test_prefix_prefill_full_size_sampled_rows():
+    wl = prefix_prefill()
+    log("prefix_prefill full: build")
+    pool, _ = build_device_pool(wl)
+    st = pool.stats()
+    assert st["allocated_blocks"] == 768 and pool.refcount(pool.block_table(0)[0]) == 16
+    qp = prefill_queries(wl)
+    seqs = [s for s, _ in wl.prefill]
+    q_lens = [n for _, n in wl.prefill]
+    log("prefix_prefill full: prefill")
+    out = to_host_f64(pool.prefill(seqs, q_lens, to_device(qp, wl.dtype)))
+    torch.cuda.synchronize()
+    sample_seqs = [0, 7, 15]
+    rows = logical_kv(wl, sample_seqs)
+    rng = np.random.default_rng(1)
+    log("prefix_prefill full: oracle on sampled rows")
+    for s in sample_seqs:
+        K, V = (to_f64(x, wl.dtype) for x in rows[s])
+        L = K.shape[0]
+        for t in sorted(set([0, 1, 15, 16, 255, 511] + list(rng.integers(0, 512, 6)))):
+            r = s * 512 + t
+            vis = L - 512 + t + 1
+            exp = oracle.attention(to_f64(qp[r:r + 1], wl.dtype), K[:vis], V[:vis])[0]
+            assert_close(out[r], exp, *BF16_TOL, what=f"seq {s} row {t}")
