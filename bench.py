@@ -82,6 +82,22 @@ def causal_flops(wl):
     return total
 
 
+def recorded_traffic(name):
+    """HBM bytes per launch from the committed counter summary of a kernel,
+    or None when the kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name + ".counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    csrc = os.path.join(ROOT, "paged_kv_cache_block_amd", "csrc")
+    digest = hashlib.sha256(open(os.path.join(csrc, "decode.hip"), "rb").read() +
+                            open(os.path.join(csrc, "device.hpp"), "rb").read()).hexdigest()
+    if digest != rec.get("kernel_source_sha256"):
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
 def run_decode(args):
     import torch
     from paged_kv_cache_block_amd import abi
@@ -153,8 +169,11 @@ def run_decode(args):
         "sum_len": int(lengths.sum()),
     }
     achieved = alg_per_step / (kernel_ms * 1e-3) / 1e9
+    traffic = recorded_traffic("decode_gqa_mfma__gqa_decode")
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                          "traffic": None if traffic is None else round(traffic / 1e9, 4),
+                          "traffic_unit": "GB per launch",
                           "kernel": "decode_gqa_mfma<128,16>",
                           "decode_plus_merge_GBs": round(alg_per_step / ((kernel_ms + merge_ms) * 1e-3) / 1e9, 1)}
     pool.close()
@@ -252,6 +271,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size reference "
+                         "for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the paged-attention path "
@@ -264,6 +286,16 @@ def main():
     torch.cuda.set_device(0)
     from paged_kv_cache_block_amd import abi
     abi.load()
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
 
     wl, dec = run_decode(args)
     line = {

@@ -216,23 +216,32 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma(DecodeArgs a) {
     const float m_new = fmaxf(m_run, mloc);
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
+    // Weights enter P.V as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi),
+    // so the product carries ~16 mantissa bits of p instead of 8: with
+    // heavy-tailed values a single bf16 rounding of p (2^-9 relative) is not
+    // enough when the output nearly cancels.
     float psum = 0.f;
-    s16x4 pb[TT];
+    s16x4 p_hi[TT], p_lo[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const __bf16 e = static_cast<__bf16>(exp2f(s[tt][i] - m_new));
-        psum += static_cast<float>(e);  // l from the same rounded weights as P.V
-        pb[tt][i] = __builtin_bit_cast(short, e);
+        const float e = exp2f(s[tt][i] - m_new);
+        const __bf16 hi = static_cast<__bf16>(e);
+        const __bf16 lo = static_cast<__bf16>(e - static_cast<float>(hi));
+        psum += e;
+        p_hi[tt][i] = __builtin_bit_cast(short, hi);
+        p_lo[tt][i] = __builtin_bit_cast(short, lo);
       }
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
       acc[nt] *= alpha;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt][tt], pb[tt], acc[nt], 0, 0, 0);
+      for (int tt = 0; tt < TT; ++tt) {
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt][tt], p_hi[tt], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt][tt], p_lo[tt], acc[nt], 0, 0, 0);
+      }
     }
   };
 
