@@ -219,6 +219,51 @@ def test_prefix_prefill_small_full_compare():
         r0 += n
 
 
+PREFILL_CASES = [
+    # (kv lengths, q_lens), Hq, Hkv, D, bs
+    (([600, 77, 40], [70, 77, 1]), 32, 8, 128, 16),     # GQA 4; no-prefix row; single row
+    (([300, 129], [129, 33]), 64, 8, 128, 16),          # GQA 8
+    (([200, 50], [31, 50]), 16, 16, 64, 32),            # MHA, D 64, bs 32
+    (([333, 64], [100, 17]), 16, 1, 128, 32),           # GQA 16
+    (([150, 90], [41, 90]), 8, 4, 64, 16),              # GQA 2
+    (([120, 61], [19, 61]), 6, 2, 64, 16),              # GQA 3: generic kernel
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"G{c[1]//c[2]}-D{c[3]}-bs{c[4]}")
+def test_prefill_shapes(case):
+    (lengths, q_lens), hq, hkv, d, bs = case
+    nb = int(sum(-(-n // bs) for n in lengths) + 5)
+    order = np.random.default_rng(11).permutation(nb).astype(np.int32)
+    ops = []
+    for i, n in enumerate(lengths):
+        ops += [("create", i), ("append", i, int(n))]
+    wl = Workload("prefill_case", 9, "bf16", nb, bs, hq, hkv, d, order, ops,
+                  prefill=[(i, q) for i, q in enumerate(q_lens)])
+    log(f"prefill case {case}")
+    pool, _ = build_device_pool(wl, check_against_oracle_pool=True)
+    qp = prefill_queries(wl)
+    out = to_host_f64(pool.prefill(list(range(len(lengths))), q_lens, to_device(qp, wl.dtype)))
+    rows = logical_kv(wl, list(range(len(lengths))))
+    r0 = 0
+    for s, n in wl.prefill:
+        K, V = (to_f64(x, wl.dtype) for x in rows[s])
+        exp = oracle.attention(to_f64(qp[r0:r0 + n], wl.dtype), K, V)
+        assert_close(out[r0:r0 + n], exp, *BF16_TOL, what=f"seq {s}")
+        r0 += n
+
+
+def test_prefill_rejects_bad_rows():
+    from paged_kv_cache_block_amd.abi import InvalidArgumentError
+    wl = _decode_case([10, 20], 8, 2, 64, 16)
+    pool, _ = build_device_pool(wl)
+    q = torch.zeros(21, 8, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(InvalidArgumentError):
+        pool.prefill([0], [11], q)
+    with pytest.raises(InvalidArgumentError):
+        pool.prefill([0, 1], [0, 5], q)
+
+
 # ------------------------------------------------------------ full size
 def test_gqa_decode_full_size():
     wl = gqa_decode()
