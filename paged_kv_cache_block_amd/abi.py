@@ -17,7 +17,10 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+# PAGEDATTN_LIB names another build of the same library (e.g. a variant
+# compiled with different kernel tile parameters).
+LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = -1

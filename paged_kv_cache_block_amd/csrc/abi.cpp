@@ -7,7 +7,9 @@
 // on the pool, and records optional per-kernel timing events.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -192,6 +194,16 @@ bool desc_ok(const pa_pool_desc* d, std::string* msg) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Decode page-range size in tokens: 0 = chosen per batch by the plan;
+// PA_DECODE_TOKENS_PER_PART in the environment fixes it (tuning override).
+int32_t decode_tokens_per_part() {
+  static const int32_t v = [] {
+    const char* s = std::getenv("PA_DECODE_TOKENS_PER_PART");
+    return s ? std::max(0, std::atoi(s)) : 0;
+  }();
+  return v;
+}
+
 float scale_log2_for(int32_t head_dim) {
   return static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
 }
@@ -304,7 +316,7 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32
   pa::DecodePlan plan;
   std::string msg;
   if (pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                            pool->geom.head_dim, 0, &plan, &msg) != pa::kOk)
+                            pool->geom.head_dim, decode_tokens_per_part(), &plan, &msg) != pa::kOk)
     return 0;
   return plan.total_bytes;
 }
@@ -324,7 +336,7 @@ pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_h
   pa::DecodePlan plan;
   std::string msg;
   pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                                       pool->geom.head_dim, 0, &plan, &msg);
+                                       pool->geom.head_dim, decode_tokens_per_part(), &plan, &msg);
   if (s != pa::kOk) return fail(s, msg);
   if (ws_bytes < plan.total_bytes)
     return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
@@ -424,6 +436,7 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
   a.q_start = reinterpret_cast<const int32_t*>(w + plan.qstart_off);
   a.tiles = reinterpret_cast<const int32_t*>(w + plan.tiles_off);
   a.row_seq = reinterpret_cast<const int32_t*>(w + plan.rowseq_off);
+  a.zeros = w + plan.zeros_off;
   a.num_heads = num_heads;
   a.num_kv_heads = pool->geom.num_kv_heads;
   a.group = group;

@@ -33,6 +33,19 @@
 #include "device.hpp"
 #include "kernels.hpp"
 
+// Tile parameters (compile-time; variant builds override them with -D).
+#ifndef PA_DECODE_WAVES_PER_EU
+#define PA_DECODE_WAVES_PER_EU 0  // occupancy hint for the GQA kernel (0 = none)
+#endif
+#if PA_DECODE_WAVES_PER_EU > 0
+#define PA_DECODE_OCC __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
+#else
+#define PA_DECODE_OCC
+#endif
+#ifndef PA_DECODE_PREFETCH
+#define PA_DECODE_PREFETCH 1  // 1: load page p + 4 while computing page p
+#endif
+
 namespace pa {
 
 namespace {
@@ -131,14 +144,16 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
 
 // ------------------------------------------------------------ GQA / MFMA ---
 template <int D, int BS>
-__global__ __launch_bounds__(256) void decode_gqa_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(256) PA_DECODE_OCC void decode_gqa_mfma(DecodeArgs a) {
   constexpr int KS = D / 32;  // k-steps of the 16x16x32 QK contraction
   constexpr int TT = BS / 16; // 16-token tiles per page
   constexpr int DT = D / 16;  // 16-wide d tiles of the P.V contraction
   constexpr int W = kDecodeWaves;
+  constexpr int ROW = D + 4;  // padded LDS row of one head's accumulator
   __shared__ float s_m[W][16];
   __shared__ float s_l[W][16];
-  __shared__ float s_acc[W][16][D + 4];
+  // [W][G][ROW]: only the G live head columns are staged for the wave merge.
+  extern __shared__ float s_acc[];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -234,32 +249,55 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma(DecodeArgs a) {
         p_lo[tt][i] = __builtin_bit_cast(short, lo);
       }
     l_run = l_run * alpha + psum;
+    // Unused slots of the last page have weight 0; their values are zeroed
+    // too, so 0 * V cannot meet non-finite bits left in an unused slot.
+    int live[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) live[tt] = tail ? L - (pg * BS + 16 * tt + 4 * grp) : 4;
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
       acc[nt] *= alpha;
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt][tt], p_hi[tt], acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt][tt], p_lo[tt], acc[nt], 0, 0, 0);
+        s16x4 v = vr[nt][tt];
+        if (tail) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i >= live[tt]) v[i] = 0;
+        }
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_hi[tt], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_lo[tt], acc[nt], 0, 0, 0);
       }
     }
   };
 
+#if PA_DECODE_PREFETCH
   {
     bf16x8 ka[TT][KS], kb[TT][KS];
     s16x4 va[DT][TT], vb[DT][TT];
+    // The prefetch is issued unconditionally (the last page of the range
+    // re-loads itself): with the same number of loads in flight on every
+    // path, the wait before a page's first use only covers that page's loads.
     int p = p0 + wave;
     if (p < p1) load_page(p, ka, va);
     while (p < p1) {
-      if (p + W < p1) load_page(p + W, kb, vb);
+      load_page(p + W < p1 ? p + W : p, kb, vb);
       process(p, ka, va);
       p += W;
       if (p >= p1) break;
-      if (p + W < p1) load_page(p + W, ka, va);
+      load_page(p + W < p1 ? p + W : p, ka, va);
       process(p, kb, vb);
       p += W;
     }
   }
+#else
+  for (int p = p0 + wave; p < p1; p += W) {
+    bf16x8 ka[TT][KS];
+    s16x4 va[DT][TT];
+    load_page(p, ka, va);
+    process(p, ka, va);
+  }
+#endif
 
   // Per-head totals over the 4 lane groups, then merge the 4 waves.
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -268,10 +306,11 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma(DecodeArgs a) {
     s_m[wave][n] = m_run;
     s_l[wave][n] = l_tot;
   }
+  if (n < G) {
+    float* dst = s_acc + (wave * G + n) * ROW + 4 * grp;
 #pragma unroll
-  for (int nt = 0; nt < DT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_acc[wave][n][16 * nt + 4 * grp + i] = acc[nt][i];
+    for (int nt = 0; nt < DT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt) = acc[nt];
+  }
   __syncthreads();
 
   const int base = a.part_base[b];
@@ -284,7 +323,7 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const float e = exp2f(s_m[w][hn] - M);  // a wave without pages has m = -inf
-      num += e * s_acc[w][hn][d];
+      num += e * s_acc[(w * G + hn) * ROW + d];
       den += e * s_l[w][hn];
     }
     const int h = g * G + hn;
@@ -351,7 +390,8 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
 
 template <int D, int BS>
 void launch_gqa(const DecodeArgs& a, int groups, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_gqa_mfma<D, BS>), dim3(groups), dim3(256), 0, stream, a);
+  const size_t shmem = static_cast<size_t>(kDecodeWaves) * a.group * (D + 4) * sizeof(float);
+  hipLaunchKernelGGL((decode_gqa_mfma<D, BS>), dim3(groups), dim3(256), shmem, stream, a);
 }
 
 }  // namespace

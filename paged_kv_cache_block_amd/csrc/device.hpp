@@ -52,4 +52,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Uniform value in a scalar register (the compiler cannot always prove it).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Read-only int32 at a wave-uniform address through the constant address
+// space, so it becomes a scalar load (counted by lgkmcnt, not vmcnt: it does
+// not wait behind the wave's in-flight vector loads).
+__device__ __forceinline__ int32_t scalar_load(const int32_t* base, int idx) {
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  return ((const const_i32*)base)[idx];  // C cast: generic -> constant address space
+}
+
 }  // namespace pa

@@ -198,6 +198,7 @@ Status build_prefill_plan(const BlockPool& pool, const int64_t* seqs, const int3
   p.qstart_off = reserve(meta, B + 1);
   p.tiles_off = reserve(meta, 2 * tiles.size());
   p.rowseq_off = reserve(meta, static_cast<size_t>(total_rows));
+  p.zeros_off = reserve(meta, 16);  // 64 bytes, left zero
   p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
   int32_t* ctx = at_bytes(meta, p.ctx_off);
   int32_t* toff = at_bytes(meta, p.tbl_off_off);

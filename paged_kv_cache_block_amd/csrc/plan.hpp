@@ -82,6 +82,7 @@ struct PrefillArgs {
   const int32_t* q_start;   // [B+1] first row of b
   const int32_t* tiles;     // [n_tiles][2] = (b, first query row of the tile within b)
   const int32_t* row_seq;   // [R] sequence of each row (generic kernel)
+  const void* zeros;        // 64 zero bytes (source of staged slots past a sequence's end)
   int32_t num_heads, num_kv_heads, group;
   int32_t n_tiles, n_rows;
   float scale_log2;
@@ -91,7 +92,7 @@ struct PrefillPlan {
   std::vector<int32_t> meta;
   size_t meta_bytes = 0, total_bytes = 0;
   size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, qstart_off = 0, tiles_off = 0,
-         rowseq_off = 0;
+         rowseq_off = 0, zeros_off = 0;
   int32_t n_tiles = 0, n_rows = 0, batch = 0;
 };
 

@@ -4,26 +4,66 @@
 // paged_attention with q_tokens > 1): the q_len query rows of a sequence are
 // its last q_len positions; row t sees keys j <= kv_len - q_len + t
 // (bottom-right causal alignment, as CMU 11-667 lecture 19's CachedDecoder
-// masks cached decoding).
+// masks cached decoding).  The one-pass running max / sum per key tile is
+// lecture 19's tiled_attention recurrence.
 //
-// prefill_gqa_mfma<D, BS, CG>  (bf16, D in {64, 128}, BS in {16, 32}, G | 16)
-//   One 256-thread workgroup = (sequence, block of query rows, KV head).  The
-//   N dimension of the MFMA tiles packs (query row, head of the group) pairs:
-//   column c of the workgroup is row t0 + c / G, head g*G + c % G, so every
-//   K/V page read serves all G query heads of the KV head.  Each wave owns
-//   CG groups of 16 columns and streams the pages its rows can see:
-//     S^T[16 tok x 16 col]  = K_page . Q^T          (v_mfma_f32_16x16x32_bf16)
-//     O^T[16 d   x 16 col] += V^T_page . P^T (hi+lo) (v_mfma_f32_16x16x16_bf16)
-//   as in the decode kernel (the S^T accumulator layout is the P^T operand
-//   layout).  Pages wholly below every row's limit need no mask; pages past
-//   the wave's last row's limit are skipped; only diagonal pages are masked.
-//   blockIdx % Hkv is the KV head, so with Hkv a multiple of 8 each XCD (and
-//   its L2) serves one KV head of every sequence: a shared prefix is read
-//   from HBM once per head and then hits in that XCD's L2.
+// prefill_gqa_mfma<D, BS, CG, NW, S>  (bf16, D in {64, 128}, BS in {16, 32}, G | 16)
+//   One workgroup of NW waves = (sequence, block of query rows, KV head).
+//   The MFMA N dimension packs (query row, head of the group) pairs: column c
+//   of the workgroup is row t0 + c / G, head g*G + c % G, so each key tile
+//   serves all G query heads of its KV head.  Each wave owns CG groups of 16
+//   columns (Q^T operands and O^T accumulators stay in registers).
+//
+//   Keys advance in tiles of 32 tokens (two 16-slot pages or one 32-slot
+//   page).  Per tile:
+//     S^T[16 tok x 16 col] = K_tile . Q^T     (x2 token halves)  v_mfma_f32_16x16x32_bf16
+//     O^T[16 d  x 16 col] += V^T_tile . P^T   (x D/16 d tiles)   v_mfma_f32_16x16x32_bf16
+//   Row m of the QK tile tt is token 8*(m/4) + 4*tt + m%4, so the lane that
+//   ends up holding S^T rows 4*grp .. 4*grp+3 of both tiles holds tokens
+//   8*grp .. 8*grp+7: its P^T operand for the 32-token P.V step is its own
+//   accumulator, and the matching V^T operand is 16 contiguous bytes of one
+//   page row.  Every K and V operand of a tile is therefore one 16-byte
+//   chunk per lane, and the tile is NB blocks of 64 such chunks.
+//
+//   The workgroup keeps an S-stage ring of tiles in LDS.  Each block is
+//   fetched with one direct global->LDS load (global_load_lds_dwordx4; lane l
+//   writes bytes 16l..16l+15 of the block), already in operand order, so the
+//   MFMA operand reads are conflict-free 16-byte LDS reads and no register
+//   holds in-flight data; loads run S-1 tiles ahead, and one barrier per
+//   tile (after each wave's own vmcnt wait) publishes a tile and frees the
+//   stage read in the previous step.  Slots past the sequence end are staged
+//   from a zero region (and the tail tile's V operands are masked), so
+//   0 * V never meets stale or non-finite bits.
+//   Tiles wholly below every row's limit are not masked; tiles past a
+//   wave's last row's limit are skipped by that wave.  blockIdx % Hkv is the
+//   KV head: with Hkv a multiple of 8 each XCD (and its L2) serves one KV
+//   head of every sequence, so a shared prefix is read from HBM once per
+//   head.
 #include <cmath>
 
 #include "device.hpp"
 #include "kernels.hpp"
+
+#ifndef PA_PREFILL_CG
+#define PA_PREFILL_CG 1
+#endif
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 3
+#endif
+#ifndef PA_PREFILL_SPLIT_P
+#define PA_PREFILL_SPLIT_P 1
+#endif
+#ifndef PA_PREFILL_WAVES_PER_EU
+#define PA_PREFILL_WAVES_PER_EU 0  // occupancy hint (0 = none)
+#endif
+#if PA_PREFILL_WAVES_PER_EU > 0
+#define PA_PREFILL_OCC __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
+#else
+#define PA_PREFILL_OCC
+#endif
 
 namespace pa {
 
@@ -31,18 +71,36 @@ hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hi
 
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillCG = 2;  // 16-column groups per wave
+constexpr int kPrefillCG = PA_PREFILL_CG;          // 16-column groups per wave
+constexpr int kPrefillWaves = PA_PREFILL_WAVES;    // waves per workgroup
+constexpr int kPrefillStages = PA_PREFILL_STAGES;  // key tiles in the LDS ring
+constexpr bool kSplitP = PA_PREFILL_SPLIT_P;       // P as bf16 hi + lo in P.V
+constexpr int kTile = 32;                          // key tokens per step
 
-template <int D, int BS, int CG>
-__global__ __launch_bounds__(256) void prefill_gqa_mfma(PrefillArgs a) {
-  constexpr int KS = D / 32;
-  constexpr int TT = BS / 16;
-  constexpr int DT = D / 16;
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// and `lgkm` LDS/scalar operations of this wave are outstanding.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
+}
+
+template <int D, int BS, int CG, int NW, int S>
+__global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(PrefillArgs a) {
+  constexpr int KS = D / 32;         // k-steps of QK per token half
+  constexpr int DT = D / 16;         // d tiles of P.V
+  constexpr int KB = 2 * KS;         // K operand blocks per key tile
+  constexpr int NB = KB + DT;        // operand blocks per key tile
+  constexpr int PAGES = kTile / BS;  // pages per key tile
+  static_assert(NB % NW == 0, "each wave stages the same number of blocks");
+  constexpr int BPW = NB / NW;       // blocks staged by each wave per tile
+  static_assert((S - 2) * BPW < 64, "vmcnt range");
+  __shared__ uint4 ring[S][NB][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
   const int n = lane & 15, grp = lane >> 4;
   const int Hkv = a.num_kv_heads, Hq = a.num_heads, G = a.group;
   const int tile = blockIdx.x / Hkv, g = blockIdx.x - tile * Hkv;
@@ -51,20 +109,23 @@ __global__ __launch_bounds__(256) void prefill_gqa_mfma(PrefillArgs a) {
   const int q_len = a.q_start[b + 1] - q0;
   const int L = a.ctx_len[b];
   const int off = L - q_len;  // row t sees keys 0 .. off + t
+  const int nblk = (L + BS - 1) / BS;
   const int32_t* table = a.tables + a.tbl_off[b];
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
   const size_t page = static_cast<size_t>(BS) * D;
 
+  // Rows of the workgroup and of this wave.
+  const int wg_rows = NW * CG * 16 / G;
+  const int wg_last = min(q_len - 1, t0 + wg_rows - 1);
+  const int n_tiles = (off + wg_last) / kTile + 1;  // key tiles any row of the workgroup sees
   const int wave_c0 = wave * CG * 16;
   const int t_first = t0 + wave_c0 / G;
-  if (t_first >= q_len) return;  // ragged last row block: no rows for this wave
+  const bool wave_live = t_first < q_len;
   const int t_last = min(q_len - 1, t0 + (wave_c0 + CG * 16 - 1) / G);
-  const int last_key = off + t_last;       // largest key any column of the wave sees
-  const int all_see = off + t_first;       // keys <= all_see are visible to every column
-  const int n_pages = last_key / BS + 1;
+  const int wave_keys = off + t_last;  // last key of any column of the wave
+  const int all_see = off + t_first;   // keys <= all_see are visible to every column
 
-  // This lane's column in each group, its row limit, and its Q^T operand.
   bf16x8 qv[CG][KS];
   int lim[CG], row[CG], head[CG];
 #pragma unroll
@@ -72,18 +133,12 @@ __global__ __launch_bounds__(256) void prefill_gqa_mfma(PrefillArgs a) {
     const int c = wave_c0 + k * 16 + n;
     row[k] = t0 + c / G;
     head[k] = g * G + c % G;
-    // A column past the last row (ragged row block) is computed with the last
-    // row's limit, so it stays finite, and is never stored.
+    // Columns past the last row are computed with its limit and not stored.
     lim[k] = off + min(row[k], q_len - 1);
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           (static_cast<size_t>(q0 + row[k]) * Hq + head[k]) * D + 8 * grp;
+                           (static_cast<size_t>(q0 + min(row[k], q_len - 1)) * Hq + head[k]) * D + 8 * grp;
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      if (row[k] < q_len)
-        qv[k][j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j);
-      else
-        qv[k][j] = bf16x8{};
-    }
+    for (int j = 0; j < KS; ++j) qv[k][j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j);
   }
 
   float m_run[CG], l_run[CG];
@@ -96,93 +151,139 @@ __global__ __launch_bounds__(256) void prefill_gqa_mfma(PrefillArgs a) {
     for (int nt = 0; nt < DT; ++nt) acc[k][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto load_page = [&](int pg, bf16x8 (&kr)[TT][KS], s16x4 (&vr)[DT][TT]) {
-    const int blk = uniform(table[pg]);
-    const uint16_t* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * page;
-    const uint16_t* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * page;
+  // Stage tile T into ring slot st: this wave's BPW blocks, one direct
+  // global->LDS load each.  Tiles past the last (issued to keep every wave's
+  // vmcnt accounting uniform) and slots past the sequence end read zeros.
+  auto stage = [&](int T, int st) {
+    int ent[PAGES];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int p = 0; p < PAGES; ++p) {
+      const int pg = T * PAGES + p;
+      ent[p] = (T < n_tiles && pg < nblk) ? scalar_load(table, pg) : 0;
+    }
 #pragma unroll
-      for (int j = 0; j < KS; ++j)
-        kr[tt][j] = *reinterpret_cast<const bf16x8*>(kp + (16 * tt + n) * D + 32 * j + 8 * grp);
-#pragma unroll
-    for (int nt = 0; nt < DT; ++nt)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-        vr[nt][tt] = *reinterpret_cast<const s16x4*>(vp + (16 * nt + n) * BS + 16 * tt + 4 * grp);
+    for (int r = 0; r < BPW; ++r) {
+      const int blkid = wave * BPW + r;
+      const void* src = a.zeros;
+      if (blkid < KB) {
+        const int tt = blkid / KS, j = blkid - tt * KS;
+        const int tok = 8 * (n >> 2) + 4 * tt + (n & 3);
+        const int pgi = tok / BS;
+        if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L) {
+          const int blk = pgi ? ent[PAGES - 1] : ent[0];
+          src = kpool + (static_cast<size_t>(blk) * Hkv + g) * page + (tok % BS) * D + 32 * j + 8 * grp;
+        }
+      } else {
+        const int nt = blkid - KB;
+        const int tok = 8 * grp;
+        const int pgi = tok / BS;
+        if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L) {
+          const int blk = pgi ? ent[PAGES - 1] : ent[0];
+          src = vpool + (static_cast<size_t>(blk) * Hkv + g) * page + (16 * nt + n) * BS + tok % BS;
+        }
+      }
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
+    }
   };
 
-  auto process = [&](int pg, const bf16x8 (&kr)[TT][KS], const s16x4 (&vr)[DT][TT]) {
-    const bool masked = pg * BS + BS - 1 > all_see;
+  auto compute = [&](int T, int st) {
+    if (!wave_live || T * kTile > wave_keys) return;
+    const bool masked = T * kTile + kTile - 1 > all_see;
+    const bool tail = T * kTile + kTile > L;
+    const bf16x8* blocks = reinterpret_cast<const bf16x8*>(&ring[st][0][0]);
+    f32x4 s[CG][2];
+#pragma unroll
+    for (int k = 0; k < CG; ++k) s[k][0] = s[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const bf16x8 kop = blocks[(tt * KS + j) * 64 + lane];
+#pragma unroll
+        for (int k = 0; k < CG; ++k)
+          s[k][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[k][j], s[k][tt], 0, 0, 0);
+      }
+    // s[k][tt][i] is the score of token T*32 + 8*grp + 4*tt + i for column n.
+    bf16x8 p_hi[CG], p_lo[CG];
 #pragma unroll
     for (int k = 0; k < CG; ++k) {
-      f32x4 s[TT];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < KS; ++j)
-          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[tt][j], qv[k][j], s[tt], 0, 0, 0);
-      }
       float mloc = -INFINITY;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = s[tt][i] * a.scale_log2;
-          if (masked && pg * BS + 16 * tt + 4 * grp + i > lim[k]) x = -INFINITY;
-          s[tt][i] = x;
+          float x = s[k][tt][i];
+          if (masked && T * kTile + 8 * grp + 4 * tt + i > lim[k]) x = -INFINITY;
+          s[k][tt][i] = x;
           mloc = fmaxf(mloc, x);
         }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      // Every column sees key 0 on page 0, so m_run is finite from then on.
+      // Raw-score maximum; every column sees key 0 in tile 0, so m_run is
+      // finite from the first tile on.
       const float m_new = fmaxf(m_run[k], mloc);
-      const float alpha = exp2f(m_run[k] - m_new);
-      m_run[k] = m_new;
+      const float ms = m_new * a.scale_log2;
       float psum = 0.f;
-      s16x4 p_hi[TT], p_lo[TT];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(s[tt][i] - m_new);
+          const float e = exp2f(fmaf(s[k][tt][i], a.scale_log2, -ms));
           const __bf16 hi = static_cast<__bf16>(e);
-          const __bf16 lo = static_cast<__bf16>(e - static_cast<float>(hi));
-          psum += e;
-          p_hi[tt][i] = __builtin_bit_cast(short, hi);
-          p_lo[tt][i] = __builtin_bit_cast(short, lo);
+          p_hi[k][4 * tt + i] = hi;
+          if constexpr (kSplitP) {
+            p_lo[k][4 * tt + i] = static_cast<__bf16>(e - static_cast<float>(hi));
+            psum += e;
+          } else {
+            psum += static_cast<float>(hi);  // l from the same rounded weights as P.V
+          }
         }
-      l_run[k] = l_run[k] * alpha + psum;
+      if (m_new != m_run[k]) {
+        // Only lanes whose column maximum moved rescale; the wave skips the
+        // multiplies when no column's maximum moved.
+        const float alpha = exp2f((m_run[k] - m_new) * a.scale_log2);
+        l_run[k] *= alpha;
 #pragma unroll
-      for (int nt = 0; nt < DT; ++nt) {
-        acc[k][nt] *= alpha;
+        for (int nt = 0; nt < DT; ++nt) acc[k][nt] *= alpha;
+      }
+      m_run[k] = m_new;
+      l_run[k] += psum;
+    }
+    const int live = L - (T * kTile + 8 * grp);  // tokens of this lane's 8 inside the sequence
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt][tt], p_hi[tt], acc[k][nt], 0, 0, 0);
-          acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[nt][tt], p_lo[tt], acc[k][nt], 0, 0, 0);
-        }
+    for (int nt = 0; nt < DT; ++nt) {
+      bf16x8 vop = blocks[(KB + nt) * 64 + lane];
+      if (tail) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= live) vop[e] = static_cast<__bf16>(0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < CG; ++k) {
+        acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, p_hi[k], acc[k][nt], 0, 0, 0);
+        if constexpr (kSplitP)
+          acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, p_lo[k], acc[k][nt], 0, 0, 0);
       }
     }
   };
 
-  {
-    bf16x8 ka[TT][KS], kb[TT][KS];
-    s16x4 va[DT][TT], vb[DT][TT];
-    int p = 0;
-    load_page(p, ka, va);
-    while (p < n_pages) {
-      if (p + 1 < n_pages) load_page(p + 1, kb, vb);
-      process(p, ka, va);
-      ++p;
-      if (p >= n_pages) break;
-      if (p + 1 < n_pages) load_page(p + 1, ka, va);
-      process(p, kb, vb);
-      ++p;
-    }
+#pragma unroll
+  for (int T = 0; T < S - 1; ++T) stage(T, T);
+  for (int T = 0; T < n_tiles; ++T) {
+    // Tile T's blocks from this wave have landed once at most the blocks of
+    // the S-2 later tiles are outstanding; the barrier then publishes the
+    // whole tile and guarantees every wave has finished reading the slot
+    // that the next stage() overwrites (read in step T-1).
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * BPW, 0));
+    __builtin_amdgcn_s_barrier();
+    stage(T + S - 1, (T + S - 1) % S);
+    compute(T, T % S);
   }
+  // Drain the zero-tile loads still in flight before the workgroup's LDS is
+  // released.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
-  // Normalise and store: lane (n, grp) holds d = 16nt + 4grp + i of its column.
+  if (!wave_live) return;
 #pragma unroll
   for (int k = 0; k < CG; ++k) {
     float l = l_run[k] + __shfl_xor(l_run[k], 16, 64);
@@ -205,7 +306,8 @@ __global__ __launch_bounds__(256) void prefill_gqa_mfma(PrefillArgs a) {
 template <int D, int BS>
 void launch_mfma(const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_tiles * a.num_kv_heads);
-  hipLaunchKernelGGL((prefill_gqa_mfma<D, BS, kPrefillCG>), grid, dim3(64 * kPrefillWaves), 0, stream, a);
+  hipLaunchKernelGGL((prefill_gqa_mfma<D, BS, kPrefillCG, kPrefillWaves, kPrefillStages>), grid,
+                     dim3(64 * kPrefillWaves), 0, stream, a);
 }
 
 }  // namespace

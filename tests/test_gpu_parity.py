@@ -253,6 +253,45 @@ def test_prefill_shapes(case):
         r0 += n
 
 
+@pytest.mark.parametrize("shape", [(32, 8, 128, 16), (16, 16, 64, 32), (8, 2, 16, 4)],
+                         ids=["G4-D128-bs16", "G1-D64-bs32", "generic"])
+def test_unused_slots_holding_nan_do_not_leak(shape):
+    """Slots past a sequence's end are never read into the result, even when
+    the caller's pool memory holds NaN there."""
+    from paged_kv_cache_block_amd import DevicePool
+    hq, hkv, d, bs = shape
+    lengths, q_lens = [37, 5, 70], [9, 5, 33]
+    nb = sum(-(-n // bs) for n in lengths) + 3
+    order = np.random.default_rng(2).permutation(nb).astype(np.int32)
+    ops = []
+    for i, n in enumerate(lengths):
+        ops += [("create", i), ("append", i, n)]
+    wl = Workload("nan_case", 12, "bf16", nb, bs, hq, hkv, d, order, ops,
+                  decode_seqs=[0, 1, 2], prefill=[(i, q) for i, q in enumerate(q_lens)])
+    pool = DevicePool(nb, bs, hkv, d, dtype="bf16", allocation_order=order)
+    pool.k.fill_(float("nan"))
+    pool.v.fill_(float("nan"))
+    for op in append_stream(wl):
+        if op[0] == "create":
+            pool.create(op[1])
+        elif op[0] == "append":
+            _, s, n, k, v = op
+            pool.write(pool.append(s, n), to_device(k, "bf16"), to_device(v, "bf16"))
+    q_bits, got = _decode(pool, wl, [0, 1, 2])
+    want = expected_decode(wl, [0, 1, 2], q_bits)
+    for i in range(3):
+        assert_close(got[i], want[i], *BF16_TOL, what=f"decode seq {i}")
+    qp = prefill_queries(wl)
+    out = to_host_f64(pool.prefill([0, 1, 2], q_lens, to_device(qp, "bf16")))
+    rows = logical_kv(wl, [0, 1, 2])
+    r0 = 0
+    for s, n in wl.prefill:
+        K, V = (to_f64(x, "bf16") for x in rows[s])
+        assert_close(out[r0:r0 + n], oracle.attention(to_f64(qp[r0:r0 + n], "bf16"), K, V),
+                     *BF16_TOL, what=f"prefill seq {s}")
+        r0 += n
+
+
 def test_prefill_rejects_bad_rows():
     from paged_kv_cache_block_amd.abi import InvalidArgumentError
     wl = _decode_case([10, 20], 8, 2, 64, 16)
