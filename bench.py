@@ -1,10 +1,10 @@
 """Paged-attention benchmark on one MI355X.
 
 One step is one decode step of one attention layer over the whole batch,
-through the C ABI: append one token to every sequence (host bookkeeping and
-slot mapping), write the new K/V rows into their slots (reshape_and_cache),
-then decode attention (plan upload, split-K partial kernel, log-sum-exp
-merge).  Workload: 32 sequences with lengths uniform in [1, 8192], 32 query /
+one call of pa_decode_step: append one token to every sequence (host
+bookkeeping and slot mapping), store the new K/V rows in their slots and
+upload the plan (one kernel), then decode attention (split-K partial kernel,
+log-sum-exp merge).  Workload: 32 sequences with lengths uniform in [1, 8192], 32 query /
 8 KV heads, head_dim 128, bf16 K/V, block_size 16, a 32768-block pool with
 shuffled block tables, Q/K/V ~ N(0, 1) (seeded, synthetic).
 
@@ -116,21 +116,16 @@ def run_decode(args):
     new_v = torch.randn((total_steps, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     lengths = np.array([pool.seq_len(s) for s in seqs], dtype=np.int64)
     # Workspace for the longest batch this run reaches (lengths grow by 1 a step).
-    ws_need = abi.pa_decode_workspace_bytes(pool.handle, seqs, wl.num_heads)
+    ws_need = abi.pa_decode_step_workspace_bytes(pool.handle, seqs, wl.num_heads)
     ws = torch.empty(2 * ws_need + (1 << 20), dtype=torch.uint8, device="cuda")
-    # Pinned slot buffers (one per step, so no copy is overwritten in flight).
-    ones = np.ones(B, dtype=np.int32)
-    slot_host = torch.empty((total_steps, B), dtype=torch.int64).pin_memory()
-    slot_dev = torch.empty((total_steps, B), dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
     handle = pool.handle
     alg = []
 
     def step(i):
-        abi.pa_append_batch(handle, seqs, ones, slot_host[i].numpy())
-        slot_dev[i].copy_(slot_host[i], non_blocking=True)
-        abi.pa_reshape_and_cache(handle, new_k[i], new_v[i], slot_dev[i], B, stream.cuda_stream)
-        abi.pa_decode(handle, seqs, wl.num_heads, q, out, ws, ws.numel(), stream.cuda_stream)
+        # append 1 token per sequence + store its K/V + decode, one C call
+        abi.pa_decode_step(handle, seqs, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws.numel(),
+                           stream.cuda_stream)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -313,7 +308,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "gqa_decode: 32 seqs, lengths U[1,8192] (seed 1), 32 query / 8 KV heads, "
                                "head_dim 128, bf16 K/V, block_size 16, 32768-block pool, one layer; "
-                               "step = append 1 token/seq + reshape_and_cache + decode",
+                               "step = pa_decode_step: append 1 token/seq + store its K/V + decode",
                    "global_batch": 32, "seq_len": "U[1,8192]", "parallelism": "single GPU"},
         "tokens_per_s": round(dec["tokens_per_s"], 1),
         "hbm_frac_step": round(dec["value"] / HBM_PEAK_GBS, 4),

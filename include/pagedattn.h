@@ -219,6 +219,28 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32
 pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                     const void* q, void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes pa_decode_step needs for this batch (sized for the lengths
+ * after its append).  0 if the arguments are invalid. */
+size_t pa_decode_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32_t B,
+                                      int32_t num_heads);
+
+/* One decode step of one layer, fused: the append of one token to every
+ * sequence of the batch (pa_append_batch with n_tokens = 1 each, all or
+ * nothing), the store of that token's K/V rows into their slots
+ * (pa_reshape_and_cache) and decode attention of q over every cached token,
+ * the new one included (pa_decode).  The plan and the slots cross to the
+ * device in one upload and one kernel both copies the plan and stores the
+ * new rows, so a step costs that kernel, the decode kernel and the merge.
+ * k_new, v_new: device [B][num_kv_heads][head_dim]; q, out as pa_decode;
+ * ws: at least pa_decode_step_workspace_bytes(...) bytes, 256-byte aligned;
+ * slots_out: host [B] or NULL, receives the new slots.
+ * Errors: as pa_decode and pa_append_batch; a too-small workspace or an
+ *   exhausted pool is reported before anything changes.  On PA_ERR_DEVICE
+ *   the append is kept (the device work could not be enqueued). */
+pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
+                         const void* k_new, const void* v_new, const void* q, void* out, void* ws,
+                         size_t ws_bytes, int64_t* slots_out, void* stream);
+
 /* Workspace bytes pa_prefill_chunk needs.  0 if the arguments are invalid. */
 size_t pa_prefill_workspace_bytes(const pa_pool* pool, const int64_t* seqs,
                                   const int32_t* q_lens, int32_t B, int32_t num_heads);

@@ -111,6 +111,9 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_size, [_c_void_p, _i64p, _i32, _i32]),
     "pa_decode": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _size,
                          _c_void_p]),
+    "pa_decode_step_workspace_bytes": (_size, [_c_void_p, _i64p, _i32, _i32]),
+    "pa_decode_step": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                              _c_void_p, _c_void_p, _size, _i64p, _c_void_p]),
     "pa_prefill_workspace_bytes": (_size, [_c_void_p, _i64p, _i32p, _i32, _i32]),
     "pa_prefill_chunk": (_i32, [_c_void_p, _i64p, _i32p, _i32, _i32, _c_void_p, _c_void_p,
                                 _c_void_p, _size, _c_void_p]),
@@ -266,6 +269,26 @@ def pa_decode(pool, seqs, num_heads, q, out, ws, ws_bytes, stream=None):
     arr, ptr = _i64_array(seqs)
     _check(load().pa_decode(pool, ptr, len(arr), num_heads, _addr(q), _addr(out), _addr(ws),
                             ws_bytes, _stream(stream)))
+
+
+def pa_decode_step_workspace_bytes(pool, seqs, num_heads):
+    arr, ptr = _i64_array(seqs)
+    return int(load().pa_decode_step_workspace_bytes(pool, ptr, len(arr), num_heads))
+
+
+def pa_decode_step(pool, seqs, num_heads, k_new, v_new, q, out, ws, ws_bytes, stream=None,
+                   slots_out=None):
+    """Fused decode step; returns the new slots (int64 [B]) when ``slots_out`` is given or True."""
+    arr, ptr = _i64_array(seqs)
+    sp = None
+    if slots_out is True:
+        slots_out = np.empty(len(arr), dtype=np.int64)
+    if slots_out is not None:
+        assert slots_out.dtype == np.int64 and slots_out.size >= len(arr)
+        sp = slots_out.ctypes.data_as(_i64p)
+    _check(load().pa_decode_step(pool, ptr, len(arr), num_heads, _addr(k_new), _addr(v_new), _addr(q),
+                                 _addr(out), _addr(ws), ws_bytes, sp, _stream(stream)))
+    return slots_out
 
 
 def pa_prefill_workspace_bytes(pool, seqs, q_lens, num_heads):

@@ -13,6 +13,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "kernels.hpp"
@@ -99,6 +100,7 @@ struct pa_pool {
   void* v = nullptr;
   struct Staging {
     void* host = nullptr;
+    void* dev = nullptr;  // device address of the same pinned buffer
     size_t cap = 0;
     hipEvent_t ev = nullptr;
     bool pending = false;
@@ -109,29 +111,51 @@ struct pa_pool {
 
   bool has_device() const { return k != nullptr; }
 
-  // Copy `bytes` of host data to device `dst` on `stream` through a pinned
-  // buffer; the buffer is reused only after its previous copy has finished.
-  pa_status upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  // Copy `bytes` of host data into the next pinned staging buffer and return
+  // its device address; the buffer is reused only after the event recorded
+  // behind its previous use (staged_done) has fired.
+  pa_status stage(const void* src, size_t bytes, const void** dev_copy) {
     Staging& st = ring[next];
-    next = (next + 1) % kRing;
     if (st.pending) {
       PA_HIP(hipEventSynchronize(st.ev));
       st.pending = false;
     }
     if (!st.ev) PA_HIP(hipEventCreateWithFlags(&st.ev, hipEventDisableTiming));
-    if (st.cap < bytes) {
+    const size_t padded = pa::align_up(bytes, 16);
+    if (st.cap < padded) {
       if (st.host) PA_HIP(hipHostFree(st.host));
-      st.host = nullptr;
+      st.host = st.dev = nullptr;
       st.cap = 0;
-      size_t cap = std::max<size_t>(bytes + bytes / 2, 1 << 16);
+      size_t cap = pa::align_up(std::max<size_t>(padded + padded / 2, 1 << 16), 16);
       PA_HIP(hipHostMalloc(&st.host, cap, hipHostMallocDefault));
+      PA_HIP(hipHostGetDevicePointer(&st.dev, st.host, 0));
       st.cap = cap;
     }
     std::memcpy(st.host, src, bytes);
-    PA_HIP(hipMemcpyAsync(dst, st.host, bytes, hipMemcpyHostToDevice, stream));
+    *dev_copy = st.dev;
+    return ok();
+  }
+
+  // Mark the buffer of the last stage() as in use by the work just enqueued.
+  pa_status staged_done(hipStream_t stream) {
+    Staging& st = ring[next];
+    next = (next + 1) % kRing;
     PA_HIP(hipEventRecord(st.ev, stream));
     st.pending = true;
     return ok();
+  }
+
+  // Copy `bytes` of host data to device `dst` (which has room for `bytes`
+  // rounded up to 16) on `stream`: a small kernel on the stream reads the
+  // pinned buffer, so the data is in place when the stream's next kernel
+  // starts, without a hand-off to a DMA engine.
+  pa_status upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+    const void* staged = nullptr;
+    pa_status r = stage(src, bytes, &staged);
+    if (r != PA_OK) return r;
+    hipError_t e = pa::launch_upload(staged, dst, pa::align_up(bytes, 16), stream);
+    if (e != hipSuccess) return hip_fail(e, "upload launch");
+    return staged_done(stream);
   }
 
   pa_status flush(hipStream_t stream) {
@@ -316,13 +340,19 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32
   pa::DecodePlan plan;
   std::string msg;
   if (pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                            pool->geom.head_dim, decode_tokens_per_part(), &plan, &msg) != pa::kOk)
+                            pool->geom.head_dim, decode_tokens_per_part(), nullptr, 0, &plan,
+                            &msg) != pa::kOk)
     return 0;
   return plan.total_bytes;
 }
 
-pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads, const void* q,
-                    void* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments every decode entry point checks.
+pa_status check_decode_args(const pa_pool* pool, int32_t num_heads, const void* q, const void* out,
+                            const void* ws) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
   if (!pool->has_device()) return fail(PA_ERR_INVALID_ARG, "metadata-only pool has no device memory");
   if (!q || !out || !ws) return fail(PA_ERR_INVALID_ARG, "q, out and ws must be non-NULL");
@@ -333,19 +363,12 @@ pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_h
   if (pool->geom.dtype == PA_DTYPE_BF16 &&
       (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) % 16)
     return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
-  pa::DecodePlan plan;
-  std::string msg;
-  pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                                       pool->geom.head_dim, decode_tokens_per_part(), &plan, &msg);
-  if (s != pa::kOk) return fail(s, msg);
-  if (ws_bytes < plan.total_bytes)
-    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
-                                        " bytes, got " + std::to_string(ws_bytes));
-  hipStream_t st = as_stream(stream);
-  pa_status r = pool->flush(st);
-  if (r != PA_OK) return r;
-  r = pool->upload(plan.meta.data(), plan.meta.size() * sizeof(int32_t), ws, st);
-  if (r != PA_OK) return r;
+  return ok();
+}
+
+// Decode partial kernel (+ merge) over a plan already on its way into `ws`.
+pa_status launch_decode_plan(pa_pool* pool, const pa::DecodePlan& plan, int32_t B, int32_t num_heads,
+                             const void* q, void* out, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   pa::DecodeArgs a{};
   a.k_pool = pool->k;
@@ -383,6 +406,104 @@ pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_h
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return ok();
+}
+
+// Tokens each batch row will have gained after appending one token per
+// entry (a sequence listed twice gains two).
+std::vector<int32_t> step_extra_tokens(const int64_t* seqs, int32_t B) {
+  std::unordered_map<int64_t, int32_t> count;
+  for (int32_t b = 0; b < B; ++b) ++count[seqs[b]];
+  std::vector<int32_t> extra(B);
+  for (int32_t b = 0; b < B; ++b) extra[b] = count[seqs[b]];
+  return extra;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads, const void* q,
+                    void* out, void* ws, size_t ws_bytes, void* stream) {
+  pa_status r = check_decode_args(pool, num_heads, q, out, ws);
+  if (r != PA_OK) return r;
+  pa::DecodePlan plan;
+  std::string msg;
+  pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                                       pool->geom.head_dim, decode_tokens_per_part(), nullptr, 0,
+                                       &plan, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  if (ws_bytes < plan.total_bytes)
+    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
+                                        " bytes, got " + std::to_string(ws_bytes));
+  hipStream_t st = as_stream(stream);
+  r = pool->flush(st);
+  if (r != PA_OK) return r;
+  r = pool->upload(plan.meta.data(), plan.meta.size() * sizeof(int32_t), ws, st);
+  if (r != PA_OK) return r;
+  return launch_decode_plan(pool, plan, B, num_heads, q, out, ws, st);
+}
+
+size_t pa_decode_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32_t B,
+                                      int32_t num_heads) {
+  if (!pool || B <= 0 || !seqs) return 0;
+  std::vector<int32_t> extra = step_extra_tokens(seqs, B);
+  pa::DecodePlan plan;
+  std::string msg;
+  if (pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                            pool->geom.head_dim, decode_tokens_per_part(), extra.data(), B, &plan,
+                            &msg) != pa::kOk)
+    return 0;
+  return plan.total_bytes;
+}
+
+pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
+                         const void* k_new, const void* v_new, const void* q, void* out, void* ws,
+                         size_t ws_bytes, int64_t* slots_out, void* stream) {
+  pa_status r = check_decode_args(pool, num_heads, q, out, ws);
+  if (r != PA_OK) return r;
+  if (!k_new || !v_new) return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+  if (B <= 0 || !seqs) return fail(PA_ERR_INVALID_ARG, "batch must be positive with a non-NULL seqs array");
+  std::string msg;
+  // Size and validate against the lengths after the append, before anything changes.
+  std::vector<int32_t> extra = step_extra_tokens(seqs, B);
+  pa::DecodePlan plan;
+  pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                                       pool->geom.head_dim, decode_tokens_per_part(), extra.data(), B,
+                                       &plan, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  if (ws_bytes < plan.total_bytes)
+    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
+                                        " bytes, got " + std::to_string(ws_bytes));
+  std::vector<int32_t> ones(B, 1);
+  std::vector<int64_t> slots(B);
+  s = pool->meta.append_batch(seqs, ones.data(), B, slots.data(), &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  // Same lengths as the sizing plan, so the same layout and size.
+  s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                            pool->geom.head_dim, decode_tokens_per_part(), nullptr, B, &plan, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  std::memcpy(reinterpret_cast<char*>(plan.meta.data()) + plan.slots_off, slots.data(),
+              sizeof(int64_t) * B);
+  if (slots_out) std::memcpy(slots_out, slots.data(), sizeof(int64_t) * B);
+  hipStream_t st = as_stream(stream);
+  r = pool->flush(st);  // copy-on-write copies of this append come first
+  if (r != PA_OK) return r;
+  const void* staged = nullptr;
+  const size_t bytes = plan.meta.size() * sizeof(int32_t);
+  r = pool->stage(plan.meta.data(), bytes, &staged);
+  if (r != PA_OK) return r;
+  {
+    TimedLaunch t(PA_KERNEL_CACHE, st);
+    hipError_t e = pa::launch_step_prep(
+        pool->geom, staged, ws, pa::align_up(bytes, 16),
+        reinterpret_cast<const int64_t*>(static_cast<const char*>(staged) + plan.slots_off), pool->k,
+        pool->v, k_new, v_new, B, st);
+    t.done();
+    if (e != hipSuccess) return hip_fail(e, "decode step prologue launch");
+  }
+  r = pool->staged_done(st);
+  if (r != PA_OK) return r;
+  return launch_decode_plan(pool, plan, B, num_heads, q, out, ws, st);
 }
 
 size_t pa_prefill_workspace_bytes(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,

@@ -14,6 +14,17 @@ constexpr int kMaxCopiesPerLaunch = 64;
 hipError_t launch_copy_blocks(const PoolGeom& geom, void* k_pool, void* v_pool,
                               const int32_t* src, const int32_t* dst, int n, hipStream_t stream);
 
+// Copy `bytes` (a multiple of 16) from device-visible pinned host memory to
+// device memory with a kernel on `stream`, so the copy is ordered with the
+// stream's kernels without a hand-off to a DMA engine.
+hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t stream);
+
+// One kernel: upload `bytes` of plan (pinned -> device) and store n new K/V
+// rows at `slots` (a device-visible pinned array).
+hipError_t launch_step_prep(const PoolGeom& geom, const void* plan_src, void* plan_dst, size_t bytes,
+                            const int64_t* slots, void* k_pool, void* v_pool, const void* k_new,
+                            const void* v_new, int32_t n, hipStream_t stream);
+
 // Kpool[slot/bs][h][slot%bs][:] = k_new[i][h][:], Vpool[slot/bs][h][:][slot%bs] = v_new[i][h][:].
 hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_pool,
                                     const void* k_new, const void* v_new, const int64_t* slots,

@@ -29,7 +29,8 @@ constexpr int64_t kTargetGroups = 2048;
 
 Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t tokens_per_part,
-                         DecodePlan* plan, std::string* msg) {
+                         const int32_t* extra_tokens, int32_t slot_count, DecodePlan* plan,
+                         std::string* msg) {
   if (B <= 0 || !seqs) {
     *msg = "batch must be positive with a non-NULL seqs array";
     return kInvalidArg;
@@ -40,6 +41,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   }
   const int32_t bs = pool.block_size();
   std::vector<const Sequence*> rows(B);
+  std::vector<int64_t> len(B), nblk(B);
   int64_t total_pages = 0;
   for (int32_t b = 0; b < B; ++b) {
     rows[b] = pool.find(seqs[b]);
@@ -47,11 +49,13 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
       *msg = "unknown sequence: " + std::to_string(seqs[b]);
       return kUnknownSeq;
     }
-    if (rows[b]->length == 0) {
+    len[b] = rows[b]->length + (extra_tokens ? extra_tokens[b] : 0);
+    nblk[b] = ceil_div(len[b], bs);
+    if (len[b] == 0) {
       *msg = "kv_len must be positive (sequence " + std::to_string(seqs[b]) + " is empty)";
       return kInvalidArg;
     }
-    total_pages += static_cast<int64_t>(rows[b]->table.size());
+    total_pages += nblk[b];
   }
 
   // Pages per partition: the largest candidate that still yields enough
@@ -62,7 +66,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   };
   auto groups_for = [&](int32_t ppp) {
     int64_t g = 0;
-    for (int32_t b = 0; b < B; ++b) g += ceil_div(static_cast<int64_t>(rows[b]->table.size()), ppp);
+    for (int32_t b = 0; b < B; ++b) g += ceil_div(nblk[b], ppp);
     return g * num_kv_heads;
   };
   int32_t ppp;
@@ -86,10 +90,10 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   std::vector<int32_t> part_base(B, -1), merge;
   int32_t n_parts = 0;
   for (int32_t b = 0; b < B; ++b) {
-    int32_t nblk = static_cast<int32_t>(rows[b]->table.size());
-    int32_t np = static_cast<int32_t>(ceil_div(nblk, ppp));
+    int32_t nb = static_cast<int32_t>(nblk[b]);
+    int32_t np = static_cast<int32_t>(ceil_div(nb, ppp));
     n_parts_of[b] = np;
-    for (int32_t c = 0; c < np; ++c) items.push_back({b, c, std::min(ppp, nblk - c * ppp)});
+    for (int32_t c = 0; c < np; ++c) items.push_back({b, c, std::min(ppp, nb - c * ppp)});
     if (np > 1) {
       part_base[b] = n_parts;
       n_parts += np;
@@ -115,6 +119,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.work_off = reserve(meta, 2 * items.size());
   p.merge_off = reserve(meta, std::max<size_t>(1, merge.size()));
   p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
+  p.slots_off = reserve(meta, 2 * static_cast<size_t>(std::max(slot_count, 0)));
   int32_t* ctx = at_bytes(meta, p.ctx_off);
   int32_t* toff = at_bytes(meta, p.tbl_off_off);
   int32_t* base = at_bytes(meta, p.base_off);
@@ -124,12 +129,14 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   int32_t* tables = at_bytes(meta, p.tables_off);
   int64_t cursor = 0;
   for (int32_t b = 0; b < B; ++b) {
-    ctx[b] = static_cast<int32_t>(rows[b]->length);
+    ctx[b] = static_cast<int32_t>(len[b]);
     toff[b] = static_cast<int32_t>(cursor);
     base[b] = part_base[b];
     npo[b] = n_parts_of[b];
-    std::copy(rows[b]->table.begin(), rows[b]->table.end(), tables + cursor);
-    cursor += static_cast<int64_t>(rows[b]->table.size());
+    // With extra tokens (sizing only) the pages not allocated yet stay 0.
+    const size_t have = std::min<size_t>(rows[b]->table.size(), static_cast<size_t>(nblk[b]));
+    std::copy(rows[b]->table.begin(), rows[b]->table.begin() + have, tables + cursor);
+    cursor += nblk[b];
   }
   for (size_t i = 0; i < items.size(); ++i) {
     work[2 * i] = items[i].b;

@@ -58,7 +58,7 @@ struct DecodePlan {
   size_t meta_bytes = 0;      // aligned
   size_t part_m_off = 0, part_l_off = 0, part_acc_off = 0, total_bytes = 0;
   size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, work_off = 0, base_off = 0,
-         merge_off = 0, nparts_off = 0;  // byte offsets in the workspace
+         merge_off = 0, nparts_off = 0, slots_off = 0;  // byte offsets in the workspace
   int32_t n_work = 0, n_merge = 0, n_parts = 0, pages_per_part = 0, batch = 0;
   int64_t total_pages = 0;
 };
@@ -66,9 +66,14 @@ struct DecodePlan {
 // Build the decode plan for `seqs`.  Validates the batch (known sequences,
 // non-empty contexts); returns kUnknownSeq / kInvalidArg with msg.
 // `tokens_per_part` = 0 chooses the partition size automatically.
+// `extra_tokens` (nullable, [B]) sizes the plan as if row b had that many
+// more tokens (page ids of not-yet-allocated pages are left 0: such a plan
+// is for sizing only).  `slot_count` reserves an int64 slot array (slots_off)
+// for the caller to fill.
 Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t tokens_per_part,
-                         DecodePlan* plan, std::string* msg);
+                         const int32_t* extra_tokens, int32_t slot_count, DecodePlan* plan,
+                         std::string* msg);
 
 // Kernel arguments of the prefill kernels.
 struct PrefillArgs {

@@ -141,6 +141,20 @@ class DevicePool:
         abi.pa_decode(self.handle, seqs, num_heads, q, out, ws, ws.numel(), self._stream(stream))
         return out
 
+    def decode_step(self, seqs, k_new, v_new, q, out=None, stream=None, ws=None):
+        """Append one token per sequence, store its K/V, decode over the caches.
+
+        Returns ``(out, slots)``."""
+        num_heads = q.shape[1]
+        if out is None:
+            out = _torch().empty_like(q)
+        need = abi.pa_decode_step_workspace_bytes(self.handle, seqs, num_heads) or 256
+        if ws is None:
+            ws = self.workspace(need)
+        slots = abi.pa_decode_step(self.handle, seqs, num_heads, k_new, v_new, q, out, ws, ws.numel(),
+                                   self._stream(stream), slots_out=True)
+        return out, slots
+
     def prefill(self, seqs, q_lens, q, out=None, stream=None, ws=None):
         """Last ``q_lens[b]`` positions of each sequence: ``q`` [sum q_lens, Hq, D]."""
         num_heads = q.shape[1]

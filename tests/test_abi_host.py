@@ -124,6 +124,20 @@ def test_device_calls_on_metadata_only_pool_are_rejected():
     abi.pa_flush_copies(pool.handle, None)
 
 
+def test_decode_step_argument_errors_change_nothing():
+    pool = _meta(16, 4)
+    pool.create(0)
+    pool.append(0, 5)
+    before = (pool.stats(), pool.block_table(0).tolist())
+    with pytest.raises(InvalidArgumentError):
+        abi.pa_decode_step(pool.handle, [0], 2, 256, 256, 256, 256, 256, 1 << 20, None)
+    assert before == (pool.stats(), pool.block_table(0).tolist())
+    h = pool.handle
+    step = abi.pa_decode_step_workspace_bytes(h, [0, 0], 4)
+    assert step >= abi.pa_decode_workspace_bytes(h, [0, 0], 4) > 0
+    assert abi.pa_decode_step_workspace_bytes(h, [5], 4) == 0
+
+
 def test_workspace_queries():
     pool = _meta(64, 4)
     for s, n in enumerate([3, 17, 40]):

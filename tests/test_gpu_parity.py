@@ -15,7 +15,7 @@ import pytest
 import oracle
 from synth import (append_stream, decode_queries, gqa_decode, heavy_tail, logical_kv,
                    long_decode, prefill_queries, prefix_prefill, tiny_fp32)
-from synth.workloads import Workload, to_f64
+from synth.workloads import Workload, bf16_round, to_f64
 
 from gpu_support import (BF16_TOL, F32_TOL, assert_close, build_device_pool, expected_decode, log,
                          to_device, to_host_f64, tol)
@@ -168,6 +168,70 @@ def test_decode_batch_with_duplicates_and_shared_prefix():
     for i in range(4):
         assert_close(got[i], want[i], *BF16_TOL, what=f"row {i}")
     assert (got[0] == got[2]).all()
+
+
+@pytest.mark.parametrize("shape", [(32, 8, 128, 16), (16, 16, 64, 32), (4, 2, 8, 4)],
+                         ids=["G4-D128-bs16", "G1-D64-bs32", "generic-fp32"])
+def test_decode_step_matches_oracle(shape):
+    """Fused step = batched append + cache write + decode, five steps in a
+    row; sequence 3 is a fork of 0, so the first step copies a shared tail."""
+    from paged_kv_cache_block_amd import DevicePool
+    hq, hkv, d, bs = shape
+    dtype = "f32" if d == 8 else "bf16"
+    tol_ = F32_TOL if dtype == "f32" else BF16_TOL
+    nb = 128
+    order = np.random.default_rng(21).permutation(nb).astype(np.int32)
+    pool = DevicePool(nb, bs, hkv, d, dtype=dtype, allocation_order=order)
+    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order)
+    rng = np.random.default_rng(5)
+
+    def draw(shape_):
+        x = rng.standard_normal(shape_).astype(np.float32)
+        return bf16_round(x) if dtype == "bf16" else x
+
+    for s, n in enumerate([37, 15, 200]):
+        pool.create(s)
+        ref.create(s)
+        k, v = draw((n, hkv, d)), draw((n, hkv, d))
+        slots = pool.append(s, n)
+        assert slots.tolist() == ref.append(s, n)
+        pool.write(slots, to_device(k, dtype), to_device(v, dtype))
+        ref.write(slots, to_f64(k, dtype), to_f64(v, dtype))
+    pool.fork(0, 3)
+    ref.fork(0, 3)
+    seqs = [0, 1, 2, 3]
+    for step in range(5):
+        k, v = draw((4, hkv, d)), draw((4, hkv, d))
+        q = draw((4, hq, d))
+        out, slots = pool.decode_step(seqs, to_device(k, dtype), to_device(v, dtype), to_device(q, dtype))
+        want_slots = []
+        for i, s in enumerate(seqs):
+            want_slots += ref.append(s, 1)
+        assert slots.tolist() == want_slots
+        ref.write(want_slots, to_f64(k, dtype), to_f64(v, dtype))
+        got = to_host_f64(out)
+        for i, s in enumerate(seqs):
+            want = oracle.paged_attention(ref, s, to_f64(q[i:i + 1], dtype))[0]
+            assert_close(got[i], want, *tol_, what=f"step {step} seq {s}")
+    for s in seqs:
+        assert pool.block_table(s).tolist() == ref.tables[s]
+    assert [pool.refcount(b) for b in range(nb)] == ref.refs.tolist()
+
+
+def test_decode_step_small_workspace_changes_nothing():
+    from paged_kv_cache_block_amd.abi import InvalidArgumentError
+    wl = _decode_case([10, 20], 8, 2, 64, 16)
+    pool, _ = build_device_pool(wl)
+    before = (pool.stats(), pool.block_table(0).tolist(), pool.seq_len(1))
+    k = torch.zeros(2, 2, 64, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    from paged_kv_cache_block_amd import abi
+    need = abi.pa_decode_step_workspace_bytes(pool.handle, [0, 1], 8)
+    assert need >= 256
+    with pytest.raises(InvalidArgumentError):
+        abi.pa_decode_step(pool.handle, [0, 1], 8, k, k, q, torch.empty_like(q), ws, need - 1, None)
+    assert before == (pool.stats(), pool.block_table(0).tolist(), pool.seq_len(1))
 
 
 def test_copy_on_write_on_device():
