@@ -399,7 +399,7 @@ pa_status launch_decode_plan(pa_pool* pool, const pa::DecodePlan& plan, int32_t 
     t.done();
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
-  if (a.n_merge > 0 && pa::pick_decode_kernel(pool->geom, a.group) != pa::DecodeKernel::kGeneric) {
+  if (a.n_merge > 0 && pa::decode_needs_merge_kernel(pool->geom, a.group)) {
     TimedLaunch t(PA_KERNEL_MERGE, st);
     hipError_t e = pa::launch_decode_merge(pool->geom, a, st);
     t.done();

@@ -430,9 +430,12 @@ hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& a, hipS
   return hipGetLastError();
 }
 
+bool decode_needs_merge_kernel(const PoolGeom& geom, int32_t group) {
+  return pick_decode_kernel(geom, group) != DecodeKernel::kGeneric;  // the generic kernel never splits
+}
+
 hipError_t launch_decode_merge(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream) {
-  if (a.n_merge == 0 || pick_decode_kernel(geom, a.group) == DecodeKernel::kGeneric)
-    return hipSuccess;
+  if (a.n_merge == 0 || !decode_needs_merge_kernel(geom, a.group)) return hipSuccess;
   const dim3 grid(a.n_merge * a.num_heads);
   if (geom.head_dim == 128)
     hipLaunchKernelGGL((decode_merge<128, uint16_t>), grid, dim3(256), 0, stream, a);

@@ -37,6 +37,9 @@ DecodeKernel pick_decode_kernel(const PoolGeom& geom, int32_t group);
 // Decode: partial kernel, then (if any sequence was split) the merge.
 hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_merge(const PoolGeom& geom, const DecodeArgs& args, hipStream_t stream);
+// Whether split sequences need the separate merge kernel (false when the
+// partial kernel merges in its last workgroup, or never splits).
+bool decode_needs_merge_kernel(const PoolGeom& geom, int32_t group);
 
 // Prefill (chunked, causal).
 hipError_t launch_prefill(const PoolGeom& geom, const PrefillArgs& args, hipStream_t stream);
