@@ -15,7 +15,8 @@ Sources (the pages, cited by title and section):
   ownership mechanics).
 * vladkulikov.com course notebook "Модуль 10. KV-кэши и эффективный инференс"
   -- ``PagedKVPool`` (preflighted multi-token append, share_prefix, release,
-  fill accounting, ``validate``) and its embedded reference contract.
+  fill accounting, ``validate``) and its embedded reference contract; its
+  KV-compression experiment (per-row absmax codes, ``fake_quantize_rows``).
 * docs.rs ferrum-kv 0.4.0 ``src/attention.rs`` -- ``paged_attention``
   (GQA head grouping, 1/sqrt(head_dim) scale, bottom-right causal mask).
 * CMU 11-667 lecture 19 ``infer_world.py``, section 3 "online softmax and
@@ -26,6 +27,8 @@ Modules:
 
 * :mod:`oracle.pool` -- the pool model (integer bookkeeping, exact) with its
   own float64 K/V storage.
+* :mod:`oracle.quant` -- per-row absmax quantisation of K/V rows (codes,
+  fp32 scales, read-back values); a ``Pool(quant_bits=8)`` stores through it.
 * :mod:`oracle.attention` -- the attention definition, its online-softmax
   restatement, the log-sum-exp merge of partial results and a pure-Python
   brute force for tiny inputs.
@@ -36,6 +39,14 @@ Parity status: every function here is pinned by ``-m "not gpu"`` tests
 """
 
 from .pool import Pool, OutOfBlocks, UnknownSequence, SequenceExists
+from .quant import (
+    code_limit,
+    quantize_rows,
+    stored_scale,
+    dequantize_rows,
+    fake_quantize_rows,
+    packed_bytes,
+)
 from .attention import (
     attention,
     paged_attention,
@@ -58,4 +69,10 @@ __all__ = [
     "brute_force_attention",
     "partial_attention",
     "merge_partials",
+    "code_limit",
+    "quantize_rows",
+    "stored_scale",
+    "dequantize_rows",
+    "fake_quantize_rows",
+    "packed_bytes",
 ]

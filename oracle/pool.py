@@ -48,6 +48,8 @@ import math
 
 import numpy as np
 
+from .quant import code_limit, dequantize_rows, quantize_rows, stored_scale
+
 
 class OutOfBlocks(MemoryError):
     """The preflight found fewer free blocks than the operation needs."""
@@ -81,7 +83,7 @@ class Pool:
     """Fixed pool of physical KV blocks shared by refcounted block tables."""
 
     def __init__(self, num_blocks, block_size, num_kv_heads=1, head_dim=1,
-                 allocation_order=None, store_values=True):
+                 allocation_order=None, store_values=True, quant_bits=None):
         self.num_blocks = _positive_int(num_blocks, "num_blocks")
         self.block_size = _positive_int(block_size, "block_size")
         self.num_kv_heads = _positive_int(num_kv_heads, "num_kv_heads")
@@ -110,6 +112,18 @@ class Pool:
             shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
             self.K = np.zeros(shape, dtype=np.float64)
             self.V = np.zeros(shape, dtype=np.float64)
+        # Quantised storage (oracle.quant): integer codes and the fp32 scale
+        # of every (slot, head) row; K / V then hold the values read back.
+        self.quant_bits = None
+        if quant_bits is not None:
+            if not self.store_values:
+                raise ValueError("quant_bits needs store_values")
+            self.quant_bits = int(quant_bits)
+            code_limit(self.quant_bits)
+            self.Kc = np.zeros(shape, dtype=np.int64)
+            self.Vc = np.zeros(shape, dtype=np.int64)
+            self.Ks = np.ones(shape[:3], dtype=np.float64)
+            self.Vs = np.ones(shape[:3], dtype=np.float64)
 
     # ------------------------------------------------------------ lookups
     def _existing(self, seq):
@@ -191,6 +205,9 @@ class Pool:
                 if self.store_values:
                     self.K[new] = self.K[old]
                     self.V[new] = self.V[old]
+                if self.quant_bits is not None:
+                    for arr in (self.Kc, self.Vc, self.Ks, self.Vs):
+                        arr[new] = arr[old]
                 self.copies.append((old, new))
                 table[-1] = new
                 self._drop_ref(old)
@@ -240,13 +257,25 @@ class Pool:
         return block * self.block_size + offset
 
     def write(self, slots, k, v):
-        """Store rows ``k[i], v[i]`` (each ``[num_kv_heads, head_dim]``) at slots."""
+        """Store rows ``k[i], v[i]`` (each ``[num_kv_heads, head_dim]``) at slots.
+
+        A quantised pool stores the codes and fp32 scales of each head's row
+        and keeps the values they read back as K / V."""
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
         for i, slot in enumerate(slots):
             block, offset = divmod(int(slot), self.block_size)
-            self.K[block, offset] = k[i]
-            self.V[block, offset] = v[i]
+            if self.quant_bits is None:
+                self.K[block, offset] = k[i]
+                self.V[block, offset] = v[i]
+                continue
+            for rows, codes_arr, scale_arr, vals in ((k[i], self.Kc, self.Ks, self.K),
+                                                     (v[i], self.Vc, self.Vs, self.V)):
+                codes, scale = quantize_rows(rows, self.quant_bits)
+                scale = stored_scale(scale)
+                codes_arr[block, offset] = codes
+                scale_arr[block, offset] = scale[:, 0]
+                vals[block, offset] = dequantize_rows(codes, scale)
 
     def gather(self, seq):
         """Live K/V rows in logical order: two arrays ``[len, Hkv, D]``."""
