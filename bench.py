@@ -12,7 +12,8 @@ Printed: one JSON line.  ``value`` = decode KV GB/s over whole steps
 (algorithmic bytes: every cached K and V row once, plus Q, O and the block
 tables; decimal GB).  ``roofline`` covers the decode partial kernel alone,
 timed with HIP events recorded on the stream it is launched on.
-``prefill`` measures the chunked causal prefill of 16 sequences x 512 rows on
+``int8_decode`` repeats the decode steps over int8 pages (codes plus one fp32
+scale per row).  ``prefill`` measures the chunked causal prefill of 16 sequences x 512 rows on
 a shared 4096-token prefix (TFLOP/s on causal FLOPs).  ``cpu_baseline`` times
 the float64 oracle on a bounded sample of the same decode workload.
 """
@@ -47,10 +48,13 @@ def to_device(arr, dtype):
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
 
 
-def build_pool(wl):
+def build_pool(wl, kv=None):
+    """Replay ``wl`` into a DevicePool whose pages hold ``kv`` ("bf16", "f32"
+    or "i8"; default the workload's dtype).  New rows are in the workload's
+    dtype either way (an int8 pool quantises them as it stores them)."""
     from paged_kv_cache_block_amd import DevicePool
     from synth import append_stream
-    pool = DevicePool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, dtype=wl.dtype,
+    pool = DevicePool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, dtype=kv or wl.dtype,
                       allocation_order=wl.allocation_order)
     for op in append_stream(wl):
         if op[0] == "create":
@@ -63,10 +67,12 @@ def build_pool(wl):
     return pool
 
 
-def decode_alg_bytes(lengths, wl):
-    """K and V rows once each, plus Q, O and the block tables."""
+def decode_alg_bytes(lengths, wl, kv_dtype=None):
+    """K and V rows once each, plus Q, O and the block tables.  An int8 row
+    is head_dim code bytes plus its 4-byte fp32 scale."""
     elt = wl.elt_bytes
-    kv = sum(lengths) * wl.num_kv_heads * wl.head_dim * 2 * elt
+    row = wl.head_dim + 4 if kv_dtype == "i8" else wl.head_dim * elt
+    kv = sum(lengths) * wl.num_kv_heads * row * 2
     qo = 2 * len(lengths) * wl.num_heads * wl.head_dim * elt
     tables = sum(-(-n // wl.block_size) for n in lengths) * 4
     return kv + qo + tables
@@ -98,14 +104,14 @@ def recorded_traffic(name):
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
-def run_decode(args):
+def run_decode(args, kv="bf16"):
     import torch
     from paged_kv_cache_block_amd import abi
     from synth import decode_queries, gqa_decode
 
     wl = gqa_decode()
-    log("building the decode workload (32 x U[1,8192], 32/8 heads, d 128, bf16, bs 16)")
-    pool = build_pool(wl)
+    log(f"building the decode workload (32 x U[1,8192], 32/8 heads, d 128, {kv} pages, bs 16)")
+    pool = build_pool(wl, kv)
     seqs = list(wl.decode_seqs)
     B = len(seqs)
     q = to_device(decode_queries(wl), wl.dtype)
@@ -140,7 +146,7 @@ def run_decode(args):
     for i in range(args.warmup, total_steps):
         step(i)
         lengths += 1
-        alg.append(decode_alg_bytes(lengths, wl))
+        alg.append(decode_alg_bytes(lengths, wl, kv))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     abi.pa_timing_enable(False)
@@ -164,12 +170,13 @@ def run_decode(args):
         "sum_len": int(lengths.sum()),
     }
     achieved = alg_per_step / (kernel_ms * 1e-3) / 1e9
-    traffic = recorded_traffic("decode_gqa_mfma__gqa_decode")
+    kernel = "decode_q8_mfma" if kv == "i8" else "decode_gqa_mfma"
+    traffic = recorded_traffic(f"{kernel}__gqa_decode")
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                           "traffic": None if traffic is None else round(traffic / 1e9, 4),
                           "traffic_unit": "GB per launch",
-                          "kernel": "decode_gqa_mfma<128,16>",
+                          "kernel": f"{kernel}<128,16>",
                           "decode_plus_merge_GBs": round(alg_per_step / ((kernel_ms + merge_ms) * 1e-3) / 1e9, 1)}
     pool.close()
     return wl, result
@@ -264,6 +271,7 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--prefill-warmup", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-int8", action="store_true", help="skip the int8-page decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -316,6 +324,18 @@ def main():
                                         "alg_bytes_per_step", "kernel_launches", "sum_len")},
         "roofline": dec["roofline"],
     }
+    if not args.no_int8:
+        _, q8 = run_decode(args, kv="i8")
+        line["int8_decode"] = {
+            "workload": "the same decode steps over int8 K/V pages (one fp32 scale per token and "
+                        "KV head row; bf16 q, out and new rows)",
+            "ms_per_step": round(q8["ms_per_step"], 5),
+            "tokens_per_s": round(q8["tokens_per_s"], 1),
+            "kv_GBs_step": round(q8["value"], 2),
+            "decode": {k: q8[k] for k in ("decode_kernel_us", "merge_kernel_us", "cache_kernel_us",
+                                           "alg_bytes_per_step", "kernel_launches", "sum_len")},
+            "roofline": q8["roofline"],
+        }
     if not args.no_prefill:
         line["prefill"] = run_prefill(args)
     if not args.no_cpu_baseline:

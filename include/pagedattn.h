@@ -14,6 +14,9 @@
  *               PagedKvCacheManager::write_kv as its caller uses it.
  *   [lecture19] CMU 11-667 lecture 19 infer_world.py, section 3 (online
  *               softmax statistics, tiled attention).
+ *   [KVquant]   vladkulikov.com notebook "Модуль 10", the KV-compression
+ *               experiment (per-row absmax codes, fake_quantize_rows, and
+ *               the packed size of codes plus one fp32 scale per row).
  *
  * Conventions for every call
  *   - Sequence ids are arbitrary int64 values chosen by the caller.
@@ -47,7 +50,25 @@
  *   q / out for prefill  [sum(q_lens)][num_heads][head_dim] (sequence-major,
  *                        [ferrum] "[q_tokens, num_heads, head_dim]")
  *   k_new / v_new        [n][num_kv_heads][head_dim]
- *   q, out, k_new and v_new use the pool dtype; accumulation is fp32.
+ *   q, out, k_new and v_new use the pool dtype (bf16 for PA_DTYPE_I8);
+ *   accumulation is fp32.
+ *
+ * PA_DTYPE_I8 pools ([KVquant]) store each (token, KV head) row of K and of
+ * V as head_dim int8 codes plus one fp32 scale; the row reads back as
+ * code * scale.  The cache writes derive them from the bf16 row x, in
+ * float64: scale = max|x| / 127 (1 for an all-zero row), code =
+ * x / scale rounded to nearest, ties to even, clipped to [-127, 127]; the
+ * stored scale is that float64 value rounded to fp32.  Requires block_size
+ * and head_dim to be multiples of 16.  One page (block, KV head) of either
+ * pool is page_bytes = block_size * head_dim + 4 * block_size bytes:
+ *   K page  codes [block_size][head_dim] row-major, then scales [block_size]
+ *   V page  codes in MFMA operand order, then scales [block_size]: the code
+ *           of token t, dim d sits at byte
+ *             (t / 16) * 16 * head_dim + ((t % 16) / 4 * 16 + d % 16) *
+ *             (head_dim / 4) + (d / 16) * 4 + t % 4
+ *           (per 16-token tile: for every group of 4 tokens and every d % 16,
+ *           the head_dim / 16 runs of 4 tokens are contiguous).
+ *   pool bytes = num_blocks * num_kv_heads * page_bytes (each of K, V).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -70,7 +91,11 @@ typedef enum {
   PA_ERR_DEVICE = -5         /* a HIP call failed (message in pa_last_error) */
 } pa_status;
 
-typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+typedef enum {
+  PA_DTYPE_F32 = 0,  /* fp32 K/V, q, out */
+  PA_DTYPE_BF16 = 1, /* bf16 K/V, q, out */
+  PA_DTYPE_I8 = 2    /* int8 K/V codes + fp32 row scales; bf16 q, out, new rows */
+} pa_dtype;
 
 typedef struct {
   int32_t num_blocks;   /* physical blocks in the pool, > 0 */
@@ -94,8 +119,10 @@ typedef struct {
 /* ---------------------------------------------------------------- pool --- */
 
 /* Bytes of ONE of the K / V pools for `desc`:
- * num_blocks * num_kv_heads * block_size * head_dim * element size.
- * Returns 0 for an invalid descriptor. */
+ * num_blocks * num_kv_heads * block_size * head_dim * element size, or for
+ * PA_DTYPE_I8 num_blocks * num_kv_heads * (block_size * head_dim +
+ * 4 * block_size).  Returns 0 for an invalid descriptor (including an I8
+ * descriptor whose block_size or head_dim is not a multiple of 16). */
 size_t pa_pool_bytes(const pa_pool_desc* desc);
 
 /* Create a pool over caller-allocated device pools ([KVPool] physical_pool).
@@ -181,6 +208,8 @@ pa_status pa_flush_copies(pa_pool* pool, void* stream);
  *   Kpool[slot / bs][h][slot % bs][:] = k_new[i][h][:]
  *   Vpool[slot / bs][h][:][slot % bs] = v_new[i][h][:]   for i < n, every h.
  * k_new, v_new: device [n][num_kv_heads][head_dim]; slots: device int64 [n].
+ * An I8 pool stores each row's codes and scale instead ([KVquant]; the
+ * layout and rounding are in the header comment).
  * A slot outside [0, num_blocks * block_size) is skipped.  Two rows naming
  * one slot race.  Pending copies are flushed first on `stream`.
  * Errors: PA_ERR_INVALID_ARG (NULL pointers with n > 0, n < 0,
@@ -207,6 +236,7 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32
  * Long sequences are split into page ranges whose partial (max, sum, acc)
  * are merged by log-sum-exp ([lecture19] online_softmax_stats applied
  * across ranges).
+ * On an I8 pool K_j and V_j are the rows read back (code * scale).
  * seqs: host [B] live ids (duplicates allowed); q, out: device
  *   [B][num_heads][head_dim] in the pool dtype; ws: device, at least
  *   pa_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by the

@@ -29,8 +29,11 @@ CXX_SOURCES = ["abi.cpp", "pool.cpp", "plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 instructions are disabled for every device compile.
-HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-ffast-math", "-fno-finite-math-only"]
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Fast math for the attention kernels.  The cache writes stay IEEE: the int8
+# codes are decided by a float64 division and rounding that must be exact.
+FAST_MATH = ["-ffast-math", "-fno-finite-math-only"]
+PRECISE_SOURCES = {"cache.hip"}
 
 
 def _hipcc():
@@ -42,7 +45,8 @@ def _compile(src, build_dir, extra):
     path = os.path.join(CSRC, src)
     obj = os.path.join(build_dir, src + ".o")
     if src.endswith(".hip"):
-        cmd = [_hipcc(), "-c", *COMMON, *HIP_FLAGS, *extra, path, "-o", obj]
+        fp = [] if src in PRECISE_SOURCES else FAST_MATH
+        cmd = [_hipcc(), "-c", *COMMON, *HIP_FLAGS, *fp, *extra, path, "-o", obj]
     else:
         cmd = [_hipcc(), "-c", "-x", "c++", *COMMON, *extra, f"-I{ROCM}/include",
                "-D__HIP_PLATFORM_AMD__", path, "-o", obj]

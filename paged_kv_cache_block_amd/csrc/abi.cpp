@@ -209,8 +209,12 @@ bool desc_ok(const pa_pool_desc* d, std::string* msg) {
     *msg = "head_dim must be at most 512";
     return false;
   }
-  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16) {
-    *msg = "dtype must be PA_DTYPE_F32 or PA_DTYPE_BF16";
+  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16 && d->dtype != PA_DTYPE_I8) {
+    *msg = "dtype must be PA_DTYPE_F32, PA_DTYPE_BF16 or PA_DTYPE_I8";
+    return false;
+  }
+  if (d->dtype == PA_DTYPE_I8 && (d->block_size % 16 || d->head_dim % 16)) {
+    *msg = "PA_DTYPE_I8 needs block_size and head_dim to be multiples of 16";
     return false;
   }
   return true;
@@ -239,8 +243,9 @@ extern "C" {
 size_t pa_pool_bytes(const pa_pool_desc* desc) {
   std::string msg;
   if (!desc_ok(desc, &msg)) return 0;
-  return static_cast<size_t>(desc->num_blocks) * desc->num_kv_heads * desc->block_size *
-         desc->head_dim * (desc->dtype == PA_DTYPE_BF16 ? 2 : 4);
+  const pa::PoolGeom geom{desc->num_blocks, desc->block_size, desc->num_kv_heads, desc->head_dim,
+                         desc->dtype};
+  return static_cast<size_t>(desc->num_blocks) * geom.block_bytes();
 }
 
 pa_status pa_pool_create(const pa_pool_desc* desc, const int32_t* allocation_order, void* k_pool,
@@ -360,7 +365,7 @@ pa_status check_decode_args(const pa_pool* pool, int32_t num_heads, const void* 
     return fail(PA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   if (num_heads <= 0 || num_heads % pool->geom.num_kv_heads)
     return fail(PA_ERR_INVALID_ARG, "num_heads must be a positive multiple of num_kv_heads");
-  if (pool->geom.dtype == PA_DTYPE_BF16 &&
+  if (pool->geom.dtype != PA_DTYPE_F32 &&
       (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) % 16)
     return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   return ok();
@@ -528,7 +533,7 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
     return fail(PA_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   if (num_heads <= 0 || num_heads % pool->geom.num_kv_heads)
     return fail(PA_ERR_INVALID_ARG, "num_heads must be a positive multiple of num_kv_heads");
-  if (pool->geom.dtype == PA_DTYPE_BF16 &&
+  if (pool->geom.dtype != PA_DTYPE_F32 &&
       (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) % 16)
     return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   const int32_t group = num_heads / pool->geom.num_kv_heads;

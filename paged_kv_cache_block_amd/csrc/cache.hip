@@ -62,6 +62,101 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// ---------------------------------------------------------- int8 pages ---
+// Per-row absmax quantisation (vladkulikov.com notebook "Модуль 10", the
+// KV-compression experiment): scale = max|x| / 127 (1 for a zero row), code =
+// x / scale rounded to nearest even and clipped to [-127, 127], decided in
+// float64; the page keeps the scale rounded to fp32.  This file is compiled
+// without fast math, so the float64 division and rounding are the IEEE
+// operations.
+__device__ __forceinline__ int8_t q8_code(float x, double scale) {
+  const double c = rint(static_cast<double>(x) / scale);
+  return static_cast<int8_t>(static_cast<int>(fmin(fmax(c, -127.0), 127.0)));
+}
+
+__device__ __forceinline__ double q8_scale(float absmax) {
+  const double s = static_cast<double>(absmax) / 127.0;
+  return s == 0.0 ? 1.0 : s;
+}
+
+// One wave quantises one (row, head): K codes row-major, V codes in operand
+// order, then the two fp32 scales.  D <= 512 (8 values per lane).
+__device__ __forceinline__ void q8_store_row_head(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_row,
+                                                  const uint16_t* v_row, int64_t blk, int32_t off,
+                                                  int32_t h, int32_t hkv, int32_t bs, int32_t dim, int lane) {
+  float kx[8], vx[8];
+  float kmax = 0.f, vmax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int d = lane + 64 * k;
+    kx[k] = d < dim ? bf16_to_f32(k_row[d]) : 0.f;
+    vx[k] = d < dim ? bf16_to_f32(v_row[d]) : 0.f;
+    kmax = fmaxf(kmax, fabsf(kx[k]));
+    vmax = fmaxf(vmax, fabsf(vx[k]));
+  }
+  kmax = wave_max(kmax);
+  vmax = wave_max(vmax);
+  const double ks = q8_scale(kmax), vs = q8_scale(vmax);
+  const size_t page_bytes = static_cast<size_t>(bs) * dim + 4 * static_cast<size_t>(bs);
+  uint8_t* kp = k_pool + (blk * hkv + h) * page_bytes;
+  uint8_t* vp = v_pool + (blk * hkv + h) * page_bytes;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int d = lane + 64 * k;
+    if (d < dim) {
+      kp[static_cast<size_t>(off) * dim + d] = static_cast<uint8_t>(q8_code(kx[k], ks));
+      vp[q8_v_offset(off, d, dim)] = static_cast<uint8_t>(q8_code(vx[k], vs));
+    }
+  }
+  if (lane == 0) {
+    reinterpret_cast<float*>(kp + static_cast<size_t>(bs) * dim)[off] = static_cast<float>(ks);
+    reinterpret_cast<float*>(vp + static_cast<size_t>(bs) * dim)[off] = static_cast<float>(vs);
+  }
+}
+
+// reshape_and_cache for int8 pools: one wave per (row i, head h).
+__global__ __launch_bounds__(256) void reshape_and_cache_q8(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slots, int64_t n, int32_t hkv,
+    int32_t bs, int32_t dim, int64_t num_slots) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = n * hkv;
+  for (int64_t rh = blockIdx.x * 4ll + (threadIdx.x >> 6); rh < rows; rh += gridDim.x * 4ll) {
+    const int64_t i = rh / hkv;
+    const int32_t h = static_cast<int32_t>(rh - i * hkv);
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / bs;
+    q8_store_row_head(k_pool, v_pool, k_new + rh * dim, v_new + rh * dim, blk,
+                      static_cast<int32_t>(slot - blk * bs), h, hkv, bs, dim, lane);
+  }
+}
+
+// Decode-step prologue for int8 pools: blocks [0, nu) copy the plan, the
+// others quantise and store the new rows (one wave per (row, head)).
+__global__ __launch_bounds__(256) void step_prep_q8(
+    const uint4* __restrict__ plan_src, uint4* __restrict__ plan_dst, int64_t n16, int nu,
+    const int64_t* __restrict__ slots, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int64_t n, int32_t hkv,
+    int32_t bs, int32_t dim, int64_t num_slots) {
+  if (static_cast<int>(blockIdx.x) < nu) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n16; i += nu * 256ll) plan_dst[i] = plan_src[i];
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = n * hkv;
+  const int64_t stride = (gridDim.x - nu) * 4ll;
+  for (int64_t rh = (blockIdx.x - nu) * 4ll + (threadIdx.x >> 6); rh < rows; rh += stride) {
+    const int64_t i = rh / hkv;
+    const int32_t h = static_cast<int32_t>(rh - i * hkv);
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / bs;
+    q8_store_row_head(k_pool, v_pool, k_new + rh * dim, v_new + rh * dim, blk,
+                      static_cast<int32_t>(slot - blk * bs), h, hkv, bs, dim, lane);
+  }
+}
+
 __global__ __launch_bounds__(256) void upload_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                      int64_t n16) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n16; i += gridDim.x * 256ll) dst[i] = src[i];
@@ -146,6 +241,15 @@ hipError_t launch_step_prep(const PoolGeom& geom, const void* plan_src, void* pl
   const int64_t total = static_cast<int64_t>(n) * geom.num_kv_heads * geom.head_dim;
   const int nc = grid_for(total, 256, 4096);
   const int64_t num_slots = static_cast<int64_t>(geom.num_blocks) * geom.block_size;
+  if (geom.q8()) {
+    const int nq = grid_for(static_cast<int64_t>(n) * geom.num_kv_heads, 4, 4096);
+    hipLaunchKernelGGL(step_prep_q8, dim3(nu + nq), dim3(256), 0, stream,
+                       static_cast<const uint4*>(plan_src), static_cast<uint4*>(plan_dst), n16, nu, slots,
+                       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       static_cast<int64_t>(n), geom.num_kv_heads, geom.block_size, geom.head_dim, num_slots);
+    return hipGetLastError();
+  }
   const dim3 grid(nu + nc);
   if (geom.dtype == 1)
     hipLaunchKernelGGL(step_prep_kernel<uint16_t>, grid, dim3(256), 0, stream,
@@ -169,7 +273,13 @@ hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_
   const int64_t total = static_cast<int64_t>(n) * geom.num_kv_heads * geom.head_dim;
   const int64_t num_slots = static_cast<int64_t>(geom.num_blocks) * geom.block_size;
   const int grid = grid_for(total, 256, 65536);
-  if (geom.dtype == 1) {
+  if (geom.q8()) {
+    const int gq = grid_for(static_cast<int64_t>(n) * geom.num_kv_heads, 4, 65536);
+    hipLaunchKernelGGL(reshape_and_cache_q8, dim3(gq), dim3(256), 0, stream, static_cast<uint8_t*>(k_pool),
+                       static_cast<uint8_t*>(v_pool), static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), slots, static_cast<int64_t>(n), geom.num_kv_heads,
+                       geom.block_size, geom.head_dim, num_slots);
+  } else if (geom.dtype == 1) {
     hipLaunchKernelGGL(reshape_and_cache_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
                        static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),

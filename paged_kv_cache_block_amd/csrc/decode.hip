@@ -67,7 +67,9 @@ struct GenericArgs {
   float scale_log2;
 };
 
-template <typename T>
+// Q8: int8 pages (codes + fp32 row scales, q / out bf16); T is the q / out
+// element type.
+template <typename T, bool Q8>
 __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
   extern __shared__ float smem[];
   float* qs = smem;                                            // [D]
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
   const int32_t* table = a.tables + a.tbl_off[b];
   const T* K = static_cast<const T*>(a.k_pool);
   const T* V = static_cast<const T*>(a.v_pool);
+  const size_t q8_page = static_cast<size_t>(BS) * D + 4 * static_cast<size_t>(BS);
   const T* q = static_cast<const T*>(a.q) + (static_cast<size_t>(r) * a.num_heads + h) * D;
   for (int d = lane; d < D; d += 64) qs[d] = Elt<T>::load(q + d);
   __syncthreads();
@@ -107,15 +110,28 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
     if (j < visible) {
       blk = table[j / BS];
       off = j - (j / BS) * BS;
-      const T* kr = K + ((static_cast<size_t>(blk) * Hkv + g) * BS + off) * D;
       float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot += qs[d] * Elt<T>::load(kr + d);
+      if constexpr (Q8) {
+        const uint8_t* kp = static_cast<const uint8_t*>(a.k_pool) + (static_cast<size_t>(blk) * Hkv + g) * q8_page;
+        const int8_t* kr = reinterpret_cast<const int8_t*>(kp) + off * D;
+        for (int d = 0; d < D; ++d) dot += qs[d] * static_cast<float>(kr[d]);
+        dot *= reinterpret_cast<const float*>(kp + BS * D)[off];
+      } else {
+        const T* kr = K + ((static_cast<size_t>(blk) * Hkv + g) * BS + off) * D;
+        for (int d = 0; d < D; ++d) dot += qs[d] * Elt<T>::load(kr + d);
+      }
       s = dot * a.scale_log2;
     }
     const float m_new = fmaxf(m, wave_max(s));  // finite: key c0 is visible
     const float alpha = exp2f(m - m_new);
-    const float p = j < visible ? exp2f(s - m_new) : 0.f;
+    float p = j < visible ? exp2f(s - m_new) : 0.f;
     l = l * alpha + wave_sum(p);
+    if constexpr (Q8) {
+      // The V scale joins the weight: sum_j p_j sv_j cv_j.
+      if (j < visible)
+        p *= reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.v_pool) +
+                                            (static_cast<size_t>(blk) * Hkv + g) * q8_page + BS * D)[off];
+    }
     ps[lane] = p;
     blks[lane] = blk;
     offs[lane] = off;
@@ -125,9 +141,17 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
     for (int k = 0; k < 8; ++k) {
       const int d = lane + 64 * k;
       float x = acc[k] * alpha;
-      if (d < D)
-        for (int jj = 0; jj < nj; ++jj)
-          x += ps[jj] * Elt<T>::load(V + ((static_cast<size_t>(blks[jj]) * Hkv + g) * D + d) * BS + offs[jj]);
+      if (d < D) {
+        if constexpr (Q8) {
+          const int8_t* vb = static_cast<const int8_t*>(a.v_pool);
+          for (int jj = 0; jj < nj; ++jj)
+            x += ps[jj] * static_cast<float>(vb[(static_cast<size_t>(blks[jj]) * Hkv + g) * q8_page +
+                                               q8_v_offset(offs[jj], d, D)]);
+        } else {
+          for (int jj = 0; jj < nj; ++jj)
+            x += ps[jj] * Elt<T>::load(V + ((static_cast<size_t>(blks[jj]) * Hkv + g) * D + d) * BS + offs[jj]);
+        }
+      }
       acc[k] = x;
     }
     m = m_new;
@@ -340,6 +364,216 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_gqa_mfma(DecodeArgs 
   }
 }
 
+// ---------------------------------------------------------- int8 pages ---
+// 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).
+__device__ __forceinline__ s16x4 i8x4_to_bf16x4(uint32_t w) {
+  s16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float f = static_cast<float>(static_cast<int8_t>(w >> (8 * i)));
+    r[i] = static_cast<short>(__float_as_uint(f) >> 16);
+  }
+  return r;
+}
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const s16x4 a = i8x4_to_bf16x4(lo), b = i8x4_to_bf16x4(hi);
+  const short v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, v[i]);
+  return r;
+}
+
+// decode_q8_mfma: decode_gqa_mfma over int8 pages (vladkulikov.com notebook
+// "Модуль 10", KV-compression experiment: a row reads back as code * scale).
+// With codes c and row scales sk / sv:
+//   s_j = (q . ck_j) * sk_j / sqrt(D)        (MFMA on the codes as bf16, exact)
+//   o   = sum_j p_j sv_j cv_j / sum_j p_j     (sv folded into the P operand)
+// The QK contraction runs over a permuted d order: in k-step j lane group grp
+// takes d in [grp * D/4 + 8j, +8), so a lane's K codes of one token are D/4
+// contiguous bytes; the V page's operand order gives the same for V.
+template <int D, int BS>
+__global__ __launch_bounds__(256) PA_DECODE_OCC void decode_q8_mfma(DecodeArgs a) {
+  constexpr int KS = D / 32;   // k-steps of the 16x16x32 QK contraction
+  constexpr int TT = BS / 16;  // 16-token tiles per page
+  constexpr int DT = D / 16;   // 16-wide d tiles of the P.V contraction
+  constexpr int KW = D / 16;   // dwords of K codes per lane and tile (= 2 KS)
+  constexpr int W = kDecodeWaves;
+  constexpr int ROW = D + 4;
+  constexpr int PB = BS * D + 4 * BS;  // page bytes: codes, then fp32 scales
+  __shared__ float s_m[W][16];
+  __shared__ float s_l[W][16];
+  extern __shared__ float s_acc[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n = lane & 15, grp = lane >> 4;
+  const int Hkv = a.num_kv_heads, Hq = a.num_heads, G = a.group;
+  const int wid = blockIdx.x / Hkv, g = blockIdx.x - wid * Hkv;
+  const int b = a.work[2 * wid], c = a.work[2 * wid + 1];
+  const int L = a.ctx_len[b];
+  const int nblk = (L + BS - 1) / BS;
+  const int p0 = c * a.pages_per_part;
+  const int p1 = min(nblk, p0 + a.pages_per_part);
+  const int32_t* table = a.tables + a.tbl_off[b];
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
+
+  bf16x8 qv[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<size_t>(b) * Hq + g * G + n) * D + (D / 4) * grp;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      if (n < G)
+        qv[j] = *reinterpret_cast<const bf16x8*>(qrow + 8 * j);
+      else
+        qv[j] = bf16x8{};
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Page {
+    uint32_t k[TT][KW];  // K codes: token 16tt + n, d in [grp * D/4, +D/4)
+    uint32_t v[TT][DT];  // V codes: d = 16nt + n, tokens 16tt + 4grp .. +4
+    f32x4 ks[TT], vs[TT];  // scales of tokens 16tt + 4grp .. +4
+  };
+
+  auto load_page = [&](int pg, Page& P) {
+    const int blk = uniform(table[pg]);
+    const uint8_t* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
+    const uint8_t* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const uint4* ks = reinterpret_cast<const uint4*>(kp + (16 * tt + n) * D + (D / 4) * grp);
+      const uint4* vs = reinterpret_cast<const uint4*>(vp + 16 * tt * D + (16 * grp + n) * (D / 4));
+#pragma unroll
+      for (int w = 0; w < KW / 4; ++w) {
+        const uint4 x = ks[w];
+        P.k[tt][4 * w] = x.x; P.k[tt][4 * w + 1] = x.y; P.k[tt][4 * w + 2] = x.z; P.k[tt][4 * w + 3] = x.w;
+        const uint4 y = vs[w];
+        P.v[tt][4 * w] = y.x; P.v[tt][4 * w + 1] = y.y; P.v[tt][4 * w + 2] = y.z; P.v[tt][4 * w + 3] = y.w;
+      }
+      P.ks[tt] = *reinterpret_cast<const f32x4*>(kp + BS * D + 4 * (16 * tt + 4 * grp));
+      P.vs[tt] = *reinterpret_cast<const f32x4*>(vp + BS * D + 4 * (16 * tt + 4 * grp));
+    }
+  };
+
+  auto process = [&](int pg, const Page& P) {
+    f32x4 s[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(P.k[tt][2 * j], P.k[tt][2 * j + 1]),
+                                                        qv[j], s[tt], 0, 0, 0);
+    }
+    const bool tail = pg == nblk - 1;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[tt][i] * (P.ks[tt][i] * a.scale_log2);
+        if (tail && pg * BS + 16 * tt + 4 * grp + i >= L) x = -INFINITY;
+        s[tt][i] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    // P enters the P.V contraction as p * sv in two bf16 terms (hi, lo).
+    float psum = 0.f;
+    s16x4 p_hi[TT], p_lo[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = exp2f(s[tt][i] - m_new);
+        psum += e;
+        float w = e * P.vs[tt][i];
+        // An unused slot of the last page may hold any scale bits: weight 0.
+        if (tail && pg * BS + 16 * tt + 4 * grp + i >= L) w = 0.f;
+        const __bf16 hi = static_cast<__bf16>(w);
+        const __bf16 lo = static_cast<__bf16>(w - static_cast<float>(hi));
+        p_hi[tt][i] = __builtin_bit_cast(short, hi);
+        p_lo[tt][i] = __builtin_bit_cast(short, lo);
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) {
+      acc[nt] *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const s16x4 v = i8x4_to_bf16x4(P.v[tt][nt]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_hi[tt], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_lo[tt], acc[nt], 0, 0, 0);
+      }
+    }
+  };
+
+  {
+    Page pa_, pb_;
+    int p = p0 + wave;
+    if (p < p1) load_page(p, pa_);
+    while (p < p1) {
+      load_page(p + W < p1 ? p + W : p, pb_);
+      process(p, pa_);
+      p += W;
+      if (p >= p1) break;
+      load_page(p + W < p1 ? p + W : p, pa_);
+      process(p, pb_);
+      p += W;
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (grp == 0) {
+    s_m[wave][n] = m_run;
+    s_l[wave][n] = l_tot;
+  }
+  if (n < G) {
+    float* dst = s_acc + (wave * G + n) * ROW + 4 * grp;
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt) = acc[nt];
+  }
+  __syncthreads();
+
+  const int base = a.part_base[b];
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int hn = idx / D, d = idx - hn * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][hn]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float e = exp2f(s_m[w][hn] - M);
+      num += e * s_acc[(w * G + hn) * ROW + d];
+      den += e * s_l[w][hn];
+    }
+    const int h = g * G + hn;
+    if (base < 0) {
+      static_cast<uint16_t*>(a.out)[(static_cast<size_t>(b) * Hq + h) * D + d] = f32_to_bf16(num / den);
+    } else {
+      const size_t row = static_cast<size_t>(base + c) * Hq + h;
+      a.part_acc[row * D + d] = num;
+      if (d == 0) {
+        a.part_m[row] = M;
+        a.part_l[row] = den;
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------- merge ---
 template <int D, typename T>
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
@@ -394,12 +628,31 @@ void launch_gqa(const DecodeArgs& a, int groups, hipStream_t stream) {
   hipLaunchKernelGGL((decode_gqa_mfma<D, BS>), dim3(groups), dim3(256), shmem, stream, a);
 }
 
+template <int D, int BS>
+void launch_q8(const DecodeArgs& a, int groups, hipStream_t stream) {
+  const size_t shmem = static_cast<size_t>(kDecodeWaves) * a.group * (D + 4) * sizeof(float);
+  hipLaunchKernelGGL((decode_q8_mfma<D, BS>), dim3(groups), dim3(256), shmem, stream, a);
+}
+
+void launch_generic(const PoolGeom& geom, const GenericArgs& g, dim3 grid, hipStream_t stream) {
+  const size_t shmem = (geom.head_dim + 64) * sizeof(float) + 128 * sizeof(int);
+  if (geom.q8())
+    hipLaunchKernelGGL((attn_generic<uint16_t, true>), grid, dim3(64), shmem, stream, g);
+  else if (geom.dtype == 1)
+    hipLaunchKernelGGL((attn_generic<uint16_t, false>), grid, dim3(64), shmem, stream, g);
+  else
+    hipLaunchKernelGGL((attn_generic<float, false>), grid, dim3(64), shmem, stream, g);
+}
+
 }  // namespace
 
 DecodeKernel pick_decode_kernel(const PoolGeom& geom, int32_t group) {
   const bool d_ok = geom.head_dim == 64 || geom.head_dim == 128;
   const bool bs_ok = geom.block_size == 16 || geom.block_size == 32;
-  if (geom.dtype == 1 && d_ok && bs_ok && group <= 16) return DecodeKernel::kGqaMfma;
+  if (d_ok && bs_ok && group <= 16) {
+    if (geom.dtype == 1) return DecodeKernel::kGqaMfma;
+    if (geom.q8()) return DecodeKernel::kQ8Mfma;
+  }
   return DecodeKernel::kGeneric;
 }
 
@@ -414,16 +667,20 @@ hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& a, hipS
       else launch_gqa<64, 32>(a, groups, stream);
       break;
     }
+    case DecodeKernel::kQ8Mfma: {
+      const int groups = a.n_work * a.num_kv_heads;
+      const int D = geom.head_dim, BS = geom.block_size;
+      if (D == 128 && BS == 16) launch_q8<128, 16>(a, groups, stream);
+      else if (D == 128 && BS == 32) launch_q8<128, 32>(a, groups, stream);
+      else if (D == 64 && BS == 16) launch_q8<64, 16>(a, groups, stream);
+      else launch_q8<64, 32>(a, groups, stream);
+      break;
+    }
     default: {
       GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, nullptr, nullptr,
                     a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,
                     a.scale_log2};
-      const size_t shmem = (geom.head_dim + 64) * sizeof(float) + 128 * sizeof(int);
-      const dim3 grid(a.batch * a.num_heads);
-      if (geom.dtype == 1)
-        hipLaunchKernelGGL(attn_generic<uint16_t>, grid, dim3(64), shmem, stream, g);
-      else
-        hipLaunchKernelGGL(attn_generic<float>, grid, dim3(64), shmem, stream, g);
+      launch_generic(geom, g, dim3(a.batch * a.num_heads), stream);
       break;
     }
   }
@@ -449,12 +706,7 @@ hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hi
   GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, a.q_start,
                 a.row_seq, a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,
                 a.scale_log2};
-  const size_t shmem = (geom.head_dim + 64) * sizeof(float) + 128 * sizeof(int);
-  const dim3 grid(a.n_rows * a.num_heads);
-  if (geom.dtype == 1)
-    hipLaunchKernelGGL(attn_generic<uint16_t>, grid, dim3(64), shmem, stream, g);
-  else
-    hipLaunchKernelGGL(attn_generic<float>, grid, dim3(64), shmem, stream, g);
+  launch_generic(geom, g, dim3(a.n_rows * a.num_heads), stream);
   return hipGetLastError();
 }
 

@@ -49,6 +49,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Byte offset of the code of token t (within its block), dim d, inside an
+// int8 V page of head_dim D: each 16-token tile of a page is stored in the
+// operand order of the P.V MFMA, so that one lane's codes are contiguous.
+__device__ __forceinline__ int q8_v_offset(int t, int d, int D) {
+  return (t >> 4) * 16 * D + (((t & 15) >> 2) * 16 + (d & 15)) * (D >> 2) + (d >> 4) * 4 + (t & 3);
+}
+
 // Uniform value in a scalar register (the compiler cannot always prove it).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -31,7 +31,7 @@ hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_
                                     int32_t n, hipStream_t stream);
 
 // Which decode kernel serves a geometry (for timing labels and tests).
-enum class DecodeKernel { kGqaMfma, kMhaValu, kGeneric };
+enum class DecodeKernel { kGqaMfma, kQ8Mfma, kGeneric };
 DecodeKernel pick_decode_kernel(const PoolGeom& geom, int32_t group);
 
 // Decode: partial kernel, then (if any sequence was split) the merge.

@@ -19,14 +19,20 @@ constexpr int kDecodeWaves = 4;  // waves per decode workgroup
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Geometry of a pool (dtype: 0 = fp32, 1 = bf16).
+// Geometry of a pool.  dtype: 0 = fp32, 1 = bf16, 2 = int8 codes with one
+// fp32 scale per (token, KV head) row (q / out / new rows are then bf16).
 struct PoolGeom {
-  int32_t num_blocks, block_size, num_kv_heads, head_dim, dtype;  // dtype: 0 f32, 1 bf16
-  int32_t elt() const { return dtype == 1 ? 2 : 4; }
+  int32_t num_blocks, block_size, num_kv_heads, head_dim, dtype;
+  bool q8() const { return dtype == 2; }
+  // Element size of q, out, k_new and v_new.
+  int32_t io_elt() const { return dtype == 0 ? 4 : 2; }
   size_t page_elems() const { return static_cast<size_t>(block_size) * head_dim; }
-  size_t block_bytes() const {
-    return static_cast<size_t>(num_kv_heads) * page_elems() * elt();
+  // Bytes of one (block, KV head) page: codes then scales for int8 pools.
+  size_t page_bytes() const {
+    if (q8()) return page_elems() + 4 * static_cast<size_t>(block_size);
+    return page_elems() * (dtype == 1 ? 2 : 4);
   }
+  size_t block_bytes() const { return static_cast<size_t>(num_kv_heads) * page_bytes(); }
 };
 
 

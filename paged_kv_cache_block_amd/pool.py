@@ -12,7 +12,7 @@ import numpy as np
 
 from . import abi
 
-_DTYPES = {"f32": abi.PA_DTYPE_F32, "bf16": abi.PA_DTYPE_BF16}
+_DTYPES = {"f32": abi.PA_DTYPE_F32, "bf16": abi.PA_DTYPE_BF16, "i8": abi.PA_DTYPE_I8}
 
 
 def _torch():
@@ -23,6 +23,10 @@ def _torch():
 class DevicePool:
     """One pool of ``num_blocks`` blocks; K and V live on ``device``.
 
+    ``dtype`` is "bf16", "f32" or "i8" (int8 codes with one fp32 scale per
+    (token, KV head) row; queries, outputs and new rows are then bf16, and
+    ``k`` / ``v`` are raw byte tensors ``[num_blocks, num_kv_heads,
+    page_bytes]`` in the library's int8 page layout).
     With ``metadata_only=True`` no device memory is allocated and only the
     bookkeeping calls work (usable on a machine without a GPU).
     """
@@ -38,13 +42,24 @@ class DevicePool:
         self.handle = None
         if not metadata_only:
             torch = _torch()
-            tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-            shape_k = (num_blocks, num_kv_heads, block_size, head_dim)
-            shape_v = (num_blocks, num_kv_heads, head_dim, block_size)
+            if dtype == "i8":
+                page = block_size * head_dim + 4 * block_size
+                shape_k = shape_v = (num_blocks, num_kv_heads, page)
+                tdt = torch.uint8
+            else:
+                tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+                shape_k = (num_blocks, num_kv_heads, block_size, head_dim)
+                shape_v = (num_blocks, num_kv_heads, head_dim, block_size)
             self.k = torch.zeros(shape_k, dtype=tdt, device=device)
             self.v = torch.zeros(shape_v, dtype=tdt, device=device)
             assert self.k.numel() * self.k.element_size() == abi.pa_pool_bytes(self.desc)
         self.handle = abi.pa_pool_create(self.desc, allocation_order, self.k, self.v)
+
+    @property
+    def io_dtype(self):
+        """torch dtype of queries, outputs and new K/V rows."""
+        torch = _torch()
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
     # ------------------------------------------------------------ lifetime
     def close(self):
@@ -114,7 +129,7 @@ class DevicePool:
         if not torch.is_tensor(slots) or slots.device.type != "cuda":
             slots = torch.as_tensor(np.asarray(slots, dtype=np.int64)).to(self.k.device, non_blocking=False)
         n = int(slots.numel())
-        assert k_new.shape == (n, self.num_kv_heads, self.head_dim) and k_new.dtype == self.k.dtype
+        assert k_new.shape == (n, self.num_kv_heads, self.head_dim) and k_new.dtype == self.io_dtype
         assert v_new.shape == k_new.shape and v_new.dtype == k_new.dtype
         assert k_new.is_contiguous() and v_new.is_contiguous() and slots.dtype == torch.int64
         abi.pa_reshape_and_cache(self.handle, k_new, v_new, slots, n, self._stream(stream))

@@ -10,6 +10,8 @@ import os
 import re
 
 import numpy as np
+
+import oracle
 import pytest
 
 from oracle import Pool
@@ -108,6 +110,23 @@ def test_bad_descriptors_and_orders():
         DevicePool(4, 4, 1, 1024, metadata_only=True)
     assert abi.pa_pool_bytes(abi.make_desc(10, 16, 8, 128, abi.PA_DTYPE_BF16)) == 10 * 16 * 8 * 128 * 2
     assert abi.pa_pool_bytes(abi.make_desc(10, 16, 8, 0, abi.PA_DTYPE_BF16)) == 0
+
+
+def test_int8_pool_descriptor():
+    # Codes plus one fp32 scale per row: the packed size of the notebook's
+    # KV-compression experiment (2 n d + 2 n 4 bytes for n rows of K and V).
+    per_pool = abi.pa_pool_bytes(abi.make_desc(10, 16, 8, 128, abi.PA_DTYPE_I8))
+    assert per_pool == 10 * 8 * (16 * 128 + 16 * 4)
+    n_rows = 10 * 16 * 8
+    assert 2 * per_pool == oracle.packed_bytes(n_rows, 128, 8)
+    for bs, d in ((8, 128), (16, 40), (4, 8)):
+        assert abi.pa_pool_bytes(abi.make_desc(10, bs, 8, d, abi.PA_DTYPE_I8)) == 0
+        with pytest.raises(InvalidArgumentError):
+            DevicePool(10, bs, 1, d, dtype="i8", metadata_only=True)
+    assert abi.pa_pool_bytes(abi.make_desc(10, 16, 8, 128, 3)) == 0
+    pool = DevicePool(8, 16, 2, 64, dtype="i8", metadata_only=True)
+    pool.create(1)
+    assert pool.append(1, 20).tolist() == list(range(32))[:20]
 
 
 def test_device_calls_on_metadata_only_pool_are_rejected():

@@ -1,0 +1,297 @@
+"""GPU parity of int8 KV pages (codes + one fp32 scale per (token, KV head)
+row) against the oracle's quantised pool.
+
+Source of the quantisation: vladkulikov.com notebook "Модуль 10", the
+KV-compression experiment; the oracle (oracle.quant) decides codes in
+float64 and keeps the scale as fp32, and so do the cache-write kernels.
+
+Bar: codes and scales written by the cache kernels are bit-exact against the
+oracle; attention over int8 pages is within the bf16 tolerance (2e-3, 1e-2)
+of the float64 oracle attention over the rows read back (code * scale).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import append_stream, decode_queries, gqa_decode, logical_kv, prefill_queries
+from synth.workloads import Workload, bf16_round, to_f64
+
+from gpu_support import BF16_TOL, assert_close, log, to_device, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_block_amd import abi
+    abi.load()
+
+
+# ------------------------------------------------------------ helpers
+def _v_index(bs, d):
+    """Byte of the code of (token t, dim j) in an int8 V page, as the header
+    documents it: (t/16)*16*D + ((t%16)/4*16 + j%16)*(D/4) + (j/16)*4 + t%4."""
+    t = np.arange(bs)[:, None]
+    j = np.arange(d)[None, :]
+    return (t // 16) * 16 * d + ((t % 16) // 4 * 16 + j % 16) * (d // 4) + (j // 16) * 4 + t % 4
+
+
+def _device_codes(pool):
+    """(K codes, K scales, V codes, V scales) of the whole device pool, in the
+    oracle's [block][slot][head][dim] order (views where possible)."""
+    bs, d = pool.block_size, pool.head_dim
+
+    def split(raw):
+        codes = np.ascontiguousarray(raw[..., :bs * d]).view(np.int8)     # [N, Hkv, bs*D]
+        scales = np.ascontiguousarray(raw[..., bs * d:]).view(np.float32)  # [N, Hkv, bs]
+        return codes, scales.transpose(0, 2, 1)
+
+    kcodes, kscales = split(pool.k.cpu().numpy())
+    vcodes, vscales = split(pool.v.cpu().numpy())
+    kc = kcodes.reshape(kcodes.shape[0], kcodes.shape[1], bs, d).transpose(0, 2, 1, 3)
+    vc = vcodes[..., _v_index(bs, d)].transpose(0, 2, 1, 3)
+    return kc, kscales, vc, vscales
+
+
+def _replay(wl, mirror=True):
+    """Build an i8 DevicePool from ``wl``'s op list and (``mirror``) the
+    oracle's quantised pool from the same rows."""
+    from paged_kv_cache_block_amd import DevicePool
+    pool = DevicePool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, dtype="i8",
+                      allocation_order=wl.allocation_order)
+    ref = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
+                      allocation_order=wl.allocation_order, quant_bits=8) if mirror else None
+    for op in append_stream(wl):
+        if op[0] == "create":
+            pool.create(op[1])
+            if ref:
+                ref.create(op[1])
+        elif op[0] == "share":
+            pool.share(*op[1:])
+            if ref:
+                ref.share(*op[1:])
+        else:
+            _, s, n, k, v = op
+            slots = pool.append(s, n)
+            pool.write(slots, to_device(k, "bf16"), to_device(v, "bf16"))
+            if ref:
+                assert slots.tolist() == ref.append(s, n)
+                ref.write(slots, to_f64(k, "bf16"), to_f64(v, "bf16"))
+    torch.cuda.synchronize()
+    return pool, ref
+
+
+def _case(lengths, hq, hkv, d, bs, seed=5):
+    nb = int(sum(-(-n // bs) for n in lengths) + 7)
+    order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    ops = []
+    for i, n in enumerate(lengths):
+        ops += [("create", i), ("append", i, int(n))]
+    return Workload("q8_case", seed, "bf16", nb, bs, hq, hkv, d, order, ops,
+                    decode_seqs=list(range(len(lengths))))
+
+
+def _check_codes(pool, ref, seqs):
+    kc, ks, vc, vs = _device_codes(pool)
+    for s in seqs:
+        n = ref.lengths[s]
+        blk = np.asarray(ref.tables[s])[np.arange(n) // ref.block_size]
+        off = np.arange(n) % ref.block_size
+        np.testing.assert_array_equal(kc[blk, off], ref.Kc[blk, off], err_msg=f"K codes of seq {s}")
+        np.testing.assert_array_equal(vc[blk, off], ref.Vc[blk, off], err_msg=f"V codes of seq {s}")
+        np.testing.assert_array_equal(ks[blk, off], ref.Ks[blk, off].astype(np.float32))
+        np.testing.assert_array_equal(vs[blk, off], ref.Vs[blk, off].astype(np.float32))
+
+
+# ------------------------------------------------------------ cache writes
+def test_q8_cache_write_codes_and_scales_bit_exact():
+    wl = _case([1, 15, 16, 17, 200], 32, 8, 128, 16)
+    log("q8 codes: build")
+    pool, ref = _replay(wl)
+    # Rows with zeros (scale 1), ties and extremes: whole-number bf16 values
+    # with absmax 127 make x / scale exact, so half-way codes occur.
+    pool.create(9)
+    ref.create(9)
+    rows = np.zeros((3, 8, 128), np.float32)
+    rows[1] = np.linspace(-127, 127, 128, dtype=np.float32)[None, :]
+    rows[2, :, :4] = [127.0, -63.5, 0.5, 2.5]
+    k = bf16_round(rows)
+    v = bf16_round(rows[::-1].copy())
+    slots = pool.append(9, 3)
+    assert slots.tolist() == ref.append(9, 3)
+    pool.write(slots, to_device(k, "bf16"), to_device(v, "bf16"))
+    ref.write(slots, to_f64(k, "bf16"), to_f64(v, "bf16"))
+    torch.cuda.synchronize()
+    assert ref.Ks[slots[0] // 16, slots[0] % 16].tolist() == [1.0] * 8
+    assert ref.Kc[slots[2] // 16, slots[2] % 16, 0, :4].tolist() == [127, -64, 0, 2]
+    _check_codes(pool, ref, [0, 1, 2, 3, 4, 9])
+
+
+def test_q8_pool_bytes_and_copy_on_write():
+    from paged_kv_cache_block_amd import DevicePool, abi
+    assert abi.pa_pool_bytes(abi.make_desc(10, 16, 2, 64, abi.PA_DTYPE_I8)) == 10 * 2 * (16 * 64 + 64)
+    rng = np.random.default_rng(3)
+    pool = DevicePool(16, 16, 2, 64, dtype="i8", allocation_order=rng.permutation(16))
+    k = torch.randn(21, 2, 64, dtype=torch.bfloat16, device="cuda")
+    pool.create(0)
+    pool.write(pool.append(0, 21), k, -k)
+    pool.fork(0, 1)
+    s1 = pool.append(1, 1)             # COW of the shared partial tail (5 live rows)
+    (src, dst), = pool.pending_copies()
+    src_bytes = pool.k[src].clone(), pool.v[src].clone()
+    pool.write(s1, k[:1], k[:1])
+    torch.cuda.synchronize()
+    assert pool.pending_copies() == []
+    kc, ks, vc, vs = _device_codes(pool)
+    for a in (kc, ks, vc, vs):
+        np.testing.assert_array_equal(a[dst, :5], a[src, :5])
+    assert torch.equal(pool.k[src], src_bytes[0]) and torch.equal(pool.v[src], src_bytes[1])
+
+
+# ------------------------------------------------------------ decode
+Q8_DECODE_CASES = [
+    # lengths, Hq, Hkv, D, bs
+    ([1, 2, 15, 16, 17, 33, 200, 700], 32, 8, 128, 16),     # GQA 4, ragged tails
+    ([1, 64, 129, 1000, 4100], 64, 8, 128, 16),             # GQA 8, split-K
+    ([5, 31, 32, 33, 517, 2049], 16, 16, 64, 32),            # MHA, D 64, bs 32
+    ([3, 100, 1500], 16, 1, 128, 16),                        # GQA 16
+    ([9, 300, 3000], 16, 2, 128, 32),                        # GQA 8, bs 32
+    ([7, 77, 777], 8, 4, 64, 16),                            # GQA 2, D 64
+    ([2, 90, 1200], 6, 2, 32, 16),                           # generic kernel (D 32)
+]
+
+
+@pytest.mark.parametrize("case", Q8_DECODE_CASES, ids=lambda c: f"L{max(c[0])}-G{c[1]//c[2]}-D{c[3]}-bs{c[4]}")
+def test_q8_decode_shapes(case):
+    lengths, hq, hkv, d, bs = case
+    wl = _case(lengths, hq, hkv, d, bs)
+    log(f"q8 decode {case}: build")
+    pool, ref = _replay(wl)
+    seqs = list(range(len(lengths)))
+    q_bits = decode_queries(wl, seqs)
+    got = to_host_f64(pool.decode(seqs, to_device(q_bits, "bf16")))
+    for i in seqs:
+        want = oracle.paged_attention(ref, i, to_f64(q_bits[i:i + 1], "bf16"))[0]
+        assert_close(got[i], want, *BF16_TOL, what=f"seq {i} (L={lengths[i]})")
+
+
+def test_q8_unused_slots_hold_garbage():
+    """Unused slots of a tail page may hold any bytes (NaN scales included):
+    they take no part in the result."""
+    wl = _case([17, 33, 250], 32, 8, 128, 16)
+    pool, ref = _replay(wl, mirror=True)
+    q_bits = decode_queries(wl, [0, 1, 2])
+    want = [oracle.paged_attention(ref, i, to_f64(q_bits[i:i + 1], "bf16"))[0] for i in range(3)]
+    bs, d = 16, 128
+    for s in range(3):
+        n = ref.lengths[s]
+        blk = ref.tables[s][-1]
+        for raw in (pool.k, pool.v):
+            raw[blk, :, bs * d:].view(torch.float32)[:, n % bs:] = float("nan")
+            if raw is pool.k:
+                raw[blk, :, (n % bs) * d:bs * d] = 0x7F
+    got = to_host_f64(pool.decode([0, 1, 2], to_device(q_bits, "bf16")))
+    for i in range(3):
+        assert_close(got[i], want[i], *BF16_TOL, what=f"seq {i}")
+
+
+def test_q8_decode_step_with_fork():
+    from paged_kv_cache_block_amd import DevicePool
+    hq, hkv, d, bs, nb = 32, 8, 128, 16, 128
+    order = np.random.default_rng(21).permutation(nb).astype(np.int32)
+    pool = DevicePool(nb, bs, hkv, d, dtype="i8", allocation_order=order)
+    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8)
+    rng = np.random.default_rng(5)
+
+    def draw(shape_):
+        return bf16_round(rng.standard_normal(shape_).astype(np.float32))
+
+    for s, n in enumerate([37, 15, 200]):
+        pool.create(s)
+        ref.create(s)
+        k, v = draw((n, hkv, d)), draw((n, hkv, d))
+        slots = pool.append(s, n)
+        assert slots.tolist() == ref.append(s, n)
+        pool.write(slots, to_device(k, "bf16"), to_device(v, "bf16"))
+        ref.write(slots, to_f64(k, "bf16"), to_f64(v, "bf16"))
+    pool.fork(0, 3)
+    ref.fork(0, 3)
+    seqs = [0, 1, 2, 3]
+    for step in range(5):
+        k, v, q = draw((4, hkv, d)), draw((4, hkv, d)), draw((4, hq, d))
+        out, slots = pool.decode_step(seqs, to_device(k, "bf16"), to_device(v, "bf16"), to_device(q, "bf16"))
+        want_slots = []
+        for s in seqs:
+            want_slots += ref.append(s, 1)
+        assert slots.tolist() == want_slots
+        ref.write(want_slots, to_f64(k, "bf16"), to_f64(v, "bf16"))
+        got = to_host_f64(out)
+        for i, s in enumerate(seqs):
+            want = oracle.paged_attention(ref, s, to_f64(q[i:i + 1], "bf16"))[0]
+            assert_close(got[i], want, *BF16_TOL, what=f"step {step} seq {s}")
+    torch.cuda.synchronize()
+    _check_codes(pool, ref, seqs)
+
+
+# ------------------------------------------------------------ prefill
+@pytest.mark.parametrize("case", [(([300, 77], [70, 77]), 32, 8, 128, 16),
+                                  (([200, 50], [31, 1]), 16, 16, 64, 32)],
+                         ids=["G4-D128-bs16", "G1-D64-bs32"])
+def test_q8_prefill(case):
+    (lengths, q_lens), hq, hkv, d, bs = case
+    wl = _case(lengths, hq, hkv, d, bs)
+    wl.prefill = list(enumerate(q_lens))
+    wl.decode_seqs = []
+    pool, ref = _replay(wl)
+    qp = prefill_queries(wl)
+    out = to_host_f64(pool.prefill(list(range(len(lengths))), q_lens, to_device(qp, "bf16")))
+    r0 = 0
+    for s, n in wl.prefill:
+        keys, values = ref.gather(s)
+        exp = oracle.attention(to_f64(qp[r0:r0 + n], "bf16"), keys, values)
+        assert_close(out[r0:r0 + n], exp, *BF16_TOL, what=f"seq {s}")
+        r0 += n
+
+
+# ------------------------------------------------------------ full size
+def test_q8_full_size_gqa_decode_step_sampled():
+    """32 x U[1, 8192], 32/8 heads, d 128, bs 16 in int8 pages, one fused
+    decode step as the benchmark times it; sampled sequences against the
+    oracle (codes bit-exact, outputs within tolerance)."""
+    wl = gqa_decode()
+    log("q8 full size: build")
+    pool, _ = _replay(wl, mirror=False)
+    seqs = list(wl.decode_seqs)
+    lengths = wl.final_lengths()
+    sample = sorted({int(np.argmax([lengths[s] for s in seqs])), int(np.argmin([lengths[s] for s in seqs])),
+                     3, 17, 30})
+    rng = np.random.default_rng(77)
+    k_new = bf16_round(rng.standard_normal((32, 8, 128)).astype(np.float32))
+    v_new = bf16_round(rng.standard_normal((32, 8, 128)).astype(np.float32))
+    q = decode_queries(wl, seqs)
+    log("q8 full size: decode step")
+    out, slots = pool.decode_step(seqs, to_device(k_new, "bf16"), to_device(v_new, "bf16"), to_device(q, "bf16"))
+    got = to_host_f64(out)
+    kc, ks, vc, vs = _device_codes(pool)
+    rows = logical_kv(wl, sample)
+    bs = wl.block_size
+    for s in sample:
+        K = np.concatenate([to_f64(rows[s][0], "bf16"), to_f64(k_new[s:s + 1], "bf16")])
+        V = np.concatenate([to_f64(rows[s][1], "bf16"), to_f64(v_new[s:s + 1], "bf16")])
+        table = pool.block_table(s)
+        n = K.shape[0]
+        blk = table[np.arange(n) // bs]
+        off = np.arange(n) % bs
+        codes, scale = oracle.quantize_rows(K, 8)
+        np.testing.assert_array_equal(kc[blk, off], codes, err_msg=f"K codes seq {s}")
+        np.testing.assert_array_equal(ks[blk, off], oracle.stored_scale(scale[..., 0]).astype(np.float32))
+        codes, scale = oracle.quantize_rows(V, 8)
+        np.testing.assert_array_equal(vc[blk, off], codes, err_msg=f"V codes seq {s}")
+        want = oracle.attention(to_f64(q[s:s + 1], "bf16"), oracle.fake_quantize_rows(K, 8),
+                                oracle.fake_quantize_rows(V, 8))[0]
+        assert_close(got[s], want, *BF16_TOL, what=f"seq {s} (L={n})")
