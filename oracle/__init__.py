@@ -16,7 +16,8 @@ Sources (the pages, cited by title and section):
 * vladkulikov.com course notebook "Модуль 10. KV-кэши и эффективный инференс"
   -- ``PagedKVPool`` (preflighted multi-token append, share_prefix, release,
   fill accounting, ``validate``) and its embedded reference contract; its
-  KV-compression experiment (per-row absmax codes, ``fake_quantize_rows``).
+  KV-compression experiment (per-row absmax codes, ``fake_quantize_rows``);
+  its prefix-caching cell (``prefix_key``, ``run_prefix_trace``).
 * docs.rs ferrum-kv 0.4.0 ``src/attention.rs`` -- ``paged_attention``
   (GQA head grouping, 1/sqrt(head_dim) scale, bottom-right causal mask).
 * CMU 11-667 lecture 19 ``infer_world.py``, section 3 "online softmax and
@@ -29,6 +30,8 @@ Modules:
   own float64 K/V storage.
 * :mod:`oracle.quant` -- per-row absmax quantisation of K/V rows (codes,
   fp32 scales, read-back values); a ``Pool(quant_bits=8)`` stores through it.
+* :mod:`oracle.prefix` -- prefix-hash block reuse: complete-block keys
+  (scope, revision, all preceding tokens) mapped to pinned pool blocks.
 * :mod:`oracle.attention` -- the attention definition, its online-softmax
   restatement, the log-sum-exp merge of partial results and a pure-Python
   brute force for tiny inputs.
@@ -47,6 +50,7 @@ from .quant import (
     fake_quantize_rows,
     packed_bytes,
 )
+from .prefix import PrefixCache, prefix_key, run_prefix_trace
 from .attention import (
     attention,
     paged_attention,
@@ -75,4 +79,7 @@ __all__ = [
     "dequantize_rows",
     "fake_quantize_rows",
     "packed_bytes",
+    "PrefixCache",
+    "prefix_key",
+    "run_prefix_trace",
 ]

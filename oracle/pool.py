@@ -32,6 +32,12 @@ Where the two pages differ, the readings are:
 * ``fork(src, dst)`` is ``share(src, dst, len(src))``; the first page's
   context tuple is not modelled (one pool per model and layer).
 
+Pins: a block can also be referenced from outside every block table (the
+prefix cache of :mod:`oracle.prefix` holds one reference per cached block).
+Such a reference counts in the refcount, so the block stays allocated after
+every sequence holding it is released; a block only pins hold has fill 0 (no
+live sequence uses its slots), so it counts as capacity, not payload.
+
 Storage: ``K`` and ``V`` are float64 arrays ``[num_blocks, block_size,
 num_kv_heads, head_dim]`` -- block, slot, head, dim -- the first page's
 ``keys[num_blocks, block_size, dim]`` with a KV-head axis added in the
@@ -100,6 +106,8 @@ class Pool:
         for position, block in enumerate(self.order):
             self.rank[block] = position
         self.refs = np.zeros(self.num_blocks, dtype=np.int64)
+        # References held outside the block tables (the prefix cache's).
+        self.pins = np.zeros(self.num_blocks, dtype=np.int64)
         self.free = set(range(self.num_blocks))
         # Free blocks keyed by rank; heap pop = first free id in the order.
         self._free_heap = [(self.rank[b], b) for b in range(self.num_blocks)]
@@ -235,6 +243,35 @@ class Pool:
         self._existing(src)
         self.share(src, dst, self.lengths[src])
 
+    def adopt(self, seq, blocks, length):
+        """New sequence ``seq`` whose table is ``blocks`` (each refcount + 1)
+        and whose length is ``length``; ``ceil(length / block_size)`` must be
+        ``len(blocks)`` and every block must be referenced already."""
+        self._new(seq)
+        length = _non_negative_int(length, "length")
+        blocks = [int(b) for b in blocks]
+        if _ceil_div(length, self.block_size) != len(blocks) or len(set(blocks)) != len(blocks):
+            raise ValueError("blocks must cover length exactly, each once")
+        if any(not 0 <= b < self.num_blocks or self.refs[b] == 0 for b in blocks):
+            raise ValueError("adopted blocks must be live")
+        for b in blocks:
+            self.refs[b] += 1
+        self.tables[seq] = blocks
+        self.lengths[seq] = length
+
+    def pin(self, block):
+        """One more reference to a live block, held outside every table."""
+        if self.refs[block] == 0:
+            raise ValueError("only a live block can be pinned")
+        self.refs[block] += 1
+        self.pins[block] += 1
+
+    def unpin(self, block):
+        if self.pins[block] == 0:
+            raise ValueError("block is not pinned")
+        self.pins[block] -= 1
+        self._drop_ref(block)
+
     def release(self, seq):
         """Drop one reference per block; blocks at zero become free."""
         self._existing(seq)
@@ -335,9 +372,12 @@ class Pool:
                 expected[block] += 1
         fill = self.fills()
         for block in range(self.num_blocks):
-            assert self.refs[block] == expected[block], "refcount != table references"
+            assert self.refs[block] == expected[block] + self.pins[block], \
+                "refcount != table references + pins"
             if self.refs[block] == 0:
                 assert block in self.free and fill[block] == 0, "unreferenced block not free"
+            elif expected[block] == 0:
+                assert block not in self.free and fill[block] == 0, "pinned-only block"
             else:
                 assert block not in self.free, "referenced block is free"
                 assert 1 <= fill[block] <= self.block_size, "fill out of range"

@@ -21,6 +21,7 @@ from .workloads import (
     decode_queries,
     prefill_queries,
     logical_kv,
+    prefix_trace_requests,
 )
 
 __all__ = [
@@ -37,4 +38,5 @@ __all__ = [
     "decode_queries",
     "prefill_queries",
     "logical_kv",
+    "prefix_trace_requests",
 ]

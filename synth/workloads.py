@@ -278,3 +278,16 @@ def logical_kv(wl, seqs):
         ks, vs, _ = rows[s]
         out[s] = (np.concatenate(ks, axis=0), np.concatenate(vs, axis=0))
     return out
+
+
+def prefix_trace_requests(users=100, turns=5):
+    """Token-id requests of the prefix-caching trace on the vladkulikov.com
+    notebook "Модуль 10" (prefix-caching cell): user u, turn t sends
+    [100 + u % 10] + 0..30 + [1000 + u, 2000 + t] + 0..13 (48 ids), users
+    outer, turns inner.  Returns ``[(user, turn, tokens)]``."""
+    out = []
+    for user in range(users):
+        for turn in range(turns):
+            tokens = [100 + user % 10] + list(range(31)) + [1000 + user, 2000 + turn] + list(range(14))
+            out.append((user, turn, tokens))
+    return out
