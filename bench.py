@@ -226,6 +226,37 @@ def run_prefill(args):
     }
 
 
+def run_prefix_cache(reps=20):
+    """Host cost of prefix-hash block reuse through the C ABI: the 500-request
+    trace of the "Модуль 10" notebook (100 users x 5 turns, 48-token requests,
+    block size 16), each request attach + append + register + release, with
+    one shared scope; the cache is cleared between repetitions."""
+    from paged_kv_cache_block_amd import DevicePool
+    from synth import prefix_trace_requests
+    reqs = [r[2] for r in prefix_trace_requests()]
+    pool = DevicePool(1024, 16, 8, 128, metadata_only=True)
+    hits = cached = 0
+    t0 = time.perf_counter()
+    for rep in range(reps):
+        hits = cached = 0
+        for i, tokens in enumerate(reqs):
+            hit = pool.prefix_attach(i, tokens, "shared-public-template", "model-r1")
+            pool.append(i, len(tokens) - hit)
+            pool.prefix_register(i, tokens, "shared-public-template", "model-r1")
+            pool.release(i)
+            hits += hit > 0
+            cached += hit
+        pool.prefix_clear()
+    dt = time.perf_counter() - t0
+    pool.close()
+    n = reps * len(reqs)
+    return {"workload": "notebook prefix trace: 500 requests x 48 tokens, block 16, shared scope, "
+                        "attach + append + register + release per request (Python ctypes calls)",
+            "requests_per_s": round(n / dt, 1), "us_per_request": round(dt / n * 1e6, 2),
+            "hit_request_fraction": hits / len(reqs),
+            "reused_input_fraction": round(cached / (48 * len(reqs)), 6)}
+
+
 def run_cpu_baseline(wl, seconds):
     """The float64 oracle (gather through its pool, then attention) on the
     first sequences of the same decode workload, repeated for ~``seconds``."""
@@ -338,6 +369,7 @@ def main():
         }
     if not args.no_prefill:
         line["prefill"] = run_prefill(args)
+    line["prefix_cache"] = run_prefix_cache()
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         line["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)

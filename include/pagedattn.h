@@ -14,6 +14,9 @@
  *               PagedKvCacheManager::write_kv as its caller uses it.
  *   [lecture19] CMU 11-667 lecture 19 infer_world.py, section 3 (online
  *               softmax statistics, tiled attention).
+ *   [KVprefix]  vladkulikov.com notebook "Модуль 10", the prefix-caching
+ *               cell (prefix_key, run_prefix_trace) and its key-identity
+ *               checks.
  *   [KVquant]   vladkulikov.com notebook "Модуль 10", the KV-compression
  *               experiment (per-row absmax codes, fake_quantize_rows, and
  *               the packed size of codes plus one fp32 scale per row).
@@ -192,6 +195,46 @@ pa_status pa_fork(pa_pool* pool, int64_t src, int64_t dst);
  * Host-only; device contents are left as they are. */
 pa_status pa_release(pa_pool* pool, int64_t seq);
 
+/* ---------------------------------------------------------- prefix cache --- */
+/* Prefix-hash block reuse ([KVprefix]).  Each pool owns one cache.  A key
+ * exists only at a complete block boundary end (a multiple of block_size)
+ * and is (scope, revision, token ids [0, end)): equal block contents after a
+ * different context, or under another scope or model revision, are
+ * different keys.  A cached key maps to the physical block holding tokens
+ * [end - block_size, end) and holds one reference to it (a pin: the block
+ * outlives the sequences that wrote it, refcounts include pins, and a block
+ * only pins hold counts as capacity, not payload, in pa_stats).  The cache
+ * has no eviction ([KVprefix] has none); pa_prefix_clear drops every key.
+ * scope, revision: NUL-terminated byte strings; tokens: host int32 ids.
+ * All calls are host-only. */
+
+/* Hit of tokens[0 .. n_tokens): the largest h (a multiple of block_size) such
+ * that every complete-block key up to h is cached.  Nothing changes. */
+pa_status pa_prefix_lookup(const pa_pool* pool, const char* scope, const char* revision,
+                           const int32_t* tokens, int32_t n_tokens, int32_t* hit_tokens);
+
+/* New sequence `seq` holding the cached blocks of its hit h (refcount + 1
+ * each, like pa_share) with length h; *hit_tokens receives h.  The caller
+ * then appends and stores the remaining n_tokens - h positions.
+ * Errors: PA_ERR_SEQ_EXISTS, PA_ERR_INVALID_ARG (NULL pointers, n < 0). */
+pa_status pa_prefix_attach(pa_pool* pool, int64_t seq, const char* scope, const char* revision,
+                           const int32_t* tokens, int32_t n_tokens, int32_t* hit_tokens);
+
+/* Add the keys of the complete blocks of `seq`'s first n_tokens positions,
+ * whose token ids are tokens[0 .. n_tokens) and whose K/V the caller has
+ * stored (or enqueued).  A key already cached keeps its block; each new key
+ * pins seq's block.  *added_blocks (may be NULL) receives the new key count.
+ * Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG (n_tokens > length(seq)). */
+pa_status pa_prefix_register(pa_pool* pool, int64_t seq, const char* scope, const char* revision,
+                             const int32_t* tokens, int32_t n_tokens, int32_t* added_blocks);
+
+/* Drop every key and its pin (blocks no table holds become free);
+ * *dropped_entries (may be NULL) receives the number of keys. */
+pa_status pa_prefix_clear(pa_pool* pool, int32_t* dropped_entries);
+
+/* Number of cached keys (= pinned block references). */
+pa_status pa_prefix_entries(const pa_pool* pool, int64_t* entries);
+
 /* Pending copy-on-write copies, oldest first, as (src, dst) block pairs.
  * pairs_out: host [2 * cap]; *n receives the number pending (may exceed cap;
  * then only the first cap are written).  Errors: PA_ERR_INVALID_ARG. */
@@ -298,9 +341,10 @@ pa_status pa_seq_len(const pa_pool* pool, int64_t seq, int32_t* len);
 pa_status pa_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap, int32_t* n);
 pa_status pa_refcount(const pa_pool* pool, int32_t block, int32_t* rc);
 pa_status pa_stats(const pa_pool* pool, pa_pool_stats* stats);
-/* [PagedPool] validate: refcount == table references, free <=> refcount 0,
- * table length == ceil(len / block_size), no block twice in one table, fill
- * of a referenced block in [1, block_size], logical >= payload.
+/* [PagedPool] validate: refcount == table references + prefix-cache pins,
+ * free <=> refcount 0, table length == ceil(len / block_size), no block
+ * twice in one table, fill of a block some table holds in [1, block_size]
+ * (a block only pins hold has fill 0 and is not free), logical >= payload.
  * Returns PA_ERR_INVALID_ARG with the broken invariant in pa_last_error. */
 pa_status pa_validate(const pa_pool* pool);
 /* Number of live sequences; ids_out (host [cap], may be NULL) receives them

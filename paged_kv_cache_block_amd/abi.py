@@ -106,6 +106,11 @@ SIGNATURES = {
     "pa_share": (_i32, [_c_void_p, _i64, _i64, _i32]),
     "pa_fork": (_i32, [_c_void_p, _i64, _i64]),
     "pa_release": (_i32, [_c_void_p, _i64]),
+    "pa_prefix_lookup": (_i32, [_c_void_p, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
+    "pa_prefix_attach": (_i32, [_c_void_p, _i64, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
+    "pa_prefix_register": (_i32, [_c_void_p, _i64, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
+    "pa_prefix_clear": (_i32, [_c_void_p, _i32p]),
+    "pa_prefix_entries": (_i32, [_c_void_p, _i64p]),
     "pa_pending_copies": (_i32, [_c_void_p, _i32p, _i32, _i32p]),
     "pa_flush_copies": (_i32, [_c_void_p, _c_void_p]),
     "pa_reshape_and_cache": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p]),
@@ -240,6 +245,49 @@ def pa_fork(pool, src, dst):
 
 def pa_release(pool, seq):
     _check(load().pa_release(pool, seq))
+
+
+def _bytes(x):
+    return x if isinstance(x, bytes) else str(x).encode()
+
+
+def pa_prefix_lookup(pool, scope, revision, tokens):
+    """Hit (tokens) of ``tokens`` in the pool's prefix cache."""
+    arr, ptr = _i32_array(tokens)
+    hit = _i32()
+    _check(load().pa_prefix_lookup(pool, _bytes(scope), _bytes(revision), ptr, len(arr), ctypes.byref(hit)))
+    return hit.value
+
+
+def pa_prefix_attach(pool, seq, scope, revision, tokens):
+    """New sequence holding the cached blocks of its hit; returns the hit."""
+    arr, ptr = _i32_array(tokens)
+    hit = _i32()
+    _check(load().pa_prefix_attach(pool, seq, _bytes(scope), _bytes(revision), ptr, len(arr),
+                                   ctypes.byref(hit)))
+    return hit.value
+
+
+def pa_prefix_register(pool, seq, scope, revision, tokens):
+    """Cache the complete blocks of ``seq``'s first len(tokens) positions;
+    returns the number of new keys."""
+    arr, ptr = _i32_array(tokens)
+    added = _i32()
+    _check(load().pa_prefix_register(pool, seq, _bytes(scope), _bytes(revision), ptr, len(arr),
+                                     ctypes.byref(added)))
+    return added.value
+
+
+def pa_prefix_clear(pool):
+    n = _i32()
+    _check(load().pa_prefix_clear(pool, ctypes.byref(n)))
+    return n.value
+
+
+def pa_prefix_entries(pool):
+    n = _i64()
+    _check(load().pa_prefix_entries(pool, ctypes.byref(n)))
+    return n.value
 
 
 def pa_pending_copies(pool):

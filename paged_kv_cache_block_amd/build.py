@@ -25,7 +25,7 @@ ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["cache.hip", "decode.hip", "prefill.hip"]
-CXX_SOURCES = ["abi.cpp", "pool.cpp", "plan.cpp"]
+CXX_SOURCES = ["abi.cpp", "pool.cpp", "plan.cpp", "prefix.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 instructions are disabled for every device compile.

@@ -20,6 +20,7 @@
 #include "pagedattn.h"
 #include "plan.hpp"
 #include "pool.hpp"
+#include "prefix.hpp"
 
 namespace {
 
@@ -95,6 +96,7 @@ void drain_timing_locked() {
 // -------------------------------------------------------------------- pool
 struct pa_pool {
   pa::BlockPool meta;
+  pa::PrefixCache prefix;  // complete-block prefix keys -> pinned blocks
   pa::PoolGeom geom{};
   void* k = nullptr;
   void* v = nullptr;
@@ -306,6 +308,47 @@ pa_status pa_release(pa_pool* pool, int64_t seq) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
   std::string msg;
   return from(pool->meta.release(seq, &msg), msg);
+}
+
+pa_status pa_prefix_lookup(const pa_pool* pool, const char* scope, const char* revision,
+                           const int32_t* tokens, int32_t n_tokens, int32_t* hit_tokens) {
+  if (!pool || !scope || !revision || !hit_tokens || n_tokens < 0 || (n_tokens > 0 && !tokens))
+    return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  *hit_tokens = static_cast<int32_t>(pool->prefix.lookup(scope, revision, tokens, n_tokens));
+  return ok();
+}
+
+pa_status pa_prefix_attach(pa_pool* pool, int64_t seq, const char* scope, const char* revision,
+                           const int32_t* tokens, int32_t n_tokens, int32_t* hit_tokens) {
+  if (!pool || !scope || !revision || !hit_tokens) return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  std::string msg;
+  int64_t hit = 0;
+  pa::Status s = pool->prefix.attach(pool->meta, seq, scope, revision, tokens, n_tokens, &hit, &msg);
+  if (s == pa::kOk) *hit_tokens = static_cast<int32_t>(hit);
+  return from(s, msg);
+}
+
+pa_status pa_prefix_register(pa_pool* pool, int64_t seq, const char* scope, const char* revision,
+                             const int32_t* tokens, int32_t n_tokens, int32_t* added_blocks) {
+  if (!pool || !scope || !revision) return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  std::string msg;
+  int64_t added = 0;
+  pa::Status s = pool->prefix.add(pool->meta, seq, scope, revision, tokens, n_tokens, &added, &msg);
+  if (s == pa::kOk && added_blocks) *added_blocks = static_cast<int32_t>(added);
+  return from(s, msg);
+}
+
+pa_status pa_prefix_clear(pa_pool* pool, int32_t* dropped_entries) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  const int64_t n = pool->prefix.clear(pool->meta);
+  if (dropped_entries) *dropped_entries = static_cast<int32_t>(n);
+  return ok();
+}
+
+pa_status pa_prefix_entries(const pa_pool* pool, int64_t* entries) {
+  if (!pool || !entries) return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  *entries = pool->prefix.size();
+  return ok();
 }
 
 pa_status pa_pending_copies(const pa_pool* pool, int32_t* pairs_out, int32_t cap, int32_t* n) {

@@ -31,6 +31,7 @@ Status BlockPool::make(int32_t num_blocks, int32_t block_size, const int32_t* or
     p.rank_[b] = r;
   }
   p.refs_.assign(num_blocks, 0);
+  p.pins_.assign(num_blocks, 0);
   std::vector<int32_t> ranks(num_blocks);
   for (int32_t r = 0; r < num_blocks; ++r) ranks[r] = r;
   p.free_heap_ = decltype(p.free_heap_)(std::greater<int32_t>(), std::move(ranks));
@@ -209,6 +210,59 @@ Status BlockPool::release(int64_t seq, std::string* msg) {
   return kOk;
 }
 
+Status BlockPool::adopt(int64_t seq, const int32_t* blocks, int32_t n_blocks, int64_t length,
+                        std::string* msg) {
+  if (seqs_.count(seq)) {
+    *msg = "sequence already exists: " + std::to_string(seq);
+    return kSeqExists;
+  }
+  if (n_blocks < 0 || length < 0 || (n_blocks > 0 && !blocks) || ceil_div(length, block_size_) != n_blocks) {
+    *msg = "adopted blocks must cover the length exactly";
+    return kInvalidArg;
+  }
+  std::vector<int32_t> table(blocks, blocks + n_blocks);
+  std::vector<int32_t> sorted = table;
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) {
+    *msg = "adopted blocks must be distinct";
+    return kInvalidArg;
+  }
+  for (int32_t b : table)
+    if (b < 0 || b >= num_blocks_ || refs_[b] == 0) {
+      *msg = "adopted blocks must be live";
+      return kInvalidArg;
+    }
+  for (int32_t b : table) ++refs_[b];
+  Sequence s;
+  s.length = length;
+  s.table = std::move(table);
+  seqs_.emplace(seq, std::move(s));
+  ++version_;
+  return kOk;
+}
+
+Status BlockPool::pin(int32_t block, std::string* msg) {
+  if (block < 0 || block >= num_blocks_ || refs_[block] == 0) {
+    *msg = "only a live block can be pinned";
+    return kInvalidArg;
+  }
+  ++refs_[block];
+  ++pins_[block];
+  ++version_;
+  return kOk;
+}
+
+Status BlockPool::unpin(int32_t block, std::string* msg) {
+  if (block < 0 || block >= num_blocks_ || pins_[block] == 0) {
+    *msg = "block is not pinned";
+    return kInvalidArg;
+  }
+  --pins_[block];
+  drop_ref(block);
+  ++version_;
+  return kOk;
+}
+
 std::vector<std::pair<int32_t, int32_t>> BlockPool::take_pending_copies() {
   std::vector<std::pair<int32_t, int32_t>> out;
   out.swap(pending_);
@@ -277,9 +331,14 @@ Status BlockPool::validate(std::string* msg) const {
   }
   std::vector<int32_t> fill = fills();
   for (int32_t b = 0; b < num_blocks_; ++b) {
-    if (refs_[b] != expected[b]) { *msg = "physical ref_count does not match page tables"; return kInvalidArg; }
+    if (refs_[b] != expected[b] + pins_[b]) {
+      *msg = "physical ref_count does not match page tables plus pins";
+      return kInvalidArg;
+    }
     if (refs_[b] == 0) {
       if (!is_free[b] || fill[b] != 0) { *msg = "unreferenced block is not clean and free"; return kInvalidArg; }
+    } else if (expected[b] == 0) {
+      if (is_free[b]) { *msg = "pinned block appears in free list"; return kInvalidArg; }
     } else {
       if (is_free[b]) { *msg = "referenced block appears in free list"; return kInvalidArg; }
       if (fill[b] < 1 || fill[b] > block_size_) { *msg = "referenced block has invalid fill"; return kInvalidArg; }

@@ -55,6 +55,15 @@ class BlockPool {
   Status share(int64_t src, int64_t dst, int32_t prefix, std::string* msg);
   Status fork(int64_t src, int64_t dst, std::string* msg);
   Status release(int64_t seq, std::string* msg);
+  // New sequence `seq` whose table is blocks[0..n_blocks) (each refcount + 1)
+  // and whose length is `length`; ceil(length / block_size) must equal
+  // n_blocks, the blocks must be live and distinct.
+  Status adopt(int64_t seq, const int32_t* blocks, int32_t n_blocks, int64_t length, std::string* msg);
+  // A reference held outside every table (the prefix cache's); only a live
+  // block can be pinned.  unpin drops it (the block is freed at refcount 0).
+  Status pin(int32_t block, std::string* msg);
+  Status unpin(int32_t block, std::string* msg);
+  int32_t pins(int32_t block) const { return pins_[block]; }
 
   const Sequence* find(int64_t seq) const;
   int32_t refcount(int32_t block) const { return refs_[block]; }
@@ -90,6 +99,7 @@ class BlockPool {
   std::vector<int32_t> order_;  // rank -> block
   std::vector<int32_t> rank_;   // block -> rank
   std::vector<int32_t> refs_;
+  std::vector<int32_t> pins_;   // references held outside the tables
   // Free blocks by rank: the top is the first free block of the order.
   std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_heap_;
   std::unordered_map<int64_t, Sequence> seqs_;

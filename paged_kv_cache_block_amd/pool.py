@@ -92,6 +92,22 @@ class DevicePool:
     def release(self, seq):
         abi.pa_release(self.handle, seq)
 
+    # ------------------------------------------------------------ prefix cache
+    def prefix_lookup(self, tokens, scope, revision):
+        return abi.pa_prefix_lookup(self.handle, scope, revision, tokens)
+
+    def prefix_attach(self, seq, tokens, scope, revision):
+        return abi.pa_prefix_attach(self.handle, seq, scope, revision, tokens)
+
+    def prefix_register(self, seq, tokens, scope, revision):
+        return abi.pa_prefix_register(self.handle, seq, scope, revision, tokens)
+
+    def prefix_clear(self):
+        return abi.pa_prefix_clear(self.handle)
+
+    def prefix_entries(self):
+        return abi.pa_prefix_entries(self.handle)
+
     def pending_copies(self):
         return abi.pa_pending_copies(self.handle)
 
