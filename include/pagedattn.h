@@ -314,6 +314,31 @@ pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t 
                          const void* k_new, const void* v_new, const void* q, void* out, void* ws,
                          size_t ws_bytes, int64_t* slots_out, void* stream);
 
+/* Workspace bytes pa_verify_step needs for this batch (sized for the lengths
+ * after its appends).  0 if the arguments are invalid. */
+size_t pa_verify_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,
+                                      int32_t B, int32_t num_heads);
+
+/* Multi-token step (speculative verification, short chunks): append
+ * q_lens[b] >= 1 tokens to each sequence (pa_append_batch, all or nothing),
+ * store their K/V rows and compute causal attention for those q_lens[b]
+ * rows, the last positions of the sequence ([ferrum] paged_attention with
+ * q_tokens = q_lens[b]: row t sees keys j <= L - q_lens[b] + t, L the length
+ * after the append).  All q_lens[b] * G query columns of a sequence share
+ * each K/V page load of the split-K decode kernels.
+ * seqs: host [B], each at most once; q_lens: host [B]; R = sum q_lens;
+ * k_new, v_new: device [R][num_kv_heads][head_dim]; q, out: device
+ * [R][num_heads][head_dim] (rows sequence-major, as pa_prefill_chunk);
+ * ws: at least pa_verify_step_workspace_bytes(...) bytes, 256-byte aligned;
+ * slots_out: host [R] or NULL.
+ * Needs bf16 or int8 pages, head_dim 64 or 128, block_size 16 or 32 and
+ * q_lens[b] * (num_heads / num_kv_heads) <= 32.
+ * Errors: as pa_decode_step; PA_ERR_INVALID_ARG for a repeated sequence, a
+ *   q_len < 1 or a shape the kernels do not cover, before anything changes. */
+pa_status pa_verify_step(pa_pool* pool, const int64_t* seqs, const int32_t* q_lens, int32_t B,
+                         int32_t num_heads, const void* k_new, const void* v_new, const void* q, void* out,
+                         void* ws, size_t ws_bytes, int64_t* slots_out, void* stream);
+
 /* Workspace bytes pa_prefill_chunk needs.  0 if the arguments are invalid. */
 size_t pa_prefill_workspace_bytes(const pa_pool* pool, const int64_t* seqs,
                                   const int32_t* q_lens, int32_t B, int32_t num_heads);
@@ -326,6 +351,8 @@ size_t pa_prefill_workspace_bytes(const pa_pool* pool, const int64_t* seqs,
  *     out[r][h] = sum_{j visible} softmax(s)_j V_j[g],  r = row offset of b + t
  * seqs, q_lens: host [B]; q, out: device [sum q_lens][num_heads][head_dim];
  * ws: as for pa_decode.
+ * Chunks whose every q_lens[b] * G <= 32 (on the MFMA decode shapes) run on
+ * the split-K decode kernels; longer ones on the prefill kernel.
  * Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG (q_lens[b] < 1 or > L,
  *   head mismatch, small ws, NULL pointers), PA_ERR_DEVICE. */
 pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,

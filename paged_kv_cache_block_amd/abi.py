@@ -120,6 +120,9 @@ SIGNATURES = {
     "pa_decode_step_workspace_bytes": (_size, [_c_void_p, _i64p, _i32, _i32]),
     "pa_decode_step": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _size, _i64p, _c_void_p]),
+    "pa_verify_step_workspace_bytes": (_size, [_c_void_p, _i64p, _i32p, _i32, _i32]),
+    "pa_verify_step": (_i32, [_c_void_p, _i64p, _i32p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                              _c_void_p, _c_void_p, _size, _i64p, _c_void_p]),
     "pa_prefill_workspace_bytes": (_size, [_c_void_p, _i64p, _i32p, _i32, _i32]),
     "pa_prefill_chunk": (_i32, [_c_void_p, _i64p, _i32p, _i32, _i32, _c_void_p, _c_void_p,
                                 _c_void_p, _size, _c_void_p]),
@@ -337,6 +340,29 @@ def pa_decode_step(pool, seqs, num_heads, k_new, v_new, q, out, ws, ws_bytes, st
         sp = slots_out.ctypes.data_as(_i64p)
     _check(load().pa_decode_step(pool, ptr, len(arr), num_heads, _addr(k_new), _addr(v_new), _addr(q),
                                  _addr(out), _addr(ws), ws_bytes, sp, _stream(stream)))
+    return slots_out
+
+
+def pa_verify_step_workspace_bytes(pool, seqs, q_lens, num_heads):
+    arr, ptr = _i64_array(seqs)
+    ql, qptr = _i32_array(q_lens)
+    return int(load().pa_verify_step_workspace_bytes(pool, ptr, qptr, len(arr), num_heads))
+
+
+def pa_verify_step(pool, seqs, q_lens, num_heads, k_new, v_new, q, out, ws, ws_bytes, stream=None,
+                   slots_out=None):
+    """Multi-token step; returns the new slots (int64 [sum q_lens]) when
+    ``slots_out`` is given or True."""
+    arr, ptr = _i64_array(seqs)
+    ql, qptr = _i32_array(q_lens)
+    sp = None
+    if slots_out is True:
+        slots_out = np.empty(int(ql.sum()), dtype=np.int64)
+    if slots_out is not None:
+        assert slots_out.dtype == np.int64 and slots_out.size >= int(ql.sum())
+        sp = slots_out.ctypes.data_as(_i64p)
+    _check(load().pa_verify_step(pool, ptr, qptr, len(arr), num_heads, _addr(k_new), _addr(v_new),
+                                 _addr(q), _addr(out), _addr(ws), ws_bytes, sp, _stream(stream)))
     return slots_out
 
 

@@ -388,7 +388,7 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32
   pa::DecodePlan plan;
   std::string msg;
   if (pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                            pool->geom.head_dim, decode_tokens_per_part(), nullptr, 0, &plan,
+                            pool->geom.head_dim, decode_tokens_per_part(), nullptr, nullptr, 0, &plan,
                             &msg) != pa::kOk)
     return 0;
   return plan.total_bytes;
@@ -431,7 +431,8 @@ pa_status launch_decode_plan(pa_pool* pool, const pa::DecodePlan& plan, int32_t 
   a.part_m = reinterpret_cast<float*>(w + plan.part_m_off);
   a.part_l = reinterpret_cast<float*>(w + plan.part_l_off);
   a.part_acc = reinterpret_cast<float*>(w + plan.part_acc_off);
-  a.merge_seq = reinterpret_cast<const int32_t*>(w + plan.merge_off);
+  a.q_start = reinterpret_cast<const int32_t*>(w + plan.qstart_off);
+  a.merge_rows = reinterpret_cast<const int32_t*>(w + plan.merge_off);
   a.n_parts_of = reinterpret_cast<const int32_t*>(w + plan.nparts_off);
   a.batch = B;
   a.num_heads = num_heads;
@@ -440,6 +441,7 @@ pa_status launch_decode_plan(pa_pool* pool, const pa::DecodePlan& plan, int32_t 
   a.pages_per_part = plan.pages_per_part;
   a.n_work = plan.n_work;
   a.n_merge = plan.n_merge;
+  a.max_cols = plan.max_q_len * a.group;
   a.scale_log2 = scale_log2_for(pool->geom.head_dim);
   {
     TimedLaunch t(PA_KERNEL_DECODE, st);
@@ -456,14 +458,96 @@ pa_status launch_decode_plan(pa_pool* pool, const pa::DecodePlan& plan, int32_t 
   return ok();
 }
 
-// Tokens each batch row will have gained after appending one token per
-// entry (a sequence listed twice gains two).
-std::vector<int32_t> step_extra_tokens(const int64_t* seqs, int32_t B) {
-  std::unordered_map<int64_t, int32_t> count;
-  for (int32_t b = 0; b < B; ++b) ++count[seqs[b]];
+// Tokens each batch row will have gained after the step's appends of
+// n_tokens[b] (1 each when NULL) tokens: a sequence listed twice gains both.
+std::vector<int32_t> step_extra_tokens(const int64_t* seqs, const int32_t* n_tokens, int32_t B) {
+  std::unordered_map<int64_t, int64_t> count;
+  for (int32_t b = 0; b < B; ++b) count[seqs[b]] += n_tokens ? std::max(n_tokens[b], 0) : 1;
   std::vector<int32_t> extra(B);
-  for (int32_t b = 0; b < B; ++b) extra[b] = count[seqs[b]];
+  for (int32_t b = 0; b < B; ++b) extra[b] = static_cast<int32_t>(std::min<int64_t>(count[seqs[b]], INT32_MAX));
   return extra;
+}
+
+// Append n_tokens[b] (1 each when NULL) tokens to every sequence, store
+// their K/V rows and run attention for those rows: the fused decode step
+// (n_tokens NULL) and the multi-token verify step.
+pa_status step_impl(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens, int32_t B,
+                    int32_t num_heads, const void* k_new, const void* v_new, const void* q, void* out,
+                    void* ws, size_t ws_bytes, int64_t* slots_out, void* stream) {
+  pa_status r = check_decode_args(pool, num_heads, q, out, ws);
+  if (r != PA_OK) return r;
+  if (!k_new || !v_new) return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+  if (B <= 0 || !seqs) return fail(PA_ERR_INVALID_ARG, "batch must be positive with a non-NULL seqs array");
+  int64_t rows = B;
+  int32_t max_q = 1;
+  if (n_tokens) {
+    std::unordered_map<int64_t, int32_t> seen;
+    rows = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      if (n_tokens[b] < 1) return fail(PA_ERR_INVALID_ARG, "q_lens[b] must be >= 1");
+      if (seen[seqs[b]]++) return fail(PA_ERR_INVALID_ARG, "a sequence appears twice in a verify step");
+      rows += n_tokens[b];
+      max_q = std::max(max_q, n_tokens[b]);
+    }
+    if (rows > INT32_MAX / 2) return fail(PA_ERR_INVALID_ARG, "too many query rows");
+    const int32_t group = num_heads / pool->geom.num_kv_heads;
+    if (!pa::decode_handles_rows(pool->geom, group, max_q))
+      return fail(PA_ERR_INVALID_ARG,
+                  "verify step needs an MFMA decode shape (bf16 or int8 pages, head_dim 64/128, "
+                  "block_size 16/32) and q_len * group <= 32");
+  }
+  std::string msg;
+  // Size and validate against the lengths after the append, before anything changes.
+  std::vector<int32_t> extra = step_extra_tokens(seqs, n_tokens, B);
+  pa::DecodePlan plan;
+  pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                                       pool->geom.head_dim, decode_tokens_per_part(), extra.data(),
+                                       n_tokens, static_cast<int32_t>(rows), &plan, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  if (ws_bytes < plan.total_bytes)
+    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
+                                        " bytes, got " + std::to_string(ws_bytes));
+  std::vector<int32_t> ones;
+  if (!n_tokens) ones.assign(B, 1);
+  std::vector<int64_t> slots(rows);
+  s = pool->meta.append_batch(seqs, n_tokens ? n_tokens : ones.data(), B, slots.data(), &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  // Same lengths as the sizing plan, so the same layout and size.
+  s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                            pool->geom.head_dim, decode_tokens_per_part(), nullptr, n_tokens,
+                            static_cast<int32_t>(rows), &plan, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  std::memcpy(reinterpret_cast<char*>(plan.meta.data()) + plan.slots_off, slots.data(),
+              sizeof(int64_t) * rows);
+  if (slots_out) std::memcpy(slots_out, slots.data(), sizeof(int64_t) * rows);
+  hipStream_t st = as_stream(stream);
+  r = pool->flush(st);  // copy-on-write copies of this append come first
+  if (r != PA_OK) return r;
+  const void* staged = nullptr;
+  const size_t bytes = plan.meta.size() * sizeof(int32_t);
+  r = pool->stage(plan.meta.data(), bytes, &staged);
+  if (r != PA_OK) return r;
+  {
+    TimedLaunch t(PA_KERNEL_CACHE, st);
+    hipError_t e = pa::launch_step_prep(
+        pool->geom, staged, ws, pa::align_up(bytes, 16),
+        reinterpret_cast<const int64_t*>(static_cast<const char*>(staged) + plan.slots_off), pool->k,
+        pool->v, k_new, v_new, static_cast<int32_t>(rows), st);
+    t.done();
+    if (e != hipSuccess) return hip_fail(e, "decode step prologue launch");
+  }
+  r = pool->staged_done(st);
+  if (r != PA_OK) return r;
+  return launch_decode_plan(pool, plan, B, num_heads, q, out, ws, st);
+}
+
+// Whether a prefill chunk goes through the split-K decode kernels (every
+// q_len small enough for one workgroup's query columns).
+bool prefill_via_decode(const pa_pool* pool, const int32_t* q_lens, int32_t B, int32_t num_heads) {
+  if (!q_lens || B <= 0 || num_heads <= 0 || num_heads % pool->geom.num_kv_heads) return false;
+  int32_t max_q = 0;
+  for (int32_t b = 0; b < B; ++b) max_q = std::max(max_q, q_lens[b]);
+  return max_q >= 1 && pa::decode_handles_rows(pool->geom, num_heads / pool->geom.num_kv_heads, max_q);
 }
 
 }  // namespace
@@ -477,8 +561,8 @@ pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_h
   pa::DecodePlan plan;
   std::string msg;
   pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                                       pool->geom.head_dim, decode_tokens_per_part(), nullptr, 0,
-                                       &plan, &msg);
+                                       pool->geom.head_dim, decode_tokens_per_part(), nullptr, nullptr,
+                                       0, &plan, &msg);
   if (s != pa::kOk) return fail(s, msg);
   if (ws_bytes < plan.total_bytes)
     return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
@@ -494,12 +578,12 @@ pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_h
 size_t pa_decode_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32_t B,
                                       int32_t num_heads) {
   if (!pool || B <= 0 || !seqs) return 0;
-  std::vector<int32_t> extra = step_extra_tokens(seqs, B);
+  std::vector<int32_t> extra = step_extra_tokens(seqs, nullptr, B);
   pa::DecodePlan plan;
   std::string msg;
   if (pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                            pool->geom.head_dim, decode_tokens_per_part(), extra.data(), B, &plan,
-                            &msg) != pa::kOk)
+                            pool->geom.head_dim, decode_tokens_per_part(), extra.data(), nullptr, B,
+                            &plan, &msg) != pa::kOk)
     return 0;
   return plan.total_bytes;
 }
@@ -507,58 +591,50 @@ size_t pa_decode_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, 
 pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                          const void* k_new, const void* v_new, const void* q, void* out, void* ws,
                          size_t ws_bytes, int64_t* slots_out, void* stream) {
-  pa_status r = check_decode_args(pool, num_heads, q, out, ws);
-  if (r != PA_OK) return r;
-  if (!k_new || !v_new) return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
-  if (B <= 0 || !seqs) return fail(PA_ERR_INVALID_ARG, "batch must be positive with a non-NULL seqs array");
-  std::string msg;
-  // Size and validate against the lengths after the append, before anything changes.
-  std::vector<int32_t> extra = step_extra_tokens(seqs, B);
-  pa::DecodePlan plan;
-  pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                                       pool->geom.head_dim, decode_tokens_per_part(), extra.data(), B,
-                                       &plan, &msg);
-  if (s != pa::kOk) return fail(s, msg);
-  if (ws_bytes < plan.total_bytes)
-    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
-                                        " bytes, got " + std::to_string(ws_bytes));
-  std::vector<int32_t> ones(B, 1);
-  std::vector<int64_t> slots(B);
-  s = pool->meta.append_batch(seqs, ones.data(), B, slots.data(), &msg);
-  if (s != pa::kOk) return fail(s, msg);
-  // Same lengths as the sizing plan, so the same layout and size.
-  s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
-                            pool->geom.head_dim, decode_tokens_per_part(), nullptr, B, &plan, &msg);
-  if (s != pa::kOk) return fail(s, msg);
-  std::memcpy(reinterpret_cast<char*>(plan.meta.data()) + plan.slots_off, slots.data(),
-              sizeof(int64_t) * B);
-  if (slots_out) std::memcpy(slots_out, slots.data(), sizeof(int64_t) * B);
-  hipStream_t st = as_stream(stream);
-  r = pool->flush(st);  // copy-on-write copies of this append come first
-  if (r != PA_OK) return r;
-  const void* staged = nullptr;
-  const size_t bytes = plan.meta.size() * sizeof(int32_t);
-  r = pool->stage(plan.meta.data(), bytes, &staged);
-  if (r != PA_OK) return r;
-  {
-    TimedLaunch t(PA_KERNEL_CACHE, st);
-    hipError_t e = pa::launch_step_prep(
-        pool->geom, staged, ws, pa::align_up(bytes, 16),
-        reinterpret_cast<const int64_t*>(static_cast<const char*>(staged) + plan.slots_off), pool->k,
-        pool->v, k_new, v_new, B, st);
-    t.done();
-    if (e != hipSuccess) return hip_fail(e, "decode step prologue launch");
+  return step_impl(pool, seqs, nullptr, B, num_heads, k_new, v_new, q, out, ws, ws_bytes, slots_out,
+                   stream);
+}
+
+size_t pa_verify_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,
+                                      int32_t B, int32_t num_heads) {
+  if (!pool || B <= 0 || !seqs || !q_lens) return 0;
+  int64_t rows = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (q_lens[b] < 1) return 0;
+    rows += q_lens[b];
   }
-  r = pool->staged_done(st);
-  if (r != PA_OK) return r;
-  return launch_decode_plan(pool, plan, B, num_heads, q, out, ws, st);
+  if (rows > INT32_MAX / 2) return 0;
+  std::vector<int32_t> extra = step_extra_tokens(seqs, q_lens, B);
+  pa::DecodePlan plan;
+  std::string msg;
+  if (pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                            pool->geom.head_dim, decode_tokens_per_part(), extra.data(), q_lens,
+                            static_cast<int32_t>(rows), &plan, &msg) != pa::kOk)
+    return 0;
+  return plan.total_bytes;
+}
+
+pa_status pa_verify_step(pa_pool* pool, const int64_t* seqs, const int32_t* q_lens, int32_t B,
+                         int32_t num_heads, const void* k_new, const void* v_new, const void* q, void* out,
+                         void* ws, size_t ws_bytes, int64_t* slots_out, void* stream) {
+  if (!q_lens) return fail(PA_ERR_INVALID_ARG, "q_lens must be non-NULL");
+  return step_impl(pool, seqs, q_lens, B, num_heads, k_new, v_new, q, out, ws, ws_bytes, slots_out,
+                   stream);
 }
 
 size_t pa_prefill_workspace_bytes(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,
                                   int32_t B, int32_t num_heads) {
   if (!pool || num_heads <= 0 || num_heads % pool->geom.num_kv_heads) return 0;
-  pa::PrefillPlan plan;
   std::string msg;
+  if (prefill_via_decode(pool, q_lens, B, num_heads)) {
+    pa::DecodePlan dplan;
+    if (pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                              pool->geom.head_dim, decode_tokens_per_part(), nullptr, q_lens, 0, &dplan,
+                              &msg) != pa::kOk)
+      return 0;
+    return dplan.total_bytes;
+  }
+  pa::PrefillPlan plan;
   const int32_t group = num_heads / pool->geom.num_kv_heads;
   if (pa::build_prefill_plan(pool->meta, seqs, q_lens, B, num_heads, pool->geom.num_kv_heads,
                              pa::prefill_rows_per_tile(pool->geom, group), &plan, &msg) != pa::kOk)
@@ -580,8 +656,26 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
       (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) % 16)
     return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   const int32_t group = num_heads / pool->geom.num_kv_heads;
-  pa::PrefillPlan plan;
   std::string msg;
+  if (prefill_via_decode(pool, q_lens, B, num_heads)) {
+    // Short chunks (q_len * group <= 32): the split-K decode kernels, all
+    // query rows of a sequence as MFMA columns of each K/V page.
+    pa::DecodePlan dplan;
+    pa::Status ds = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                                          pool->geom.head_dim, decode_tokens_per_part(), nullptr, q_lens,
+                                          0, &dplan, &msg);
+    if (ds != pa::kOk) return fail(ds, msg);
+    if (ws_bytes < dplan.total_bytes)
+      return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(dplan.total_bytes) +
+                                          " bytes, got " + std::to_string(ws_bytes));
+    hipStream_t st = as_stream(stream);
+    pa_status r = pool->flush(st);
+    if (r != PA_OK) return r;
+    r = pool->upload(dplan.meta.data(), dplan.meta.size() * sizeof(int32_t), ws, st);
+    if (r != PA_OK) return r;
+    return launch_decode_plan(pool, dplan, B, num_heads, q, out, ws, st);
+  }
+  pa::PrefillPlan plan;
   pa::Status s = pa::build_prefill_plan(pool->meta, seqs, q_lens, B, num_heads, pool->geom.num_kv_heads,
                                         pa::prefill_rows_per_tile(pool->geom, group), &plan, &msg);
   if (s != pa::kOk) return fail(s, msg);

@@ -1,27 +1,27 @@
 // Paged decode attention for gfx950.
 //
 // What is computed (docs.rs ferrum-kv 0.4.0 src/attention.rs,
-// paged_attention with q_tokens = 1; abhik.ai "examples/pagedattention.py",
-// region paged_attention): for sequence b, query head h, KV head
-// g = h / G, scores s_j = q . K_j / sqrt(D) over every cached token j, softmax,
-// output sum_j p_j V_j, with K_j / V_j found through the block table.
+// paged_attention; abhik.ai "examples/pagedattention.py", region
+// paged_attention): for sequence b of length L with q_len query rows (its
+// last q_len positions; q_len = 1 for decode), row t, query head h, KV head
+// g = h / G: scores s_j = q . K_j / sqrt(D) over the cached tokens
+// j <= L - q_len + t, softmax, output sum_j p_j V_j, with K_j / V_j found
+// through the block table.
 //
 // Kernels
-//   decode_gqa_mfma  bf16, D in {64, 128}, block_size in {16, 32}, G <= 16.
+//   decode_mfma      bf16 or int8 pages, D in {64, 128}, block_size in
+//       {16, 32}, G <= 16, q_len * G <= 32 query columns per sequence.
 //       One workgroup = (work item = (sequence, page range), KV head); its 4
-//       waves stride over the pages of the range.  The G query heads of the
-//       KV head form the N dimension of two MFMA contractions per page:
-//         S^T[16 tok x 16 heads]  = K_page[16 x D]   . Q^T[D x 16]  (16x16x32)
-//         O^T[16 d   x 16 heads] += V^T_page[16 x 16] . P^T[16 x 16] (16x16x16)
-//       The C layout of the first (lane holds 4 tokens of one head) is
-//       exactly the B layout of the second, so P never leaves registers, and
-//       the transposed V page makes every V operand an 8-byte contiguous load.
-//       Online softmax per page (running max / sum in registers, exp2 with
+//       waves stride over the pages of the range.  The query rows x heads of
+//       the KV head form the N dimension of two MFMA contractions per page
+//       (S^T = K . Q^T, then O^T += V^T . P^T, P kept in registers); the
+//       transposed (bf16) or operand-ordered (int8) V page makes every V
+//       operand a contiguous load.  Online softmax per page (exp2 with
 //       log2(e) folded into the scale); the 4 waves merge in LDS; a range
 //       that is the whole sequence writes bf16 output, otherwise fp32
 //       partials (m, l, acc) for the merge kernel.
 //   decode_merge     log-sum-exp combination of the partials of one
-//       (sequence, head): M = max m_c, o = sum e^(m_c-M) acc_c / sum e^(m_c-M) l_c
+//       (query row, head): M = max m_c, o = sum e^(m_c-M) acc_c / sum e^(m_c-M) l_c
 //       (CMU 11-667 lecture 19 section 3, online_softmax_stats, applied
 //       across page ranges).
 //   attn_generic     any dtype / head_dim <= 512 / block_size / group; one
@@ -167,204 +167,6 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
 }
 
 // ------------------------------------------------------------ GQA / MFMA ---
-template <int D, int BS>
-__global__ __launch_bounds__(256) PA_DECODE_OCC void decode_gqa_mfma(DecodeArgs a) {
-  constexpr int KS = D / 32;  // k-steps of the 16x16x32 QK contraction
-  constexpr int TT = BS / 16; // 16-token tiles per page
-  constexpr int DT = D / 16;  // 16-wide d tiles of the P.V contraction
-  constexpr int W = kDecodeWaves;
-  constexpr int ROW = D + 4;  // padded LDS row of one head's accumulator
-  __shared__ float s_m[W][16];
-  __shared__ float s_l[W][16];
-  // [W][G][ROW]: only the G live head columns are staged for the wave merge.
-  extern __shared__ float s_acc[];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int n = lane & 15, grp = lane >> 4;
-  const int Hkv = a.num_kv_heads, Hq = a.num_heads, G = a.group;
-  const int wid = blockIdx.x / Hkv, g = blockIdx.x - wid * Hkv;
-  const int b = a.work[2 * wid], c = a.work[2 * wid + 1];
-  const int L = a.ctx_len[b];
-  const int nblk = (L + BS - 1) / BS;
-  const int p0 = c * a.pages_per_part;
-  const int p1 = min(nblk, p0 + a.pages_per_part);
-  const int32_t* table = a.tables + a.tbl_off[b];
-  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
-  const size_t page = static_cast<size_t>(BS) * D;
-
-  // Q^T operand: lane (n, grp) holds q[head g*G+n][32j + 8grp .. +8].
-  bf16x8 qv[KS];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           (static_cast<size_t>(b) * Hq + g * G + n) * D + 8 * grp;
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      if (n < G)
-        qv[j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j);
-      else
-        qv[j] = bf16x8{};
-    }
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[DT];
-#pragma unroll
-  for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto load_page = [&](int pg, bf16x8 (&kr)[TT][KS], s16x4 (&vr)[DT][TT]) {
-    const int blk = uniform(table[pg]);
-    const uint16_t* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * page;
-    const uint16_t* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * page;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int j = 0; j < KS; ++j)
-        kr[tt][j] = *reinterpret_cast<const bf16x8*>(kp + (16 * tt + n) * D + 32 * j + 8 * grp);
-#pragma unroll
-    for (int nt = 0; nt < DT; ++nt)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-        vr[nt][tt] = *reinterpret_cast<const s16x4*>(vp + (16 * nt + n) * BS + 16 * tt + 4 * grp);
-  };
-
-  auto process = [&](int pg, const bf16x8 (&kr)[TT][KS], const s16x4 (&vr)[DT][TT]) {
-    f32x4 s[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < KS; ++j)
-        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[tt][j], qv[j], s[tt], 0, 0, 0);
-    }
-    // s[tt][i] = score of token pg*BS + 16tt + 4grp + i for head n.
-    const bool tail = pg == nblk - 1;
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = s[tt][i] * a.scale_log2;
-        if (tail && pg * BS + 16 * tt + 4 * grp + i >= L) x = -INFINITY;
-        s[tt][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    // Weights enter P.V as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi),
-    // so the product carries ~16 mantissa bits of p instead of 8: with
-    // heavy-tailed values a single bf16 rounding of p (2^-9 relative) is not
-    // enough when the output nearly cancels.
-    float psum = 0.f;
-    s16x4 p_hi[TT], p_lo[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = exp2f(s[tt][i] - m_new);
-        const __bf16 hi = static_cast<__bf16>(e);
-        const __bf16 lo = static_cast<__bf16>(e - static_cast<float>(hi));
-        psum += e;
-        p_hi[tt][i] = __builtin_bit_cast(short, hi);
-        p_lo[tt][i] = __builtin_bit_cast(short, lo);
-      }
-    l_run = l_run * alpha + psum;
-    // Unused slots of the last page have weight 0; their values are zeroed
-    // too, so 0 * V cannot meet non-finite bits left in an unused slot.
-    int live[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) live[tt] = tail ? L - (pg * BS + 16 * tt + 4 * grp) : 4;
-#pragma unroll
-    for (int nt = 0; nt < DT; ++nt) {
-      acc[nt] *= alpha;
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        s16x4 v = vr[nt][tt];
-        if (tail) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (i >= live[tt]) v[i] = 0;
-        }
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_hi[tt], acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_lo[tt], acc[nt], 0, 0, 0);
-      }
-    }
-  };
-
-#if PA_DECODE_PREFETCH
-  {
-    bf16x8 ka[TT][KS], kb[TT][KS];
-    s16x4 va[DT][TT], vb[DT][TT];
-    // The prefetch is issued unconditionally (the last page of the range
-    // re-loads itself): with the same number of loads in flight on every
-    // path, the wait before a page's first use only covers that page's loads.
-    int p = p0 + wave;
-    if (p < p1) load_page(p, ka, va);
-    while (p < p1) {
-      load_page(p + W < p1 ? p + W : p, kb, vb);
-      process(p, ka, va);
-      p += W;
-      if (p >= p1) break;
-      load_page(p + W < p1 ? p + W : p, ka, va);
-      process(p, kb, vb);
-      p += W;
-    }
-  }
-#else
-  for (int p = p0 + wave; p < p1; p += W) {
-    bf16x8 ka[TT][KS];
-    s16x4 va[DT][TT];
-    load_page(p, ka, va);
-    process(p, ka, va);
-  }
-#endif
-
-  // Per-head totals over the 4 lane groups, then merge the 4 waves.
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (grp == 0) {
-    s_m[wave][n] = m_run;
-    s_l[wave][n] = l_tot;
-  }
-  if (n < G) {
-    float* dst = s_acc + (wave * G + n) * ROW + 4 * grp;
-#pragma unroll
-    for (int nt = 0; nt < DT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt) = acc[nt];
-  }
-  __syncthreads();
-
-  const int base = a.part_base[b];
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int hn = idx / D, d = idx - hn * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][hn]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float e = exp2f(s_m[w][hn] - M);  // a wave without pages has m = -inf
-      num += e * s_acc[(w * G + hn) * ROW + d];
-      den += e * s_l[w][hn];
-    }
-    const int h = g * G + hn;
-    if (base < 0) {
-      static_cast<uint16_t*>(a.out)[(static_cast<size_t>(b) * Hq + h) * D + d] = f32_to_bf16(num / den);
-    } else {
-      const size_t row = static_cast<size_t>(base + c) * Hq + h;
-      a.part_acc[row * D + d] = num;
-      if (d == 0) {
-        a.part_m[row] = M;
-        a.part_l[row] = den;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------- int8 pages ---
 // 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).
 __device__ __forceinline__ s16x4 i8x4_to_bf16x4(uint32_t w) {
   s16x4 r;
@@ -384,25 +186,56 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-// decode_q8_mfma: decode_gqa_mfma over int8 pages (vladkulikov.com notebook
-// "Модуль 10", KV-compression experiment: a row reads back as code * scale).
-// With codes c and row scales sk / sv:
-//   s_j = (q . ck_j) * sk_j / sqrt(D)        (MFMA on the codes as bf16, exact)
-//   o   = sum_j p_j sv_j cv_j / sum_j p_j     (sv folded into the P operand)
-// The QK contraction runs over a permuted d order: in k-step j lane group grp
-// takes d in [grp * D/4 + 8j, +8), so a lane's K codes of one token are D/4
-// contiguous bytes; the V page's operand order gives the same for V.
-template <int D, int BS>
-__global__ __launch_bounds__(256) PA_DECODE_OCC void decode_q8_mfma(DecodeArgs a) {
+// One page of one KV head, as one lane holds it.
+//   bf16: k[tt][j] = K[16tt + n][32j + 8grp .. +8], v[nt][tt] = V^T[16nt + n][16tt + 4grp .. +4]
+//   int8: kc[tt][.] = K codes of token 16tt + n, d in [grp * D/4, +D/4) (the QK
+//         contraction runs over that permuted d order, Q takes the same),
+//         vc[tt][nt] = V codes of d = 16nt + n, tokens 16tt + 4grp .. +4,
+//         ks / vs = the row scales of tokens 16tt + 4grp .. +4.
+template <int D, int BS, bool Q8> struct PageRegs;
+template <int D, int BS> struct PageRegs<D, BS, false> {
+  bf16x8 k[BS / 16][D / 32];
+  s16x4 v[D / 16][BS / 16];
+};
+template <int D, int BS> struct PageRegs<D, BS, true> {
+  uint32_t kc[BS / 16][D / 16];
+  uint32_t vc[BS / 16][D / 16];
+  f32x4 ks[BS / 16], vs[BS / 16];
+};
+
+// decode_mfma: split-K paged attention for query rows that are the last
+// q_len positions of their sequence (q_len = 1: decode).
+//
+// What is computed (docs.rs ferrum-kv 0.4.0 src/attention.rs,
+// paged_attention: GQA head g = h / G, scale 1/sqrt(D), query row t of q_len
+// sees keys j <= L - q_len + t), over the page range of one work item; with
+// Q8 over int8 pages whose rows read back as code * scale (vladkulikov.com
+// notebook "Модуль 10", KV-compression experiment):
+//   s_j = (q . ck_j) * sk_j / sqrt(D),  o = sum_j p_j sv_j cv_j / sum_j p_j
+// with sk folded into the scores and sv into the P operand.
+//
+// One workgroup = (work item = (sequence, page range), KV head); its 4 waves
+// stride over the pages.  The MFMA N dimension holds CT tiles of 16 columns;
+// column col = (t, hn) = (col / G, col % G) is query row t of head g*G + hn,
+// so the q_len * G columns of a sequence share every K/V page load:
+//   S^T[16 tok x 16 col]  = K_page[16 x D] . Q^T[D x 16]      (16x16x32)
+//   O^T[16 d   x 16 col] += V^T_page[16 x 16] . P^T[16 x 16]  (16x16x16)
+// The C layout of the first (lane = 4 tokens of one column) is the B layout
+// of the second, so P never leaves registers.  Online softmax per page, P
+// split into bf16 hi + lo terms (~16 mantissa bits of p); the 4 waves merge
+// in LDS; a range that is the whole sequence writes bf16 output, otherwise
+// fp32 partials (m, l, acc) for the merge kernel.
+template <int D, int BS, int CT, bool Q8>
+__global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
   constexpr int KS = D / 32;   // k-steps of the 16x16x32 QK contraction
   constexpr int TT = BS / 16;  // 16-token tiles per page
   constexpr int DT = D / 16;   // 16-wide d tiles of the P.V contraction
-  constexpr int KW = D / 16;   // dwords of K codes per lane and tile (= 2 KS)
   constexpr int W = kDecodeWaves;
-  constexpr int ROW = D + 4;
-  constexpr int PB = BS * D + 4 * BS;  // page bytes: codes, then fp32 scales
+  constexpr int ROW = D + 4;   // padded LDS row of one column's accumulator
+  constexpr size_t PB = Q8 ? static_cast<size_t>(BS) * D + 4 * BS : static_cast<size_t>(BS) * D * 2;
   __shared__ float s_m[W][16];
   __shared__ float s_l[W][16];
+  // [W][Cn][ROW]: the live columns of one 16-column tile, staged for the wave merge.
   extern __shared__ float s_acc[];
 
   const int lane = threadIdx.x & 63;
@@ -412,115 +245,187 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_q8_mfma(DecodeArgs a
   const int wid = blockIdx.x / Hkv, g = blockIdx.x - wid * Hkv;
   const int b = a.work[2 * wid], c = a.work[2 * wid + 1];
   const int L = a.ctx_len[b];
+  const int row0 = a.q_start[b], qlen = a.q_start[b + 1] - row0;
+  const int C = qlen * G;  // live columns
   const int nblk = (L + BS - 1) / BS;
   const int p0 = c * a.pages_per_part;
   const int p1 = min(nblk, p0 + a.pages_per_part);
+  // Pages from mask0 on hold keys some column must not see (or past-end slots).
+  const int mask0 = (L - qlen + 1) / BS;
   const int32_t* table = a.tables + a.tbl_off[b];
-  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
-  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
 
-  bf16x8 qv[KS];
-  {
+  // Q^T operand and visible-key limit of this lane's column in each tile.
+  bf16x8 qv[CT][KS];
+  int lim[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = 16 * ct + n;
+    const int t = col / G, hn = col - t * G;
+    const bool live = col < C;
+    lim[ct] = live ? L - qlen + t + 1 : L;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           (static_cast<size_t>(b) * Hq + g * G + n) * D + (D / 4) * grp;
+                           (static_cast<size_t>(row0 + (live ? t : 0)) * Hq + g * G + hn) * D +
+                           (Q8 ? (D / 4) * grp : 8 * grp);
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      if (n < G)
-        qv[j] = *reinterpret_cast<const bf16x8*>(qrow + 8 * j);
+      if (live)
+        qv[ct][j] = *reinterpret_cast<const bf16x8*>(qrow + (Q8 ? 8 * j : 32 * j));
       else
-        qv[j] = bf16x8{};
+        qv[ct][j] = bf16x8{};
     }
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[DT];
+  float m_run[CT], l_run[CT];
+  f32x4 acc[CT][DT];
 #pragma unroll
-  for (int nt = 0; nt < DT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < CT; ++ct) {
+    m_run[ct] = -INFINITY;
+    l_run[ct] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < DT; ++nt) acc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  struct Page {
-    uint32_t k[TT][KW];  // K codes: token 16tt + n, d in [grp * D/4, +D/4)
-    uint32_t v[TT][DT];  // V codes: d = 16nt + n, tokens 16tt + 4grp .. +4
-    f32x4 ks[TT], vs[TT];  // scales of tokens 16tt + 4grp .. +4
-  };
-
+  using Page = PageRegs<D, BS, Q8>;
   auto load_page = [&](int pg, Page& P) {
     const int blk = uniform(table[pg]);
-    const uint8_t* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
-    const uint8_t* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
+    const char* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
+    const char* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
+    if constexpr (Q8) {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const uint4* ks = reinterpret_cast<const uint4*>(kp + (16 * tt + n) * D + (D / 4) * grp);
-      const uint4* vs = reinterpret_cast<const uint4*>(vp + 16 * tt * D + (16 * grp + n) * (D / 4));
+      for (int tt = 0; tt < TT; ++tt) {
+        const uint4* ks = reinterpret_cast<const uint4*>(kp + (16 * tt + n) * D + (D / 4) * grp);
+        const uint4* vs = reinterpret_cast<const uint4*>(vp + 16 * tt * D + (16 * grp + n) * (D / 4));
 #pragma unroll
-      for (int w = 0; w < KW / 4; ++w) {
-        const uint4 x = ks[w];
-        P.k[tt][4 * w] = x.x; P.k[tt][4 * w + 1] = x.y; P.k[tt][4 * w + 2] = x.z; P.k[tt][4 * w + 3] = x.w;
-        const uint4 y = vs[w];
-        P.v[tt][4 * w] = y.x; P.v[tt][4 * w + 1] = y.y; P.v[tt][4 * w + 2] = y.z; P.v[tt][4 * w + 3] = y.w;
+        for (int w = 0; w < DT / 4; ++w) {
+          const uint4 x = ks[w], y = vs[w];
+          P.kc[tt][4 * w] = x.x; P.kc[tt][4 * w + 1] = x.y; P.kc[tt][4 * w + 2] = x.z; P.kc[tt][4 * w + 3] = x.w;
+          P.vc[tt][4 * w] = y.x; P.vc[tt][4 * w + 1] = y.y; P.vc[tt][4 * w + 2] = y.z; P.vc[tt][4 * w + 3] = y.w;
+        }
+        P.ks[tt] = *reinterpret_cast<const f32x4*>(kp + BS * D + 4 * (16 * tt + 4 * grp));
+        P.vs[tt] = *reinterpret_cast<const f32x4*>(vp + BS * D + 4 * (16 * tt + 4 * grp));
       }
-      P.ks[tt] = *reinterpret_cast<const f32x4*>(kp + BS * D + 4 * (16 * tt + 4 * grp));
-      P.vs[tt] = *reinterpret_cast<const f32x4*>(vp + BS * D + 4 * (16 * tt + 4 * grp));
+    } else {
+      const uint16_t* k16 = reinterpret_cast<const uint16_t*>(kp);
+      const uint16_t* v16 = reinterpret_cast<const uint16_t*>(vp);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+          P.k[tt][j] = *reinterpret_cast<const bf16x8*>(k16 + (16 * tt + n) * D + 32 * j + 8 * grp);
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          P.v[nt][tt] = *reinterpret_cast<const s16x4*>(v16 + (16 * nt + n) * BS + 16 * tt + 4 * grp);
     }
   };
 
   auto process = [&](int pg, const Page& P) {
-    f32x4 s[TT];
+    // s[ct][tt][i] = score of token pg*BS + 16tt + 4grp + i for column 16ct + n.
+    f32x4 s[CT][TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 kop[KS];
 #pragma unroll
-      for (int j = 0; j < KS; ++j)
-        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(P.k[tt][2 * j], P.k[tt][2 * j + 1]),
-                                                        qv[j], s[tt], 0, 0, 0);
+      for (int j = 0; j < KS; ++j) {
+        if constexpr (Q8)
+          kop[j] = i8x8_to_bf16x8(P.kc[tt][2 * j], P.kc[tt][2 * j + 1]);
+        else
+          kop[j] = P.k[tt][j];
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        s[ct][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+          s[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j], qv[ct][j], s[ct][tt], 0, 0, 0);
+      }
     }
+    const bool edge = pg >= mask0;
+    s16x4 p_hi[CT][TT], p_lo[CT][TT];
+    float alpha[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[ct][tt][i];
+          if constexpr (Q8)
+            x *= P.ks[tt][i] * a.scale_log2;
+          else
+            x *= a.scale_log2;
+          if (edge && pg * BS + 16 * tt + 4 * grp + i >= lim[ct]) x = -INFINITY;
+          s[ct][tt][i] = x;
+          mloc = fmaxf(mloc, x);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float m_new = fmaxf(m_run[ct], mloc);
+      // A column with no visible key so far keeps m = -inf; exponents are
+      // then taken against 0, giving weight 0 instead of -inf - -inf.
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      alpha[ct] = exp2f(m_run[ct] - m_ref);
+      m_run[ct] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2f(s[ct][tt][i] - m_ref);
+          psum += e;
+          float w = e;
+          if constexpr (Q8) {
+            w = e * P.vs[tt][i];
+            // A masked or past-end slot may hold any scale bits: weight 0.
+            if (edge && pg * BS + 16 * tt + 4 * grp + i >= lim[ct]) w = 0.f;
+          }
+          const __bf16 hi = static_cast<__bf16>(w);
+          const __bf16 lo = static_cast<__bf16>(w - static_cast<float>(hi));
+          p_hi[ct][tt][i] = __builtin_bit_cast(short, hi);
+          p_lo[ct][tt][i] = __builtin_bit_cast(short, lo);
+        }
+      l_run[ct] = l_run[ct] * alpha[ct] + psum;
+    }
+    // bf16 pages: past-end slots of the last page have weight 0 and their
+    // values are zeroed too, so 0 * V cannot meet non-finite bits left there.
     const bool tail = pg == nblk - 1;
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = s[tt][i] * (P.ks[tt][i] * a.scale_log2);
-        if (tail && pg * BS + 16 * tt + 4 * grp + i >= L) x = -INFINITY;
-        s[tt][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    // P enters the P.V contraction as p * sv in two bf16 terms (hi, lo).
-    float psum = 0.f;
-    s16x4 p_hi[TT], p_lo[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = exp2f(s[tt][i] - m_new);
-        psum += e;
-        float w = e * P.vs[tt][i];
-        // An unused slot of the last page may hold any scale bits: weight 0.
-        if (tail && pg * BS + 16 * tt + 4 * grp + i >= L) w = 0.f;
-        const __bf16 hi = static_cast<__bf16>(w);
-        const __bf16 lo = static_cast<__bf16>(w - static_cast<float>(hi));
-        p_hi[tt][i] = __builtin_bit_cast(short, hi);
-        p_lo[tt][i] = __builtin_bit_cast(short, lo);
-      }
-    l_run = l_run * alpha + psum;
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
-      acc[nt] *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct][nt] *= alpha[ct];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const s16x4 v = i8x4_to_bf16x4(P.v[tt][nt]);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_hi[tt], acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_lo[tt], acc[nt], 0, 0, 0);
+        s16x4 v;
+        if constexpr (Q8) {
+          v = i8x4_to_bf16x4(P.vc[tt][nt]);
+        } else {
+          v = P.v[nt][tt];
+          if (tail) {
+            const int live = L - (pg * BS + 16 * tt + 4 * grp);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i >= live) v[i] = 0;
+          }
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          acc[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_hi[ct][tt], acc[ct][nt], 0, 0, 0);
+          acc[ct][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p_lo[ct][tt], acc[ct][nt], 0, 0, 0);
+        }
       }
     }
   };
 
+#if PA_DECODE_PREFETCH
   {
     Page pa_, pb_;
+    // The prefetch is issued unconditionally (the last page of the range
+    // re-loads itself): with the same number of loads in flight on every
+    // path, the wait before a page's first use only covers that page's loads.
     int p = p0 + wave;
     if (p < p1) load_page(p, pa_);
     while (p < p1) {
@@ -533,48 +438,68 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_q8_mfma(DecodeArgs a
       p += W;
     }
   }
-
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (grp == 0) {
-    s_m[wave][n] = m_run;
-    s_l[wave][n] = l_tot;
+#else
+  for (int p = p0 + wave; p < p1; p += W) {
+    Page P;
+    load_page(p, P);
+    process(p, P);
   }
-  if (n < G) {
-    float* dst = s_acc + (wave * G + n) * ROW + 4 * grp;
-#pragma unroll
-    for (int nt = 0; nt < DT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt) = acc[nt];
-  }
-  __syncthreads();
+#endif
 
+  // Per-column totals over the 4 lane groups, then merge the 4 waves, one
+  // 16-column tile at a time (LDS holds one tile of the 4 waves).
   const int base = a.part_base[b];
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int hn = idx / D, d = idx - hn * D;
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][hn]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float e = exp2f(s_m[w][hn] - M);
-      num += e * s_acc[(w * G + hn) * ROW + d];
-      den += e * s_l[w][hn];
+  for (int ct = 0; ct < CT; ++ct) {
+    const int Cn = min(16, C - 16 * ct);  // live columns of this tile (uniform)
+    if (Cn <= 0) break;
+    if (ct > 0) __syncthreads();  // the previous tile's readers are done
+    float l_tot = l_run[ct] + __shfl_xor(l_run[ct], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (grp == 0) {
+      s_m[wave][n] = m_run[ct];
+      s_l[wave][n] = l_tot;
     }
-    const int h = g * G + hn;
-    if (base < 0) {
-      static_cast<uint16_t*>(a.out)[(static_cast<size_t>(b) * Hq + h) * D + d] = f32_to_bf16(num / den);
-    } else {
-      const size_t row = static_cast<size_t>(base + c) * Hq + h;
-      a.part_acc[row * D + d] = num;
-      if (d == 0) {
-        a.part_m[row] = M;
-        a.part_l[row] = den;
+    if (n < Cn) {
+      float* dst = s_acc + (wave * Cn + n) * ROW + 4 * grp;
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt) = acc[ct][nt];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < Cn * D; idx += 256) {
+      const int cn = idx / D, d = idx - cn * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][cn]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        // A wave without visible keys has m = -inf and contributes nothing.
+        const float e = s_m[w][cn] == -INFINITY ? 0.f : exp2f(s_m[w][cn] - M);
+        num += e * s_acc[(w * Cn + cn) * ROW + d];
+        den += e * s_l[w][cn];
+      }
+      const int col = 16 * ct + cn;
+      const int t = col / G, h = g * G + (col - t * G);
+      if (base < 0) {
+        static_cast<uint16_t*>(a.out)[(static_cast<size_t>(row0 + t) * Hq + h) * D + d] = f32_to_bf16(num / den);
+      } else {
+        const size_t row = static_cast<size_t>(base) + (static_cast<size_t>(c) * qlen + t) * Hq + h;
+        a.part_acc[row * D + d] = num;
+        if (d == 0) {
+          a.part_m[row] = M;
+          a.part_l[row] = den;
+        }
       }
     }
   }
 }
 
 // ----------------------------------------------------------------- merge ---
+// Log-sum-exp combination of the partials of one (query row, head) of a
+// split sequence: M = max m_c, o = sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c
+// (CMU 11-667 lecture 19 section 3, online_softmax_stats, applied across
+// page ranges).  A range with no visible key has m = -inf and weight 0.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   constexpr int V4 = D / 4;      // float4 lanes per partial row
@@ -585,11 +510,13 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int Hq = a.num_heads;
   const int mi = blockIdx.x / Hq, h = blockIdx.x - mi * Hq;
-  const int b = a.merge_seq[mi];
+  const int b = a.merge_rows[2 * mi], t = a.merge_rows[2 * mi + 1];
+  const int row0 = a.q_start[b], qlen = a.q_start[b + 1] - row0;
   const int base = a.part_base[b], np = a.n_parts_of[b];
+  auto prow = [&](int c) { return static_cast<size_t>(base) + (static_cast<size_t>(c) * qlen + t) * Hq + h; };
 
   float M = -INFINITY;
-  for (int c = tid; c < np; c += 256) M = fmaxf(M, a.part_m[static_cast<size_t>(base + c) * Hq + h]);
+  for (int c = tid; c < np; c += 256) M = fmaxf(M, a.part_m[prow(c)]);
   M = wave_max(M);
   if ((tid & 63) == 0) s_red[tid >> 6] = M;
   __syncthreads();
@@ -599,8 +526,9 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int c = r; c < np; c += R) {
-    const size_t row = static_cast<size_t>(base + c) * Hq + h;
-    const float w = exp2f(a.part_m[row] - M);
+    const size_t row = prow(c);
+    const float mc = a.part_m[row];
+    const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
     num += w * reinterpret_cast<const f32x4*>(a.part_acc + row * D)[v];
     den += w * a.part_l[row];
   }
@@ -616,22 +544,26 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
       dtot += s_den[k];
     }
     const float inv = 1.f / dtot;
-    T* o = static_cast<T*>(a.out) + (static_cast<size_t>(b) * Hq + h) * D + 4 * tid;
+    T* o = static_cast<T*>(a.out) + (static_cast<size_t>(row0 + t) * Hq + h) * D + 4 * tid;
 #pragma unroll
     for (int i = 0; i < 4; ++i) Elt<T>::store(o + i, tot[i] * inv);
   }
 }
 
-template <int D, int BS>
-void launch_gqa(const DecodeArgs& a, int groups, hipStream_t stream) {
-  const size_t shmem = static_cast<size_t>(kDecodeWaves) * a.group * (D + 4) * sizeof(float);
-  hipLaunchKernelGGL((decode_gqa_mfma<D, BS>), dim3(groups), dim3(256), shmem, stream, a);
+template <int D, int BS, int CT, bool Q8>
+void launch_mfma(const DecodeArgs& a, int groups, hipStream_t stream) {
+  const size_t shmem = static_cast<size_t>(kDecodeWaves) * min(a.max_cols, 16) * (D + 4) * sizeof(float);
+  hipLaunchKernelGGL((decode_mfma<D, BS, CT, Q8>), dim3(groups), dim3(256), shmem, stream, a);
 }
 
-template <int D, int BS>
-void launch_q8(const DecodeArgs& a, int groups, hipStream_t stream) {
-  const size_t shmem = static_cast<size_t>(kDecodeWaves) * a.group * (D + 4) * sizeof(float);
-  hipLaunchKernelGGL((decode_q8_mfma<D, BS>), dim3(groups), dim3(256), shmem, stream, a);
+template <int CT, bool Q8>
+void launch_mfma_shape(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream) {
+  const int groups = a.n_work * a.num_kv_heads;
+  const int D = geom.head_dim, BS = geom.block_size;
+  if (D == 128 && BS == 16) launch_mfma<128, 16, CT, Q8>(a, groups, stream);
+  else if (D == 128 && BS == 32) launch_mfma<128, 32, CT, Q8>(a, groups, stream);
+  else if (D == 64 && BS == 16) launch_mfma<64, 16, CT, Q8>(a, groups, stream);
+  else launch_mfma<64, 32, CT, Q8>(a, groups, stream);
 }
 
 void launch_generic(const PoolGeom& geom, const GenericArgs& g, dim3 grid, hipStream_t stream) {
@@ -656,26 +588,25 @@ DecodeKernel pick_decode_kernel(const PoolGeom& geom, int32_t group) {
   return DecodeKernel::kGeneric;
 }
 
+bool decode_handles_rows(const PoolGeom& geom, int32_t group, int32_t max_q_len) {
+  return pick_decode_kernel(geom, group) != DecodeKernel::kGeneric &&
+         static_cast<int64_t>(max_q_len) * group <= kDecodeMaxCols;
+}
+
 hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream) {
-  switch (pick_decode_kernel(geom, a.group)) {
-    case DecodeKernel::kGqaMfma: {
-      const int groups = a.n_work * a.num_kv_heads;
-      const int D = geom.head_dim, BS = geom.block_size;
-      if (D == 128 && BS == 16) launch_gqa<128, 16>(a, groups, stream);
-      else if (D == 128 && BS == 32) launch_gqa<128, 32>(a, groups, stream);
-      else if (D == 64 && BS == 16) launch_gqa<64, 16>(a, groups, stream);
-      else launch_gqa<64, 32>(a, groups, stream);
+  const DecodeKernel k = pick_decode_kernel(geom, a.group);
+  if (k != DecodeKernel::kGeneric && a.max_cols > kDecodeMaxCols) return hipErrorInvalidValue;
+  if (k == DecodeKernel::kGeneric && a.max_cols > a.group) return hipErrorInvalidValue;  // q_len 1 only
+  const bool two = a.max_cols > 16;
+  switch (k) {
+    case DecodeKernel::kGqaMfma:
+      if (two) launch_mfma_shape<2, false>(geom, a, stream);
+      else launch_mfma_shape<1, false>(geom, a, stream);
       break;
-    }
-    case DecodeKernel::kQ8Mfma: {
-      const int groups = a.n_work * a.num_kv_heads;
-      const int D = geom.head_dim, BS = geom.block_size;
-      if (D == 128 && BS == 16) launch_q8<128, 16>(a, groups, stream);
-      else if (D == 128 && BS == 32) launch_q8<128, 32>(a, groups, stream);
-      else if (D == 64 && BS == 16) launch_q8<64, 16>(a, groups, stream);
-      else launch_q8<64, 32>(a, groups, stream);
+    case DecodeKernel::kQ8Mfma:
+      if (two) launch_mfma_shape<2, true>(geom, a, stream);
+      else launch_mfma_shape<1, true>(geom, a, stream);
       break;
-    }
     default: {
       GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, nullptr, nullptr,
                     a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,

@@ -34,6 +34,12 @@ hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_
 enum class DecodeKernel { kGqaMfma, kQ8Mfma, kGeneric };
 DecodeKernel pick_decode_kernel(const PoolGeom& geom, int32_t group);
 
+// Query-row columns (q_len * group) one decode workgroup covers.
+constexpr int32_t kDecodeMaxCols = 32;
+// Whether the split-K decode kernels serve query rows of up to max_q_len
+// positions per sequence (the MFMA kernels, q_len * group <= 32).
+bool decode_handles_rows(const PoolGeom& geom, int32_t group, int32_t max_q_len);
+
 // Decode: partial kernel, then (if any sequence was split) the merge.
 hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_merge(const PoolGeom& geom, const DecodeArgs& args, hipStream_t stream);

@@ -29,8 +29,8 @@ constexpr int64_t kTargetGroups = 2048;
 
 Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t tokens_per_part,
-                         const int32_t* extra_tokens, int32_t slot_count, DecodePlan* plan,
-                         std::string* msg) {
+                         const int32_t* extra_tokens, const int32_t* q_lens, int32_t slot_count,
+                         DecodePlan* plan, std::string* msg) {
   if (B <= 0 || !seqs) {
     *msg = "batch must be positive with a non-NULL seqs array";
     return kInvalidArg;
@@ -55,7 +55,26 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
       *msg = "kv_len must be positive (sequence " + std::to_string(seqs[b]) + " is empty)";
       return kInvalidArg;
     }
+    if (q_lens && (q_lens[b] < 1 || q_lens[b] > len[b])) {
+      *msg = "q_lens[b] must be in 1..length(seq) (the rows are the last positions)";
+      return kInvalidArg;
+    }
     total_pages += nblk[b];
+  }
+  std::vector<int32_t> qlen(B, 1);
+  int64_t n_rows = B;
+  int32_t max_q = 1;
+  if (q_lens) {
+    n_rows = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      qlen[b] = q_lens[b];
+      n_rows += qlen[b];
+      max_q = std::max(max_q, qlen[b]);
+    }
+    if (n_rows > INT32_MAX / 2) {
+      *msg = "too many query rows";
+      return kInvalidArg;
+    }
   }
 
   // Pages per partition: the largest candidate that still yields enough
@@ -89,15 +108,24 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   std::vector<Item> items;
   std::vector<int32_t> part_base(B, -1), merge;
   int32_t n_parts = 0;
+  int64_t row_heads = 0;
   for (int32_t b = 0; b < B; ++b) {
     int32_t nb = static_cast<int32_t>(nblk[b]);
     int32_t np = static_cast<int32_t>(ceil_div(nb, ppp));
     n_parts_of[b] = np;
     for (int32_t c = 0; c < np; ++c) items.push_back({b, c, std::min(ppp, nb - c * ppp)});
     if (np > 1) {
-      part_base[b] = n_parts;
+      if (row_heads + static_cast<int64_t>(np) * qlen[b] * num_heads > INT32_MAX) {
+        *msg = "too many split-K partial rows";
+        return kInvalidArg;
+      }
+      part_base[b] = static_cast<int32_t>(row_heads);
+      row_heads += static_cast<int64_t>(np) * qlen[b] * num_heads;
       n_parts += np;
-      merge.push_back(b);
+      for (int32_t t = 0; t < qlen[b]; ++t) {
+        merge.push_back(b);
+        merge.push_back(t);
+      }
     }
   }
   // Longest page ranges first so short tails fill in at the end.
@@ -108,16 +136,19 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.batch = B;
   p.pages_per_part = ppp;
   p.n_work = static_cast<int32_t>(items.size());
-  p.n_merge = static_cast<int32_t>(merge.size());
+  p.n_merge = static_cast<int32_t>(merge.size() / 2);
   p.n_parts = n_parts;
+  p.n_rows = static_cast<int32_t>(n_rows);
+  p.max_q_len = max_q;
   p.total_pages = total_pages;
   std::vector<int32_t>& meta = p.meta;
   p.ctx_off = reserve(meta, B);
   p.tbl_off_off = reserve(meta, B);
+  p.qstart_off = reserve(meta, B + 1);
   p.base_off = reserve(meta, B);
   p.nparts_off = reserve(meta, B);
   p.work_off = reserve(meta, 2 * items.size());
-  p.merge_off = reserve(meta, std::max<size_t>(1, merge.size()));
+  p.merge_off = reserve(meta, std::max<size_t>(2, merge.size()));
   p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
   p.slots_off = reserve(meta, 2 * static_cast<size_t>(std::max(slot_count, 0)));
   int32_t* ctx = at_bytes(meta, p.ctx_off);
@@ -127,8 +158,12 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   int32_t* work = at_bytes(meta, p.work_off);
   int32_t* mrg = at_bytes(meta, p.merge_off);
   int32_t* tables = at_bytes(meta, p.tables_off);
+  int32_t* qs = at_bytes(meta, p.qstart_off);
   int64_t cursor = 0;
+  int32_t row = 0;
   for (int32_t b = 0; b < B; ++b) {
+    qs[b] = row;
+    row += qlen[b];
     ctx[b] = static_cast<int32_t>(len[b]);
     toff[b] = static_cast<int32_t>(cursor);
     base[b] = part_base[b];
@@ -142,10 +177,11 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     work[2 * i] = items[i].b;
     work[2 * i + 1] = items[i].c;
   }
+  qs[B] = row;
   std::copy(merge.begin(), merge.end(), mrg);
 
   p.meta_bytes = align_up(meta.size() * sizeof(int32_t), kWsAlign);
-  size_t rows_hq = static_cast<size_t>(n_parts) * num_heads;
+  size_t rows_hq = static_cast<size_t>(row_heads);
   p.part_m_off = p.meta_bytes;
   p.part_l_off = p.part_m_off + align_up(rows_hq * sizeof(float), kWsAlign);
   p.part_acc_off = p.part_l_off + align_up(rows_hq * sizeof(float), kWsAlign);

@@ -37,25 +37,32 @@ struct PoolGeom {
 
 
 // Kernel arguments of the decode partial kernels.  Every pointer is device
-// memory inside the workspace, except q / out / pools.
+// memory inside the workspace, except q / out / pools.  Sequence b has
+// q_len_b = q_start[b+1] - q_start[b] query rows (its last q_len_b
+// positions; 1 for plain decode); a split sequence keeps one partial row per
+// (partition, query row, head).
 struct DecodeArgs {
   const void* k_pool;
   const void* v_pool;
-  const void* q;            // [B][Hq][D]
-  void* out;                // [B][Hq][D]
+  const void* q;            // [R][Hq][D], R = q_start[B]
+  void* out;                // [R][Hq][D]
   const int32_t* ctx_len;   // [B] tokens per sequence
   const int32_t* tbl_off;   // [B] offset of the sequence's table in `tables`
   const int32_t* tables;    // concatenated block tables
+  const int32_t* q_start;   // [B+1] first query row of b
   const int32_t* work;      // [n_work][2] = (b, partition index)
-  const int32_t* part_base; // [B] first partial row of b, or -1 = single partition
-  float* part_m;            // [n_parts][Hq]
-  float* part_l;            // [n_parts][Hq]
-  float* part_acc;          // [n_parts][Hq][D]
-  const int32_t* merge_seq; // [n_merge] sequences with more than one partition
+  const int32_t* part_base; // [B] first partial row-head of b, or -1 = single partition;
+                            // row-head of (partition c, row t, head h) =
+                            // part_base + (c * q_len_b + t) * Hq + h
+  float* part_m;            // [row-heads]
+  float* part_l;            // [row-heads]
+  float* part_acc;          // [row-heads][D]
+  const int32_t* merge_rows;// [n_merge][2] = (b, t) query rows of split sequences
   const int32_t* n_parts_of;// [B] partitions of b
   int32_t batch, num_heads, num_kv_heads, group;
   int32_t pages_per_part;
   int32_t n_work, n_merge;
+  int32_t max_cols;         // max over b of q_len_b * group (MFMA columns)
   float scale_log2;         // log2(e) / sqrt(head_dim)
 };
 
@@ -63,23 +70,26 @@ struct DecodePlan {
   std::vector<int32_t> meta;  // host image of the metadata region
   size_t meta_bytes = 0;      // aligned
   size_t part_m_off = 0, part_l_off = 0, part_acc_off = 0, total_bytes = 0;
-  size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, work_off = 0, base_off = 0,
+  size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, qstart_off = 0, work_off = 0, base_off = 0,
          merge_off = 0, nparts_off = 0, slots_off = 0;  // byte offsets in the workspace
   int32_t n_work = 0, n_merge = 0, n_parts = 0, pages_per_part = 0, batch = 0;
+  int32_t n_rows = 0, max_q_len = 1;
   int64_t total_pages = 0;
 };
 
 // Build the decode plan for `seqs`.  Validates the batch (known sequences,
-// non-empty contexts); returns kUnknownSeq / kInvalidArg with msg.
+// non-empty contexts, 1 <= q_lens[b] <= length); returns kUnknownSeq /
+// kInvalidArg with msg.
 // `tokens_per_part` = 0 chooses the partition size automatically.
 // `extra_tokens` (nullable, [B]) sizes the plan as if row b had that many
 // more tokens (page ids of not-yet-allocated pages are left 0: such a plan
-// is for sizing only).  `slot_count` reserves an int64 slot array (slots_off)
-// for the caller to fill.
+// is for sizing only).  `q_lens` (nullable = all 1) gives the query rows of
+// each sequence.  `slot_count` reserves an int64 slot array (slots_off) for
+// the caller to fill.
 Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t tokens_per_part,
-                         const int32_t* extra_tokens, int32_t slot_count, DecodePlan* plan,
-                         std::string* msg);
+                         const int32_t* extra_tokens, const int32_t* q_lens, int32_t slot_count,
+                         DecodePlan* plan, std::string* msg);
 
 // Kernel arguments of the prefill kernels.
 struct PrefillArgs {

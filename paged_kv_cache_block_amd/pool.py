@@ -186,6 +186,20 @@ class DevicePool:
                                    self._stream(stream), slots_out=True)
         return out, slots
 
+    def verify_step(self, seqs, q_lens, k_new, v_new, q, out=None, stream=None, ws=None):
+        """Append ``q_lens[b]`` tokens per sequence, store their K/V rows
+        ([sum q_lens, Hkv, D]) and attend causally for those rows (``q``
+        [sum q_lens, Hq, D]).  Returns ``(out, slots)``."""
+        num_heads = q.shape[1]
+        if out is None:
+            out = _torch().empty_like(q)
+        need = abi.pa_verify_step_workspace_bytes(self.handle, seqs, q_lens, num_heads) or 256
+        if ws is None:
+            ws = self.workspace(need)
+        slots = abi.pa_verify_step(self.handle, seqs, q_lens, num_heads, k_new, v_new, q, out, ws,
+                                   ws.numel(), self._stream(stream), slots_out=True)
+        return out, slots
+
     def prefill(self, seqs, q_lens, q, out=None, stream=None, ws=None):
         """Last ``q_lens[b]`` positions of each sequence: ``q`` [sum q_lens, Hq, D]."""
         num_heads = q.shape[1]

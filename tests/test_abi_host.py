@@ -172,6 +172,21 @@ def test_workspace_queries():
     assert abi.pa_prefill_workspace_bytes(h, [1, 2], [17, 1], 2) > 0
     assert abi.pa_prefill_workspace_bytes(h, [1], [18], 2) == 0  # q_len > length
     assert abi.pa_prefill_workspace_bytes(h, [1], [0], 2) == 0
+    # Multi-token step: sized for the lengths after appending q_lens tokens.
+    assert abi.pa_verify_step_workspace_bytes(h, [0, 1], [4, 2], 4) > 0
+    assert abi.pa_verify_step_workspace_bytes(h, [9], [3], 4) > 0     # empty before, 3 after
+    assert abi.pa_verify_step_workspace_bytes(h, [0], [0], 4) == 0
+    assert abi.pa_verify_step_workspace_bytes(h, [77], [1], 4) == 0
+
+
+def test_verify_step_on_metadata_only_pool_changes_nothing():
+    pool = _meta(16, 4)
+    pool.create(0)
+    pool.append(0, 5)
+    before = (pool.stats(), pool.block_table(0).tolist())
+    with pytest.raises(InvalidArgumentError):
+        abi.pa_verify_step(pool.handle, [0], [3], 2, 256, 256, 256, 256, 256, 1 << 20, None)
+    assert before == (pool.stats(), pool.block_table(0).tolist())
 
 
 def _compare(pool, ref):
