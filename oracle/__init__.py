@@ -17,7 +17,8 @@ Sources (the pages, cited by title and section):
   -- ``PagedKVPool`` (preflighted multi-token append, share_prefix, release,
   fill accounting, ``validate``) and its embedded reference contract; its
   KV-compression experiment (per-row absmax codes, ``fake_quantize_rows``);
-  its prefix-caching cell (``prefix_key``, ``run_prefix_trace``).
+  its prefix-caching cell (``prefix_key``, ``run_prefix_trace``); its
+  eviction cell (``streaming_keep_indices``) and explicit window caches.
 * docs.rs ferrum-kv 0.4.0 ``src/attention.rs`` -- ``paged_attention``
   (GQA head grouping, 1/sqrt(head_dim) scale, bottom-right causal mask).
 * CMU 11-667 lecture 19 ``infer_world.py``, section 3 "online softmax and
@@ -32,6 +33,9 @@ Modules:
   fp32 scales, read-back values); a ``Pool(quant_bits=8)`` stores through it.
 * :mod:`oracle.prefix` -- prefix-hash block reuse: complete-block keys
   (scope, revision, all preceding tokens) mapped to pinned pool blocks.
+* :mod:`oracle.window` -- sliding-window attention with sinks
+  (``streaming_keep_indices``) over the resident rows of a windowed pool
+  sequence.
 * :mod:`oracle.attention` -- the attention definition, its online-softmax
   restatement, the log-sum-exp merge of partial results and a pure-Python
   brute force for tiny inputs.
@@ -51,6 +55,7 @@ from .quant import (
     packed_bytes,
 )
 from .prefix import PrefixCache, prefix_key, run_prefix_trace
+from .window import streaming_keep_indices, windowed_attention
 from .attention import (
     attention,
     paged_attention,
@@ -82,4 +87,6 @@ __all__ = [
     "PrefixCache",
     "prefix_key",
     "run_prefix_trace",
+    "streaming_keep_indices",
+    "windowed_attention",
 ]

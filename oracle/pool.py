@@ -38,6 +38,12 @@ Such a reference counts in the refcount, so the block stays allocated after
 every sequence holding it is released; a block only pins hold has fill 0 (no
 live sequence uses its slots), so it counts as capacity, not payload.
 
+Windows: a sequence can carry a (sinks, recent) window (oracle.window).  An
+append then releases the pages that lie wholly between the sink pages and
+the window of its first appended row; such a table entry becomes ``HOLE``
+(its position stays counted in the length).  A rollback (``truncate``) may
+not fall before the resident window.
+
 Storage: ``K`` and ``V`` are float64 arrays ``[num_blocks, block_size,
 num_kv_heads, head_dim]`` -- block, slot, head, dim -- the first page's
 ``keys[num_blocks, block_size, dim]`` with a KV-head axis added in the
@@ -85,6 +91,9 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
+HOLE = -1  # table entry of a page released by the window policy
+
+
 class Pool:
     """Fixed pool of physical KV blocks shared by refcounted block tables."""
 
@@ -114,6 +123,9 @@ class Pool:
         heapq.heapify(self._free_heap)
         self.tables: dict[int, list[int]] = {}
         self.lengths: dict[int, int] = {}
+        # Window policy (sinks, recent) of windowed sequences (oracle.window);
+        # an evicted page's table entry is HOLE.
+        self.windows: dict = {}
         self.copies: list[tuple[int, int]] = []
         self.store_values = bool(store_values)
         if self.store_values:
@@ -223,7 +235,78 @@ class Pool:
         for _ in range(_ceil_div(length + n, self.block_size) - len(table)):
             table.append(self._allocate())
         self.lengths[seq] = length + n
-        return [self.slot(seq, p) for p in range(first, first + n)]
+        slots = [self.slot(seq, p) for p in range(first, first + n)]
+        if n and seq in self.windows:
+            self._evict(seq, first)
+        return slots
+
+    # ------------------------------------------------------------ windows
+    def set_window(self, seq, sinks, recent):
+        """Give ``seq`` a (sinks, recent) window: its queries see the
+        positions oracle.window.streaming_keep_indices keeps with budget
+        ``sinks + recent``, and appends release the pages no later query of
+        the appended rows can see."""
+        self._existing(seq)
+        sinks = _non_negative_int(sinks, "sinks")
+        recent = _non_negative_int(recent, "recent")
+        if sinks + recent < 1:
+            raise ValueError("the window must keep at least one token")
+        self.windows[seq] = (sinks, recent)
+
+    def _evict(self, seq, first_new):
+        """Release the pages that lie wholly after the sink pages and before
+        the window of the first appended row (position ``first_new``, which
+        sees ``[first_new + 1 - recent, first_new]``); pages holding appended
+        rows are kept."""
+        sinks, recent = self.windows[seq]
+        bs = self.block_size
+        table = self.tables[seq]
+        sink_pages = _ceil_div(sinks, bs)
+        lo = first_new + 1 - recent
+        end = min(max(lo, 0) // bs, first_new // bs)
+        for j in range(sink_pages, end):
+            if table[j] != HOLE:
+                self._drop_ref(table[j])
+                table[j] = HOLE
+
+    def evicted_end(self, seq):
+        """Position where the resident part after the sinks starts (0 when
+        nothing was released)."""
+        table = self.tables[self._existing(seq)]
+        last = max((j for j, b in enumerate(table) if b == HOLE), default=-1)
+        return (last + 1) * self.block_size if last >= 0 else 0
+
+    def truncate(self, seq, new_length):
+        """Drop the positions from ``new_length`` on (a rollback).  Evicted
+        positions cannot come back: ``new_length`` must not fall before the
+        resident window."""
+        self._existing(seq)
+        new_length = _non_negative_int(new_length, "new_length")
+        length = self.lengths[seq]
+        if new_length > length:
+            raise ValueError("new_length exceeds the sequence length")
+        if new_length < self.evicted_end(seq):
+            raise ValueError("rollback lies outside the retained interval")
+        table = self.tables[seq]
+        keep = _ceil_div(new_length, self.block_size)
+        for block in table[keep:]:
+            if block != HOLE:
+                self._drop_ref(block)
+        del table[keep:]
+        self.lengths[seq] = new_length
+
+    def resident(self, seq):
+        """(positions, K, V) of the resident positions of ``seq``, ascending."""
+        length = self.lengths[self._existing(seq)]
+        table = self.tables[seq]
+        pos = [p for p in range(length) if table[p // self.block_size] != HOLE]
+        keys = np.empty((len(pos), self.num_kv_heads, self.head_dim))
+        values = np.empty_like(keys)
+        for i, p in enumerate(pos):
+            block, offset = table[p // self.block_size], p % self.block_size
+            keys[i] = self.K[block, offset]
+            values[i] = self.V[block, offset]
+        return pos, keys, values
 
     def share(self, src, dst, prefix):
         """New sequence ``dst`` holding the blocks covering ``src[:prefix]``."""
@@ -234,9 +317,12 @@ class Pool:
         self._new(dst)
         table = self.tables[src][:_ceil_div(prefix, self.block_size)]
         for block in table:
-            self.refs[block] += 1
+            if block != HOLE:
+                self.refs[block] += 1
         self.tables[dst] = list(table)
         self.lengths[dst] = prefix
+        if src in self.windows:
+            self.windows[dst] = self.windows[src]
 
     def fork(self, src, dst):
         """Child with the parent's whole table (every refcount + 1)."""
@@ -276,9 +362,11 @@ class Pool:
         """Drop one reference per block; blocks at zero become free."""
         self._existing(seq)
         for block in self.tables[seq]:
-            self._drop_ref(block)
+            if block != HOLE:
+                self._drop_ref(block)
         del self.tables[seq]
         del self.lengths[seq]
+        self.windows.pop(seq, None)
 
     # ------------------------------------------------------------ addressing
     def address(self, seq, p):
@@ -287,6 +375,8 @@ class Pool:
         if not 0 <= p < self.lengths[seq]:
             raise ValueError("token index must address a live token")
         logical, offset = divmod(p, self.block_size)
+        if self.tables[seq][logical] == HOLE:
+            raise ValueError("token index addresses an evicted page")
         return self.tables[seq][logical], offset
 
     def slot(self, seq, p):
@@ -332,7 +422,8 @@ class Pool:
         for seq, table in self.tables.items():
             length = self.lengths[seq]
             for j, block in enumerate(table):
-                fill[block] = max(fill[block], min(self.block_size, length - j * self.block_size))
+                if block != HOLE:
+                    fill[block] = max(fill[block], min(self.block_size, length - j * self.block_size))
         return fill
 
     def stats(self):
@@ -366,8 +457,11 @@ class Pool:
             length = self.lengths[seq]
             assert length >= 0, "negative length"
             assert len(table) == _ceil_div(length, self.block_size), "table length"
-            assert len(set(table)) == len(table), "block twice in one table"
-            for block in table:
+            live = [b for b in table if b != HOLE]
+            assert len(set(live)) == len(live), "block twice in one table"
+            if table and length % self.block_size:
+                assert table[-1] != HOLE, "a partially filled tail page is evicted"
+            for block in live:
                 assert 0 <= block < self.num_blocks, "block id out of range"
                 expected[block] += 1
         fill = self.fills()
