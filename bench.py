@@ -170,16 +170,68 @@ def run_decode(args, kv="bf16"):
         "sum_len": int(lengths.sum()),
     }
     achieved = alg_per_step / (kernel_ms * 1e-3) / 1e9
-    kernel = "decode_q8_mfma" if kv == "i8" else "decode_gqa_mfma"
+    kernel = "decode_mfma_i8" if kv == "i8" else "decode_mfma_bf16"
     traffic = recorded_traffic(f"{kernel}__gqa_decode")
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                           "traffic": None if traffic is None else round(traffic / 1e9, 4),
                           "traffic_unit": "GB per launch",
-                          "kernel": f"{kernel}<128,16>",
+                          "kernel": f"decode_mfma<128,16,1,{'int8' if kv == 'i8' else 'bf16'}>",
                           "decode_plus_merge_GBs": round(alg_per_step / ((kernel_ms + merge_ms) * 1e-3) / 1e9, 1)}
     pool.close()
     return wl, result
+
+
+def run_verify(args, q_len=4):
+    """Multi-token steps: every sequence of the decode workload appends and
+    verifies ``q_len`` tokens per step (pa_verify_step); the K/V pages are
+    read once for all q_len rows."""
+    import torch
+    from paged_kv_cache_block_amd import abi
+    from synth import gqa_decode
+
+    wl = gqa_decode()
+    log(f"building the verify workload ({q_len} rows per sequence and step)")
+    pool = build_pool(wl)
+    seqs = list(wl.decode_seqs)
+    B = len(seqs)
+    q_lens = [q_len] * B
+    R = B * q_len
+    total_steps = args.warmup + args.steps
+    gen = torch.Generator(device="cuda").manual_seed(4321)
+    new_k = torch.randn((total_steps, R, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    new_v = torch.randn((total_steps, R, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    q = torch.randn((R, wl.num_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lengths = np.array([pool.seq_len(s) for s in seqs], dtype=np.int64)
+    need = abi.pa_verify_step_workspace_bytes(pool.handle, seqs, q_lens, wl.num_heads)
+    ws = torch.empty(2 * need + (1 << 20), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(args.warmup):
+        abi.pa_verify_step(pool.handle, seqs, q_lens, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws.numel(), stream)
+        lengths += q_len
+    torch.cuda.synchronize()
+    abi.pa_timing_reset()
+    abi.pa_timing_enable(True)
+    alg = []
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        abi.pa_verify_step(pool.handle, seqs, q_lens, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws.numel(), stream)
+        lengths += q_len
+        alg.append(decode_alg_bytes(lengths, wl) + 2 * (R - B) * wl.num_heads * wl.head_dim * wl.elt_bytes)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    abi.pa_timing_enable(False)
+    dec_ms, dec_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
+    pool.validate()
+    pool.close()
+    ms = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = dec_ms / max(dec_n, 1)
+    return {"workload": f"gqa_decode with {q_len} query rows per sequence and step (pa_verify_step: "
+                        f"append {q_len} tokens + store their K/V + causal attention)",
+            "ms_per_step": round(ms, 5), "rows_per_s": round(R / (ms * 1e-3), 1),
+            "decode_kernel_us": round(kernel_ms * 1e3, 2),
+            "kernel_GBs": round(float(np.mean(alg)) / (kernel_ms * 1e-3) / 1e9, 1)}
 
 
 def run_prefill(args):
@@ -367,6 +419,7 @@ def main():
                                            "alg_bytes_per_step", "kernel_launches", "sum_len")},
             "roofline": q8["roofline"],
         }
+    line["verify_q4"] = run_verify(args, 4)
     if not args.no_prefill:
         line["prefill"] = run_prefill(args)
     line["prefix_cache"] = run_prefix_cache()

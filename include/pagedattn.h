@@ -17,6 +17,9 @@
  *   [KVprefix]  vladkulikov.com notebook "Модуль 10", the prefix-caching
  *               cell (prefix_key, run_prefix_trace) and its key-identity
  *               checks.
+ *   [KVwindow]  vladkulikov.com notebook "Модуль 10", the eviction cell
+ *               (streaming_keep_indices) and the explicit window caches
+ *               (window, truncate).
  *   [KVquant]   vladkulikov.com notebook "Модуль 10", the KV-compression
  *               experiment (per-row absmax codes, fake_quantize_rows, and
  *               the packed size of codes plus one fp32 scale per row).
@@ -182,7 +185,8 @@ pa_status pa_append_batch(pa_pool* pool, const int64_t* seqs, const int32_t* n_t
  * blocks of `src` with every refcount + 1 and length prefix_tokens
  * ([PagedPool] share_prefix).  Host-only.
  * Errors: PA_ERR_UNKNOWN_SEQ (src), PA_ERR_SEQ_EXISTS (dst),
- *   PA_ERR_INVALID_ARG (prefix_tokens < 0 or > length of src). */
+ *   PA_ERR_INVALID_ARG (prefix_tokens < 0, > length of src, or before the
+ *   end of pages src's window released). */
 pa_status pa_share(pa_pool* pool, int64_t src, int64_t dst, int32_t prefix_tokens);
 
 /* pa_share(pool, src, dst, length of src): the child holds the parent's whole
@@ -194,6 +198,31 @@ pa_status pa_fork(pa_pool* pool, int64_t src, int64_t dst);
  * release).  A second release of the same id is PA_ERR_UNKNOWN_SEQ.
  * Host-only; device contents are left as they are. */
 pa_status pa_release(pa_pool* pool, int64_t seq);
+
+/* ------------------------------------------------------ windows, rollback --- */
+/* Sliding window with attention sinks ([KVwindow]).  After this call every
+ * query row of `seq` (position p, causal limit p + 1) sees the positions
+ * streaming_keep_indices(p + 1, sink_tokens + recent_tokens, sink_tokens)
+ * keeps: all of [0, p] while p + 1 <= sink_tokens + recent_tokens, else
+ * [0, sink_tokens) and [p + 1 - recent_tokens, p].  Each later append of n
+ * tokens at old length L0 releases (refcount - 1, the table entry becomes
+ * -1) the pages lying wholly after the sink pages and before position
+ * L0 + 1 - recent_tokens (the window of its first appended row), never a
+ * page holding an appended row; the decode kernels skip the pages no row
+ * sees.  Released positions stay counted in the length and are gone:
+ * a row sees the kept positions that are still resident.  fork / share
+ * copy the window and the released entries.  Host-only.
+ * Errors: PA_ERR_UNKNOWN_SEQ; PA_ERR_INVALID_ARG unless sink_tokens >= 0,
+ *   recent_tokens >= 0 and 1 <= sink_tokens + recent_tokens. */
+pa_status pa_seq_set_window(pa_pool* pool, int64_t seq, int32_t sink_tokens, int32_t recent_tokens);
+
+/* Roll `seq` back to new_length (speculative tokens rejected): positions
+ * [new_length, length) are dropped and pages past ceil(new_length /
+ * block_size) released.  new_length may not fall before the first position
+ * after the last released page ([KVwindow] rollback cannot bring evicted
+ * tokens back).  A later append into a shared partial tail copies it first.
+ * Host-only.  Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG. */
+pa_status pa_truncate(pa_pool* pool, int64_t seq, int32_t new_length);
 
 /* ---------------------------------------------------------- prefix cache --- */
 /* Prefix-hash block reuse ([KVprefix]).  Each pool owns one cache.  A key
@@ -285,10 +314,11 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32
  *   pa_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by the
  *   caller and overwritten by this call (do not reuse it for another call
  *   until this one has finished on `stream`).
+ * A windowed sequence's row sees its window (pa_seq_set_window).
  * Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG (B <= 0, num_heads not a
  *   positive multiple of num_kv_heads, a sequence of length 0 ([ferrum]
- *   "kv_len must be positive"), small or misaligned ws, NULL pointers,
- *   metadata-only pool), PA_ERR_DEVICE. */
+ *   "kv_len must be positive"), a query row in a released page, small or
+ *   misaligned ws, NULL pointers, metadata-only pool), PA_ERR_DEVICE. */
 pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                     const void* q, void* out, void* ws, size_t ws_bytes, void* stream);
 
@@ -364,7 +394,8 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
  * page_table, the per-block ref_count, the accounting properties and
  * validate).  They never touch the device. */
 pa_status pa_seq_len(const pa_pool* pool, int64_t seq, int32_t* len);
-/* out: host [cap]; *n receives the table length (only min(n, cap) written). */
+/* out: host [cap]; *n receives the table length (only min(n, cap) written);
+ * a page a window released reads -1. */
 pa_status pa_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap, int32_t* n);
 pa_status pa_refcount(const pa_pool* pool, int32_t block, int32_t* rc);
 pa_status pa_stats(const pa_pool* pool, pa_pool_stats* stats);

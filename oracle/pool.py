@@ -309,11 +309,15 @@ class Pool:
         return pos, keys, values
 
     def share(self, src, dst, prefix):
-        """New sequence ``dst`` holding the blocks covering ``src[:prefix]``."""
+        """New sequence ``dst`` holding the blocks covering ``src[:prefix]``
+        (a windowed source's released pages included; the prefix may not end
+        before its resident window)."""
         self._existing(src)
         prefix = _non_negative_int(prefix, "prefix_tokens")
         if prefix > self.lengths[src]:
             raise ValueError("prefix_tokens exceeds source length")
+        if prefix < self.evicted_end(src):
+            raise ValueError("the prefix ends among released positions")
         self._new(dst)
         table = self.tables[src][:_ceil_div(prefix, self.block_size)]
         for block in table:

@@ -23,11 +23,14 @@ Readings taken here (the notebook's cache is a set of keys with no pool):
   each, as a shared prefix) with length = hit; the caller appends and stores
   the rest;
 * ``register`` adds the keys of a sequence's complete blocks once their K/V
-  are stored; a key already present keeps its block (adding to a set);
+  are stored, up to the first page a sliding window released; a key already
+  present keeps its block (adding to a set);
 * the notebook has no eviction; ``clear`` drops every key and its pin.
 """
 
 from __future__ import annotations
+
+from .pool import HOLE
 
 
 def prefix_key(tokens, end, scope, revision):
@@ -71,6 +74,8 @@ class PrefixCache:
         table = pool.tables[seq]
         added = 0
         for end in range(bs, len(tokens) + 1, bs):
+            if table[end // bs - 1] == HOLE:
+                break  # keys stop at the first page a window released
             key = prefix_key(tokens, end, scope, revision)
             if key in self.entries:
                 continue

@@ -106,6 +106,8 @@ SIGNATURES = {
     "pa_share": (_i32, [_c_void_p, _i64, _i64, _i32]),
     "pa_fork": (_i32, [_c_void_p, _i64, _i64]),
     "pa_release": (_i32, [_c_void_p, _i64]),
+    "pa_seq_set_window": (_i32, [_c_void_p, _i64, _i32, _i32]),
+    "pa_truncate": (_i32, [_c_void_p, _i64, _i32]),
     "pa_prefix_lookup": (_i32, [_c_void_p, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
     "pa_prefix_attach": (_i32, [_c_void_p, _i64, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
     "pa_prefix_register": (_i32, [_c_void_p, _i64, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
@@ -248,6 +250,14 @@ def pa_fork(pool, src, dst):
 
 def pa_release(pool, seq):
     _check(load().pa_release(pool, seq))
+
+
+def pa_seq_set_window(pool, seq, sink_tokens, recent_tokens):
+    _check(load().pa_seq_set_window(pool, seq, sink_tokens, recent_tokens))
+
+
+def pa_truncate(pool, seq, new_length):
+    _check(load().pa_truncate(pool, seq, new_length))
 
 
 def _bytes(x):

@@ -310,6 +310,18 @@ pa_status pa_release(pa_pool* pool, int64_t seq) {
   return from(pool->meta.release(seq, &msg), msg);
 }
 
+pa_status pa_seq_set_window(pa_pool* pool, int64_t seq, int32_t sink_tokens, int32_t recent_tokens) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.set_window(seq, sink_tokens, recent_tokens, &msg), msg);
+}
+
+pa_status pa_truncate(pa_pool* pool, int64_t seq, int32_t new_length) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  std::string msg;
+  return from(pool->meta.truncate(seq, new_length, &msg), msg);
+}
+
 pa_status pa_prefix_lookup(const pa_pool* pool, const char* scope, const char* revision,
                            const int32_t* tokens, int32_t n_tokens, int32_t* hit_tokens) {
   if (!pool || !scope || !revision || !hit_tokens || n_tokens < 0 || (n_tokens > 0 && !tokens))
@@ -433,6 +445,7 @@ pa_status launch_decode_plan(pa_pool* pool, const pa::DecodePlan& plan, int32_t 
   a.part_acc = reinterpret_cast<float*>(w + plan.part_acc_off);
   a.q_start = reinterpret_cast<const int32_t*>(w + plan.qstart_off);
   a.merge_rows = reinterpret_cast<const int32_t*>(w + plan.merge_off);
+  a.seq_win = reinterpret_cast<const int32_t*>(w + plan.win_off);
   a.n_parts_of = reinterpret_cast<const int32_t*>(w + plan.nparts_off);
   a.batch = B;
   a.num_heads = num_heads;
@@ -700,6 +713,8 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
   a.tiles = reinterpret_cast<const int32_t*>(w + plan.tiles_off);
   a.row_seq = reinterpret_cast<const int32_t*>(w + plan.rowseq_off);
   a.zeros = w + plan.zeros_off;
+  a.seq_win = reinterpret_cast<const int32_t*>(w + plan.win_off);
+  a.windowed = plan.windowed ? 1 : 0;
   a.num_heads = num_heads;
   a.num_kv_heads = pool->geom.num_kv_heads;
   a.group = group;

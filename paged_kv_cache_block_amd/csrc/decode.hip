@@ -63,6 +63,7 @@ struct GenericArgs {
   const int32_t* tables;
   const int32_t* q_start;  // nullptr: decode, row r is sequence r with q_len 1
   const int32_t* row_seq;
+  const int32_t* seq_win;  // [B][4]: sinks, recent (nullptr: no windows)
   int32_t num_heads, num_kv_heads, group, head_dim, block_size;
   float scale_log2;
 };
@@ -89,7 +90,12 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
     q_len = 1;
   }
   const int L = a.ctx_len[b];
-  const int visible = L - q_len + t + 1;  // keys 0 .. visible-1
+  const int visible = L - q_len + t + 1;  // causal: keys 0 .. visible-1
+  // Window: key j is kept if j < sinks or j >= visible - recent; keys in
+  // released pages (table entry < 0) are gone.
+  const int sinks = a.seq_win ? a.seq_win[4 * b] : 0;
+  const int recent = a.seq_win ? a.seq_win[4 * b + 1] : kNoWindowRecent;
+  const int win_lo = visible - recent;
   const int g = h / a.group;
   const int D = a.head_dim, BS = a.block_size, Hkv = a.num_kv_heads;
   const int32_t* table = a.tables + a.tbl_off[b];
@@ -107,8 +113,12 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
     const int j = c0 + lane;
     float s = -INFINITY;
     int blk = 0, off = 0;
-    if (j < visible) {
+    bool keep = j < visible && (j < sinks || j >= win_lo);
+    if (keep) {
       blk = table[j / BS];
+      keep = blk >= 0;
+    }
+    if (keep) {
       off = j - (j / BS) * BS;
       float dot = 0.f;
       if constexpr (Q8) {
@@ -122,18 +132,20 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
       }
       s = dot * a.scale_log2;
     }
-    const float m_new = fmaxf(m, wave_max(s));  // finite: key c0 is visible
-    const float alpha = exp2f(m - m_new);
-    float p = j < visible ? exp2f(s - m_new) : 0.f;
+    const float m_new = fmaxf(m, wave_max(s));
+    // No kept key so far (m_new = -inf): exponents against 0 give weight 0.
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m - m_ref);
+    float p = keep ? exp2f(s - m_ref) : 0.f;
     l = l * alpha + wave_sum(p);
     if constexpr (Q8) {
       // The V scale joins the weight: sum_j p_j sv_j cv_j.
-      if (j < visible)
+      if (keep)
         p *= reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.v_pool) +
                                             (static_cast<size_t>(blk) * Hkv + g) * q8_page + BS * D)[off];
     }
     ps[lane] = p;
-    blks[lane] = blk;
+    blks[lane] = keep ? blk : -1;  // -1: not kept (its page may be released)
     offs[lane] = off;
     __syncthreads();
     const int nj = min(64, visible - c0);
@@ -145,11 +157,13 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
         if constexpr (Q8) {
           const int8_t* vb = static_cast<const int8_t*>(a.v_pool);
           for (int jj = 0; jj < nj; ++jj)
-            x += ps[jj] * static_cast<float>(vb[(static_cast<size_t>(blks[jj]) * Hkv + g) * q8_page +
-                                               q8_v_offset(offs[jj], d, D)]);
+            if (blks[jj] >= 0)
+              x += ps[jj] * static_cast<float>(vb[(static_cast<size_t>(blks[jj]) * Hkv + g) * q8_page +
+                                                 q8_v_offset(offs[jj], d, D)]);
         } else {
           for (int jj = 0; jj < nj; ++jj)
-            x += ps[jj] * Elt<T>::load(V + ((static_cast<size_t>(blks[jj]) * Hkv + g) * D + d) * BS + offs[jj]);
+            if (blks[jj] >= 0)
+              x += ps[jj] * Elt<T>::load(V + ((static_cast<size_t>(blks[jj]) * Hkv + g) * D + d) * BS + offs[jj]);
         }
       }
       acc[k] = x;
@@ -248,23 +262,31 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
   const int row0 = a.q_start[b], qlen = a.q_start[b + 1] - row0;
   const int C = qlen * G;  // live columns
   const int nblk = (L + BS - 1) / BS;
+  // Window of the sequence: sinks, recent, and the visited pages (compact
+  // index i < nvis is page i below the sink pages, else page i + gap).
+  const int sinks = a.seq_win[4 * b], recent = a.seq_win[4 * b + 1];
+  const int sink_pages = a.seq_win[4 * b + 2], gap = a.seq_win[4 * b + 3];
+  const int nvis = nblk - gap;
   const int p0 = c * a.pages_per_part;
-  const int p1 = min(nblk, p0 + a.pages_per_part);
-  // Pages from mask0 on hold keys some column must not see (or past-end slots).
+  const int p1 = min(nvis, p0 + a.pages_per_part);
+  // Pages from mask0 on hold keys some column must not see (or past-end
+  // slots); pages starting before win_hi may hold keys left of a window.
   const int mask0 = (L - qlen + 1) / BS;
+  const int win_hi = L - recent;
   const int32_t* table = a.tables + a.tbl_off[b];
   const char* kpool = static_cast<const char*>(a.k_pool);
   const char* vpool = static_cast<const char*>(a.v_pool);
 
   // Q^T operand and visible-key limit of this lane's column in each tile.
   bf16x8 qv[CT][KS];
-  int lim[CT];
+  int lim[CT], wlo[CT];  // column sees key p iff p < lim and (p < sinks or p >= wlo)
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int col = 16 * ct + n;
     const int t = col / G, hn = col - t * G;
     const bool live = col < C;
     lim[ct] = live ? L - qlen + t + 1 : L;
+    wlo[ct] = lim[ct] - recent;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            (static_cast<size_t>(row0 + (live ? t : 0)) * Hq + g * G + hn) * D +
                            (Q8 ? (D / 4) * grp : 8 * grp);
@@ -288,8 +310,9 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
   }
 
   using Page = PageRegs<D, BS, Q8>;
-  auto load_page = [&](int pg, Page& P) {
-    const int blk = uniform(table[pg]);
+  auto page_of = [&](int ci) { return ci < sink_pages ? ci : ci + gap; };
+  auto load_page = [&](int ci, Page& P) {
+    const int blk = uniform(table[page_of(ci)]);
     const char* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
     const char* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
     if constexpr (Q8) {
@@ -322,7 +345,8 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
     }
   };
 
-  auto process = [&](int pg, const Page& P) {
+  auto process = [&](int ci, const Page& P) {
+    const int pg = page_of(ci);
     // s[ct][tt][i] = score of token pg*BS + 16tt + 4grp + i for column 16ct + n.
     f32x4 s[CT][TT];
 #pragma unroll
@@ -343,7 +367,7 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
           s[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j], qv[ct][j], s[ct][tt], 0, 0, 0);
       }
     }
-    const bool edge = pg >= mask0;
+    const bool edge = pg >= mask0 || (pg * BS < win_hi && pg * BS + BS > sinks);
     s16x4 p_hi[CT][TT], p_lo[CT][TT];
     float alpha[CT];
 #pragma unroll
@@ -358,7 +382,8 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
             x *= P.ks[tt][i] * a.scale_log2;
           else
             x *= a.scale_log2;
-          if (edge && pg * BS + 16 * tt + 4 * grp + i >= lim[ct]) x = -INFINITY;
+          const int pos = pg * BS + 16 * tt + 4 * grp + i;
+          if (edge && (pos >= lim[ct] || (pos >= sinks && pos < wlo[ct]))) x = -INFINITY;
           s[ct][tt][i] = x;
           mloc = fmaxf(mloc, x);
         }
@@ -381,7 +406,8 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
           if constexpr (Q8) {
             w = e * P.vs[tt][i];
             // A masked or past-end slot may hold any scale bits: weight 0.
-            if (edge && pg * BS + 16 * tt + 4 * grp + i >= lim[ct]) w = 0.f;
+            const int pos = pg * BS + 16 * tt + 4 * grp + i;
+            if (edge && (pos >= lim[ct] || (pos >= sinks && pos < wlo[ct]))) w = 0.f;
           }
           const __bf16 hi = static_cast<__bf16>(w);
           const __bf16 lo = static_cast<__bf16>(w - static_cast<float>(hi));
@@ -609,7 +635,7 @@ hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& a, hipS
       break;
     default: {
       GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, nullptr, nullptr,
-                    a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,
+                    a.seq_win, a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,
                     a.scale_log2};
       launch_generic(geom, g, dim3(a.batch * a.num_heads), stream);
       break;
@@ -635,8 +661,8 @@ hipError_t launch_decode_merge(const PoolGeom& geom, const DecodeArgs& a, hipStr
 // Prefill through the generic kernel (query rows with their causal limits).
 hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream) {
   GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, a.q_start,
-                a.row_seq, a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,
-                a.scale_log2};
+                a.row_seq, a.seq_win, a.num_heads, a.num_kv_heads, a.group, geom.head_dim,
+                geom.block_size, a.scale_log2};
   launch_generic(geom, g, dim3(a.n_rows * a.num_heads), stream);
   return hipGetLastError();
 }

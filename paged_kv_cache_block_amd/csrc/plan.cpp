@@ -41,7 +41,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   }
   const int32_t bs = pool.block_size();
   std::vector<const Sequence*> rows(B);
-  std::vector<int64_t> len(B), nblk(B);
+  std::vector<int64_t> len(B), nblk(B), nvis(B);
   int64_t total_pages = 0;
   for (int32_t b = 0; b < B; ++b) {
     rows[b] = pool.find(seqs[b]);
@@ -62,6 +62,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     total_pages += nblk[b];
   }
   std::vector<int32_t> qlen(B, 1);
+  std::vector<int32_t> win(4 * static_cast<size_t>(B));
   int64_t n_rows = B;
   int32_t max_q = 1;
   if (q_lens) {
@@ -76,6 +77,34 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
       return kInvalidArg;
     }
   }
+  // Pages each sequence's rows may see: the sink pages, then from the first
+  // page of row 0's window (or the first resident page after released ones).
+  for (int32_t b = 0; b < B; ++b) {
+    const Sequence& s = *rows[b];
+    int32_t* w = &win[4 * static_cast<size_t>(b)];
+    if (!s.windowed()) {
+      w[0] = 0;
+      w[1] = kNoWindowRecent;
+      w[2] = static_cast<int32_t>(nblk[b]);
+      w[3] = 0;
+      nvis[b] = nblk[b];
+      continue;
+    }
+    if (len[b] - qlen[b] < pool.evicted_end(s)) {
+      *msg = "a query row of sequence " + std::to_string(seqs[b]) + " lies in a released page";
+      return kInvalidArg;
+    }
+    const int64_t sink_pages = std::min<int64_t>(ceil_div(s.sinks, bs), nblk[b]);
+    const int64_t lo = std::max<int64_t>(0, len[b] - qlen[b] + 1 - s.recent);
+    int64_t start = std::max<int64_t>(lo / bs, sink_pages);
+    start = std::max<int64_t>(start, pool.evicted_end(s) / bs);
+    start = std::min<int64_t>(start, nblk[b]);
+    w[0] = s.sinks;
+    w[1] = s.recent;
+    w[2] = static_cast<int32_t>(sink_pages);
+    w[3] = static_cast<int32_t>(start - sink_pages);
+    nvis[b] = nblk[b] - (start - sink_pages);
+  }
 
   // Pages per partition: the largest candidate that still yields enough
   // workgroups; each partition is split over kDecodeWaves waves.
@@ -85,7 +114,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   };
   auto groups_for = [&](int32_t ppp) {
     int64_t g = 0;
-    for (int32_t b = 0; b < B; ++b) g += ceil_div(nblk[b], ppp);
+    for (int32_t b = 0; b < B; ++b) g += ceil_div(nvis[b], ppp);
     return g * num_kv_heads;
   };
   int32_t ppp;
@@ -110,7 +139,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   int32_t n_parts = 0;
   int64_t row_heads = 0;
   for (int32_t b = 0; b < B; ++b) {
-    int32_t nb = static_cast<int32_t>(nblk[b]);
+    int32_t nb = static_cast<int32_t>(nvis[b]);
     int32_t np = static_cast<int32_t>(ceil_div(nb, ppp));
     n_parts_of[b] = np;
     for (int32_t c = 0; c < np; ++c) items.push_back({b, c, std::min(ppp, nb - c * ppp)});
@@ -147,6 +176,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.qstart_off = reserve(meta, B + 1);
   p.base_off = reserve(meta, B);
   p.nparts_off = reserve(meta, B);
+  p.win_off = reserve(meta, 4 * static_cast<size_t>(B));
   p.work_off = reserve(meta, 2 * items.size());
   p.merge_off = reserve(meta, std::max<size_t>(2, merge.size()));
   p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
@@ -179,6 +209,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   }
   qs[B] = row;
   std::copy(merge.begin(), merge.end(), mrg);
+  std::copy(win.begin(), win.end(), at_bytes(meta, p.win_off));
 
   p.meta_bytes = align_up(meta.size() * sizeof(int32_t), kWsAlign);
   size_t rows_hq = static_cast<size_t>(row_heads);
@@ -213,6 +244,10 @@ Status build_prefill_plan(const BlockPool& pool, const int64_t* seqs, const int3
       *msg = "q_lens[b] must be in 1..length(seq) (the rows are the last positions)";
       return kInvalidArg;
     }
+    if (rows[b]->length - q_lens[b] < pool.evicted_end(*rows[b])) {
+      *msg = "a query row of sequence " + std::to_string(seqs[b]) + " lies in a released page";
+      return kInvalidArg;
+    }
     total_pages += static_cast<int64_t>(rows[b]->table.size());
     total_rows += q_lens[b];
   }
@@ -242,6 +277,7 @@ Status build_prefill_plan(const BlockPool& pool, const int64_t* seqs, const int3
   p.tiles_off = reserve(meta, 2 * tiles.size());
   p.rowseq_off = reserve(meta, static_cast<size_t>(total_rows));
   p.zeros_off = reserve(meta, 16);  // 64 bytes, left zero
+  p.win_off = reserve(meta, 4 * static_cast<size_t>(B));
   p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
   int32_t* ctx = at_bytes(meta, p.ctx_off);
   int32_t* toff = at_bytes(meta, p.tbl_off_off);
@@ -258,6 +294,10 @@ Status build_prefill_plan(const BlockPool& pool, const int64_t* seqs, const int3
     row += q_lens[b];
     std::copy(rows[b]->table.begin(), rows[b]->table.end(), tables + cursor);
     cursor += static_cast<int64_t>(rows[b]->table.size());
+    int32_t* w = at_bytes(meta, p.win_off) + 4 * static_cast<size_t>(b);
+    w[0] = rows[b]->windowed() ? rows[b]->sinks : 0;
+    w[1] = rows[b]->windowed() ? rows[b]->recent : kNoWindowRecent;
+    p.windowed = p.windowed || rows[b]->windowed();
   }
   qs[B] = static_cast<int32_t>(row);
   for (size_t i = 0; i < tiles.size(); ++i) {

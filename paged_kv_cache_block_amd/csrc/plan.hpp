@@ -15,6 +15,7 @@
 namespace pa {
 
 constexpr size_t kWsAlign = 256;
+constexpr int32_t kNoWindowRecent = 1 << 29;  // "recent" of a sequence without a window
 constexpr int kDecodeWaves = 4;  // waves per decode workgroup
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -58,6 +59,11 @@ struct DecodeArgs {
   float* part_l;            // [row-heads]
   float* part_acc;          // [row-heads][D]
   const int32_t* merge_rows;// [n_merge][2] = (b, t) query rows of split sequences
+  const int32_t* seq_win;   // [B][4] = (sinks, recent, sink pages, gap): the pages
+                            // visited are the compact indices i < n_visit = nblk - gap,
+                            // page i for i < sink pages, else page i + gap; a key p is
+                            // visible to a row whose causal limit is lim (p < lim) if
+                            // p < sinks or p >= lim - recent (no window: recent huge)
   const int32_t* n_parts_of;// [B] partitions of b
   int32_t batch, num_heads, num_kv_heads, group;
   int32_t pages_per_part;
@@ -71,7 +77,7 @@ struct DecodePlan {
   size_t meta_bytes = 0;      // aligned
   size_t part_m_off = 0, part_l_off = 0, part_acc_off = 0, total_bytes = 0;
   size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, qstart_off = 0, work_off = 0, base_off = 0,
-         merge_off = 0, nparts_off = 0, slots_off = 0;  // byte offsets in the workspace
+         merge_off = 0, nparts_off = 0, win_off = 0, slots_off = 0;  // byte offsets in the workspace
   int32_t n_work = 0, n_merge = 0, n_parts = 0, pages_per_part = 0, batch = 0;
   int32_t n_rows = 0, max_q_len = 1;
   int64_t total_pages = 0;
@@ -103,9 +109,11 @@ struct PrefillArgs {
   const int32_t* q_start;   // [B+1] first row of b
   const int32_t* tiles;     // [n_tiles][2] = (b, first query row of the tile within b)
   const int32_t* row_seq;   // [R] sequence of each row (generic kernel)
+  const int32_t* seq_win;   // [B][4] as in DecodeArgs (the generic kernel reads sinks, recent)
   const void* zeros;        // 64 zero bytes (source of staged slots past a sequence's end)
   int32_t num_heads, num_kv_heads, group;
   int32_t n_tiles, n_rows;
+  int32_t windowed;         // some sequence has a window: the generic kernel serves the call
   float scale_log2;
 };
 
@@ -113,8 +121,9 @@ struct PrefillPlan {
   std::vector<int32_t> meta;
   size_t meta_bytes = 0, total_bytes = 0;
   size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, qstart_off = 0, tiles_off = 0,
-         rowseq_off = 0, zeros_off = 0;
+         rowseq_off = 0, zeros_off = 0, win_off = 0;
   int32_t n_tiles = 0, n_rows = 0, batch = 0;
+  bool windowed = false;  // some sequence has a window (the MFMA prefill kernel has none)
 };
 
 // `rows_per_tile` query rows (of one sequence) per prefill workgroup.

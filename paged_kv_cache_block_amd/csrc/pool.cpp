@@ -32,6 +32,8 @@ Status BlockPool::make(int32_t num_blocks, int32_t block_size, const int32_t* or
   }
   p.refs_.assign(num_blocks, 0);
   p.pins_.assign(num_blocks, 0);
+  p.is_free_.assign(num_blocks, 1);
+  p.n_free_ = num_blocks;
   std::vector<int32_t> ranks(num_blocks);
   for (int32_t r = 0; r < num_blocks; ++r) ranks[r] = r;
   p.free_heap_ = decltype(p.free_heap_)(std::greater<int32_t>(), std::move(ranks));
@@ -44,17 +46,89 @@ const Sequence* BlockPool::find(int64_t seq) const {
   return it == seqs_.end() ? nullptr : &it->second;
 }
 
+void BlockPool::touch(int32_t block) {
+  if (undo_) undo_->blocks.emplace(block, std::make_pair(refs_[block], is_free_[block]));
+}
+
 int32_t BlockPool::allocate() {
-  // Caller has preflighted; the heap is non-empty.
-  int32_t block = order_[free_heap_.top()];
-  free_heap_.pop();
+  // Caller has preflighted: a free block exists.
+  int32_t block;
+  do {
+    block = order_[free_heap_.top()];
+    free_heap_.pop();
+  } while (!is_free_[block]);
+  touch(block);
+  is_free_[block] = 0;
+  --n_free_;
   refs_[block] = 1;
-  if (undo_) undo_->taken.push_back(block);
   return block;
 }
 
 void BlockPool::drop_ref(int32_t block) {
-  if (--refs_[block] == 0) free_heap_.push(rank_[block]);
+  touch(block);
+  if (--refs_[block] == 0) {
+    is_free_[block] = 1;
+    ++n_free_;
+    free_heap_.push(rank_[block]);
+  }
+}
+
+void BlockPool::evict(Sequence& s, int64_t first_new) {
+  const int64_t sink_pages = ceil_div(s.sinks, block_size_);
+  const int64_t lo = first_new + 1 - s.recent;
+  const int64_t end = std::min(std::max<int64_t>(lo, 0) / block_size_, first_new / block_size_);
+  for (int64_t j = sink_pages; j < end; ++j) {
+    if (s.table[j] == kHole) continue;
+    drop_ref(s.table[j]);
+    s.table[j] = kHole;
+  }
+}
+
+int64_t BlockPool::evicted_end(const Sequence& s) const {
+  for (int64_t j = static_cast<int64_t>(s.table.size()) - 1; j >= 0; --j)
+    if (s.table[j] == kHole) return (j + 1) * block_size_;
+  return 0;
+}
+
+Status BlockPool::set_window(int64_t seq, int32_t sinks, int32_t recent, std::string* msg) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end()) {
+    *msg = "unknown sequence: " + std::to_string(seq);
+    return kUnknownSeq;
+  }
+  if (sinks < 0 || recent < 0 || static_cast<int64_t>(sinks) + recent < 1 ||
+      static_cast<int64_t>(sinks) + recent > INT32_MAX / 2) {
+    *msg = "sinks and recent must be >= 0 with 1 <= sinks + recent";
+    return kInvalidArg;
+  }
+  it->second.sinks = sinks;
+  it->second.recent = recent;
+  ++version_;
+  return kOk;
+}
+
+Status BlockPool::truncate(int64_t seq, int64_t new_length, std::string* msg) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end()) {
+    *msg = "unknown sequence: " + std::to_string(seq);
+    return kUnknownSeq;
+  }
+  Sequence& s = it->second;
+  if (new_length < 0 || new_length > s.length) {
+    *msg = "new_length must be in 0..length(seq)";
+    return kInvalidArg;
+  }
+  if (new_length < evicted_end(s)) {
+    *msg = "rollback lies outside the retained interval (evicted positions cannot come back)";
+    return kInvalidArg;
+  }
+  const size_t keep = static_cast<size_t>(ceil_div(new_length, block_size_));
+  for (size_t j = keep; j < s.table.size(); ++j)
+    if (s.table[j] != kHole) drop_ref(s.table[j]);
+  s.table.resize(keep);
+  s.length = new_length;
+  ++version_;
+  return kOk;
 }
 
 Status BlockPool::create(int64_t seq, std::string* msg) {
@@ -104,7 +178,6 @@ Status BlockPool::append(int64_t seq, int32_t n, int64_t* slots_out, std::string
       pending_.emplace_back(old, fresh);
       s.table.back() = fresh;
       drop_ref(old);  // old stays referenced by another sequence
-      if (undo_) undo_->dropped.push_back(old);
     }
   }
   int64_t first = s.length;
@@ -115,6 +188,7 @@ Status BlockPool::append(int64_t seq, int32_t n, int64_t* slots_out, std::string
   for (int64_t p = first; p < total; ++p)
     slots_out[p - first] =
         static_cast<int64_t>(s.table[p / block_size_]) * block_size_ + p % block_size_;
+  if (s.windowed()) evict(s, first);
   ++version_;
   return kOk;
 }
@@ -125,12 +199,11 @@ Status BlockPool::append_batch(const int64_t* seqs, const int32_t* n, int32_t co
     *msg = "count must be >= 0 with non-NULL seqs and n_tokens";
     return kInvalidArg;
   }
-  // Undo log: the first-seen state of every touched sequence, the blocks the
-  // batch took from the free heap, the shared tails whose refcount a
-  // copy-on-write dropped, and the pending-copy list length.  Blocks taken
-  // by the batch are private tails or new blocks, so none of them is freed
-  // again inside the batch; restoring the heap's rank set restores the
-  // allocation order exactly.
+  // Undo log: the first-seen state of every touched sequence and of every
+  // block whose refcount or free flag the batch changed (allocations,
+  // copy-on-write drops, window releases), and the pending-copy list
+  // length.  Restoring the free flags restores the free set, and with it
+  // the allocation order (stale heap entries are skipped).
   std::unordered_map<int64_t, Sequence> saved;
   UndoLog log;
   const size_t pending_before = pending_.size();
@@ -154,11 +227,16 @@ Status BlockPool::append_batch(const int64_t* seqs, const int32_t* n, int32_t co
   undo_ = nullptr;
   if (s == kOk) return kOk;
   for (auto& kv : saved) seqs_[kv.first] = std::move(kv.second);
-  for (int32_t b : log.taken) {
-    refs_[b] = 0;
-    free_heap_.push(rank_[b]);
+  for (const auto& kv : log.blocks) {
+    const int32_t b = kv.first;
+    refs_[b] = kv.second.first;
+    const char was_free = kv.second.second;
+    if (is_free_[b] != was_free) {
+      is_free_[b] = was_free;
+      n_free_ += was_free ? 1 : -1;
+      if (was_free) free_heap_.push(rank_[b]);
+    }
   }
-  for (int32_t b : log.dropped) ++refs_[b];
   pending_.resize(pending_before);
   version_ = version_before;
   *msg = "append_batch entry " + std::to_string(i) + ": " + *msg;
@@ -175,6 +253,10 @@ Status BlockPool::share(int64_t src, int64_t dst, int32_t prefix, std::string* m
     *msg = "prefix_tokens must be in 0..length(src)";
     return kInvalidArg;
   }
+  if (prefix < evicted_end(it->second)) {
+    *msg = "prefix_tokens ends among positions a window released";
+    return kInvalidArg;
+  }
   if (seqs_.count(dst)) {
     *msg = "sequence already exists: " + std::to_string(dst);
     return kSeqExists;
@@ -183,7 +265,10 @@ Status BlockPool::share(int64_t src, int64_t dst, int32_t prefix, std::string* m
   child.length = prefix;
   child.table.assign(it->second.table.begin(),
                      it->second.table.begin() + ceil_div(prefix, block_size_));
-  for (int32_t b : child.table) ++refs_[b];
+  child.sinks = it->second.sinks;
+  child.recent = it->second.recent;
+  for (int32_t b : child.table)
+    if (b != kHole) ++refs_[b];
   seqs_.emplace(dst, std::move(child));
   ++version_;
   return kOk;
@@ -204,7 +289,8 @@ Status BlockPool::release(int64_t seq, std::string* msg) {
     *msg = "unknown or released sequence: " + std::to_string(seq);
     return kUnknownSeq;
   }
-  for (int32_t b : it->second.table) drop_ref(b);
+  for (int32_t b : it->second.table)
+    if (b != kHole) drop_ref(b);
   seqs_.erase(it);
   ++version_;
   return kOk;
@@ -274,6 +360,7 @@ std::vector<int32_t> BlockPool::fills() const {
   for (const auto& kv : seqs_) {
     const Sequence& s = kv.second;
     for (size_t j = 0; j < s.table.size(); ++j) {
+      if (s.table[j] == kHole) continue;
       int64_t used = std::min<int64_t>(block_size_, s.length - static_cast<int64_t>(j) * block_size_);
       fill[s.table[j]] = std::max<int32_t>(fill[s.table[j]], static_cast<int32_t>(used));
     }
@@ -308,27 +395,39 @@ Status BlockPool::validate(std::string* msg) const {
       *msg = "page-table length does not match sequence length";
       return kInvalidArg;
     }
-    std::vector<int32_t> sorted = s.table;
+    std::vector<int32_t> sorted;
+    for (int32_t b : s.table)
+      if (b != kHole) sorted.push_back(b);
     std::sort(sorted.begin(), sorted.end());
     if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) {
       *msg = "one sequence references a physical block twice";
       return kInvalidArg;
     }
-    for (int32_t b : s.table) {
+    if (!s.table.empty() && s.length % block_size_ && s.table.back() == kHole) {
+      *msg = "a partially filled tail page was released";
+      return kInvalidArg;
+    }
+    for (int32_t b : sorted) {
       if (b < 0 || b >= num_blocks_) { *msg = "page table contains an invalid block id"; return kInvalidArg; }
       ++expected[b];
     }
   }
-  // Free set = blocks whose rank sits in the heap.
-  std::vector<char> is_free(num_blocks_, 0);
+  // Free set = the free flags; every free block has an entry in the heap.
+  const std::vector<char>& is_free = is_free_;
+  std::vector<char> in_heap(num_blocks_, 0);
   auto heap = free_heap_;
   while (!heap.empty()) {
     int32_t r = heap.top();
     heap.pop();
     if (r < 0 || r >= num_blocks_) { *msg = "free list contains an invalid block id"; return kInvalidArg; }
-    if (is_free[order_[r]]) { *msg = "free list contains duplicates"; return kInvalidArg; }
-    is_free[order_[r]] = 1;
+    in_heap[order_[r]] = 1;
   }
+  int64_t n_free = 0;
+  for (int32_t b = 0; b < num_blocks_; ++b) {
+    if (is_free[b] && !in_heap[b]) { *msg = "free block missing from the free list"; return kInvalidArg; }
+    n_free += is_free[b];
+  }
+  if (n_free != n_free_) { *msg = "free count does not match the free flags"; return kInvalidArg; }
   std::vector<int32_t> fill = fills();
   for (int32_t b = 0; b < num_blocks_; ++b) {
     if (refs_[b] != expected[b] + pins_[b]) {

@@ -29,9 +29,15 @@ enum Status : int {
   kDevice = -5,
 };
 
+constexpr int32_t kHole = -1;  // table entry of a page the window released
+
 struct Sequence {
   int64_t length = 0;
   std::vector<int32_t> table;
+  // Window (vladkulikov.com notebook "Модуль 10", streaming_keep_indices
+  // with budget sinks + recent); sinks < 0: no window.
+  int32_t sinks = -1, recent = 0;
+  bool windowed() const { return sinks >= 0; }
 };
 
 struct PoolStats {
@@ -64,12 +70,22 @@ class BlockPool {
   Status pin(int32_t block, std::string* msg);
   Status unpin(int32_t block, std::string* msg);
   int32_t pins(int32_t block) const { return pins_[block]; }
+  // Give `seq` a (sinks, recent) window: each append then releases the
+  // pages lying wholly between the sink pages and the window of its first
+  // appended row (position p sees [p + 1 - recent, p]); their table entries
+  // become kHole.
+  Status set_window(int64_t seq, int32_t sinks, int32_t recent, std::string* msg);
+  // Drop positions [new_length, length) (a rollback).  new_length may not
+  // fall before evicted_end(seq): evicted positions cannot come back.
+  Status truncate(int64_t seq, int64_t new_length, std::string* msg);
+  // First position after the last released page (0 if none).
+  int64_t evicted_end(const Sequence& s) const;
 
   const Sequence* find(int64_t seq) const;
   int32_t refcount(int32_t block) const { return refs_[block]; }
   int32_t num_blocks() const { return num_blocks_; }
   int32_t block_size() const { return block_size_; }
-  int64_t free_count() const { return static_cast<int64_t>(free_heap_.size()); }
+  int64_t free_count() const { return n_free_; }
   PoolStats stats() const;
   Status validate(std::string* msg) const;
   std::vector<int64_t> sequence_ids() const;
@@ -85,13 +101,15 @@ class BlockPool {
   uint64_t version() const { return version_; }
 
  private:
+  // First-touch values of every block an append_batch changed.
   struct UndoLog {
-    std::vector<int32_t> taken;    // blocks allocated
-    std::vector<int32_t> dropped;  // shared tails whose refcount a COW decremented
+    std::unordered_map<int32_t, std::pair<int32_t, char>> blocks;  // block -> (refs, free)
   };
 
+  void touch(int32_t block);
   int32_t allocate();
   void drop_ref(int32_t block);
+  void evict(Sequence& s, int64_t first_new);
   std::vector<int32_t> fills() const;
 
   int32_t num_blocks_ = 0;
@@ -100,7 +118,10 @@ class BlockPool {
   std::vector<int32_t> rank_;   // block -> rank
   std::vector<int32_t> refs_;
   std::vector<int32_t> pins_;   // references held outside the tables
-  // Free blocks by rank: the top is the first free block of the order.
+  std::vector<char> is_free_;
+  int64_t n_free_ = 0;
+  // Ranks of free blocks, smallest first; entries of blocks allocated since
+  // they were pushed are stale and skipped (an undone batch re-pushes).
   std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_heap_;
   std::unordered_map<int64_t, Sequence> seqs_;
   std::vector<std::pair<int32_t, int32_t>> pending_;

@@ -325,7 +325,7 @@ int32_t prefill_rows_per_tile(const PoolGeom& geom, int32_t group) {
 }
 
 hipError_t launch_prefill(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream) {
-  if (!prefill_uses_mfma(geom, a.group)) return launch_prefill_generic(geom, a, stream);
+  if (!prefill_uses_mfma(geom, a.group) || a.windowed) return launch_prefill_generic(geom, a, stream);
   const int D = geom.head_dim, BS = geom.block_size;
   if (D == 128 && BS == 16) launch_mfma<128, 16>(a, stream);
   else if (D == 128 && BS == 32) launch_mfma<128, 32>(a, stream);

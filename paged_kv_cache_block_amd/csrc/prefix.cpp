@@ -81,6 +81,12 @@ Status PrefixCache::add(BlockPool& pool, int64_t seq, const std::string& scope, 
     return kInvalidArg;
   }
   block_size_ = pool.block_size();
+  // Keys stop at the first page a window released (its block is gone).
+  for (int64_t j = 0; j < n / block_size_; ++j)
+    if (s->table[j] == kHole) {
+      n = j * block_size_;
+      break;
+    }
   const std::string rk = root_key(scope, revision);
   auto r = roots_.find(rk);
   if (r == roots_.end()) r = roots_.emplace(rk, static_cast<int64_t>(roots_.size())).first;

@@ -31,7 +31,8 @@ class PrefixCache {
   Status attach(BlockPool& pool, int64_t seq, const std::string& scope, const std::string& revision,
                 const int32_t* tokens, int64_t n, int64_t* hit, std::string* msg);
   // Add the keys of the complete blocks of `seq`'s first n tokens (token ids
-  // tokens[0..n), n <= length); a key already cached keeps its block.
+  // tokens[0..n), n <= length), up to the first page a window released; a
+  // key already cached keeps its block.
   // *added receives the number of new keys (each pins its block).
   Status add(BlockPool& pool, int64_t seq, const std::string& scope, const std::string& revision,
              const int32_t* tokens, int64_t n, int64_t* added, std::string* msg);

@@ -92,6 +92,12 @@ class DevicePool:
     def release(self, seq):
         abi.pa_release(self.handle, seq)
 
+    def set_window(self, seq, sink_tokens, recent_tokens):
+        abi.pa_seq_set_window(self.handle, seq, sink_tokens, recent_tokens)
+
+    def truncate(self, seq, new_length):
+        abi.pa_truncate(self.handle, seq, new_length)
+
     # ------------------------------------------------------------ prefix cache
     def prefix_lookup(self, tokens, scope, revision):
         return abi.pa_prefix_lookup(self.handle, scope, revision, tokens)
