@@ -104,14 +104,27 @@ def recorded_traffic(name):
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
-def run_decode(args, kv="bf16"):
+def window_alg_bytes(lengths, wl, sinks, recent):
+    """Bytes of the keys a windowed decode row sees: min(L, sinks + recent)
+    K and V rows per sequence, plus Q, O and the visited table entries."""
+    seen = [min(int(n), sinks + recent) for n in lengths]
+    kv = sum(seen) * wl.num_kv_heads * wl.head_dim * 2 * wl.elt_bytes
+    qo = 2 * len(lengths) * wl.num_heads * wl.head_dim * wl.elt_bytes
+    return kv + qo + sum(-(-n // wl.block_size) for n in seen) * 4
+
+
+def run_decode(args, kv="bf16", window=None):
     import torch
     from paged_kv_cache_block_amd import abi
     from synth import decode_queries, gqa_decode
 
     wl = gqa_decode()
-    log(f"building the decode workload (32 x U[1,8192], 32/8 heads, d 128, {kv} pages, bs 16)")
+    log(f"building the decode workload (32 x U[1,8192], 32/8 heads, d 128, {kv} pages, bs 16"
+        + (f", window {window}" if window else "") + ")")
     pool = build_pool(wl, kv)
+    if window:
+        for s in wl.decode_seqs:
+            pool.set_window(s, *window)
     seqs = list(wl.decode_seqs)
     B = len(seqs)
     q = to_device(decode_queries(wl), wl.dtype)
@@ -146,7 +159,7 @@ def run_decode(args, kv="bf16"):
     for i in range(args.warmup, total_steps):
         step(i)
         lengths += 1
-        alg.append(decode_alg_bytes(lengths, wl, kv))
+        alg.append(window_alg_bytes(lengths, wl, *window) if window else decode_alg_bytes(lengths, wl, kv))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     abi.pa_timing_enable(False)
@@ -420,6 +433,16 @@ def main():
             "roofline": q8["roofline"],
         }
     line["verify_q4"] = run_verify(args, 4)
+    _, wdec = run_decode(args, kv="bf16", window=(4, 1024))
+    line["window_decode"] = {
+        "workload": "the same decode steps with a window on every sequence: 4 sink tokens + the "
+                    "1024 most recent (pages outside released by the appends)",
+        "ms_per_step": round(wdec["ms_per_step"], 5),
+        "tokens_per_s": round(wdec["tokens_per_s"], 1),
+        "decode_kernel_us": round(wdec["decode_kernel_us"], 2),
+        "kernel_GBs": wdec["roofline"]["achieved"],
+        "kv_GBs_step": round(wdec["value"], 2),
+    }
     if not args.no_prefill:
         line["prefill"] = run_prefill(args)
     line["prefix_cache"] = run_prefix_cache()

@@ -29,6 +29,7 @@
 //       for fp32 pools and shapes the MFMA kernel does not cover; it also
 //       serves prefill rows (bottom-right causal mask).
 #include <cmath>
+#include <type_traits>
 
 #include "device.hpp"
 #include "kernels.hpp"
@@ -345,7 +346,10 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
     }
   };
 
-  auto process = [&](int ci, const Page& P) {
+  // EDGE: the page holds keys some column must not see (causal limit,
+  // window, past-end slots); other pages take the path without masks.
+  auto process_page = [&](int ci, const Page& P, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int pg = page_of(ci);
     // s[ct][tt][i] = score of token pg*BS + 16tt + 4grp + i for column 16ct + n.
     f32x4 s[CT][TT];
@@ -367,7 +371,6 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
           s[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j], qv[ct][j], s[ct][tt], 0, 0, 0);
       }
     }
-    const bool edge = pg >= mask0 || (pg * BS < win_hi && pg * BS + BS > sinks);
     s16x4 p_hi[CT][TT], p_lo[CT][TT];
     float alpha[CT];
 #pragma unroll
@@ -382,8 +385,10 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
             x *= P.ks[tt][i] * a.scale_log2;
           else
             x *= a.scale_log2;
-          const int pos = pg * BS + 16 * tt + 4 * grp + i;
-          if (edge && (pos >= lim[ct] || (pos >= sinks && pos < wlo[ct]))) x = -INFINITY;
+          if constexpr (EDGE) {
+            const int pos = pg * BS + 16 * tt + 4 * grp + i;
+            if (pos >= lim[ct] || (pos >= sinks && pos < wlo[ct])) x = -INFINITY;
+          }
           s[ct][tt][i] = x;
           mloc = fmaxf(mloc, x);
         }
@@ -406,8 +411,10 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
           if constexpr (Q8) {
             w = e * P.vs[tt][i];
             // A masked or past-end slot may hold any scale bits: weight 0.
-            const int pos = pg * BS + 16 * tt + 4 * grp + i;
-            if (edge && (pos >= lim[ct] || (pos >= sinks && pos < wlo[ct]))) w = 0.f;
+            if constexpr (EDGE) {
+              const int pos = pg * BS + 16 * tt + 4 * grp + i;
+              if (pos >= lim[ct] || (pos >= sinks && pos < wlo[ct])) w = 0.f;
+            }
           }
           const __bf16 hi = static_cast<__bf16>(w);
           const __bf16 lo = static_cast<__bf16>(w - static_cast<float>(hi));
@@ -418,7 +425,7 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
     }
     // bf16 pages: past-end slots of the last page have weight 0 and their
     // values are zeroed too, so 0 * V cannot meet non-finite bits left there.
-    const bool tail = pg == nblk - 1;
+    const bool tail = EDGE && pg == nblk - 1;
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
 #pragma unroll
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
           v = i8x4_to_bf16x4(P.vc[tt][nt]);
         } else {
           v = P.v[nt][tt];
-          if (tail) {
+          if (EDGE && tail) {
             const int live = L - (pg * BS + 16 * tt + 4 * grp);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -444,6 +451,14 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
         }
       }
     }
+  };
+
+  auto process = [&](int ci, const Page& P) {
+    const int pg = page_of(ci);
+    if (pg >= mask0 || (pg * BS < win_hi && pg * BS + BS > sinks))
+      process_page(ci, P, std::true_type{});
+    else
+      process_page(ci, P, std::false_type{});
   };
 
 #if PA_DECODE_PREFETCH
