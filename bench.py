@@ -367,7 +367,9 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--prefill-warmup", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-int8", action="store_true", help="skip the int8-page decode leg")
+    ap.add_argument("--legs", default="int8,verify,window,prefix",
+                    help="comma list of the legs after the headline decode leg: int8, verify, window, "
+                         "prefix (prefill and the CPU baseline have their own switches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -420,7 +422,8 @@ def main():
                                         "alg_bytes_per_step", "kernel_launches", "sum_len")},
         "roofline": dec["roofline"],
     }
-    if not args.no_int8:
+    legs = {x.strip() for x in args.legs.split(",") if x.strip()}
+    if "int8" in legs:
         _, q8 = run_decode(args, kv="i8")
         line["int8_decode"] = {
             "workload": "the same decode steps over int8 K/V pages (one fp32 scale per token and "
@@ -432,20 +435,23 @@ def main():
                                            "alg_bytes_per_step", "kernel_launches", "sum_len")},
             "roofline": q8["roofline"],
         }
-    line["verify_q4"] = run_verify(args, 4)
-    _, wdec = run_decode(args, kv="bf16", window=(4, 1024))
-    line["window_decode"] = {
-        "workload": "the same decode steps with a window on every sequence: 4 sink tokens + the "
-                    "1024 most recent (pages outside released by the appends)",
-        "ms_per_step": round(wdec["ms_per_step"], 5),
-        "tokens_per_s": round(wdec["tokens_per_s"], 1),
-        "decode_kernel_us": round(wdec["decode_kernel_us"], 2),
-        "kernel_GBs": wdec["roofline"]["achieved"],
-        "kv_GBs_step": round(wdec["value"], 2),
-    }
+    if "verify" in legs:
+        line["verify_q4"] = run_verify(args, 4)
+    if "window" in legs:
+        _, wdec = run_decode(args, kv="bf16", window=(4, 1024))
+        line["window_decode"] = {
+            "workload": "the same decode steps with a window on every sequence: 4 sink tokens + the "
+                        "1024 most recent (pages outside released by the appends)",
+            "ms_per_step": round(wdec["ms_per_step"], 5),
+            "tokens_per_s": round(wdec["tokens_per_s"], 1),
+            "decode_kernel_us": round(wdec["decode_kernel_us"], 2),
+            "kernel_GBs": wdec["roofline"]["achieved"],
+            "kv_GBs_step": round(wdec["value"], 2),
+        }
     if not args.no_prefill:
         line["prefill"] = run_prefill(args)
-    line["prefix_cache"] = run_prefix_cache()
+    if "prefix" in legs:
+        line["prefix_cache"] = run_prefix_cache()
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         line["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
