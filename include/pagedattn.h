@@ -425,6 +425,11 @@ typedef enum {
   PA_KERNEL_COUNT = 5
 } pa_kernel;
 pa_status pa_timing_enable(int on);
+/* Which kernel families get events while timing is on: bit k = pa_kernel k
+ * (default all).  Each timed launch adds two event records to its stream,
+ * which take time between kernels, so a caller timing whole steps can time
+ * only the family it reports. */
+pa_status pa_timing_select(uint32_t kernel_mask);
 pa_status pa_timing_reset(void);
 pa_status pa_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
 

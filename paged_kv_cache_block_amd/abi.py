@@ -137,6 +137,7 @@ SIGNATURES = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_timing_enable": (_i32, [ctypes.c_int]),
     "pa_timing_reset": (_i32, []),
+    "pa_timing_select": (_i32, [ctypes.c_uint32]),
     "pa_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), _i64p]),
 }
 
@@ -436,6 +437,12 @@ def pa_last_error():
 
 def pa_timing_enable(on=True):
     _check(load().pa_timing_enable(1 if on else 0))
+
+
+def pa_timing_select(kernels=None):
+    """Time only the listed kernel families (PA_KERNEL_*); None = all."""
+    mask = 0xFFFFFFFF if kernels is None else sum(1 << int(k) for k in kernels)
+    _check(load().pa_timing_select(mask))
 
 
 def pa_timing_reset():

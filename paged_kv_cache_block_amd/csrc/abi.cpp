@@ -54,7 +54,9 @@ struct TimingRecord {
 };
 std::mutex g_tmu;
 bool g_timing = false;
+uint32_t g_timing_mask = ~0u;  // kernel families that get events while timing is on
 std::vector<TimingRecord> g_records;
+std::vector<hipEvent_t> g_spare_events;  // drained events, reused by later launches
 double g_total_ms[PA_KERNEL_COUNT] = {};
 int64_t g_launches[PA_KERNEL_COUNT] = {};
 
@@ -64,11 +66,22 @@ struct TimedLaunch {
   hipEvent_t start = nullptr, stop = nullptr;
   TimedLaunch(int k, hipStream_t s) : kernel(k), stream(s) {
     std::lock_guard<std::mutex> lock(g_tmu);
-    if (!g_timing) return;
-    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess ||
-        hipEventRecord(start, stream) != hipSuccess) {
+    if (!g_timing || !(g_timing_mask & (1u << k))) return;
+    if (!take(&start) || !take(&stop) || hipEventRecord(start, stream) != hipSuccess) {
+      if (start) g_spare_events.push_back(start);
+      if (stop) g_spare_events.push_back(stop);
       start = stop = nullptr;
     }
+  }
+  static bool take(hipEvent_t* e) {
+    if (!g_spare_events.empty()) {
+      *e = g_spare_events.back();
+      g_spare_events.pop_back();
+      return true;
+    }
+    if (hipEventCreate(e) == hipSuccess) return true;
+    *e = nullptr;
+    return false;
   }
   void done() {
     if (!start) return;
@@ -85,8 +98,8 @@ void drain_timing_locked() {
       g_total_ms[r.kernel] += ms;
       g_launches[r.kernel] += 1;
     }
-    (void)hipEventDestroy(r.start);
-    (void)hipEventDestroy(r.stop);
+    g_spare_events.push_back(r.start);
+    g_spare_events.push_back(r.stop);
   }
   g_records.clear();
 }
@@ -784,6 +797,12 @@ const char* pa_last_error(void) { return g_err.c_str(); }
 pa_status pa_timing_enable(int on) {
   std::lock_guard<std::mutex> lock(g_tmu);
   g_timing = on != 0;
+  return ok();
+}
+
+pa_status pa_timing_select(uint32_t kernel_mask) {
+  std::lock_guard<std::mutex> lock(g_tmu);
+  g_timing_mask = kernel_mask;
   return ok();
 }
 

@@ -43,8 +43,14 @@
 #else
 #define PA_DECODE_OCC
 #endif
-#ifndef PA_DECODE_PREFETCH
-#define PA_DECODE_PREFETCH 1  // 1: load page p + 4 while computing page p
+#ifndef PA_DECODE_PERMLANE
+#define PA_DECODE_PERMLANE 1  // cross-group reductions with permlane swaps (not LDS)
+#endif
+#ifndef PA_DECODE_TABLE_AHEAD
+#define PA_DECODE_TABLE_AHEAD 1  // load each block id one page step before its page
+#endif
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 1  // pages each wave loads ahead of the page it computes
 #endif
 
 namespace pa {
@@ -258,15 +264,16 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
   const int n = lane & 15, grp = lane >> 4;
   const int Hkv = a.num_kv_heads, Hq = a.num_heads, G = a.group;
   const int wid = blockIdx.x / Hkv, g = blockIdx.x - wid * Hkv;
-  const int b = a.work[2 * wid], c = a.work[2 * wid + 1];
-  const int L = a.ctx_len[b];
-  const int row0 = a.q_start[b], qlen = a.q_start[b + 1] - row0;
+  const int32_t* item = a.work + kWorkInts * wid;
+  const int c = item[1];  // item[0] is the sequence (its data is in the item)
+  const int L = item[2];
+  const int row0 = item[3], qlen = item[4];
   const int C = qlen * G;  // live columns
   const int nblk = (L + BS - 1) / BS;
   // Window of the sequence: sinks, recent, and the visited pages (compact
   // index i < nvis is page i below the sink pages, else page i + gap).
-  const int sinks = a.seq_win[4 * b], recent = a.seq_win[4 * b + 1];
-  const int sink_pages = a.seq_win[4 * b + 2], gap = a.seq_win[4 * b + 3];
+  const int sinks = item[5], recent = item[6];
+  const int sink_pages = item[7], gap = item[8];
   const int nvis = nblk - gap;
   const int p0 = c * a.pages_per_part;
   const int p1 = min(nvis, p0 + a.pages_per_part);
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
   // slots); pages starting before win_hi may hold keys left of a window.
   const int mask0 = (L - qlen + 1) / BS;
   const int win_hi = L - recent;
-  const int32_t* table = a.tables + a.tbl_off[b];
+  const int32_t* table = a.tables + item[9];
   const char* kpool = static_cast<const char*>(a.k_pool);
   const char* vpool = static_cast<const char*>(a.v_pool);
 
@@ -312,8 +319,8 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
 
   using Page = PageRegs<D, BS, Q8>;
   auto page_of = [&](int ci) { return ci < sink_pages ? ci : ci + gap; };
-  auto load_page = [&](int ci, Page& P) {
-    const int blk = uniform(table[page_of(ci)]);
+  auto block_of = [&](int ci) { return uniform(table[page_of(ci)]); };
+  auto load_page_blk = [&](int blk, Page& P) {
     const char* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
     const char* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
     if constexpr (Q8) {
@@ -345,6 +352,8 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
           P.v[nt][tt] = *reinterpret_cast<const s16x4*>(v16 + (16 * nt + n) * BS + 16 * tt + 4 * grp);
     }
   };
+
+  auto load_page = [&](int ci, Page& P) { load_page_blk(block_of(ci), P); };
 
   // EDGE: the page holds keys some column must not see (causal limit,
   // window, past-end slots); other pages take the path without masks.
@@ -392,8 +401,12 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
           s[ct][tt][i] = x;
           mloc = fmaxf(mloc, x);
         }
+#if PA_DECODE_PERMLANE
+      mloc = rows4_max(mloc);
+#else
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+#endif
       const float m_new = fmaxf(m_run[ct], mloc);
       // A column with no visible key so far keeps m = -inf; exponents are
       // then taken against 0, giving weight 0 instead of -inf - -inf.
@@ -461,42 +474,60 @@ __global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
       process_page(ci, P, std::false_type{});
   };
 
-#if PA_DECODE_PREFETCH
+  // Page loop: each wave keeps DEPTH pages in flight ahead of the one it
+  // computes, in a ring of DEPTH + 1 register buffers (the loop is unrolled
+  // over the ring so every buffer index is static).  Loads are issued
+  // unconditionally (past the range end a wave re-loads its current page,
+  // an L2 hit): with the same number of loads in flight on every path, the
+  // wait before a page's first use covers only that page's loads.
   {
-    Page pa_, pb_;
-    // The prefetch is issued unconditionally (the last page of the range
-    // re-loads itself): with the same number of loads in flight on every
-    // path, the wait before a page's first use only covers that page's loads.
+    constexpr int DEPTH = PA_DECODE_DEPTH;
+    constexpr int NP = DEPTH + 1;
+    Page buf[NP];
     int p = p0 + wave;
-    if (p < p1) load_page(p, pa_);
-    while (p < p1) {
-      load_page(p + W < p1 ? p + W : p, pb_);
-      process(p, pa_);
-      p += W;
-      if (p >= p1) break;
-      load_page(p + W < p1 ? p + W : p, pa_);
-      process(p, pb_);
-      p += W;
-    }
-  }
-#else
-  for (int p = p0 + wave; p < p1; p += W) {
-    Page P;
-    load_page(p, P);
-    process(p, P);
-  }
+    if (p < p1) {
+      // The first page's block id comes with the work item (no table hop).
+      load_page_blk(item[12 + wave], buf[0]);
+#pragma unroll
+      for (int k = 1; k < DEPTH; ++k) load_page(p + k * W < p1 ? p + k * W : p, buf[k]);
+#if PA_DECODE_TABLE_AHEAD
+      // The block id of the page to load next iteration is fetched one
+      // iteration early, so its scalar load is back before it is needed.
+      int blk_ahead = block_of(min(p + DEPTH * W, p1 - 1));
 #endif
+      while (true) {
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+#if PA_DECODE_TABLE_AHEAD
+          load_page_blk(blk_ahead, buf[(u + DEPTH) % NP]);
+          blk_ahead = block_of(min(p + (DEPTH + 1) * W, p1 - 1));
+#else
+          const int ahead = p + DEPTH * W;
+          load_page(ahead < p1 ? ahead : p, buf[(u + DEPTH) % NP]);
+#endif
+          process(p, buf[u]);
+          p += W;
+          if (p >= p1) goto pages_done;
+        }
+      }
+    }
+  pages_done:;
+  }
 
   // Per-column totals over the 4 lane groups, then merge the 4 waves, one
   // 16-column tile at a time (LDS holds one tile of the 4 waves).
-  const int base = a.part_base[b];
+  const int base = item[10];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int Cn = min(16, C - 16 * ct);  // live columns of this tile (uniform)
     if (Cn <= 0) break;
     if (ct > 0) __syncthreads();  // the previous tile's readers are done
+#if PA_DECODE_PERMLANE
+    const float l_tot = rows4_sum(l_run[ct]);
+#else
     float l_tot = l_run[ct] + __shfl_xor(l_run[ct], 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
+#endif
     if (grp == 0) {
       s_m[wave][n] = m_run[ct];
       s_l[wave][n] = l_tot;

@@ -49,6 +49,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the same row of the four
+// 16-lane groups), through gfx950's row-swap permutes: no LDS traffic, so no
+// wait on the LDS / scalar-memory counter.  Each swap returns the pair
+// {x_l, x_(l^16)} (resp. ^32) in some order; max and sum are symmetric.
+__device__ __forceinline__ float rows4_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Byte offset of the code of token t (within its block), dim d, inside an
 // int8 V page of head_dim D: each 16-token tile of a page is stored in the
 // operand order of the P.V MFMA, so that one lane's codes are contiguous.

@@ -177,7 +177,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.base_off = reserve(meta, B);
   p.nparts_off = reserve(meta, B);
   p.win_off = reserve(meta, 4 * static_cast<size_t>(B));
-  p.work_off = reserve(meta, 2 * items.size());
+  p.work_off = reserve(meta, kWorkInts * items.size());
   p.merge_off = reserve(meta, std::max<size_t>(2, merge.size()));
   p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
   p.slots_off = reserve(meta, 2 * static_cast<size_t>(std::max(slot_count, 0)));
@@ -204,8 +204,29 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     cursor += nblk[b];
   }
   for (size_t i = 0; i < items.size(); ++i) {
-    work[2 * i] = items[i].b;
-    work[2 * i + 1] = items[i].c;
+    const int32_t b = items[i].b, c = items[i].c;
+    const int32_t* w8 = &win[4 * static_cast<size_t>(b)];
+    int32_t* w = work + kWorkInts * i;
+    w[0] = b;
+    w[1] = c;
+    w[2] = ctx[b];
+    w[3] = qs[b];
+    w[4] = qlen[b];
+    w[5] = w8[0];
+    w[6] = w8[1];
+    w[7] = w8[2];
+    w[8] = w8[3];
+    w[9] = toff[b];
+    w[10] = part_base[b];
+    w[11] = 0;
+    const int64_t p0 = static_cast<int64_t>(c) * ppp, p1 = std::min<int64_t>(nvis[b], p0 + ppp);
+    for (int32_t wave = 0; wave < kDecodeWaves; ++wave) {
+      const int64_t ci = p0 + wave;
+      const int64_t page = ci < w8[2] ? ci : ci + w8[3];
+      w[12 + wave] = (ci < p1 && static_cast<size_t>(page) < rows[b]->table.size())
+                         ? rows[b]->table[static_cast<size_t>(page)]
+                         : 0;
+    }
   }
   qs[B] = row;
   std::copy(merge.begin(), merge.end(), mrg);

@@ -17,6 +17,7 @@ namespace pa {
 constexpr size_t kWsAlign = 256;
 constexpr int32_t kNoWindowRecent = 1 << 29;  // "recent" of a sequence without a window
 constexpr int kDecodeWaves = 4;  // waves per decode workgroup
+constexpr int kWorkInts = 16;    // ints per decode work item
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -51,7 +52,11 @@ struct DecodeArgs {
   const int32_t* tbl_off;   // [B] offset of the sequence's table in `tables`
   const int32_t* tables;    // concatenated block tables
   const int32_t* q_start;   // [B+1] first query row of b
-  const int32_t* work;      // [n_work][2] = (b, partition index)
+  const int32_t* work;      // [n_work][kWorkInts]: b, partition c, L, row0, q_len, sinks,
+                            // recent, sink pages, gap, table offset, part_base, 0, then the
+                            // block of compact page c * pages_per_part + w for waves w < 4
+                            // (everything a workgroup needs before its first page, in one
+                            // 64-byte scalar load)
   const int32_t* part_base; // [B] first partial row-head of b, or -1 = single partition;
                             // row-head of (partition c, row t, head h) =
                             // part_base + (c * q_len_b + t) * Hq + h
