@@ -35,13 +35,8 @@
 #include "kernels.hpp"
 
 // Tile parameters (compile-time; variant builds override them with -D).
-#ifndef PA_DECODE_WAVES_PER_EU
-#define PA_DECODE_WAVES_PER_EU 0  // occupancy hint for the GQA kernel (0 = none)
-#endif
-#if PA_DECODE_WAVES_PER_EU > 0
-#define PA_DECODE_OCC __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
-#else
-#define PA_DECODE_OCC
+#ifndef PA_DECODE_WAVES_I8
+#define PA_DECODE_WAVES_I8 3
 #endif
 #ifndef PA_DECODE_PERMLANE
 #define PA_DECODE_PERMLANE 1  // cross-group reductions with permlane swaps (not LDS)
@@ -224,6 +219,18 @@ template <int D, int BS> struct PageRegs<D, BS, true> {
   f32x4 ks[BS / 16], vs[BS / 16];
 };
 
+// Minimum waves per SIMD a decode kernel variant is compiled for (its
+// register budget).  int8 pages move fewer bytes per load, so the 16-column
+// int8 kernel asks for 3 resident waves to keep enough bytes in flight; the
+// d 128 / 32-slot / 32-column variants hold two 32-token pages for two
+// column tiles and would spill under 2, so they take what they need.
+template <int D, int BS, int CT, bool Q8>
+constexpr int decode_waves() {
+  if (Q8 && CT == 1 && BS == 16) return PA_DECODE_WAVES_I8;
+  if (D == 128 && BS == 32 && CT == 2) return 1;
+  return 2;
+}
+
 // decode_mfma: split-K paged attention for query rows that are the last
 // q_len positions of their sequence (q_len = 1: decode).
 //
@@ -247,7 +254,9 @@ template <int D, int BS> struct PageRegs<D, BS, true> {
 // in LDS; a range that is the whole sequence writes bf16 output, otherwise
 // fp32 partials (m, l, acc) for the merge kernel.
 template <int D, int BS, int CT, bool Q8>
-__global__ __launch_bounds__(256) PA_DECODE_OCC void decode_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(decode_waves<D, BS, CT, Q8>())))
+void decode_mfma(DecodeArgs a) {
   constexpr int KS = D / 32;   // k-steps of the 16x16x32 QK contraction
   constexpr int TT = BS / 16;  // 16-token tiles per page
   constexpr int DT = D / 16;   // 16-wide d tiles of the P.V contraction
