@@ -420,14 +420,14 @@ void decode_mfma(DecodeArgs a) {
       // A column with no visible key so far keeps m = -inf; exponents are
       // then taken against 0, giving weight 0 instead of -inf - -inf.
       const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-      alpha[ct] = exp2f(m_run[ct] - m_ref);
+      alpha[ct] = exp2_flush(m_run[ct] - m_ref);
       m_run[ct] = m_new;
       float psum = 0.f;
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(s[ct][tt][i] - m_ref);
+          const float e = exp2_flush(s[ct][tt][i] - m_ref);
           psum += e;
           float w = e;
           if constexpr (Q8) {

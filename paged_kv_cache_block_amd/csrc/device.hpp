@@ -49,6 +49,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// 2^x with the hardware instruction alone (v_exp_f32): results below 2^-126
+// flush to 0 instead of going through the denormal-safe expansion exp2f
+// adds around it.  Softmax weights that small are negligible next to the
+// maximum weight 1.
+__device__ __forceinline__ float exp2_flush(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the same row of the four
 // 16-lane groups), through gfx950's row-swap permutes: no LDS traffic, so no
 // wait on the LDS / scalar-memory counter.  Each swap returns the pair

@@ -154,7 +154,41 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   // Stage tile T into ring slot st: this wave's BPW blocks, one direct
   // global->LDS load each.  Tiles past the last (issued to keep every wave's
   // vmcnt accounting uniform) and slots past the sequence end read zeros.
+  // Per-lane element offsets of this wave's blocks inside their page (and
+  // which page of the tile each comes from): loop-invariant, so a tile
+  // wholly inside the sequence is staged with one multiply-add per block.
+  int blk_off[BPW], blk_pgi[BPW];
+#pragma unroll
+  for (int r = 0; r < BPW; ++r) {
+    const int blkid = wave * BPW + r;
+    if (blkid < KB) {
+      const int tt = blkid / KS, j = blkid - tt * KS;
+      const int tok = 8 * (n >> 2) + 4 * tt + (n & 3);
+      blk_pgi[r] = tok / BS;
+      blk_off[r] = (tok % BS) * D + 32 * j + 8 * grp;
+    } else {
+      const int nt = blkid - KB;
+      const int tok = 8 * grp;
+      blk_pgi[r] = tok / BS;
+      blk_off[r] = (16 * nt + n) * BS + tok % BS;
+    }
+  }
+
   auto stage = [&](int T, int st) {
+    if (T < n_tiles && T * kTile + kTile <= L) {
+      int ent[PAGES];
+#pragma unroll
+      for (int p = 0; p < PAGES; ++p) ent[p] = scalar_load(table, T * PAGES + p);
+#pragma unroll
+      for (int r = 0; r < BPW; ++r) {
+        const int blkid = wave * BPW + r;
+        const uint16_t* pool = blkid < KB ? kpool : vpool;
+        const int blk = blk_pgi[r] ? ent[PAGES - 1] : ent[0];
+        const uint16_t* src = pool + (static_cast<size_t>(blk) * Hkv + g) * page + blk_off[r];
+        __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
+      }
+      return;
+    }
     int ent[PAGES];
 #pragma unroll
     for (int p = 0; p < PAGES; ++p) {
@@ -186,8 +220,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     }
   };
 
-  auto compute = [&](int T, int st) {
-    if (!wave_live || T * kTile > wave_keys) return;
+  auto compute_tile = [&](int T, int st) {
     const bool masked = T * kTile + kTile - 1 > all_see;
     const bool tail = T * kTile + kTile > L;
     const bf16x8* blocks = reinterpret_cast<const bf16x8*>(&ring[st][0][0]);
@@ -217,8 +250,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
           s[k][tt][i] = x;
           mloc = fmaxf(mloc, x);
         }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      mloc = rows4_max(mloc);
       // Raw-score maximum; every column sees key 0 in tile 0, so m_run is
       // finite from the first tile on.
       const float m_new = fmaxf(m_run[k], mloc);
@@ -228,7 +260,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(fmaf(s[k][tt][i], a.scale_log2, -ms));
+          const float e = exp2_flush(fmaf(s[k][tt][i], a.scale_log2, -ms));
           const __bf16 hi = static_cast<__bf16>(e);
           p_hi[k][4 * tt + i] = hi;
           if constexpr (kSplitP) {
@@ -241,7 +273,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       if (m_new != m_run[k]) {
         // Only lanes whose column maximum moved rescale; the wave skips the
         // multiplies when no column's maximum moved.
-        const float alpha = exp2f((m_run[k] - m_new) * a.scale_log2);
+        const float alpha = exp2_flush((m_run[k] - m_new) * a.scale_log2);
         l_run[k] *= alpha;
 #pragma unroll
         for (int nt = 0; nt < DT; ++nt) acc[k][nt] *= alpha;
@@ -267,6 +299,11 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     }
   };
 
+  auto compute = [&](int T, int st) {
+    if (!wave_live || T * kTile > wave_keys) return;
+    compute_tile(T, st);
+  };
+
 #pragma unroll
   for (int T = 0; T < S - 1; ++T) stage(T, T);
   for (int T = 0; T < n_tiles; ++T) {
@@ -286,8 +323,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   if (!wave_live) return;
 #pragma unroll
   for (int k = 0; k < CG; ++k) {
-    float l = l_run[k] + __shfl_xor(l_run[k], 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = rows4_sum(l_run[k]);
     if (row[k] >= q_len) continue;
     const float inv = 1.f / l;
     uint16_t* o = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(q0 + row[k]) * Hq + head[k]) * D;
