@@ -1,0 +1,116 @@
+"""GPU parity at the edges of the supported shapes: the largest head_dim
+(512), large and tiny blocks, a single slot per block, group 16 and a
+single query head per KV head, int8 pages on the generic kernel (head_dim
+256), one-token sequences, a batch of one, and chunks whose rows reach the
+first position of the sequence.
+
+Source: docs.rs ferrum-kv 0.4.0 src/attention.rs, paged_attention (decode and
+q_tokens > 1); int8 rows as in the vladkulikov.com notebook "Модуль 10"
+KV-compression experiment.  Bar: (1e-5, 1e-5) fp32, (2e-3, 1e-2) bf16 / int8.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth.workloads import bf16_round, to_f64
+
+from gpu_support import BF16_TOL, F32_TOL, assert_close, log, to_device, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_block_amd import abi
+    abi.load()
+
+
+def _io(kv):
+    return "f32" if kv == "f32" else "bf16"
+
+
+def _draw(rng, shape, kv):
+    x = rng.standard_normal(shape).astype(np.float32)
+    return x if kv == "f32" else bf16_round(x)
+
+
+def _pool(lengths, hkv, d, bs, kv, seed=1):
+    from paged_kv_cache_block_amd import DevicePool
+    nb = int(sum(-(-n // bs) for n in lengths) + 5)
+    order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    pool = DevicePool(nb, bs, hkv, d, dtype=kv, allocation_order=order)
+    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv == "i8" else None)
+    rng = np.random.default_rng(seed + 7)
+    io = _io(kv)
+    for s, n in enumerate(lengths):
+        pool.create(s)
+        ref.create(s)
+        k, v = _draw(rng, (n, hkv, d), kv), _draw(rng, (n, hkv, d), kv)
+        slots = pool.append(s, n)
+        assert slots.tolist() == ref.append(s, n)
+        pool.write(slots, to_device(k, io), to_device(v, io))
+        ref.write(slots, to_f64(k, io), to_f64(v, io))
+    torch.cuda.synchronize()
+    return pool, ref, rng
+
+
+EDGE_CASES = [
+    # lengths, Hq, Hkv, D, bs, kv
+    ([1, 3, 700], 4, 2, 512, 16, "f32"),        # largest head_dim, generic fp32
+    ([2, 65, 300], 8, 4, 512, 8, "bf16"),       # largest head_dim, bf16 generic
+    ([1, 129, 1000], 8, 1, 64, 1, "f32"),       # one slot per block
+    ([5, 300, 2000], 8, 8, 128, 128, "bf16"),   # large block (generic), MHA
+    ([1, 2, 17, 900], 16, 1, 128, 16, "bf16"),  # group 16 on the MFMA kernel
+    ([1, 40, 1200], 16, 2, 256, 32, "i8"),      # int8 pages, head_dim 256 (generic)
+    ([7], 32, 8, 128, 16, "bf16"),              # a batch of one
+    ([1, 1, 1], 32, 8, 128, 16, "i8"),          # one-token sequences, int8
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES,
+                         ids=lambda c: f"D{c[3]}-bs{c[4]}-G{c[1]//c[2]}-{c[5]}-L{max(c[0])}")
+def test_decode_and_prefill_edges(case):
+    lengths, hq, hkv, d, bs, kv = case
+    log(f"edge {case}")
+    pool, ref, rng = _pool(lengths, hkv, d, bs, kv)
+    io = _io(kv)
+    tol = F32_TOL if kv == "f32" else BF16_TOL
+    seqs = list(range(len(lengths)))
+    q = _draw(rng, (len(seqs), hq, d), io)
+    got = to_host_f64(pool.decode(seqs, to_device(q, io)))
+    for i, s in enumerate(seqs):
+        want = oracle.paged_attention(ref, s, to_f64(q[i:i + 1], io))[0]
+        assert_close(got[i], want, *tol, what=f"decode seq {s}")
+    # Prefill: every row of each sequence (rows reach position 0).
+    q_lens = list(lengths)
+    qp = _draw(rng, (sum(q_lens), hq, d), io)
+    got = to_host_f64(pool.prefill(seqs, q_lens, to_device(qp, io)))
+    r0 = 0
+    for s, n in zip(seqs, q_lens):
+        keys, values = ref.gather(s)
+        want = oracle.attention(to_f64(qp[r0:r0 + n], io), keys, values)
+        assert_close(got[r0:r0 + n], want, *tol, what=f"prefill seq {s}")
+        r0 += n
+
+
+def test_reshape_and_cache_skips_out_of_range_slots():
+    """Slots outside [0, num_blocks * block_size) are skipped (documented):
+    the pool bytes do not change."""
+    from paged_kv_cache_block_amd import DevicePool
+    pool = DevicePool(4, 16, 2, 64, dtype="bf16")
+    before = pool.k.clone(), pool.v.clone()
+    k = torch.ones(3, 2, 64, dtype=torch.bfloat16, device="cuda")
+    slots = torch.tensor([-1, 64, 1 << 40], dtype=torch.int64, device="cuda")
+    pool.write(slots, k, k)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k, before[0]) and torch.equal(pool.v, before[1])
+    q8 = DevicePool(4, 16, 2, 64, dtype="i8")
+    before = q8.k.clone()
+    q8.write(slots, k, k)
+    torch.cuda.synchronize()
+    assert torch.equal(q8.k, before)
