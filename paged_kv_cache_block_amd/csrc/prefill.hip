@@ -40,6 +40,7 @@
 //   head of every sequence, so a shared prefix is read from HBM once per
 //   head.
 #include <cmath>
+#include <type_traits>
 
 #include "device.hpp"
 #include "kernels.hpp"
@@ -79,6 +80,7 @@ constexpr int kPrefillWaves = PA_PREFILL_WAVES;    // waves per workgroup
 constexpr int kPrefillStages = PA_PREFILL_STAGES;  // key tiles in the LDS ring
 constexpr bool kSplitP = PA_PREFILL_SPLIT_P;       // P as bf16 hi + lo in P.V
 constexpr int kTile = 32;                          // key tokens per step
+constexpr float kSlackLog2 = 8.f;                  // largest softmax weight, log2
 
 // s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
 // and `lgkm` LDS/scalar operations of this wave are outstanding.
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   const bool wave_live = t_first < q_len;
   const int t_last = min(q_len - 1, t0 + (wave_c0 + CG * 16 - 1) / G);
   const int wave_keys = off + t_last;  // last key of any column of the wave
-  const int all_see = off + t_first;   // keys <= all_see are visible to every column
+  const float slack = kSlackLog2 / a.scale_log2;  // in raw-score units
 
   bf16x8 qv[CG][KS];
   int lim[CG], row[CG], head[CG];
@@ -220,9 +222,14 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     }
   };
 
-  auto compute_tile = [&](int T, int st) {
-    const bool masked = T * kTile + kTile - 1 > all_see;
-    const bool tail = T * kTile + kTile > L;
+  // One key tile.  kMasked: some key of the tile lies past some column's
+  // limit (the causal diagonal or the sequence end); kTail: the tile reaches
+  // past the sequence end, so a V chunk that straddles it may hold stale
+  // bits in its later slots, which are zeroed before they meet P = 0.  Tiles
+  // every column sees whole take the instantiation with neither.
+  auto compute_tile = [&](int T, int st, auto masked_c, auto tail_c) {
+    constexpr bool kMasked = decltype(masked_c)::value;
+    constexpr bool kTail = decltype(tail_c)::value;
     const bf16x8* blocks = reinterpret_cast<const bf16x8*>(&ring[st][0][0]);
     f32x4 s[CG][2];
 #pragma unroll
@@ -241,51 +248,59 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
     for (int k = 0; k < CG; ++k) {
       float mloc = -INFINITY;
+      const int room = kMasked ? lim[k] - (T * kTile + 8 * grp) : 0;  // last visible offset
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = s[k][tt][i];
-          if (masked && T * kTile + 8 * grp + 4 * tt + i > lim[k]) x = -INFINITY;
+          if (kMasked && 4 * tt + i > room) x = -INFINITY;
           s[k][tt][i] = x;
           mloc = fmaxf(mloc, x);
         }
       mloc = rows4_max(mloc);
-      // Raw-score maximum; every column sees key 0 in tile 0, so m_run is
-      // finite from the first tile on.
-      const float m_new = fmaxf(m_run[k], mloc);
-      const float ms = m_new * a.scale_log2;
-      float psum = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2_flush(fmaf(s[k][tt][i], a.scale_log2, -ms));
-          const __bf16 hi = static_cast<__bf16>(e);
-          p_hi[k][4 * tt + i] = hi;
-          if constexpr (kSplitP) {
-            p_lo[k][4 * tt + i] = static_cast<__bf16>(e - static_cast<float>(hi));
-            psum += e;
-          } else {
-            psum += static_cast<float>(hi);  // l from the same rounded weights as P.V
-          }
-        }
-      if (m_new != m_run[k]) {
-        // Only lanes whose column maximum moved rescale; the wave skips the
-        // multiplies when no column's maximum moved.
-        const float alpha = exp2_flush((m_run[k] - m_new) * a.scale_log2);
+      // The exponent reference m_run moves only when a score passes it by
+      // more than `slack` (2^kSlackLog2 in weight), so weights stay at most
+      // 2^kSlackLog2 and the accumulators are rescaled on few tiles: mostly
+      // the first, where m_run is -inf and the factor is 0.  Every column
+      // sees key 0 in tile 0, so m_run is finite from then on.
+      if (mloc - m_run[k] > slack) {
+        const float alpha = exp2_flush((m_run[k] - mloc) * a.scale_log2);
         l_run[k] *= alpha;
 #pragma unroll
         for (int nt = 0; nt < DT; ++nt) acc[k][nt] *= alpha;
+        m_run[k] = mloc;
       }
-      m_run[k] = m_new;
+      const float ms = m_run[k] * a.scale_log2;
+      float psum = 0.f;
+      uint32_t hi_w[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // Weights of tokens 2w, 2w+1 of this lane's 8.
+        float e[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int idx = 2 * w + h;
+          e[h] = exp2_flush(fmaf(s[k][idx / 4][idx % 4], a.scale_log2, -ms));
+          // hi = e with the low 16 bits cleared (a bf16 value); e - hi is exact.
+          const float lo = e[h] - __uint_as_float(__float_as_uint(e[h]) & 0xffff0000u);
+          if constexpr (kSplitP) {
+            p_lo[k][idx] = static_cast<__bf16>(lo);
+            psum += e[h];
+          } else {
+            psum += e[h] - lo;  // l from the same weights as P.V
+          }
+        }
+        hi_w[w] = __builtin_amdgcn_perm(__float_as_uint(e[1]), __float_as_uint(e[0]), 0x07060302u);
+      }
+      p_hi[k] = __builtin_bit_cast(bf16x8, (uint4{hi_w[0], hi_w[1], hi_w[2], hi_w[3]}));
       l_run[k] += psum;
     }
-    const int live = L - (T * kTile + 8 * grp);  // tokens of this lane's 8 inside the sequence
+    const int live = kTail ? L - (T * kTile + 8 * grp) : kTile;  // tokens of this lane's 8 inside the sequence
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
       bf16x8 vop = blocks[(KB + nt) * 64 + lane];
-      if (tail) {
+      if constexpr (kTail) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (e >= live) vop[e] = static_cast<__bf16>(0.f);
@@ -299,22 +314,35 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     }
   };
 
-  auto compute = [&](int T, int st) {
-    if (!wave_live || T * kTile > wave_keys) return;
-    compute_tile(T, st);
+  // One pipeline step: tile T's blocks from this wave have landed once at
+  // most the blocks of the S-2 later tiles are outstanding; the barrier then
+  // publishes the whole tile and guarantees every wave has finished reading
+  // the slot that the next stage() overwrites (read in step T-1).
+  auto step = [&](int T) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * BPW, 0));
+    __builtin_amdgcn_s_barrier();
+    stage(T + S - 1, (T + S - 1) % S);
   };
 
 #pragma unroll
   for (int T = 0; T < S - 1; ++T) stage(T, T);
-  for (int T = 0; T < n_tiles; ++T) {
-    // Tile T's blocks from this wave have landed once at most the blocks of
-    // the S-2 later tiles are outstanding; the barrier then publishes the
-    // whole tile and guarantees every wave has finished reading the slot
-    // that the next stage() overwrites (read in step T-1).
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * BPW, 0));
-    __builtin_amdgcn_s_barrier();
-    stage(T + S - 1, (T + S - 1) % S);
-    compute(T, T % S);
+  // Tiles below t_split are seen whole by every row of the workgroup and take
+  // the unmasked path; the few after it (the causal diagonal, the sequence
+  // end) take the masked one, which also zeroes V slots past the sequence
+  // end.  Every wave runs the same steps (the barrier counts all of them).
+  const int t_split = min(n_tiles, (off + t0 + 1) / kTile);
+  int T = 0;
+  if (wave_live) {
+    for (; T < t_split; ++T) {
+      step(T);
+      compute_tile(T, T % S, std::false_type{}, std::false_type{});
+    }
+    for (; T < n_tiles; ++T) {
+      step(T);
+      if (T * kTile <= wave_keys) compute_tile(T, T % S, std::true_type{}, std::true_type{});
+    }
+  } else {
+    for (; T < n_tiles; ++T) step(T);
   }
   // Drain the zero-tile loads still in flight before the workgroup's LDS is
   // released.
