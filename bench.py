@@ -265,14 +265,15 @@ def run_verify(args, q_len=4):
             "kernel_GBs": round(float(np.mean(alg)) / (kernel_ms * 1e-3) / 1e9, 1)}
 
 
-def run_prefill(args):
+def run_prefill(args, kv=None):
+    """Chunked prefill of workload 4 (pages in ``kv``, default bf16)."""
     import torch
     from paged_kv_cache_block_amd import abi
     from synth import prefill_queries, prefix_prefill
 
     wl = prefix_prefill()
-    log("building the prefill workload (16 x 512 rows on a shared 4096 prefix)")
-    pool = build_pool(wl)
+    log(f"building the prefill workload (16 x 512 rows on a shared 4096 prefix, {kv or wl.dtype} pages)")
+    pool = build_pool(wl, kv)
     seqs = [s for s, _ in wl.prefill]
     q_lens = [n for _, n in wl.prefill]
     q = to_device(prefill_queries(wl), wl.dtype)
@@ -298,7 +299,8 @@ def run_prefill(args):
     tflops = flops / (kernel_ms * 1e-3) / 1e12
     pool.close()
     return {
-        "workload": "prefix_prefill: 16 seqs share 4096 prefix + 512 own rows, 32/8 heads, d 128, bf16, bs 16",
+        "workload": "prefix_prefill: 16 seqs share 4096 prefix + 512 own rows, 32/8 heads, d 128, "
+                    + ("int8 K/V pages (bf16 q, out)" if kv == "i8" else "bf16") + ", bs 16",
         "causal_flops": flops,
         "ms_per_call": call_ms,
         "kernel_ms": kernel_ms,
@@ -386,8 +388,9 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--legs", default="int8,verify,window,prefix",
-                    help="comma list of the legs after the headline decode leg: int8, verify, window, "
-                         "prefix (prefill and the CPU baseline have their own switches)")
+                    help="comma list of the legs after the headline decode leg: int8 (decode and "
+                         "prefill over int8 pages), verify, window, prefix (the bf16 prefill and the "
+                         "CPU baseline have their own switches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -468,6 +471,8 @@ def main():
         }
     if not args.no_prefill:
         line["prefill"] = run_prefill(args)
+        if "int8" in legs:
+            line["int8_prefill"] = run_prefill(args, kv="i8")
     if "prefix" in legs:
         line["prefix_cache"] = run_prefix_cache()
     if not args.no_cpu_baseline:

@@ -52,7 +52,6 @@ namespace pa {
 
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // --------------------------------------------------------------- generic ---
 struct GenericArgs {
@@ -183,25 +182,6 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
 }
 
 // ------------------------------------------------------------ GQA / MFMA ---
-// 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).
-__device__ __forceinline__ s16x4 i8x4_to_bf16x4(uint32_t w) {
-  s16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float f = static_cast<float>(static_cast<int8_t>(w >> (8 * i)));
-    r[i] = static_cast<short>(__float_as_uint(f) >> 16);
-  }
-  return r;
-}
-__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  const s16x4 a = i8x4_to_bf16x4(lo), b = i8x4_to_bf16x4(hi);
-  const short v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, v[i]);
-  return r;
-}
-
 // One page of one KV head, as one lane holds it.
 //   bf16: k[tt][j] = K[16tt + n][32j + 8grp .. +8], v[nt][tt] = V^T[16nt + n][16tt + 4grp .. +4]
 //   int8: kc[tt][.] = K codes of token 16tt + n, d in [grp * D/4, +D/4) (the QK

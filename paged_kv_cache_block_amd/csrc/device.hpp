@@ -14,6 +14,7 @@ namespace pa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // bf16 bit pattern <-> float.  Widening is exact; narrowing is round to
 // nearest even (NaN stays NaN).
@@ -77,6 +78,25 @@ __device__ __forceinline__ float rows4_sum(float x) {
 // operand order of the P.V MFMA, so that one lane's codes are contiguous.
 __device__ __forceinline__ int q8_v_offset(int t, int d, int D) {
   return (t >> 4) * 16 * D + (((t & 15) >> 2) * 16 + (d & 15)) * (D >> 2) + (d >> 4) * 4 + (t & 3);
+}
+
+// 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).
+__device__ __forceinline__ s16x4 i8x4_to_bf16x4(uint32_t w) {
+  s16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float f = static_cast<float>(static_cast<int8_t>(w >> (8 * i)));
+    r[i] = static_cast<short>(__float_as_uint(f) >> 16);
+  }
+  return r;
+}
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const s16x4 a = i8x4_to_bf16x4(lo), b = i8x4_to_bf16x4(hi);
+  const short v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, v[i]);
+  return r;
 }
 
 // Uniform value in a scalar register (the compiler cannot always prove it).

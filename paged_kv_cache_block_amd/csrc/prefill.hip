@@ -7,7 +7,8 @@
 // masks cached decoding).  The one-pass running max / sum per key tile is
 // lecture 19's tiled_attention recurrence.
 //
-// prefill_gqa_mfma<D, BS, CG, NW, S>  (bf16, D in {64, 128}, BS in {16, 32}, G | 16)
+// prefill_gqa_mfma<D, BS, CG, NW, S, Q8>  (bf16 or int8 pages, D in {64, 128},
+//                                         BS in {16, 32}, G | 16)
 //   One workgroup of NW waves = (sequence, block of query rows, KV head).
 //   The MFMA N dimension packs (query row, head of the group) pairs: column c
 //   of the workgroup is row t0 + c / G, head g*G + c % G, so each key tile
@@ -39,6 +40,15 @@
 //   KV head: with Hkv a multiple of 8 each XCD (and its L2) serves one KV
 //   head of every sequence, so a shared prefix is read from HBM once per
 //   head.
+//
+//   int8 pages (the [KVquant] rows: codes plus one fp32 scale per token and
+//   KV head): the ring holds tiles as the pages store them (K codes, V codes
+//   in their operand order, the 64 scales), fetched with the same direct
+//   loads; each step every wave converts its share of the next tile's
+//   operand blocks to bf16 (exact: |code| <= 127) into one of two
+//   operand-ordered tiles, so the MFMA part is the bf16 one.  The scales stay
+//   in fp32: K's multiply the scores, V's the weights entering P.V (l sums
+//   the weights without them).
 #include <cmath>
 #include <type_traits>
 
@@ -53,6 +63,9 @@
 #endif
 #ifndef PA_PREFILL_STAGES
 #define PA_PREFILL_STAGES 3
+#endif
+#ifndef PA_PREFILL_STAGES_Q8
+#define PA_PREFILL_STAGES_Q8 4
 #endif
 #ifndef PA_PREFILL_SPLIT_P
 #define PA_PREFILL_SPLIT_P 1
@@ -78,6 +91,7 @@ typedef __attribute__((address_space(1))) void global_void;
 constexpr int kPrefillCG = PA_PREFILL_CG;          // 16-column groups per wave
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;    // waves per workgroup
 constexpr int kPrefillStages = PA_PREFILL_STAGES;  // key tiles in the LDS ring
+constexpr int kPrefillStagesQ8 = PA_PREFILL_STAGES_Q8;  // raw int8 tiles in the LDS ring
 constexpr bool kSplitP = PA_PREFILL_SPLIT_P;       // P as bf16 hi + lo in P.V
 constexpr int kTile = 32;                          // key tokens per step
 constexpr float kSlackLog2 = 8.f;                  // largest softmax weight, log2
@@ -88,7 +102,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
 }
 
-template <int D, int BS, int CG, int NW, int S>
+template <int D, int BS, int CG, int NW, int S, bool Q8>
 __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(PrefillArgs a) {
   constexpr int KS = D / 32;         // k-steps of QK per token half
   constexpr int DT = D / 16;         // d tiles of P.V
@@ -96,9 +110,18 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   constexpr int NB = KB + DT;        // operand blocks per key tile
   constexpr int PAGES = kTile / BS;  // pages per key tile
   static_assert(NB % NW == 0, "each wave stages the same number of blocks");
-  constexpr int BPW = NB / NW;       // blocks staged by each wave per tile
+  constexpr int BPW = NB / NW;       // blocks staged (bf16) or converted (int8) by each wave per tile
   static_assert((S - 2) * BPW < 64, "vmcnt range");
-  __shared__ uint4 ring[S][NB][64];
+  // int8 pages: a tile as the pages hold it (K codes, V codes, K scales, V
+  // scales of its 32 tokens), moved by kCodeLoads 1 KB wave loads of codes
+  // plus one 256-byte load of scales.
+  constexpr int kRawBytes = 2 * kTile * D + 2 * kTile * 4;
+  constexpr int kCodeLoads = 2 * kTile * D / 1024;
+  static_assert(!Q8 || (S >= 4 && kCodeLoads <= NW && kCodeLoads % 2 == 0), "int8 ring");
+  // bf16: an S-stage ring of operand-ordered tiles.  int8: an S-stage ring of
+  // raw tiles and two operand-ordered bf16 tiles converted from them.
+  __shared__ uint4 ring[Q8 ? 2 : S][NB][64];
+  __shared__ uint4 raw[Q8 ? S : 1][Q8 ? kRawBytes / 16 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,7 +138,10 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   const int32_t* table = a.tables + a.tbl_off[b];
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
-  const size_t page = static_cast<size_t>(BS) * D;
+  const size_t page = static_cast<size_t>(BS) * D;  // bf16 elements per page
+  const uint8_t* kq = static_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* vq = static_cast<const uint8_t*>(a.v_pool);
+  const size_t q8_page = static_cast<size_t>(BS) * D + 4 * BS;  // bytes per int8 page (codes, scales)
 
   // Rows of the workgroup and of this wave.
   const int wg_rows = NW * CG * 16 / G;
@@ -222,6 +248,84 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     }
   };
 
+  // int8: stage raw tile T into raw slot st.  Wave w < kCodeLoads moves 1 KB
+  // of codes (the first half of the loads K codes, the second V codes; page by
+  // page as the pool holds them, so token t's K codes sit at t * D and the V
+  // codes keep their operand order); wave 0's lanes 0-15 also move the 32 K
+  // and 32 V row scales.  Pages past the sequence's last read zeros; slots
+  // past its end inside the last page are staged as they are (finite codes;
+  // their scales are never used, see the masked softmax).
+  auto stage_q8 = [&](int T, int st) {
+    uint8_t* dst = reinterpret_cast<uint8_t*>(&raw[st][0]);
+    int ent[PAGES];
+#pragma unroll
+    for (int p = 0; p < PAGES; ++p) {
+      const int pg = T * PAGES + p;
+      ent[p] = (T < n_tiles && pg < nblk) ? scalar_load(table, pg) : -1;
+    }
+    if (wave < kCodeLoads) {
+      constexpr int kHalf = kCodeLoads / 2;  // loads per code region
+      const bool isv = wave >= kHalf;
+      const int o0 = (isv ? wave - kHalf : wave) * 1024;  // wave's first byte in the region
+      const int o = o0 + 16 * lane;
+      const int pgi = o / (BS * D);
+      const int blk = pgi ? ent[PAGES - 1] : ent[0];
+      const void* src = a.zeros;
+      if (blk >= 0)
+        src = (isv ? vq : kq) + (static_cast<size_t>(blk) * Hkv + g) * q8_page + (o - pgi * BS * D);
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(dst + (isv ? kTile * D : 0) + o0), 16, 0, 0);
+    }
+    if (wave == 0 && lane < 16) {
+      // Lane l: the scales of tokens 4(l % 8) .. +3, K for l < 8, V after.
+      const int tok = 4 * (lane & 7);
+      const int pgi = tok / BS;
+      const int blk = pgi ? ent[PAGES - 1] : ent[0];
+      const void* src = a.zeros;
+      if (blk >= 0)
+        src = (lane >= 8 ? vq : kq) + (static_cast<size_t>(blk) * Hkv + g) * q8_page + BS * D + 4 * (tok % BS);
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(dst + 2 * kTile * D), 16, 0, 0);
+    }
+  };
+  // Loads a wave issues per int8 tile, and waits that leave at most `tiles`
+  // later tiles' loads outstanding (a wave-uniform count).
+  const int q8_loads = (wave < kCodeLoads ? 1 : 0) + (wave == 0 ? 1 : 0);
+  auto q8_wait = [&](auto tiles_c) {
+    constexpr int kT = decltype(tiles_c)::value;
+    if (q8_loads == 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kT, 0));
+    else if (q8_loads == 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(kT, 0));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  };
+  // int8: convert this wave's BPW operand blocks of raw slot rs into bf16
+  // operand tile os (the same operand order as the bf16 ring; codes are
+  // exact in bf16, the scales stay apart in fp32).
+  int cv_lo[BPW], cv_hi[BPW];
+#pragma unroll
+  for (int r = 0; r < BPW; ++r) {
+    const int blkid = wave * BPW + r;
+    if (blkid < KB) {
+      const int tt = blkid / KS, j = blkid - tt * KS;
+      const int tok = 8 * (n >> 2) + 4 * tt + (n & 3);
+      cv_lo[r] = tok * D + 32 * j + 8 * grp;
+      cv_hi[r] = cv_lo[r] + 4;
+    } else {
+      const int d = 16 * (blkid - KB) + n;
+      cv_lo[r] = kTile * D + q8_v_offset(8 * grp, d, D);
+      cv_hi[r] = kTile * D + q8_v_offset(8 * grp + 4, d, D);
+    }
+  }
+  auto convert_q8 = [&](int rs, int os) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(&raw[rs][0]);
+#pragma unroll
+    for (int r = 0; r < BPW; ++r) {
+      const uint32_t lo = *reinterpret_cast<const uint32_t*>(src + cv_lo[r]);
+      const uint32_t hi = *reinterpret_cast<const uint32_t*>(src + cv_hi[r]);
+      ring[os][wave * BPW + r][lane] = __builtin_bit_cast(uint4, i8x8_to_bf16x8(lo, hi));
+    }
+  };
+
   // One key tile.  kMasked: some key of the tile lies past some column's
   // limit (the causal diagonal or the sequence end); kTail: the tile reaches
   // past the sequence end, so a V chunk that straddles it may hold stale
@@ -244,6 +348,18 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
           s[k][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[k][j], s[k][tt], 0, 0, 0);
       }
     // s[k][tt][i] is the score of token T*32 + 8*grp + 4*tt + i for column n.
+    // int8: the row scales of this lane's 8 tokens; K's scales the scores,
+    // V's the weights that enter P.V (not l).
+    float sk[8], sv[8];
+    if constexpr (Q8) {
+      const float4* sc = reinterpret_cast<const float4*>(
+          reinterpret_cast<const uint8_t*>(&raw[T % S][0]) + 2 * kTile * D + 32 * grp);
+      const float4 k0 = sc[0], k1 = sc[1], v0 = sc[kTile / 4], v1 = sc[kTile / 4 + 1];
+      sk[0] = k0.x, sk[1] = k0.y, sk[2] = k0.z, sk[3] = k0.w;
+      sk[4] = k1.x, sk[5] = k1.y, sk[6] = k1.z, sk[7] = k1.w;
+      sv[0] = v0.x, sv[1] = v0.y, sv[2] = v0.z, sv[3] = v0.w;
+      sv[4] = v1.x, sv[5] = v1.y, sv[6] = v1.z, sv[7] = v1.w;
+    }
     bf16x8 p_hi[CG], p_lo[CG];
 #pragma unroll
     for (int k = 0; k < CG; ++k) {
@@ -254,6 +370,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = s[k][tt][i];
+          if constexpr (Q8) x *= sk[4 * tt + i];
           if (kMasked && 4 * tt + i > room) x = -INFINITY;
           s[k][tt][i] = x;
           mloc = fmaxf(mloc, x);
@@ -281,14 +398,21 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int idx = 2 * w + h;
-          e[h] = exp2_flush(fmaf(s[k][idx / 4][idx % 4], a.scale_log2, -ms));
+          const float w8 = exp2_flush(fmaf(s[k][idx / 4][idx % 4], a.scale_log2, -ms));
+          e[h] = w8;
+          if constexpr (Q8) {
+            // A slot past the sequence end may hold any scale bits: its
+            // weight is exactly 0 and must stay so.
+            e[h] = w8 * sv[idx];
+            if (kMasked && idx > room) e[h] = 0.f;
+          }
           // hi = e with the low 16 bits cleared (a bf16 value); e - hi is exact.
           const float lo = e[h] - __uint_as_float(__float_as_uint(e[h]) & 0xffff0000u);
-          if constexpr (kSplitP) {
+          if constexpr (kSplitP || Q8) {
             p_lo[k][idx] = static_cast<__bf16>(lo);
-            psum += e[h];
+            psum += w8;
           } else {
-            psum += e[h] - lo;  // l from the same weights as P.V
+            psum += w8 - lo;  // l from the same weights as P.V
           }
         }
         hi_w[w] = __builtin_amdgcn_perm(__float_as_uint(e[1]), __float_as_uint(e[0]), 0x07060302u);
@@ -300,7 +424,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
       bf16x8 vop = blocks[(KB + nt) * 64 + lane];
-      if constexpr (kTail) {
+      if constexpr (kTail && !Q8) {  // int8 codes are always finite
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (e >= live) vop[e] = static_cast<__bf16>(0.f);
@@ -308,41 +432,74 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
       for (int k = 0; k < CG; ++k) {
         acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, p_hi[k], acc[k][nt], 0, 0, 0);
-        if constexpr (kSplitP)
+        if constexpr (kSplitP || Q8)
           acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, p_lo[k], acc[k][nt], 0, 0, 0);
       }
     }
   };
 
-  // One pipeline step: tile T's blocks from this wave have landed once at
-  // most the blocks of the S-2 later tiles are outstanding; the barrier then
-  // publishes the whole tile and guarantees every wave has finished reading
-  // the slot that the next stage() overwrites (read in step T-1).
-  auto step = [&](int T) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * BPW, 0));
-    __builtin_amdgcn_s_barrier();
-    stage(T + S - 1, (T + S - 1) % S);
-  };
-
-#pragma unroll
-  for (int T = 0; T < S - 1; ++T) stage(T, T);
   // Tiles below t_split are seen whole by every row of the workgroup and take
   // the unmasked path; the few after it (the causal diagonal, the sequence
-  // end) take the masked one, which also zeroes V slots past the sequence
-  // end.  Every wave runs the same steps (the barrier counts all of them).
+  // end) take the masked one, which also keeps slots past the sequence end
+  // out of P.V.  Every wave runs the same steps (the barrier counts all of
+  // them).
   const int t_split = min(n_tiles, (off + t0 + 1) / kTile);
-  int T = 0;
-  if (wave_live) {
-    for (; T < t_split; ++T) {
-      step(T);
-      compute_tile(T, T % S, std::false_type{}, std::false_type{});
-    }
-    for (; T < n_tiles; ++T) {
-      step(T);
-      if (T * kTile <= wave_keys) compute_tile(T, T % S, std::true_type{}, std::true_type{});
+  if constexpr (!Q8) {
+    // One pipeline step: tile T's blocks from this wave have landed once at
+    // most the blocks of the S-2 later tiles are outstanding; the barrier
+    // then publishes the whole tile and guarantees every wave has finished
+    // reading the slot that the next stage() overwrites (read in step T-1).
+    auto step = [&](int T) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * BPW, 0));
+      __builtin_amdgcn_s_barrier();
+      stage(T + S - 1, (T + S - 1) % S);
+    };
+#pragma unroll
+    for (int T = 0; T < S - 1; ++T) stage(T, T);
+    int T = 0;
+    if (wave_live) {
+      for (; T < t_split; ++T) {
+        step(T);
+        compute_tile(T, T % S, std::false_type{}, std::false_type{});
+      }
+      for (; T < n_tiles; ++T) {
+        step(T);
+        if (T * kTile <= wave_keys) compute_tile(T, T % S, std::true_type{}, std::true_type{});
+      }
+    } else {
+      for (; T < n_tiles; ++T) step(T);
     }
   } else {
-    for (; T < n_tiles; ++T) step(T);
+    // int8 step T: this wave's loads of raw tile T+1 have landed once at most
+    // those of tile T+2 are outstanding; the barrier publishes raw tile T+1
+    // and bf16 tile T (converted in step T-1) and guarantees every wave has
+    // left step T-1, the last reader of raw slot (T-1) % S (its scales) and of
+    // bf16 tile (T+1) % 2 (then tile T-1).  Step T stages raw tile T+S-1 into
+    // the former, converts raw tile T+1 into the latter and computes tile T.
+    auto step = [&](int T) {
+      q8_wait(std::integral_constant<int, S - 3>{});
+      __builtin_amdgcn_s_barrier();
+      stage_q8(T + S - 1, (T + S - 1) % S);
+      convert_q8((T + 1) % S, (T + 1) & 1);
+    };
+#pragma unroll
+    for (int T = 0; T < S - 1; ++T) stage_q8(T, T);
+    q8_wait(std::integral_constant<int, S - 2>{});  // raw tile 0
+    __builtin_amdgcn_s_barrier();
+    convert_q8(0, 0);
+    int T = 0;
+    if (wave_live) {
+      for (; T < t_split; ++T) {
+        step(T);
+        compute_tile(T, T & 1, std::false_type{}, std::false_type{});
+      }
+      for (; T < n_tiles; ++T) {
+        step(T);
+        if (T * kTile <= wave_keys) compute_tile(T, T & 1, std::true_type{}, std::true_type{});
+      }
+    } else {
+      for (; T < n_tiles; ++T) step(T);
+    }
   }
   // Drain the zero-tile loads still in flight before the workgroup's LDS is
   // released.
@@ -367,11 +524,20 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   }
 }
 
-template <int D, int BS>
+template <int D, int BS, bool Q8>
 void launch_mfma(const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_tiles * a.num_kv_heads);
-  hipLaunchKernelGGL((prefill_gqa_mfma<D, BS, kPrefillCG, kPrefillWaves, kPrefillStages>), grid,
+  constexpr int S = Q8 ? kPrefillStagesQ8 : kPrefillStages;
+  hipLaunchKernelGGL((prefill_gqa_mfma<D, BS, kPrefillCG, kPrefillWaves, S, Q8>), grid,
                      dim3(64 * kPrefillWaves), 0, stream, a);
+}
+
+template <bool Q8>
+void launch_mfma_shape(int D, int BS, const PrefillArgs& a, hipStream_t stream) {
+  if (D == 128 && BS == 16) launch_mfma<128, 16, Q8>(a, stream);
+  else if (D == 128 && BS == 32) launch_mfma<128, 32, Q8>(a, stream);
+  else if (D == 64 && BS == 16) launch_mfma<64, 16, Q8>(a, stream);
+  else launch_mfma<64, 32, Q8>(a, stream);
 }
 
 }  // namespace
@@ -380,7 +546,7 @@ bool prefill_uses_mfma(const PoolGeom& geom, int32_t group) {
   const bool d_ok = geom.head_dim == 64 || geom.head_dim == 128;
   const bool bs_ok = geom.block_size == 16 || geom.block_size == 32;
   const bool g_ok = group >= 1 && group <= 16 && 16 % group == 0;
-  return geom.dtype == 1 && d_ok && bs_ok && g_ok;
+  return (geom.dtype == 1 || geom.q8()) && d_ok && bs_ok && g_ok;
 }
 
 int32_t prefill_rows_per_tile(const PoolGeom& geom, int32_t group) {
@@ -390,11 +556,8 @@ int32_t prefill_rows_per_tile(const PoolGeom& geom, int32_t group) {
 
 hipError_t launch_prefill(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream) {
   if (!prefill_uses_mfma(geom, a.group) || a.windowed) return launch_prefill_generic(geom, a, stream);
-  const int D = geom.head_dim, BS = geom.block_size;
-  if (D == 128 && BS == 16) launch_mfma<128, 16>(a, stream);
-  else if (D == 128 && BS == 32) launch_mfma<128, 32>(a, stream);
-  else if (D == 64 && BS == 16) launch_mfma<64, 16>(a, stream);
-  else launch_mfma<64, 32>(a, stream);
+  if (geom.q8()) launch_mfma_shape<true>(geom.head_dim, geom.block_size, a, stream);
+  else launch_mfma_shape<false>(geom.head_dim, geom.block_size, a, stream);
   return hipGetLastError();
 }
 

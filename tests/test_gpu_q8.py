@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import append_stream, decode_queries, gqa_decode, logical_kv, prefill_queries
+from synth import append_stream, decode_queries, gqa_decode, logical_kv, prefill_queries, prefix_prefill
 from synth.workloads import Workload, bf16_round, to_f64
 
 from gpu_support import BF16_TOL, assert_close, log, to_device, to_host_f64
@@ -240,9 +240,17 @@ def test_q8_decode_step_with_fork():
 
 # ------------------------------------------------------------ prefill
 @pytest.mark.parametrize("case", [(([300, 77], [70, 77]), 32, 8, 128, 16),
-                                  (([200, 50], [31, 1]), 16, 16, 64, 32)],
-                         ids=["G4-D128-bs16", "G1-D64-bs32"])
+                                  (([200, 50], [31, 1]), 16, 16, 64, 32),
+                                  (([1000, 513, 33], [300, 513, 33]), 32, 4, 128, 32),
+                                  (([700, 129, 16], [257, 129, 16]), 8, 4, 64, 16),
+                                  (([500, 97], [100, 97]), 16, 16, 64, 32),
+                                  (([64, 65, 95], [64, 33, 95]), 16, 1, 128, 16)],
+                         ids=["G4-D128-bs16", "G1-D64-bs32-short", "G8-D128-bs32", "G2-D64-bs16",
+                              "G1-D64-bs32", "G16-D128-bs16"])
 def test_q8_prefill(case):
+    """Chunked causal prefill over int8 pages (the MFMA kernel for these
+    shapes; chunks with q_len * G <= 32 take the split-K decode kernels):
+    rows reaching position 0, ragged last tiles, several tiles per row."""
     (lengths, q_lens), hq, hkv, d, bs = case
     wl = _case(lengths, hq, hkv, d, bs)
     wl.prefill = list(enumerate(q_lens))
@@ -258,7 +266,70 @@ def test_q8_prefill(case):
         r0 += n
 
 
+def test_q8_prefill_shared_prefix():
+    """Three sequences share a 300-token prefix (its blocks refcounted) and
+    prefill 200-row chunks of their own tails over int8 pages."""
+    from paged_kv_cache_block_amd import DevicePool
+    hq, hkv, d, bs = 32, 8, 128, 16
+    nb = 120
+    order = np.random.default_rng(9).permutation(nb).astype(np.int32)
+    pool = DevicePool(nb, bs, hkv, d, dtype="i8", allocation_order=order)
+    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8)
+    rng = np.random.default_rng(10)
+    draw = lambda shape: bf16_round(rng.standard_normal(shape).astype(np.float32))
+    def put(s, n):
+        k, v = draw((n, hkv, d)), draw((n, hkv, d))
+        slots = pool.append(s, n)
+        assert slots.tolist() == ref.append(s, n)
+        pool.write(slots, to_device(k, "bf16"), to_device(v, "bf16"))
+        ref.write(slots, to_f64(k, "bf16"), to_f64(v, "bf16"))
+    pool.create(0)
+    ref.create(0)
+    put(0, 300)
+    for s in (1, 2):
+        pool.share(0, s, 300)
+        ref.share(0, s, 300)
+    for s, n in ((0, 200), (1, 211), (2, 200)):
+        put(s, n)
+    q_lens = [200, 211, 200]
+    qp = draw((sum(q_lens), hq, d))
+    out = to_host_f64(pool.prefill([0, 1, 2], q_lens, to_device(qp, "bf16")))
+    r0 = 0
+    for s, n in zip((0, 1, 2), q_lens):
+        keys, values = ref.gather(s)
+        exp = oracle.attention(to_f64(qp[r0:r0 + n], "bf16"), keys, values)
+        assert_close(out[r0:r0 + n], exp, *BF16_TOL, what=f"seq {s}")
+        r0 += n
+
+
 # ------------------------------------------------------------ full size
+def test_q8_full_size_prefix_prefill_sampled_rows():
+    """16 x (4096 shared + 512 own) tokens in int8 pages, 32/8 heads, d 128,
+    bs 16: the 512-row chunks of all sequences in one call; sampled rows
+    against the oracle over the dequantised rows."""
+    wl = prefix_prefill()
+    log("q8 prefix_prefill full: build")
+    pool, _ = _replay(wl, mirror=False)
+    qp = prefill_queries(wl)
+    seqs = [s for s, _ in wl.prefill]
+    q_lens = [n for _, n in wl.prefill]
+    log("q8 prefix_prefill full: prefill")
+    out = to_host_f64(pool.prefill(seqs, q_lens, to_device(qp, "bf16")))
+    torch.cuda.synchronize()
+    sample_seqs = [0, 9, 15]
+    rows = logical_kv(wl, sample_seqs)
+    rng = np.random.default_rng(2)
+    log("q8 prefix_prefill full: oracle on sampled rows")
+    for s in sample_seqs:
+        K, V = (oracle.fake_quantize_rows(to_f64(x, "bf16"), 8) for x in rows[s])
+        L = K.shape[0]
+        for t in sorted(set([0, 1, 15, 16, 255, 511] + list(rng.integers(0, 512, 5)))):
+            r = s * 512 + t
+            vis = L - 512 + t + 1
+            exp = oracle.attention(to_f64(qp[r:r + 1], "bf16"), K[:vis], V[:vis])[0]
+            assert_close(out[r], exp, *BF16_TOL, what=f"seq {s} row {t}")
+
+
 def test_q8_full_size_gqa_decode_step_sampled():
     """32 x U[1, 8192], 32/8 heads, d 128, bs 16 in int8 pages, one fused
     decode step as the benchmark times it; sampled sequences against the
