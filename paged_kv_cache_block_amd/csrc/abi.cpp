@@ -727,7 +727,6 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
   a.row_seq = reinterpret_cast<const int32_t*>(w + plan.rowseq_off);
   a.zeros = w + plan.zeros_off;
   a.seq_win = reinterpret_cast<const int32_t*>(w + plan.win_off);
-  a.windowed = plan.windowed ? 1 : 0;
   a.num_heads = num_heads;
   a.num_kv_heads = pool->geom.num_kv_heads;
   a.group = group;

@@ -281,7 +281,10 @@ Status build_prefill_plan(const BlockPool& pool, const int64_t* seqs, const int3
   for (int32_t b = 0; b < B; ++b)
     for (int32_t t0 = 0; t0 < q_lens[b]; t0 += rows_per_tile) {
       int32_t last = std::min(q_lens[b], t0 + rows_per_tile) - 1;
-      tiles.push_back({b, t0, rows[b]->length - q_lens[b] + last + 1});
+      int64_t keys = rows[b]->length - q_lens[b] + last + 1;
+      if (rows[b]->windowed())  // the sinks and the rows' windows
+        keys = std::min<int64_t>(keys, static_cast<int64_t>(rows[b]->sinks) + rows[b]->recent + rows_per_tile);
+      tiles.push_back({b, t0, keys});
     }
   // Tiles that see the most keys first.
   std::stable_sort(tiles.begin(), tiles.end(),
@@ -318,7 +321,6 @@ Status build_prefill_plan(const BlockPool& pool, const int64_t* seqs, const int3
     int32_t* w = at_bytes(meta, p.win_off) + 4 * static_cast<size_t>(b);
     w[0] = rows[b]->windowed() ? rows[b]->sinks : 0;
     w[1] = rows[b]->windowed() ? rows[b]->recent : kNoWindowRecent;
-    p.windowed = p.windowed || rows[b]->windowed();
   }
   qs[B] = static_cast<int32_t>(row);
   for (size_t i = 0; i < tiles.size(); ++i) {

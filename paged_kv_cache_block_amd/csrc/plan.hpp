@@ -114,11 +114,10 @@ struct PrefillArgs {
   const int32_t* q_start;   // [B+1] first row of b
   const int32_t* tiles;     // [n_tiles][2] = (b, first query row of the tile within b)
   const int32_t* row_seq;   // [R] sequence of each row (generic kernel)
-  const int32_t* seq_win;   // [B][4] as in DecodeArgs (the generic kernel reads sinks, recent)
+  const int32_t* seq_win;   // [B][4] as in DecodeArgs (sinks, recent; no window: 0, kNoWindowRecent)
   const void* zeros;        // 64 zero bytes (source of staged slots past a sequence's end)
   int32_t num_heads, num_kv_heads, group;
   int32_t n_tiles, n_rows;
-  int32_t windowed;         // some sequence has a window: the generic kernel serves the call
   float scale_log2;
 };
 
@@ -128,7 +127,6 @@ struct PrefillPlan {
   size_t ctx_off = 0, tbl_off_off = 0, tables_off = 0, qstart_off = 0, tiles_off = 0,
          rowseq_off = 0, zeros_off = 0, win_off = 0;
   int32_t n_tiles = 0, n_rows = 0, batch = 0;
-  bool windowed = false;  // some sequence has a window (the MFMA prefill kernel has none)
 };
 
 // `rows_per_tile` query rows (of one sequence) per prefill workgroup.

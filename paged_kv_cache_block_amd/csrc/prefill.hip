@@ -41,6 +41,13 @@
 //   head of every sequence, so a shared prefix is read from HBM once per
 //   head.
 //
+//   Windows (sinks + recent, at page granularity): a windowed workgroup walks
+//   the key tiles holding sink keys, then those from its first row's window
+//   start on, all on the masked path: key j is visible to a row at position
+//   p if j <= p and (j < sinks or j >= p + 1 - recent) and its page is still
+//   resident (released pages are -1 in the table, staged as zeros and
+//   masked).
+//
 //   int8 pages (the [KVquant] rows: codes plus one fp32 scale per token and
 //   KV head): the ring holds tiles as the pages store them (K codes, V codes
 //   in their operand order, the 64 scales), fetched with the same direct
@@ -153,6 +160,15 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   const int t_last = min(q_len - 1, t0 + (wave_c0 + CG * 16 - 1) / G);
   const int wave_keys = off + t_last;  // last key of any column of the wave
   const float slack = kSlackLog2 / a.scale_log2;  // in raw-score units
+  // The sequence's window (none: no sinks, a recent range beyond any length).
+  // A windowed workgroup walks the tiles holding sink keys, then the tiles
+  // from its first row's window start on; iteration i works on tile_of(i).
+  const int win_sinks = a.seq_win[4 * b], win_recent = a.seq_win[4 * b + 1];
+  const bool windowed = win_recent < kNoWindowRecent;
+  const int t_win = windowed ? max(0, off + t0 + 1 - win_recent) / kTile : 0;
+  const int n_sink = windowed ? min(t_win, (win_sinks + kTile - 1) / kTile) : 0;
+  const int n_iter = n_sink + n_tiles - t_win;
+  const int lo_wave = off + t_first + 1 - win_recent;  // window start of the wave's first row
 
   bf16x8 qv[CG][KS];
   int lim[CG], row[CG], head[CG];
@@ -181,7 +197,8 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 
   // Stage tile T into ring slot st: this wave's BPW blocks, one direct
   // global->LDS load each.  Tiles past the last (issued to keep every wave's
-  // vmcnt accounting uniform) and slots past the sequence end read zeros.
+  // vmcnt accounting uniform), slots past the sequence end and pages a
+  // window released read zeros.
   // Per-lane element offsets of this wave's blocks inside their page (and
   // which page of the tile each comes from): loop-invariant, so a tile
   // wholly inside the sequence is staged with one multiply-add per block.
@@ -207,15 +224,17 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       int ent[PAGES];
 #pragma unroll
       for (int p = 0; p < PAGES; ++p) ent[p] = scalar_load(table, T * PAGES + p);
+      if (ent[0] >= 0 && ent[PAGES - 1] >= 0) {  // no page released by a window
 #pragma unroll
-      for (int r = 0; r < BPW; ++r) {
-        const int blkid = wave * BPW + r;
-        const uint16_t* pool = blkid < KB ? kpool : vpool;
-        const int blk = blk_pgi[r] ? ent[PAGES - 1] : ent[0];
-        const uint16_t* src = pool + (static_cast<size_t>(blk) * Hkv + g) * page + blk_off[r];
-        __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
+        for (int r = 0; r < BPW; ++r) {
+          const int blkid = wave * BPW + r;
+          const uint16_t* pool = blkid < KB ? kpool : vpool;
+          const int blk = blk_pgi[r] ? ent[PAGES - 1] : ent[0];
+          const uint16_t* src = pool + (static_cast<size_t>(blk) * Hkv + g) * page + blk_off[r];
+          __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
+        }
+        return;
       }
-      return;
     }
     int ent[PAGES];
 #pragma unroll
@@ -231,18 +250,16 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
         const int tt = blkid / KS, j = blkid - tt * KS;
         const int tok = 8 * (n >> 2) + 4 * tt + (n & 3);
         const int pgi = tok / BS;
-        if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L) {
-          const int blk = pgi ? ent[PAGES - 1] : ent[0];
+        const int blk = pgi ? ent[PAGES - 1] : ent[0];
+        if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L && blk >= 0)
           src = kpool + (static_cast<size_t>(blk) * Hkv + g) * page + (tok % BS) * D + 32 * j + 8 * grp;
-        }
       } else {
         const int nt = blkid - KB;
         const int tok = 8 * grp;
         const int pgi = tok / BS;
-        if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L) {
-          const int blk = pgi ? ent[PAGES - 1] : ent[0];
+        const int blk = pgi ? ent[PAGES - 1] : ent[0];
+        if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L && blk >= 0)
           src = vpool + (static_cast<size_t>(blk) * Hkv + g) * page + (16 * nt + n) * BS + tok % BS;
-        }
       }
       __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
     }
@@ -331,9 +348,21 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   // past the sequence end, so a V chunk that straddles it may hold stale
   // bits in its later slots, which are zeroed before they meet P = 0.  Tiles
   // every column sees whole take the instantiation with neither.
-  auto compute_tile = [&](int T, int st, auto masked_c, auto tail_c) {
+  auto compute_tile = [&](int T, int st, int rs, auto masked_c, auto tail_c, auto win_c) {
     constexpr bool kMasked = decltype(masked_c)::value;
     constexpr bool kTail = decltype(tail_c)::value;
+    constexpr bool kWin = decltype(win_c)::value;
+    static_assert(kMasked || !kWin, "windowed tiles are masked");
+    // Under a window a page of the tile may have been released (-1 in the
+    // table, staged as zeros): its keys are gone.  Pages past the sequence
+    // end are not in the table; their keys lie past every limit anyway.
+    bool lane_hole = false;
+    if constexpr (kWin) {
+      const int pg = T * PAGES + (8 * grp) / BS;
+      const int e0 = T * PAGES < nblk ? scalar_load(table, T * PAGES) : 0;
+      const int e1 = (PAGES > 1 && T * PAGES + 1 < nblk) ? scalar_load(table, T * PAGES + 1) : 0;
+      lane_hole = pg < nblk && ((pg == T * PAGES) ? e0 : e1) < 0;
+    }
     const bf16x8* blocks = reinterpret_cast<const bf16x8*>(&ring[st][0][0]);
     f32x4 s[CG][2];
 #pragma unroll
@@ -353,7 +382,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     float sk[8], sv[8];
     if constexpr (Q8) {
       const float4* sc = reinterpret_cast<const float4*>(
-          reinterpret_cast<const uint8_t*>(&raw[T % S][0]) + 2 * kTile * D + 32 * grp);
+          reinterpret_cast<const uint8_t*>(&raw[rs][0]) + 2 * kTile * D + 32 * grp);
       const float4 k0 = sc[0], k1 = sc[1], v0 = sc[kTile / 4], v1 = sc[kTile / 4 + 1];
       sk[0] = k0.x, sk[1] = k0.y, sk[2] = k0.z, sk[3] = k0.w;
       sk[4] = k1.x, sk[5] = k1.y, sk[6] = k1.z, sk[7] = k1.w;
@@ -364,14 +393,24 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
     for (int k = 0; k < CG; ++k) {
       float mloc = -INFINITY;
-      const int room = kMasked ? lim[k] - (T * kTile + 8 * grp) : 0;  // last visible offset
+      // Key T*32 + 8*grp + x of this lane is visible to column n if x <= room
+      // and, under a window, it is a sink (x < sink_rel) or inside the
+      // column's recent range (x >= lo_rel), and its page is resident.
+      const int base = T * kTile + 8 * grp;
+      const int room = kMasked ? lim[k] - base : 0;
+      const int lo_rel = kWin ? lim[k] + 1 - win_recent - base : 0;
+      const int sink_rel = kWin ? win_sinks - base : 0;
+      auto visible = [&](int x) {
+        if constexpr (kWin) return x <= room && !lane_hole && (x < sink_rel || x >= lo_rel);
+        return x <= room;
+      };
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = s[k][tt][i];
           if constexpr (Q8) x *= sk[4 * tt + i];
-          if (kMasked && 4 * tt + i > room) x = -INFINITY;
+          if (kMasked && !visible(4 * tt + i)) x = -INFINITY;
           s[k][tt][i] = x;
           mloc = fmaxf(mloc, x);
         }
@@ -381,14 +420,16 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       // 2^kSlackLog2 and the accumulators are rescaled on few tiles: mostly
       // the first, where m_run is -inf and the factor is 0.  Every column
       // sees key 0 in tile 0, so m_run is finite from then on.
-      if (mloc - m_run[k] > slack) {
+      if (mloc > m_run[k] + slack) {
         const float alpha = exp2_flush((m_run[k] - mloc) * a.scale_log2);
         l_run[k] *= alpha;
 #pragma unroll
         for (int nt = 0; nt < DT; ++nt) acc[k][nt] *= alpha;
         m_run[k] = mloc;
       }
-      const float ms = m_run[k] * a.scale_log2;
+      // A column that has seen no visible key yet (m_run still -inf; only
+      // on masked tiles) has every weight 0.
+      const float ms = (kMasked && m_run[k] == -INFINITY) ? 0.f : m_run[k] * a.scale_log2;
       float psum = 0.f;
       uint32_t hi_w[4];
 #pragma unroll
@@ -404,7 +445,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
             // A slot past the sequence end may hold any scale bits: its
             // weight is exactly 0 and must stay so.
             e[h] = w8 * sv[idx];
-            if (kMasked && idx > room) e[h] = 0.f;
+            if (kMasked && !visible(idx)) e[h] = 0.f;
           }
           // hi = e with the low 16 bits cleared (a bf16 value); e - hi is exact.
           const float lo = e[h] - __uint_as_float(__float_as_uint(e[h]) & 0xffff0000u);
@@ -441,64 +482,86 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   // Tiles below t_split are seen whole by every row of the workgroup and take
   // the unmasked path; the few after it (the causal diagonal, the sequence
   // end) take the masked one, which also keeps slots past the sequence end
-  // out of P.V.  Every wave runs the same steps (the barrier counts all of
-  // them).
+  // out of P.V.  A windowed workgroup takes the masked path with the window
+  // rule on all its tiles.  Every wave runs the same steps (the barrier
+  // counts all of them).
   const int t_split = min(n_tiles, (off + t0 + 1) / kTile);
+  auto tile_of = [&](int i) { return i < n_sink ? i : t_win + i - n_sink; };
+  auto wave_sees = [&](int T) {
+    return T * kTile <= wave_keys && (T * kTile < win_sinks || T * kTile + kTile - 1 >= lo_wave);
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
   if constexpr (!Q8) {
-    // One pipeline step: tile T's blocks from this wave have landed once at
-    // most the blocks of the S-2 later tiles are outstanding; the barrier
-    // then publishes the whole tile and guarantees every wave has finished
-    // reading the slot that the next stage() overwrites (read in step T-1).
-    auto step = [&](int T) {
+    // One pipeline step: the blocks of iteration i's tile from this wave have
+    // landed once at most those of the S-2 later iterations are outstanding;
+    // the barrier then publishes the whole tile and guarantees every wave has
+    // finished reading the slot that the next stage() overwrites (read in
+    // iteration i-1).
+    auto step = [&](int i) {
       __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * BPW, 0));
       __builtin_amdgcn_s_barrier();
-      stage(T + S - 1, (T + S - 1) % S);
+      stage(tile_of(i + S - 1), (i + S - 1) % S);
     };
 #pragma unroll
-    for (int T = 0; T < S - 1; ++T) stage(T, T);
-    int T = 0;
-    if (wave_live) {
-      for (; T < t_split; ++T) {
-        step(T);
-        compute_tile(T, T % S, std::false_type{}, std::false_type{});
+    for (int i = 0; i < S - 1; ++i) stage(tile_of(i), i);
+    int i = 0;
+    if (!wave_live) {
+      for (; i < n_iter; ++i) step(i);
+    } else if (!windowed) {
+      for (; i < t_split; ++i) {
+        step(i);
+        compute_tile(i, i % S, 0, F{}, F{}, F{});
       }
-      for (; T < n_tiles; ++T) {
-        step(T);
-        if (T * kTile <= wave_keys) compute_tile(T, T % S, std::true_type{}, std::true_type{});
+      for (; i < n_tiles; ++i) {
+        step(i);
+        if (i * kTile <= wave_keys) compute_tile(i, i % S, 0, Tr{}, Tr{}, F{});
       }
     } else {
-      for (; T < n_tiles; ++T) step(T);
+      for (; i < n_iter; ++i) {
+        step(i);
+        const int T = tile_of(i);
+        if (wave_sees(T)) compute_tile(T, i % S, 0, Tr{}, Tr{}, Tr{});
+      }
     }
   } else {
-    // int8 step T: this wave's loads of raw tile T+1 have landed once at most
-    // those of tile T+2 are outstanding; the barrier publishes raw tile T+1
-    // and bf16 tile T (converted in step T-1) and guarantees every wave has
-    // left step T-1, the last reader of raw slot (T-1) % S (its scales) and of
-    // bf16 tile (T+1) % 2 (then tile T-1).  Step T stages raw tile T+S-1 into
-    // the former, converts raw tile T+1 into the latter and computes tile T.
-    auto step = [&](int T) {
+    // int8 step i: this wave's loads of the raw tile of iteration i+1 have
+    // landed once at most those of iteration i+2 are outstanding; the barrier
+    // publishes that raw tile and the bf16 tile of iteration i (converted in
+    // step i-1) and guarantees every wave has left step i-1, the last reader
+    // of raw slot (i-1) % S (its scales) and of bf16 tile (i+1) % 2 (then
+    // iteration i-1's).  Step i stages the raw tile of iteration i+S-1 into
+    // the former, converts iteration i+1's into the latter and computes
+    // iteration i's.
+    auto step = [&](int i) {
       q8_wait(std::integral_constant<int, S - 3>{});
       __builtin_amdgcn_s_barrier();
-      stage_q8(T + S - 1, (T + S - 1) % S);
-      convert_q8((T + 1) % S, (T + 1) & 1);
+      stage_q8(tile_of(i + S - 1), (i + S - 1) % S);
+      convert_q8((i + 1) % S, (i + 1) & 1);
     };
 #pragma unroll
-    for (int T = 0; T < S - 1; ++T) stage_q8(T, T);
-    q8_wait(std::integral_constant<int, S - 2>{});  // raw tile 0
+    for (int i = 0; i < S - 1; ++i) stage_q8(tile_of(i), i);
+    q8_wait(std::integral_constant<int, S - 2>{});  // the first raw tile
     __builtin_amdgcn_s_barrier();
     convert_q8(0, 0);
-    int T = 0;
-    if (wave_live) {
-      for (; T < t_split; ++T) {
-        step(T);
-        compute_tile(T, T & 1, std::false_type{}, std::false_type{});
+    int i = 0;
+    if (!wave_live) {
+      for (; i < n_iter; ++i) step(i);
+    } else if (!windowed) {
+      for (; i < t_split; ++i) {
+        step(i);
+        compute_tile(i, i & 1, i % S, F{}, F{}, F{});
       }
-      for (; T < n_tiles; ++T) {
-        step(T);
-        if (T * kTile <= wave_keys) compute_tile(T, T & 1, std::true_type{}, std::true_type{});
+      for (; i < n_tiles; ++i) {
+        step(i);
+        if (i * kTile <= wave_keys) compute_tile(i, i & 1, i % S, Tr{}, Tr{}, F{});
       }
     } else {
-      for (; T < n_tiles; ++T) step(T);
+      for (; i < n_iter; ++i) {
+        step(i);
+        const int T = tile_of(i);
+        if (wave_sees(T)) compute_tile(T, i & 1, i % S, Tr{}, Tr{}, Tr{});
+      }
     }
   }
   // Drain the zero-tile loads still in flight before the workgroup's LDS is
@@ -555,7 +618,7 @@ int32_t prefill_rows_per_tile(const PoolGeom& geom, int32_t group) {
 }
 
 hipError_t launch_prefill(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream) {
-  if (!prefill_uses_mfma(geom, a.group) || a.windowed) return launch_prefill_generic(geom, a, stream);
+  if (!prefill_uses_mfma(geom, a.group)) return launch_prefill_generic(geom, a, stream);
   if (geom.q8()) launch_mfma_shape<true>(geom.head_dim, geom.block_size, a, stream);
   else launch_mfma_shape<false>(geom.head_dim, geom.block_size, a, stream);
   return hipGetLastError();

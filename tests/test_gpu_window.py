@@ -161,3 +161,37 @@ def test_windowed_prefill_long_chunk_and_fp32_generic():
     got = to_host_f64(pool32.decode([0, 1], to_device(q32, "f32")))
     for s in range(2):
         assert_close(got[s], _want(ref32, s, q32[s:s + 1], "f32")[0], *F32_TOL, what=f"fp32 seq {s}")
+
+
+PREFILL_SPECS = [
+    # (length, window, wanted rows): the rows are capped at the positions
+    # still resident, so early rows of a long chunk may find pages of their
+    # own window already released (their keys are gone).
+    (1500, (4, 256), 400),
+    (3000, (0, 512), 200),
+    (700, (40, 100), 150),    # sinks over two key tiles
+    (2100, (5, 0), 50),       # sinks only
+    (90, (4, 500), 90),       # shorter than the budget; rows reach position 0
+    (1500, None, 256),        # no window, in the same call
+]
+
+
+@pytest.mark.parametrize("kv,hq,hkv,d,bs", [("bf16", 32, 8, 128, 16), ("i8", 32, 8, 128, 16),
+                                            ("bf16", 16, 16, 64, 32), ("i8", 16, 8, 64, 32)],
+                         ids=["bf16-G4-D128", "i8-G4-D128", "bf16-MHA-D64-bs32", "i8-G2-D64-bs32"])
+def test_windowed_prefill_mfma(kv, hq, hkv, d, bs):
+    """Chunked prefill over windowed sequences on the MFMA kernel: sink
+    tiles, then the tiles of the rows' windows; released pages are masked."""
+    log(f"windowed prefill {kv} G{hq // hkv} D{d} bs{bs}")
+    specs = [(n, w) for n, w, _ in PREFILL_SPECS]
+    pool, ref, rng = _build(specs, hq, hkv, d, bs, kv)
+    seqs = list(range(len(specs)))
+    q_lens = [min(want, ref.lengths[s] - ref.evicted_end(s)) for s, (_, _, want) in enumerate(PREFILL_SPECS)]
+    assert all(n >= 1 for n in q_lens) and q_lens[0] < PREFILL_SPECS[0][2]
+    q = _draw(rng, (sum(q_lens), hq, d), "bf16")
+    got = to_host_f64(pool.prefill(seqs, q_lens, to_device(q, "bf16")))
+    r0 = 0
+    for s, n in zip(seqs, q_lens):
+        assert_close(got[r0:r0 + n], _want(ref, s, q[r0:r0 + n], "bf16"), *BF16_TOL,
+                     what=f"seq {s} {PREFILL_SPECS[s]} rows {n}")
+        r0 += n
