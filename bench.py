@@ -113,7 +113,32 @@ def window_alg_bytes(lengths, wl, sinks, recent):
     return kv + qo + sum(-(-n // wl.block_size) for n in seen) * 4
 
 
-def run_decode(args, kv="bf16", window=None):
+def device_copy_gbs(mib=1024, reps=10):
+    """A plain device-to-device copy of ``mib`` MiB (context for the
+    kernel figures): bytes read + written / time, decimal GB/s."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return round(2 * (mib << 20) / (ms * 1e-3) / 1e9, 1)
+
+
+def percentiles_us(samples_ms):
+    """p10 / p50 / p90 of per-launch durations given in ms, in us."""
+    if not samples_ms:
+        return {}
+    p10, p50, p90 = np.percentile(np.asarray(samples_ms) * 1e3, [10, 50, 90])
+    return {"p10": round(float(p10), 2), "p50": round(float(p50), 2), "p90": round(float(p90), 2)}
+
+
+def run_decode(args, kv="bf16", window=None, cold_steps=0):
     import torch
     from paged_kv_cache_block_amd import abi
     from synth import decode_queries, gqa_decode
@@ -132,10 +157,9 @@ def run_decode(args, kv="bf16", window=None):
     total_steps = args.warmup + args.steps
     extra_steps = 10  # after the timed region: merge / prologue kernel timing
     gen = torch.Generator(device="cuda").manual_seed(1234)
-    new_k = torch.randn((total_steps + extra_steps, B, wl.num_kv_heads, wl.head_dim), generator=gen,
-                        device="cuda").to(torch.bfloat16)
-    new_v = torch.randn((total_steps + extra_steps, B, wl.num_kv_heads, wl.head_dim), generator=gen,
-                        device="cuda").to(torch.bfloat16)
+    n_new = total_steps + extra_steps + cold_steps
+    new_k = torch.randn((n_new, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    new_v = torch.randn((n_new, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     lengths = np.array([pool.seq_len(s) for s in seqs], dtype=np.int64)
     # Workspace for the longest batch this run reaches (lengths grow by 1 a step).
     ws_need = abi.pa_decode_step_workspace_bytes(pool.handle, seqs, wl.num_heads)
@@ -171,6 +195,7 @@ def run_decode(args, kv="bf16", window=None):
     t1 = time.perf_counter()
     abi.pa_timing_enable(False)
     dec_ms, dec_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
+    dec_pct = percentiles_us(abi.pa_timing_samples(abi.PA_KERNEL_DECODE))
     abi.pa_timing_select([abi.PA_KERNEL_MERGE, abi.PA_KERNEL_CACHE])
     abi.pa_timing_enable(True)
     for i in range(extra_steps):
@@ -182,6 +207,35 @@ def run_decode(args, kv="bf16", window=None):
     abi.pa_timing_select(None)
     mrg_ms, mrg_n = abi.pa_timing_read(abi.PA_KERNEL_MERGE)
     cache_ms, cache_n = abi.pa_timing_read(abi.PA_KERNEL_CACHE)
+    cold = None
+    if cold_steps:
+        # Cold caches: before each step a read of 1 GiB (outside the events)
+        # evicts the 256 MB last-level cache and the L2s.  A read, not a
+        # write: a write would leave dirty lines whose write-back then
+        # competes with the decode's reads.
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        sink = torch.empty(cold_steps, dtype=torch.float32, device="cuda")
+        abi.pa_timing_reset()
+        abi.pa_timing_select([abi.PA_KERNEL_DECODE])
+        abi.pa_timing_enable(True)
+        cold_alg = []
+        for i in range(cold_steps):
+            torch.sum(flush, dim=0, out=sink[i])
+            abi.pa_decode_step(handle, seqs, wl.num_heads, new_k[total_steps + extra_steps + i],
+                               new_v[total_steps + extra_steps + i], q, out, ws, ws.numel(), stream.cuda_stream)
+            lengths += 1
+            cold_alg.append(window_alg_bytes(lengths, wl, *window) if window else decode_alg_bytes(lengths, wl, kv))
+        torch.cuda.synchronize()
+        abi.pa_timing_enable(False)
+        abi.pa_timing_select(None)
+        samples = abi.pa_timing_samples(abi.PA_KERNEL_DECODE)
+        del flush, sink
+        c_ms = float(np.mean(samples))
+        c_gbs = float(np.mean(cold_alg)) / (c_ms * 1e-3) / 1e9
+        cold = {"what": "decode kernel after a 1 GiB device read that evicts the last-level cache and L2 "
+                        f"({len(samples)} steps)",
+                "decode_kernel_us": round(c_ms * 1e3, 2), **percentiles_us(samples),
+                "GBs": round(c_gbs, 1), "frac": round(c_gbs / HBM_PEAK_GBS, 4)}
     pool.validate()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     alg_per_step = float(np.mean(alg))
@@ -196,8 +250,11 @@ def run_decode(args, kv="bf16", window=None):
         "merge_kernel_us": merge_ms * 1e3,
         "cache_kernel_us": cache_ms / max(cache_n, 1) * 1e3,
         "kernel_launches": {"decode": dec_n, "merge": mrg_n, "cache": cache_n},
+        "decode_kernel_us_pct": dec_pct,
         "sum_len": int(lengths.sum()),
     }
+    if cold:
+        result["cold_cache"] = cold
     achieved = alg_per_step / (kernel_ms * 1e-3) / 1e9
     kernel = "decode_mfma_i8" if kv == "i8" else "decode_mfma_bf16"
     traffic = recorded_traffic(f"{kernel}__gqa_decode")
@@ -293,6 +350,7 @@ def run_prefill(args, kv=None):
     t1 = time.perf_counter()
     abi.pa_timing_enable(False)
     k_ms, k_n = abi.pa_timing_read(abi.PA_KERNEL_PREFILL)
+    k_pct = percentiles_us(abi.pa_timing_samples(abi.PA_KERNEL_PREFILL))
     flops = causal_flops(wl)
     kernel_ms = k_ms / max(k_n, 1)
     call_ms = (t1 - t0) * 1e3 / args.prefill_iters
@@ -304,6 +362,7 @@ def run_prefill(args, kv=None):
         "causal_flops": flops,
         "ms_per_call": call_ms,
         "kernel_ms": kernel_ms,
+        "kernel_us_pct": k_pct,
         "tflops": round(tflops, 2),
         "tokens_per_s": round(sum(q_lens) / (call_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
@@ -384,7 +443,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--prefill-iters", type=int, default=10)
+    ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--legs", default="int8,verify,window,prefix",
@@ -419,7 +478,7 @@ def main():
         log(f"calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
 
-    wl, dec = run_decode(args)
+    wl, dec = run_decode(args, cold_steps=10)
     line = {
         "metric": "paged-attn decode KV GB/s (% of HBM peak) + tokens/s; prefill TFLOP/s",
         "value": round(dec["value"], 2),
@@ -439,9 +498,11 @@ def main():
                    "global_batch": 32, "seq_len": "U[1,8192]", "parallelism": "single GPU"},
         "tokens_per_s": round(dec["tokens_per_s"], 1),
         "hbm_frac_step": round(dec["value"] / HBM_PEAK_GBS, 4),
-        "decode": {k: dec[k] for k in ("decode_kernel_us", "merge_kernel_us", "cache_kernel_us",
-                                        "alg_bytes_per_step", "kernel_launches", "sum_len")},
+        "decode": {k: dec[k] for k in ("decode_kernel_us", "decode_kernel_us_pct", "merge_kernel_us",
+                                        "cache_kernel_us", "alg_bytes_per_step", "kernel_launches", "sum_len",
+                                        "cold_cache") if k in dec},
         "roofline": dec["roofline"],
+        "device_copy_GBs": device_copy_gbs(),
     }
     legs = {x.strip() for x in args.legs.split(",") if x.strip()}
     if "int8" in legs:
@@ -452,8 +513,9 @@ def main():
             "ms_per_step": round(q8["ms_per_step"], 5),
             "tokens_per_s": round(q8["tokens_per_s"], 1),
             "kv_GBs_step": round(q8["value"], 2),
-            "decode": {k: q8[k] for k in ("decode_kernel_us", "merge_kernel_us", "cache_kernel_us",
-                                           "alg_bytes_per_step", "kernel_launches", "sum_len")},
+            "decode": {k: q8[k] for k in ("decode_kernel_us", "decode_kernel_us_pct", "merge_kernel_us",
+                                           "cache_kernel_us", "alg_bytes_per_step", "kernel_launches",
+                                           "sum_len")},
             "roofline": q8["roofline"],
         }
     if "verify" in legs:
@@ -478,6 +540,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         line["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
+        line["cpu_baseline"]["gpu_step_over_cpu"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
     print(json.dumps(line), flush=True)
 
 

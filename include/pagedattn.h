@@ -432,6 +432,12 @@ pa_status pa_timing_enable(int on);
 pa_status pa_timing_select(uint32_t kernel_mask);
 pa_status pa_timing_reset(void);
 pa_status pa_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
+/* Per-launch durations (ms, launch order) of one kernel family since the
+ * last reset: the first min(cap, *n) go to ms_out (host [cap], may be NULL
+ * when cap is 0); *n receives the count.  Synchronizes like pa_timing_read.
+ * Errors: PA_ERR_INVALID_ARG for a bad kernel id, a negative cap, a NULL n
+ * or a NULL ms_out with cap > 0. */
+pa_status pa_timing_samples(int32_t kernel, float* ms_out, int64_t cap, int64_t* n);
 
 #ifdef __cplusplus
 }

@@ -38,6 +38,7 @@ PA_KERNEL_MERGE = 1
 PA_KERNEL_PREFILL = 2
 PA_KERNEL_CACHE = 3
 PA_KERNEL_COPY = 4
+PA_KERNEL_COUNT = 5
 
 
 class PagedAttnError(Exception):
@@ -139,6 +140,7 @@ SIGNATURES = {
     "pa_timing_reset": (_i32, []),
     "pa_timing_select": (_i32, [ctypes.c_uint32]),
     "pa_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), _i64p]),
+    "pa_timing_samples": (_i32, [_i32, ctypes.POINTER(ctypes.c_float), _i64, _i64p]),
 }
 
 _lib = None
@@ -454,3 +456,12 @@ def pa_timing_read(kernel):
     n = _i64()
     _check(load().pa_timing_read(kernel, ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def pa_timing_samples(kernel):
+    """Per-launch durations (ms, launch order) of one kernel family since the last reset."""
+    n = _i64()
+    _check(load().pa_timing_samples(kernel, None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_float * max(n.value, 1))()
+    _check(load().pa_timing_samples(kernel, buf, n.value, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]

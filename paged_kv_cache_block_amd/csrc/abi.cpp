@@ -59,6 +59,7 @@ std::vector<TimingRecord> g_records;
 std::vector<hipEvent_t> g_spare_events;  // drained events, reused by later launches
 double g_total_ms[PA_KERNEL_COUNT] = {};
 int64_t g_launches[PA_KERNEL_COUNT] = {};
+std::vector<float> g_samples[PA_KERNEL_COUNT];  // per-launch ms since the last reset
 
 struct TimedLaunch {
   int kernel;
@@ -97,6 +98,7 @@ void drain_timing_locked() {
     if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
       g_total_ms[r.kernel] += ms;
       g_launches[r.kernel] += 1;
+      g_samples[r.kernel].push_back(ms);
     }
     g_spare_events.push_back(r.start);
     g_spare_events.push_back(r.stop);
@@ -811,6 +813,7 @@ pa_status pa_timing_reset(void) {
   for (int k = 0; k < PA_KERNEL_COUNT; ++k) {
     g_total_ms[k] = 0.0;
     g_launches[k] = 0;
+    g_samples[k].clear();
   }
   return ok();
 }
@@ -822,6 +825,18 @@ pa_status pa_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
   drain_timing_locked();
   *total_ms = g_total_ms[kernel];
   *launches = g_launches[kernel];
+  return ok();
+}
+
+pa_status pa_timing_samples(int32_t kernel, float* ms_out, int64_t cap, int64_t* n) {
+  if (kernel < 0 || kernel >= PA_KERNEL_COUNT || !n || cap < 0 || (cap > 0 && !ms_out))
+    return fail(PA_ERR_INVALID_ARG, "bad kernel id, cap or NULL argument");
+  std::lock_guard<std::mutex> lock(g_tmu);
+  drain_timing_locked();
+  const std::vector<float>& s = g_samples[kernel];
+  *n = static_cast<int64_t>(s.size());
+  const size_t m = std::min<size_t>(s.size(), static_cast<size_t>(cap));
+  std::copy(s.begin(), s.begin() + m, ms_out);
   return ok();
 }
 

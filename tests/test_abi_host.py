@@ -297,3 +297,17 @@ def test_append_batch_is_sequential_appends_or_nothing(seed):
             return
         _compare(pool, ref)
         pool.validate()
+
+
+def test_timing_samples_without_launches():
+    """No launch was timed since the reset: no samples and a zero total;
+    bad kernel ids and counts are rejected (host only, no GPU call)."""
+    abi.pa_timing_reset()
+    assert abi.pa_timing_samples(abi.PA_KERNEL_DECODE) == []
+    assert abi.pa_timing_read(abi.PA_KERNEL_DECODE) == (0.0, 0)
+    lib = abi.load()
+    n = abi._i64()
+    assert lib.pa_timing_samples(abi.PA_KERNEL_COUNT, None, 0, abi.ctypes.byref(n)) != 0
+    assert lib.pa_timing_samples(0, None, -1, abi.ctypes.byref(n)) != 0
+    assert lib.pa_timing_samples(0, None, 4, abi.ctypes.byref(n)) != 0
+    assert lib.pa_timing_samples(0, None, 0, None) != 0
