@@ -124,6 +124,23 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   // plus one 256-byte load of scales.
   constexpr int kRawBytes = 2 * kTile * D + 2 * kTile * 4;
   constexpr int kCodeLoads = 2 * kTile * D / 1024;
+  constexpr int kRowChunks = D / 16;      // 16-byte chunks per K row
+  constexpr int kRowChunksV = D / 64;     // 16-byte chunks per V operand-order row (D / 4 bytes)
+  // Chunk permutations of the raw int8 tile in LDS (each an involution on
+  // its range).  K: chunk c of token t's row sits at c ^ q8_k_swizzle(t), so
+  // the 32 lanes of an 8-byte conversion read (16 tokens x 2 halves of a
+  // chunk) cover all 64 banks.  V (d 128, two chunks per row): chunk q of a
+  // subtile sits at q with bit 0 flipped by bit 4, so the 16 lanes of a
+  // 16-byte read (rows n = 0..15) hit distinct bank groups; d 64 rows are
+  // one chunk and already do.
+  auto q8_k_swizzle = [](int t) {
+    if constexpr (D == 128) return ((t >> 1) & 1) | ((t >> 2) & 6);
+    else return (t >> 3) & 3;
+  };
+  auto q8_v_swizzle = [](int q) {
+    if constexpr (D == 128) return q ^ ((q >> 4) & 1);
+    else return q;
+  };
   static_assert(!Q8 || (S >= 4 && kCodeLoads <= NW && kCodeLoads % 2 == 0), "int8 ring");
   // bf16: an S-stage ring of operand-ordered tiles.  int8: an S-stage ring of
   // raw tiles and two operand-ordered bf16 tiles converted from them.
@@ -266,10 +283,12 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   };
 
   // int8: stage raw tile T into raw slot st.  Wave w < kCodeLoads moves 1 KB
-  // of codes (the first half of the loads K codes, the second V codes; page by
-  // page as the pool holds them, so token t's K codes sit at t * D and the V
-  // codes keep their operand order); wave 0's lanes 0-15 also move the 32 K
-  // and 32 V row scales.  Pages past the sequence's last read zeros; slots
+  // of codes (the first half of the loads K codes, the second V codes) in
+  // 16-byte chunks: token t's K codes fill row t (D bytes) with the chunks
+  // permuted by q8_k_swizzle(t); each 16-token subtile of V codes keeps the
+  // pages' operand order with its chunks permuted by q8_v_swizzle, so the
+  // conversion reads below hit distinct LDS banks.  Wave 0's lanes 0-15 also
+  // move the 32 K and 32 V row scales.  Pages past the sequence's last read zeros; slots
   // past its end inside the last page are staged as they are (finite codes;
   // their scales are never used, see the masked softmax).
   auto stage_q8 = [&](int T, int st) {
@@ -284,12 +303,20 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       constexpr int kHalf = kCodeLoads / 2;  // loads per code region
       const bool isv = wave >= kHalf;
       const int o0 = (isv ? wave - kHalf : wave) * 1024;  // wave's first byte in the region
-      const int o = o0 + 16 * lane;
-      const int pgi = o / (BS * D);
+      const int P = o0 / 16 + lane;                        // 16-byte chunk this lane fills
+      int tok0, within;  // first token of the chunk's page row / subtile, byte in it
+      if (!isv) {
+        tok0 = P / kRowChunks;
+        within = 16 * ((P % kRowChunks) ^ q8_k_swizzle(tok0));
+      } else {
+        tok0 = 16 * (P / D);
+        within = 16 * q8_v_swizzle(P % D);
+      }
+      const int pgi = tok0 / BS;
       const int blk = pgi ? ent[PAGES - 1] : ent[0];
       const void* src = a.zeros;
       if (blk >= 0)
-        src = (isv ? vq : kq) + (static_cast<size_t>(blk) * Hkv + g) * q8_page + (o - pgi * BS * D);
+        src = (isv ? vq : kq) + (static_cast<size_t>(blk) * Hkv + g) * q8_page + (tok0 % BS) * D + within;
       __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(dst + (isv ? kTile * D : 0) + o0), 16, 0, 0);
     }
     if (wave == 0 && lane < 16) {
@@ -315,31 +342,49 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   };
-  // int8: convert this wave's BPW operand blocks of raw slot rs into bf16
-  // operand tile os (the same operand order as the bf16 ring; codes are
-  // exact in bf16, the scales stay apart in fp32).
-  int cv_lo[BPW], cv_hi[BPW];
+  // int8: convert raw slot rs into bf16 operand tile os (the operand order
+  // of the bf16 ring; codes are exact in bf16, the scales stay apart in
+  // fp32).  Waves 0-3 convert the K blocks (8 codes per lane, one 8-byte
+  // read), waves 4-7 the V blocks: a lane reads the 16-byte chunks of its
+  // two V rows (tokens 8grp .. +3 and +4 .. +7 of d = 16nt + n) once for all
+  // the blocks it converts.
+  static_assert(!Q8 || (NW == 8 && KB % 4 == 0 && DT % 4 == 0), "int8 conversion split");
+  constexpr int kKPW = KB / 4, kVPW = DT / 4;  // blocks per K / V converting wave
+  int cv_off[kKPW > 0 ? kKPW : 1];
+  int cv_vlo = 0, cv_vhi = 0;
+  if (wave < 4) {
 #pragma unroll
-  for (int r = 0; r < BPW; ++r) {
-    const int blkid = wave * BPW + r;
-    if (blkid < KB) {
+    for (int r = 0; r < kKPW; ++r) {
+      const int blkid = wave * kKPW + r;
       const int tt = blkid / KS, j = blkid - tt * KS;
       const int tok = 8 * (n >> 2) + 4 * tt + (n & 3);
-      cv_lo[r] = tok * D + 32 * j + 8 * grp;
-      cv_hi[r] = cv_lo[r] + 4;
-    } else {
-      const int d = 16 * (blkid - KB) + n;
-      cv_lo[r] = kTile * D + q8_v_offset(8 * grp, d, D);
-      cv_hi[r] = kTile * D + q8_v_offset(8 * grp + 4, d, D);
+      const int c = 2 * j + (grp >> 1);  // 16-byte chunk of the row holding d = 32j + 8grp
+      cv_off[r] = 16 * (tok * kRowChunks + (c ^ q8_k_swizzle(tok))) + 8 * (grp & 1);
     }
+  } else {
+    const int h = 4 * (wave - 4) * kVPW / 16;  // chunk of the row (4 bytes per d tile)
+    const int row = 32 * (grp & 1) + n;        // operand-order row of tokens 8grp .. +3, d % 16 = n
+    const int q_lo = kRowChunksV * row + h, q_hi = q_lo + 16 * kRowChunksV;
+    cv_vlo = kTile * D + (grp >> 1) * 16 * D + 16 * q8_v_swizzle(q_lo);
+    cv_vhi = kTile * D + (grp >> 1) * 16 * D + 16 * q8_v_swizzle(q_hi);
   }
   auto convert_q8 = [&](int rs, int os) {
     const uint8_t* src = reinterpret_cast<const uint8_t*>(&raw[rs][0]);
+    if (wave < 4) {
 #pragma unroll
-    for (int r = 0; r < BPW; ++r) {
-      const uint32_t lo = *reinterpret_cast<const uint32_t*>(src + cv_lo[r]);
-      const uint32_t hi = *reinterpret_cast<const uint32_t*>(src + cv_hi[r]);
-      ring[os][wave * BPW + r][lane] = __builtin_bit_cast(uint4, i8x8_to_bf16x8(lo, hi));
+      for (int r = 0; r < kKPW; ++r) {
+        const uint2 c = *reinterpret_cast<const uint2*>(src + cv_off[r]);
+        ring[os][wave * kKPW + r][lane] = __builtin_bit_cast(uint4, i8x8_to_bf16x8(c.x, c.y));
+      }
+    } else {
+      const uint4 lo = *reinterpret_cast<const uint4*>(src + cv_vlo);
+      const uint4 hi = *reinterpret_cast<const uint4*>(src + cv_vhi);
+      const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w}, hw[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int r = 0; r < kVPW; ++r) {
+        const int nt = (wave - 4) * kVPW + r;
+        ring[os][KB + nt][lane] = __builtin_bit_cast(uint4, i8x8_to_bf16x8(lw[nt & 3], hw[nt & 3]));
+      }
     }
   };
 
