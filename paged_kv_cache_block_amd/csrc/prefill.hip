@@ -50,10 +50,11 @@
 //
 //   int8 pages (the [KVquant] rows: codes plus one fp32 scale per token and
 //   KV head): the ring holds tiles as the pages store them (K codes, V codes
-//   in their operand order, the 64 scales), fetched with the same direct
-//   loads; each step every wave converts its share of the next tile's
-//   operand blocks to bf16 (exact: |code| <= 127) into one of two
-//   operand-ordered tiles, so the MFMA part is the bf16 one.  The scales stay
+//   in their operand order, the 64 scales; 16-byte chunks permuted so every
+//   LDS access is conflict-free), fetched with the same direct loads; each
+//   step four waves convert the next tile's K operand blocks and four its V
+//   blocks to bf16 (exact: |code| <= 127) into one of two operand-ordered
+//   tiles, so the MFMA part is the bf16 one.  The scales stay
 //   in fp32: K's multiply the scores, V's the weights entering P.V (l sums
 //   the weights without them).
 #include <cmath>
@@ -73,9 +74,6 @@
 #endif
 #ifndef PA_PREFILL_STAGES_Q8
 #define PA_PREFILL_STAGES_Q8 4
-#endif
-#ifndef PA_PREFILL_SPLIT_P
-#define PA_PREFILL_SPLIT_P 1
 #endif
 #ifndef PA_PREFILL_WAVES_PER_EU
 #define PA_PREFILL_WAVES_PER_EU 0  // occupancy hint (0 = none)
@@ -99,7 +97,6 @@ constexpr int kPrefillCG = PA_PREFILL_CG;          // 16-column groups per wave
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;    // waves per workgroup
 constexpr int kPrefillStages = PA_PREFILL_STAGES;  // key tiles in the LDS ring
 constexpr int kPrefillStagesQ8 = PA_PREFILL_STAGES_Q8;  // raw int8 tiles in the LDS ring
-constexpr bool kSplitP = PA_PREFILL_SPLIT_P;       // P as bf16 hi + lo in P.V
 constexpr int kTile = 32;                          // key tokens per step
 constexpr float kSlackLog2 = 8.f;                  // largest softmax weight, log2
 
@@ -492,14 +489,11 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
             e[h] = w8 * sv[idx];
             if (kMasked && !visible(idx)) e[h] = 0.f;
           }
-          // hi = e with the low 16 bits cleared (a bf16 value); e - hi is exact.
+          // hi = e with the low 16 bits cleared (a bf16 value); e - hi is exact
+          // and enters P.V as a second bf16 term.
           const float lo = e[h] - __uint_as_float(__float_as_uint(e[h]) & 0xffff0000u);
-          if constexpr (kSplitP || Q8) {
-            p_lo[k][idx] = static_cast<__bf16>(lo);
-            psum += w8;
-          } else {
-            psum += w8 - lo;  // l from the same weights as P.V
-          }
+          p_lo[k][idx] = static_cast<__bf16>(lo);
+          psum += w8;
         }
         hi_w[w] = __builtin_amdgcn_perm(__float_as_uint(e[1]), __float_as_uint(e[0]), 0x07060302u);
       }
@@ -518,8 +512,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
       for (int k = 0; k < CG; ++k) {
         acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, p_hi[k], acc[k][nt], 0, 0, 0);
-        if constexpr (kSplitP || Q8)
-          acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, p_lo[k], acc[k][nt], 0, 0, 0);
+        acc[k][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, p_lo[k], acc[k][nt], 0, 0, 0);
       }
     }
   };
