@@ -61,19 +61,23 @@ double g_total_ms[PA_KERNEL_COUNT] = {};
 int64_t g_launches[PA_KERNEL_COUNT] = {};
 std::vector<float> g_samples[PA_KERNEL_COUNT];  // per-launch ms since the last reset
 
+// While timing is on, a launch of a selected kernel family takes two events
+// that its dispatch itself fills with the kernel's start and end
+// (hipExtLaunchKernel): nothing is recorded on the stream between kernels,
+// so timing does not change the spacing of a step's kernels.
 struct TimedLaunch {
   int kernel;
-  hipStream_t stream;
-  hipEvent_t start = nullptr, stop = nullptr;
-  TimedLaunch(int k, hipStream_t s) : kernel(k), stream(s) {
+  pa::KernelEvents ev;
+  explicit TimedLaunch(int k) : kernel(k) {
     std::lock_guard<std::mutex> lock(g_tmu);
     if (!g_timing || !(g_timing_mask & (1u << k))) return;
-    if (!take(&start) || !take(&stop) || hipEventRecord(start, stream) != hipSuccess) {
-      if (start) g_spare_events.push_back(start);
-      if (stop) g_spare_events.push_back(stop);
-      start = stop = nullptr;
+    if (!take(&ev.start) || !take(&ev.stop)) {
+      if (ev.start) g_spare_events.push_back(ev.start);
+      if (ev.stop) g_spare_events.push_back(ev.stop);
+      ev = pa::KernelEvents{};
     }
   }
+  const pa::KernelEvents& events() const { return ev; }
   static bool take(hipEvent_t* e) {
     if (!g_spare_events.empty()) {
       *e = g_spare_events.back();
@@ -84,11 +88,18 @@ struct TimedLaunch {
     *e = nullptr;
     return false;
   }
-  void done() {
-    if (!start) return;
-    (void)hipEventRecord(stop, stream);
+  // After the launch: keep the events for the next read (launched == false:
+  // the dispatch failed and the events go back unused).
+  void done(bool launched = true) {
+    if (!ev.start) return;
     std::lock_guard<std::mutex> lock(g_tmu);
-    g_records.push_back({kernel, start, stop});
+    if (launched) {
+      g_records.push_back({kernel, ev.start, ev.stop});
+    } else {
+      g_spare_events.push_back(ev.start);
+      g_spare_events.push_back(ev.stop);
+    }
+    ev = pa::KernelEvents{};
   }
 };
 
@@ -153,26 +164,51 @@ struct pa_pool {
     return ok();
   }
 
-  // Mark the buffer of the last stage() as in use by the work just enqueued.
+  // Mark the buffer of the last stage() as in use by the work enqueued on
+  // `stream` so far.  If the event cannot be recorded, wait for the stream
+  // instead, so the buffer is free when the ring comes back to it.
   pa_status staged_done(hipStream_t stream) {
     Staging& st = ring[next];
     next = (next + 1) % kRing;
-    PA_HIP(hipEventRecord(st.ev, stream));
+    const hipError_t e = hipEventRecord(st.ev, stream);
+    if (e != hipSuccess) {
+      (void)hipStreamSynchronize(stream);
+      st.pending = false;
+      return hip_fail(e, "hipEventRecord");
+    }
     st.pending = true;
     return ok();
   }
+
+  // Holds the buffer of the last stage() for everything a call enqueues
+  // after it: the event is recorded when the guard ends, behind the call's
+  // last kernel.  (An event recorded between two kernels makes the second
+  // wait there for the first to complete and its results to be published,
+  // ~8-10 us on the decode step.)
+  struct StagedUse {
+    pa_pool* pool = nullptr;
+    hipStream_t stream = nullptr;
+    StagedUse() = default;
+    StagedUse(const StagedUse&) = delete;
+    StagedUse& operator=(const StagedUse&) = delete;
+    ~StagedUse() {
+      if (pool) (void)pool->staged_done(stream);
+    }
+  };
 
   // Copy `bytes` of host data to device `dst` (which has room for `bytes`
   // rounded up to 16) on `stream`: a small kernel on the stream reads the
   // pinned buffer, so the data is in place when the stream's next kernel
   // starts, without a hand-off to a DMA engine.
-  pa_status upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  pa_status upload(const void* src, size_t bytes, void* dst, hipStream_t stream, StagedUse* use) {
     const void* staged = nullptr;
     pa_status r = stage(src, bytes, &staged);
     if (r != PA_OK) return r;
     hipError_t e = pa::launch_upload(staged, dst, pa::align_up(bytes, 16), stream);
     if (e != hipSuccess) return hip_fail(e, "upload launch");
-    return staged_done(stream);
+    use->pool = this;
+    use->stream = stream;
+    return ok();
   }
 
   pa_status flush(hipStream_t stream) {
@@ -193,10 +229,10 @@ struct pa_pool {
         dst.push_back(d);
         ++i;
       }
-      TimedLaunch t(PA_KERNEL_COPY, stream);
+      TimedLaunch t(PA_KERNEL_COPY);
       hipError_t e = pa::launch_copy_blocks(geom, k, v, src.data(), dst.data(),
-                                            static_cast<int>(src.size()), stream);
-      t.done();
+                                            static_cast<int>(src.size()), stream, t.events());
+      t.done(e == hipSuccess);
       if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
     }
     return ok();
@@ -403,9 +439,11 @@ pa_status pa_reshape_and_cache(pa_pool* pool, const void* k_new, const void* v_n
   hipStream_t s = as_stream(stream);
   pa_status st = pool->flush(s);
   if (st != PA_OK) return st;
-  TimedLaunch t(PA_KERNEL_CACHE, s);
-  hipError_t e = pa::launch_reshape_and_cache(pool->geom, pool->k, pool->v, k_new, v_new, slots, n, s);
-  t.done();
+  if (n == 0) return ok();  // nothing to launch (and nothing to time)
+  TimedLaunch t(PA_KERNEL_CACHE);
+  hipError_t e = pa::launch_reshape_and_cache(pool->geom, pool->k, pool->v, k_new, v_new, slots, n, s,
+                                              t.events());
+  t.done(e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "reshape_and_cache launch");
   return ok();
 }
@@ -472,15 +510,15 @@ pa_status launch_decode_plan(pa_pool* pool, const pa::DecodePlan& plan, int32_t 
   a.max_cols = plan.max_q_len * a.group;
   a.scale_log2 = scale_log2_for(pool->geom.head_dim);
   {
-    TimedLaunch t(PA_KERNEL_DECODE, st);
-    hipError_t e = pa::launch_decode_partial(pool->geom, a, st);
-    t.done();
+    TimedLaunch t(PA_KERNEL_DECODE);
+    hipError_t e = pa::launch_decode_partial(pool->geom, a, st, t.events());
+    t.done(e == hipSuccess);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   if (a.n_merge > 0 && pa::decode_needs_merge_kernel(pool->geom, a.group)) {
-    TimedLaunch t(PA_KERNEL_MERGE, st);
-    hipError_t e = pa::launch_decode_merge(pool->geom, a, st);
-    t.done();
+    TimedLaunch t(PA_KERNEL_MERGE);
+    hipError_t e = pa::launch_decode_merge(pool->geom, a, st, t.events());
+    t.done(e == hipSuccess);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return ok();
@@ -556,16 +594,17 @@ pa_status step_impl(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
   r = pool->stage(plan.meta.data(), bytes, &staged);
   if (r != PA_OK) return r;
   {
-    TimedLaunch t(PA_KERNEL_CACHE, st);
+    TimedLaunch t(PA_KERNEL_CACHE);
     hipError_t e = pa::launch_step_prep(
         pool->geom, staged, ws, pa::align_up(bytes, 16),
         reinterpret_cast<const int64_t*>(static_cast<const char*>(staged) + plan.slots_off), pool->k,
-        pool->v, k_new, v_new, static_cast<int32_t>(rows), st);
-    t.done();
+        pool->v, k_new, v_new, static_cast<int32_t>(rows), st, t.events());
+    t.done(e == hipSuccess);
     if (e != hipSuccess) return hip_fail(e, "decode step prologue launch");
   }
-  r = pool->staged_done(st);
-  if (r != PA_OK) return r;
+  pa_pool::StagedUse use;
+  use.pool = pool;
+  use.stream = st;
   return launch_decode_plan(pool, plan, B, num_heads, q, out, ws, st);
 }
 
@@ -598,7 +637,8 @@ pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_h
   hipStream_t st = as_stream(stream);
   r = pool->flush(st);
   if (r != PA_OK) return r;
-  r = pool->upload(plan.meta.data(), plan.meta.size() * sizeof(int32_t), ws, st);
+  pa_pool::StagedUse use;
+  r = pool->upload(plan.meta.data(), plan.meta.size() * sizeof(int32_t), ws, st, &use);
   if (r != PA_OK) return r;
   return launch_decode_plan(pool, plan, B, num_heads, q, out, ws, st);
 }
@@ -699,7 +739,8 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
     hipStream_t st = as_stream(stream);
     pa_status r = pool->flush(st);
     if (r != PA_OK) return r;
-    r = pool->upload(dplan.meta.data(), dplan.meta.size() * sizeof(int32_t), ws, st);
+    pa_pool::StagedUse use;
+    r = pool->upload(dplan.meta.data(), dplan.meta.size() * sizeof(int32_t), ws, st, &use);
     if (r != PA_OK) return r;
     return launch_decode_plan(pool, dplan, B, num_heads, q, out, ws, st);
   }
@@ -713,7 +754,8 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
   hipStream_t st = as_stream(stream);
   pa_status r = pool->flush(st);
   if (r != PA_OK) return r;
-  r = pool->upload(plan.meta.data(), plan.meta.size() * sizeof(int32_t), ws, st);
+  pa_pool::StagedUse use;
+  r = pool->upload(plan.meta.data(), plan.meta.size() * sizeof(int32_t), ws, st, &use);
   if (r != PA_OK) return r;
   char* w = static_cast<char*>(ws);
   pa::PrefillArgs a{};
@@ -735,9 +777,9 @@ pa_status pa_prefill_chunk(pa_pool* pool, const int64_t* seqs, const int32_t* q_
   a.n_tiles = plan.n_tiles;
   a.n_rows = plan.n_rows;
   a.scale_log2 = scale_log2_for(pool->geom.head_dim);
-  TimedLaunch t(PA_KERNEL_PREFILL, st);
-  hipError_t e = pa::launch_prefill(pool->geom, a, st);
-  t.done();
+  TimedLaunch t(PA_KERNEL_PREFILL);
+  hipError_t e = pa::launch_prefill(pool->geom, a, st, t.events());
+  t.done(e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();
 }

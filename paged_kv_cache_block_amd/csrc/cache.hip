@@ -8,6 +8,7 @@
 // layout allows, no LDS.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 
 namespace pa {
 
@@ -203,7 +204,8 @@ int grid_for(int64_t work, int64_t per_block, int64_t cap) {
 }  // namespace
 
 hipError_t launch_copy_blocks(const PoolGeom& geom, void* k_pool, void* v_pool,
-                              const int32_t* src, const int32_t* dst, int n, hipStream_t stream) {
+                              const int32_t* src, const int32_t* dst, int n, hipStream_t stream,
+                              const KernelEvents& ev) {
   if (n <= 0) return hipSuccess;
   CopyList list{};
   for (int i = 0; i < n; ++i) {
@@ -214,12 +216,12 @@ hipError_t launch_copy_blocks(const PoolGeom& geom, void* k_pool, void* v_pool,
   if (bytes % 16 == 0) {
     const int64_t words = static_cast<int64_t>(bytes / 16);
     dim3 grid(grid_for(words, 256, 1024), n, 2);
-    hipLaunchKernelGGL(copy_blocks_16, grid, dim3(256), 0, stream, static_cast<uint4*>(k_pool),
+    PA_LAUNCH(ev, copy_blocks_16, grid, dim3(256), 0, stream, static_cast<uint4*>(k_pool),
                        static_cast<uint4*>(v_pool), list, words);
   } else {
     const int64_t words = static_cast<int64_t>(bytes / 2);
     dim3 grid(grid_for(words, 256, 1024), n, 2);
-    hipLaunchKernelGGL(copy_blocks_2, grid, dim3(256), 0, stream, static_cast<uint16_t*>(k_pool),
+    PA_LAUNCH(ev, copy_blocks_2, grid, dim3(256), 0, stream, static_cast<uint16_t*>(k_pool),
                        static_cast<uint16_t*>(v_pool), list, words);
   }
   return hipGetLastError();
@@ -235,7 +237,8 @@ hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStrea
 
 hipError_t launch_step_prep(const PoolGeom& geom, const void* plan_src, void* plan_dst, size_t bytes,
                             const int64_t* slots, void* k_pool, void* v_pool, const void* k_new,
-                            const void* v_new, int32_t n, hipStream_t stream) {
+                            const void* v_new, int32_t n, hipStream_t stream,
+                            const KernelEvents& ev) {
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
   const int nu = grid_for(n16, 256, 32);
   const int64_t total = static_cast<int64_t>(n) * geom.num_kv_heads * geom.head_dim;
@@ -243,7 +246,7 @@ hipError_t launch_step_prep(const PoolGeom& geom, const void* plan_src, void* pl
   const int64_t num_slots = static_cast<int64_t>(geom.num_blocks) * geom.block_size;
   if (geom.q8()) {
     const int nq = grid_for(static_cast<int64_t>(n) * geom.num_kv_heads, 4, 4096);
-    hipLaunchKernelGGL(step_prep_q8, dim3(nu + nq), dim3(256), 0, stream,
+    PA_LAUNCH(ev, step_prep_q8, dim3(nu + nq), dim3(256), 0, stream,
                        static_cast<const uint4*>(plan_src), static_cast<uint4*>(plan_dst), n16, nu, slots,
                        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
@@ -252,13 +255,13 @@ hipError_t launch_step_prep(const PoolGeom& geom, const void* plan_src, void* pl
   }
   const dim3 grid(nu + nc);
   if (geom.dtype == 1)
-    hipLaunchKernelGGL(step_prep_kernel<uint16_t>, grid, dim3(256), 0, stream,
+    PA_LAUNCH(ev, step_prep_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        static_cast<const uint4*>(plan_src), static_cast<uint4*>(plan_dst), n16, nu, slots,
                        static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                        static_cast<int64_t>(n), geom.num_kv_heads, geom.block_size, geom.head_dim, num_slots);
   else
-    hipLaunchKernelGGL(step_prep_kernel<float>, grid, dim3(256), 0, stream,
+    PA_LAUNCH(ev, step_prep_kernel<float>, grid, dim3(256), 0, stream,
                        static_cast<const uint4*>(plan_src), static_cast<uint4*>(plan_dst), n16, nu, slots,
                        static_cast<float*>(k_pool), static_cast<float*>(v_pool),
                        static_cast<const float*>(k_new), static_cast<const float*>(v_new),
@@ -268,25 +271,25 @@ hipError_t launch_step_prep(const PoolGeom& geom, const void* plan_src, void* pl
 
 hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_pool,
                                     const void* k_new, const void* v_new, const int64_t* slots,
-                                    int32_t n, hipStream_t stream) {
+                                    int32_t n, hipStream_t stream, const KernelEvents& ev) {
   if (n <= 0) return hipSuccess;
   const int64_t total = static_cast<int64_t>(n) * geom.num_kv_heads * geom.head_dim;
   const int64_t num_slots = static_cast<int64_t>(geom.num_blocks) * geom.block_size;
   const int grid = grid_for(total, 256, 65536);
   if (geom.q8()) {
     const int gq = grid_for(static_cast<int64_t>(n) * geom.num_kv_heads, 4, 65536);
-    hipLaunchKernelGGL(reshape_and_cache_q8, dim3(gq), dim3(256), 0, stream, static_cast<uint8_t*>(k_pool),
+    PA_LAUNCH(ev, reshape_and_cache_q8, dim3(gq), dim3(256), 0, stream, static_cast<uint8_t*>(k_pool),
                        static_cast<uint8_t*>(v_pool), static_cast<const uint16_t*>(k_new),
                        static_cast<const uint16_t*>(v_new), slots, static_cast<int64_t>(n), geom.num_kv_heads,
                        geom.block_size, geom.head_dim, num_slots);
   } else if (geom.dtype == 1) {
-    hipLaunchKernelGGL(reshape_and_cache_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+    PA_LAUNCH(ev, reshape_and_cache_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
                        static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                        slots, static_cast<int64_t>(n), geom.num_kv_heads, geom.block_size,
                        geom.head_dim, num_slots);
   } else {
-    hipLaunchKernelGGL(reshape_and_cache_kernel<float>, dim3(grid), dim3(256), 0, stream,
+    PA_LAUNCH(ev, reshape_and_cache_kernel<float>, dim3(grid), dim3(256), 0, stream,
                        static_cast<float*>(k_pool), static_cast<float*>(v_pool),
                        static_cast<const float*>(k_new), static_cast<const float*>(v_new), slots,
                        static_cast<int64_t>(n), geom.num_kv_heads, geom.block_size, geom.head_dim,

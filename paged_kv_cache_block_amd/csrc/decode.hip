@@ -33,6 +33,7 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 
 // Tile parameters (compile-time; variant builds override them with -D).
 #ifndef PA_DECODE_WAVES_I8
@@ -612,29 +613,30 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
 }
 
 template <int D, int BS, int CT, bool Q8>
-void launch_mfma(const DecodeArgs& a, int groups, hipStream_t stream) {
+void launch_mfma(const DecodeArgs& a, int groups, hipStream_t stream, const KernelEvents& ev) {
   const size_t shmem = static_cast<size_t>(kDecodeWaves) * min(a.max_cols, 16) * (D + 4) * sizeof(float);
-  hipLaunchKernelGGL((decode_mfma<D, BS, CT, Q8>), dim3(groups), dim3(256), shmem, stream, a);
+  PA_LAUNCH(ev, (decode_mfma<D, BS, CT, Q8>), dim3(groups), dim3(256), shmem, stream, a);
 }
 
 template <int CT, bool Q8>
-void launch_mfma_shape(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream) {
+void launch_mfma_shape(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream, const KernelEvents& ev) {
   const int groups = a.n_work * a.num_kv_heads;
   const int D = geom.head_dim, BS = geom.block_size;
-  if (D == 128 && BS == 16) launch_mfma<128, 16, CT, Q8>(a, groups, stream);
-  else if (D == 128 && BS == 32) launch_mfma<128, 32, CT, Q8>(a, groups, stream);
-  else if (D == 64 && BS == 16) launch_mfma<64, 16, CT, Q8>(a, groups, stream);
-  else launch_mfma<64, 32, CT, Q8>(a, groups, stream);
+  if (D == 128 && BS == 16) launch_mfma<128, 16, CT, Q8>(a, groups, stream, ev);
+  else if (D == 128 && BS == 32) launch_mfma<128, 32, CT, Q8>(a, groups, stream, ev);
+  else if (D == 64 && BS == 16) launch_mfma<64, 16, CT, Q8>(a, groups, stream, ev);
+  else launch_mfma<64, 32, CT, Q8>(a, groups, stream, ev);
 }
 
-void launch_generic(const PoolGeom& geom, const GenericArgs& g, dim3 grid, hipStream_t stream) {
+void launch_generic(const PoolGeom& geom, const GenericArgs& g, dim3 grid, hipStream_t stream,
+                    const KernelEvents& ev) {
   const size_t shmem = (geom.head_dim + 64) * sizeof(float) + 128 * sizeof(int);
   if (geom.q8())
-    hipLaunchKernelGGL((attn_generic<uint16_t, true>), grid, dim3(64), shmem, stream, g);
+    PA_LAUNCH(ev, (attn_generic<uint16_t, true>), grid, dim3(64), shmem, stream, g);
   else if (geom.dtype == 1)
-    hipLaunchKernelGGL((attn_generic<uint16_t, false>), grid, dim3(64), shmem, stream, g);
+    PA_LAUNCH(ev, (attn_generic<uint16_t, false>), grid, dim3(64), shmem, stream, g);
   else
-    hipLaunchKernelGGL((attn_generic<float, false>), grid, dim3(64), shmem, stream, g);
+    PA_LAUNCH(ev, (attn_generic<float, false>), grid, dim3(64), shmem, stream, g);
 }
 
 }  // namespace
@@ -654,25 +656,26 @@ bool decode_handles_rows(const PoolGeom& geom, int32_t group, int32_t max_q_len)
          static_cast<int64_t>(max_q_len) * group <= kDecodeMaxCols;
 }
 
-hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream,
+                                 const KernelEvents& ev) {
   const DecodeKernel k = pick_decode_kernel(geom, a.group);
   if (k != DecodeKernel::kGeneric && a.max_cols > kDecodeMaxCols) return hipErrorInvalidValue;
   if (k == DecodeKernel::kGeneric && a.max_cols > a.group) return hipErrorInvalidValue;  // q_len 1 only
   const bool two = a.max_cols > 16;
   switch (k) {
     case DecodeKernel::kGqaMfma:
-      if (two) launch_mfma_shape<2, false>(geom, a, stream);
-      else launch_mfma_shape<1, false>(geom, a, stream);
+      if (two) launch_mfma_shape<2, false>(geom, a, stream, ev);
+      else launch_mfma_shape<1, false>(geom, a, stream, ev);
       break;
     case DecodeKernel::kQ8Mfma:
-      if (two) launch_mfma_shape<2, true>(geom, a, stream);
-      else launch_mfma_shape<1, true>(geom, a, stream);
+      if (two) launch_mfma_shape<2, true>(geom, a, stream, ev);
+      else launch_mfma_shape<1, true>(geom, a, stream, ev);
       break;
     default: {
       GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, nullptr, nullptr,
                     a.seq_win, a.num_heads, a.num_kv_heads, a.group, geom.head_dim, geom.block_size,
                     a.scale_log2};
-      launch_generic(geom, g, dim3(a.batch * a.num_heads), stream);
+      launch_generic(geom, g, dim3(a.batch * a.num_heads), stream, ev);
       break;
     }
   }
@@ -683,22 +686,24 @@ bool decode_needs_merge_kernel(const PoolGeom& geom, int32_t group) {
   return pick_decode_kernel(geom, group) != DecodeKernel::kGeneric;  // the generic kernel never splits
 }
 
-hipError_t launch_decode_merge(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_merge(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream,
+                               const KernelEvents& ev) {
   if (a.n_merge == 0 || !decode_needs_merge_kernel(geom, a.group)) return hipSuccess;
   const dim3 grid(a.n_merge * a.num_heads);
   if (geom.head_dim == 128)
-    hipLaunchKernelGGL((decode_merge<128, uint16_t>), grid, dim3(256), 0, stream, a);
+    PA_LAUNCH(ev, (decode_merge<128, uint16_t>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_merge<64, uint16_t>), grid, dim3(256), 0, stream, a);
+    PA_LAUNCH(ev, (decode_merge<64, uint16_t>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 // Prefill through the generic kernel (query rows with their causal limits).
-hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream,
+                                  const KernelEvents& ev) {
   GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, a.q_start,
                 a.row_seq, a.seq_win, a.num_heads, a.num_kv_heads, a.group, geom.head_dim,
                 geom.block_size, a.scale_log2};
-  launch_generic(geom, g, dim3(a.n_rows * a.num_heads), stream);
+  launch_generic(geom, g, dim3(a.n_rows * a.num_heads), stream, ev);
   return hipGetLastError();
 }
 

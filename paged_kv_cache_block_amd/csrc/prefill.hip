@@ -62,6 +62,7 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 
 #ifndef PA_PREFILL_CG
 #define PA_PREFILL_CG 1
@@ -86,7 +87,8 @@
 
 namespace pa {
 
-hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream,
+                                  const KernelEvents& ev);
 
 namespace {
 
@@ -99,6 +101,17 @@ constexpr int kPrefillStages = PA_PREFILL_STAGES;  // key tiles in the LDS ring
 constexpr int kPrefillStagesQ8 = PA_PREFILL_STAGES_Q8;  // raw int8 tiles in the LDS ring
 constexpr int kTile = 32;                          // key tokens per step
 constexpr float kSlackLog2 = 8.f;                  // largest softmax weight, log2
+
+// A wave-uniform pointer kept in scalar registers (the compiler would
+// otherwise fold a per-lane choice between two such pointers into the
+// arithmetic that forms them, and do that arithmetic per lane).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return reinterpret_cast<const T*>(lo | (hi << 32));
+}
 
 // s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
 // and `lgkm` LDS/scalar operations of this wave are outstanding.
@@ -242,9 +255,12 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
         for (int r = 0; r < BPW; ++r) {
           const int blkid = wave * BPW + r;
+          // The tile's page bases are wave-uniform (scalar arithmetic); a
+          // lane only picks one and adds its offset.
           const uint16_t* pool = blkid < KB ? kpool : vpool;
-          const int blk = blk_pgi[r] ? ent[PAGES - 1] : ent[0];
-          const uint16_t* src = pool + (static_cast<size_t>(blk) * Hkv + g) * page + blk_off[r];
+          const uint16_t* base0 = uniform_ptr(pool + (static_cast<size_t>(ent[0]) * Hkv + g) * page);
+          const uint16_t* base1 = uniform_ptr(pool + (static_cast<size_t>(ent[PAGES - 1]) * Hkv + g) * page);
+          const uint16_t* src = (blk_pgi[r] ? base1 : base0) + blk_off[r];
           __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
         }
         return;
@@ -456,18 +472,23 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
           s[k][tt][i] = x;
           mloc = fmaxf(mloc, x);
         }
-      mloc = rows4_max(mloc);
       // The exponent reference m_run moves only when a score passes it by
       // more than `slack` (2^kSlackLog2 in weight), so weights stay at most
       // 2^kSlackLog2 and the accumulators are rescaled on few tiles: mostly
       // the first, where m_run is -inf and the factor is 0.  Every column
-      // sees key 0 in tile 0, so m_run is finite from then on.
-      if (mloc > m_run[k] + slack) {
-        const float alpha = exp2_flush((m_run[k] - mloc) * a.scale_log2);
-        l_run[k] *= alpha;
+      // sees key 0 in tile 0, so m_run is finite from then on.  A lane's own
+      // maximum decides whether any column may need it; only then does the
+      // wave reduce each column's maximum over its four lanes (m_run stays
+      // the same on the four).
+      if (__builtin_amdgcn_ballot_w64(mloc > m_run[k] + slack)) {
+        const float mcol = rows4_max(mloc);
+        if (mcol > m_run[k] + slack) {
+          const float alpha = exp2_flush((m_run[k] - mcol) * a.scale_log2);
+          l_run[k] *= alpha;
 #pragma unroll
-        for (int nt = 0; nt < DT; ++nt) acc[k][nt] *= alpha;
-        m_run[k] = mloc;
+          for (int nt = 0; nt < DT; ++nt) acc[k][nt] *= alpha;
+          m_run[k] = mcol;
+        }
       }
       // A column that has seen no visible key yet (m_run still -inf; only
       // on masked tiles) has every weight 0.
@@ -626,19 +647,19 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 }
 
 template <int D, int BS, bool Q8>
-void launch_mfma(const PrefillArgs& a, hipStream_t stream) {
+void launch_mfma(const PrefillArgs& a, hipStream_t stream, const KernelEvents& ev) {
   const dim3 grid(a.n_tiles * a.num_kv_heads);
   constexpr int S = Q8 ? kPrefillStagesQ8 : kPrefillStages;
-  hipLaunchKernelGGL((prefill_gqa_mfma<D, BS, kPrefillCG, kPrefillWaves, S, Q8>), grid,
+  PA_LAUNCH(ev, (prefill_gqa_mfma<D, BS, kPrefillCG, kPrefillWaves, S, Q8>), grid,
                      dim3(64 * kPrefillWaves), 0, stream, a);
 }
 
 template <bool Q8>
-void launch_mfma_shape(int D, int BS, const PrefillArgs& a, hipStream_t stream) {
-  if (D == 128 && BS == 16) launch_mfma<128, 16, Q8>(a, stream);
-  else if (D == 128 && BS == 32) launch_mfma<128, 32, Q8>(a, stream);
-  else if (D == 64 && BS == 16) launch_mfma<64, 16, Q8>(a, stream);
-  else launch_mfma<64, 32, Q8>(a, stream);
+void launch_mfma_shape(int D, int BS, const PrefillArgs& a, hipStream_t stream, const KernelEvents& ev) {
+  if (D == 128 && BS == 16) launch_mfma<128, 16, Q8>(a, stream, ev);
+  else if (D == 128 && BS == 32) launch_mfma<128, 32, Q8>(a, stream, ev);
+  else if (D == 64 && BS == 16) launch_mfma<64, 16, Q8>(a, stream, ev);
+  else launch_mfma<64, 32, Q8>(a, stream, ev);
 }
 
 }  // namespace
@@ -655,10 +676,11 @@ int32_t prefill_rows_per_tile(const PoolGeom& geom, int32_t group) {
   return kPrefillWaves * kPrefillCG * 16 / group;
 }
 
-hipError_t launch_prefill(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream) {
-  if (!prefill_uses_mfma(geom, a.group)) return launch_prefill_generic(geom, a, stream);
-  if (geom.q8()) launch_mfma_shape<true>(geom.head_dim, geom.block_size, a, stream);
-  else launch_mfma_shape<false>(geom.head_dim, geom.block_size, a, stream);
+hipError_t launch_prefill(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream,
+                          const KernelEvents& ev) {
+  if (!prefill_uses_mfma(geom, a.group)) return launch_prefill_generic(geom, a, stream, ev);
+  if (geom.q8()) launch_mfma_shape<true>(geom.head_dim, geom.block_size, a, stream, ev);
+  else launch_mfma_shape<false>(geom.head_dim, geom.block_size, a, stream, ev);
   return hipGetLastError();
 }
 
