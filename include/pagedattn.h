@@ -412,10 +412,11 @@ pa_status pa_sequences(const pa_pool* pool, int64_t* ids_out, int32_t cap, int32
 const char* pa_last_error(void);
 
 /* ---------------------------------------------------------------- timing --- */
-/* Kernel timing with HIP events recorded on the stream each kernel is
- * launched on.  Off by default.  pa_timing_read synchronizes on the recorded
- * events and returns the summed duration and launch count of one kernel
- * family since the last reset. */
+/* Kernel timing with HIP events that each timed kernel's dispatch carries
+ * on the stream it is launched on (hipExtLaunchKernel: the events take the
+ * kernel's start and end; nothing else is put on the stream).  Off by
+ * default.  pa_timing_read synchronizes on the events and returns the summed
+ * duration and launch count of one kernel family since the last reset. */
 typedef enum {
   PA_KERNEL_DECODE = 0,   /* decode partial (split-K) kernel */
   PA_KERNEL_MERGE = 1,    /* log-sum-exp merge */
@@ -426,9 +427,9 @@ typedef enum {
 } pa_kernel;
 pa_status pa_timing_enable(int on);
 /* Which kernel families get events while timing is on: bit k = pa_kernel k
- * (default all).  Each timed launch adds two event records to its stream,
- * which take time between kernels, so a caller timing whole steps can time
- * only the family it reports. */
+ * (default all).  A timed launch still spaces the stream's kernels by a few
+ * microseconds, so a caller timing whole steps can time only the family it
+ * reports (and only some of the steps). */
 pa_status pa_timing_select(uint32_t kernel_mask);
 pa_status pa_timing_reset(void);
 pa_status pa_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
