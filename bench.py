@@ -336,6 +336,57 @@ def run_verify(args, q_len=4):
             "kernel_GBs": round(float(np.mean(alg)) / (kernel_ms * 1e-3) / 1e9, 1)}
 
 
+def run_decode_only(args, name):
+    """Decode kernels alone (pa_decode: plan upload, partial kernel, merge)
+    on the long-context workload 3 or the heavy-tailed workload 5, whose
+    pools are full or nearly so (no appends).  Every call is timed with
+    dispatch-carried events; the figures are kernel GB/s on the algorithmic
+    bytes."""
+    import torch
+    from paged_kv_cache_block_amd import abi
+    from synth import decode_queries, heavy_tail, long_decode
+
+    wl = long_decode() if name == "long" else heavy_tail()
+    log(f"building {wl.name} ({sum(wl.final_lengths().values())} tokens)")
+    pool = build_pool(wl)
+    seqs = list(wl.decode_seqs)
+    q = to_device(decode_queries(wl), wl.dtype)
+    out = torch.empty_like(q)
+    need = abi.pa_decode_workspace_bytes(pool.handle, seqs, wl.num_heads)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    lengths = np.array([pool.seq_len(s) for s in seqs], dtype=np.int64)
+    alg = decode_alg_bytes(lengths, wl)
+    for _ in range(args.warmup):
+        abi.pa_decode(pool.handle, seqs, wl.num_heads, q, out, ws, ws.numel(), stream)
+    torch.cuda.synchronize()
+    abi.pa_timing_reset()
+    abi.pa_timing_select([abi.PA_KERNEL_DECODE, abi.PA_KERNEL_MERGE])
+    abi.pa_timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        abi.pa_decode(pool.handle, seqs, wl.num_heads, q, out, ws, ws.numel(), stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    abi.pa_timing_enable(False)
+    abi.pa_timing_select(None)
+    d_ms, d_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
+    m_ms, m_n = abi.pa_timing_read(abi.PA_KERNEL_MERGE)
+    d_pct = percentiles_us(abi.pa_timing_samples(abi.PA_KERNEL_DECODE))
+    pool.close()
+    k_ms = d_ms / max(d_n, 1)
+    mg_ms = m_ms / max(m_n, 1)
+    gbs = alg / (k_ms * 1e-3) / 1e9
+    return {"workload": f"{wl.name}: {len(seqs)} seqs, sum of lengths {int(lengths.sum())}, "
+                        f"{wl.num_heads}/{wl.num_kv_heads} heads, d {wl.head_dim}, bs {wl.block_size}, bf16",
+            "alg_bytes": int(alg), "decode_kernel_us": round(k_ms * 1e3, 2), "decode_kernel_us_pct": d_pct,
+            "merge_kernel_us": round(mg_ms * 1e3, 2), "kernel_GBs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "decode_plus_merge_GBs": round(alg / ((k_ms + mg_ms) * 1e-3) / 1e9, 1),
+            "ms_per_call": round((t1 - t0) * 1e3 / args.steps, 4),
+            "tokens_per_s_kernels": round(len(seqs) / ((k_ms + mg_ms) * 1e-3), 1)}
+
+
 def run_prefill(args, kv=None):
     """Chunked prefill of workload 4 (pages in ``kv``, default bf16)."""
     import torch
@@ -460,10 +511,11 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--legs", default="int8,verify,window,prefix",
+    ap.add_argument("--legs", default="int8,verify,window,long,heavy,prefix",
                     help="comma list of the legs after the headline decode leg: int8 (decode and "
-                         "prefill over int8 pages), verify, window, prefix (the bf16 prefill and the "
-                         "CPU baseline have their own switches)")
+                         "prefill over int8 pages), verify, window, long, heavy (decode kernels on "
+                         "workloads 3 and 5), prefix (the bf16 prefill and the CPU baseline have their "
+                         "own switches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -534,6 +586,10 @@ def main():
         }
     if "verify" in legs:
         line["verify_q4"] = run_verify(args, 4)
+    if "long" in legs:
+        line["long_decode"] = run_decode_only(args, "long")
+    if "heavy" in legs:
+        line["heavy_tail_decode"] = run_decode_only(args, "heavy")
     if "window" in legs:
         _, wdec = run_decode(args, kv="bf16", window=(4, 1024))
         line["window_decode"] = {
