@@ -31,6 +31,9 @@ Modules:
   own float64 K/V storage.
 * :mod:`oracle.quant` -- per-row absmax quantisation of K/V rows (codes,
   fp32 scales, read-back values); a ``Pool(quant_bits=8)`` stores through it.
+* :mod:`oracle.fp8` -- the same row scheme with 8-bit float codes (E4M3,
+  no infinities; a reading beyond the pages, pinned to the format's
+  definition); a ``Pool(quant_fp8=True)`` stores through it.
 * :mod:`oracle.prefix` -- prefix-hash block reuse: complete-block keys
   (scope, revision, all preceding tokens) mapped to pinned pool blocks.
 * :mod:`oracle.window` -- sliding-window attention with sinks
@@ -53,6 +56,15 @@ from .quant import (
     dequantize_rows,
     fake_quantize_rows,
     packed_bytes,
+)
+from .fp8 import (
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_round,
+    e4m3_encode,
+    quantize_rows_fp8,
+    dequantize_rows_fp8,
+    fake_quantize_rows_fp8,
 )
 from .prefix import PrefixCache, prefix_key, run_prefix_trace
 from .window import streaming_keep_indices, windowed_attention
@@ -84,6 +96,13 @@ __all__ = [
     "dequantize_rows",
     "fake_quantize_rows",
     "packed_bytes",
+    "E4M3_MAX",
+    "e4m3_decode",
+    "e4m3_round",
+    "e4m3_encode",
+    "quantize_rows_fp8",
+    "dequantize_rows_fp8",
+    "fake_quantize_rows_fp8",
     "PrefixCache",
     "prefix_key",
     "run_prefix_trace",

@@ -60,6 +60,7 @@ import math
 
 import numpy as np
 
+from .fp8 import dequantize_rows_fp8, quantize_rows_fp8
 from .quant import code_limit, dequantize_rows, quantize_rows, stored_scale
 
 
@@ -98,7 +99,7 @@ class Pool:
     """Fixed pool of physical KV blocks shared by refcounted block tables."""
 
     def __init__(self, num_blocks, block_size, num_kv_heads=1, head_dim=1,
-                 allocation_order=None, store_values=True, quant_bits=None):
+                 allocation_order=None, store_values=True, quant_bits=None, quant_fp8=False):
         self.num_blocks = _positive_int(num_blocks, "num_blocks")
         self.block_size = _positive_int(block_size, "block_size")
         self.num_kv_heads = _positive_int(num_kv_heads, "num_kv_heads")
@@ -132,9 +133,15 @@ class Pool:
             shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
             self.K = np.zeros(shape, dtype=np.float64)
             self.V = np.zeros(shape, dtype=np.float64)
-        # Quantised storage (oracle.quant): integer codes and the fp32 scale
-        # of every (slot, head) row; K / V then hold the values read back.
+        # Quantised storage (oracle.quant; with quant_fp8, oracle.fp8's 8-bit
+        # float codes): codes and the fp32 scale of every (slot, head) row;
+        # K / V then hold the values read back.
         self.quant_bits = None
+        self.quant_fp8 = bool(quant_fp8)
+        if self.quant_fp8 and quant_bits is None:
+            quant_bits = 8
+        if self.quant_fp8 and quant_bits != 8:
+            raise ValueError("8-bit float codes have 8 bits")
         if quant_bits is not None:
             if not self.store_values:
                 raise ValueError("quant_bits needs store_values")
@@ -402,11 +409,16 @@ class Pool:
                 continue
             for rows, codes_arr, scale_arr, vals in ((k[i], self.Kc, self.Ks, self.K),
                                                      (v[i], self.Vc, self.Vs, self.V)):
-                codes, scale = quantize_rows(rows, self.quant_bits)
-                scale = stored_scale(scale)
+                if self.quant_fp8:
+                    codes, scale = quantize_rows_fp8(rows)
+                    scale = stored_scale(scale)
+                    vals[block, offset] = dequantize_rows_fp8(codes, scale)
+                else:
+                    codes, scale = quantize_rows(rows, self.quant_bits)
+                    scale = stored_scale(scale)
+                    vals[block, offset] = dequantize_rows(codes, scale)
                 codes_arr[block, offset] = codes
                 scale_arr[block, offset] = scale[:, 0]
-                vals[block, offset] = dequantize_rows(codes, scale)
 
     def gather(self, seq):
         """Live K/V rows in logical order: two arrays ``[len, Hkv, D]``."""
