@@ -12,8 +12,8 @@ Printed: one JSON line.  ``value`` = decode KV GB/s over whole steps
 (algorithmic bytes: every cached K and V row once, plus Q, O and the block
 tables; decimal GB).  ``roofline`` covers the decode partial kernel alone,
 timed with HIP events recorded on the stream it is launched on.
-``int8_decode`` repeats the decode steps over int8 pages (codes plus one fp32
-scale per row).  ``prefill`` measures the chunked causal prefill of 16 sequences x 512 rows on
+``int8_decode`` / ``fp8_decode`` repeat the decode steps over 8-bit pages
+(int8 or E4M3 codes plus one fp32 scale per row).  ``prefill`` measures the chunked causal prefill of 16 sequences x 512 rows on
 a shared 4096-token prefix (TFLOP/s on causal FLOPs).  ``cpu_baseline`` times
 the float64 oracle on a bounded sample of the same decode workload.
 """
@@ -49,9 +49,10 @@ def to_device(arr, dtype):
 
 
 def build_pool(wl, kv=None):
-    """Replay ``wl`` into a DevicePool whose pages hold ``kv`` ("bf16", "f32"
-    or "i8"; default the workload's dtype).  New rows are in the workload's
-    dtype either way (an int8 pool quantises them as it stores them)."""
+    """Replay ``wl`` into a DevicePool whose pages hold ``kv`` ("bf16", "f32",
+    "i8" or "fp8"; default the workload's dtype).  New rows are in the
+    workload's dtype either way (an 8-bit pool quantises them as it stores
+    them)."""
     from paged_kv_cache_block_amd import DevicePool
     from synth import append_stream
     pool = DevicePool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, dtype=kv or wl.dtype,
@@ -68,10 +69,10 @@ def build_pool(wl, kv=None):
 
 
 def decode_alg_bytes(lengths, wl, kv_dtype=None):
-    """K and V rows once each, plus Q, O and the block tables.  An int8 row
+    """K and V rows once each, plus Q, O and the block tables.  An 8-bit row
     is head_dim code bytes plus its 4-byte fp32 scale."""
     elt = wl.elt_bytes
-    row = wl.head_dim + 4 if kv_dtype == "i8" else wl.head_dim * elt
+    row = wl.head_dim + 4 if kv_dtype in ("i8", "fp8") else wl.head_dim * elt
     kv = sum(lengths) * wl.num_kv_heads * row * 2
     qo = 2 * len(lengths) * wl.num_heads * wl.head_dim * elt
     tables = sum(-(-n // wl.block_size) for n in lengths) * 4
@@ -266,13 +267,13 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     if cold:
         result["cold_cache"] = cold
     achieved = float(np.mean(alg_timed)) / (kernel_ms * 1e-3) / 1e9
-    kernel = "decode_mfma_i8" if kv == "i8" else "decode_mfma_bf16"
+    kernel = {"i8": "decode_mfma_i8", "fp8": "decode_mfma_fp8"}.get(kv, "decode_mfma_bf16")
     traffic = recorded_traffic(f"{kernel}__gqa_decode")
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                           "traffic": None if traffic is None else round(traffic / 1e9, 4),
                           "traffic_unit": "GB per launch",
-                          "kernel": f"decode_mfma<128,16,1,{'int8' if kv == 'i8' else 'bf16'}>",
+                          "kernel": f"decode_mfma<128,16,1,{ {'i8': 'int8', 'fp8': 'e4m3'}.get(kv, 'bf16')}>",
                           "decode_plus_merge_GBs": round(alg_per_step / ((kernel_ms + merge_ms) * 1e-3) / 1e9, 1)}
     pool.close()
     return wl, result
@@ -423,7 +424,8 @@ def run_prefill(args, kv=None):
     pool.close()
     return {
         "workload": "prefix_prefill: 16 seqs share 4096 prefix + 512 own rows, 32/8 heads, d 128, "
-                    + ("int8 K/V pages (bf16 q, out)" if kv == "i8" else "bf16") + ", bs 16",
+                    + {"i8": "int8 K/V pages (bf16 q, out)", "fp8": "E4M3 K/V pages (bf16 q, out)"}.get(kv, "bf16")
+                    + ", bs 16",
         "causal_flops": flops,
         "ms_per_call": call_ms,
         "kernel_ms": kernel_ms,
@@ -511,9 +513,9 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--legs", default="int8,verify,window,long,heavy,prefix",
-                    help="comma list of the legs after the headline decode leg: int8 (decode and "
-                         "prefill over int8 pages), verify, window, long, heavy (decode kernels on "
+    ap.add_argument("--legs", default="int8,fp8,verify,window,long,heavy,prefix",
+                    help="comma list of the legs after the headline decode leg: int8, fp8 (decode and "
+                         "prefill over int8 / E4M3 pages), verify, window, long, heavy (decode kernels on "
                          "workloads 3 and 5), prefix (the bf16 prefill and the CPU baseline have their "
                          "own switches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -571,10 +573,12 @@ def main():
         "device_copy_GBs": device_copy_gbs(),
     }
     legs = {x.strip() for x in args.legs.split(",") if x.strip()}
-    if "int8" in legs:
-        _, q8 = run_decode(args, kv="i8")
-        line["int8_decode"] = {
-            "workload": "the same decode steps over int8 K/V pages (one fp32 scale per token and "
+    for leg, kv, what in (("int8", "i8", "int8"), ("fp8", "fp8", "E4M3")):
+        if leg not in legs:
+            continue
+        _, q8 = run_decode(args, kv=kv)
+        line[f"{leg}_decode"] = {
+            "workload": f"the same decode steps over {what} K/V pages (one fp32 scale per token and "
                         "KV head row; bf16 q, out and new rows)",
             "ms_per_step": round(q8["ms_per_step"], 5),
             "tokens_per_s": round(q8["tokens_per_s"], 1),
@@ -605,6 +609,8 @@ def main():
         line["prefill"] = run_prefill(args)
         if "int8" in legs:
             line["int8_prefill"] = run_prefill(args, kv="i8")
+        if "fp8" in legs:
+            line["fp8_prefill"] = run_prefill(args, kv="fp8")
     if "prefix" in legs:
         line["prefix_cache"] = run_prefix_cache()
     if not args.no_cpu_baseline:

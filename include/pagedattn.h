@@ -56,7 +56,8 @@
  *   q / out for prefill  [sum(q_lens)][num_heads][head_dim] (sequence-major,
  *                        [ferrum] "[q_tokens, num_heads, head_dim]")
  *   k_new / v_new        [n][num_kv_heads][head_dim]
- *   q, out, k_new and v_new use the pool dtype (bf16 for PA_DTYPE_I8);
+ *   q, out, k_new and v_new use the pool dtype (bf16 for PA_DTYPE_I8 and
+ *   PA_DTYPE_FP8);
  *   accumulation is fp32.
  *
  * PA_DTYPE_I8 pools ([KVquant]) store each (token, KV head) row of K and of
@@ -75,6 +76,16 @@
  *           (per 16-token tile: for every group of 4 tokens and every d % 16,
  *           the head_dim / 16 runs of 4 tokens are contiguous).
  *   pool bytes = num_blocks * num_kv_heads * page_bytes (each of K, V).
+ *
+ * PA_DTYPE_FP8 pools hold the same rows and pages with 8-bit float codes
+ * instead of integers (an extension of [KVquant]'s scheme): scale = max|x| /
+ * 448 in float64 (1 for an all-zero row), code = the E4M3 value nearest to
+ * x / scale (float64; ties to the even code, magnitudes above 448 to 448; a
+ * zero is 0x00).  E4M3 here: bit 7 sign, bits 6..3 exponent with bias 7,
+ * bits 2..0 mantissa; exponent 0 holds the subnormals m * 2^-9, otherwise
+ * (1 + m / 8) * 2^(e - 7); no infinities, the magnitude 0x7F is not a number
+ * and never written, 0x7E = 448 is the largest.  A row reads back as
+ * value(code) * scale, with the scale stored as fp32.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -100,7 +111,8 @@ typedef enum {
 typedef enum {
   PA_DTYPE_F32 = 0,  /* fp32 K/V, q, out */
   PA_DTYPE_BF16 = 1, /* bf16 K/V, q, out */
-  PA_DTYPE_I8 = 2    /* int8 K/V codes + fp32 row scales; bf16 q, out, new rows */
+  PA_DTYPE_I8 = 2,   /* int8 K/V codes + fp32 row scales; bf16 q, out, new rows */
+  PA_DTYPE_FP8 = 3   /* E4M3 K/V codes + fp32 row scales; bf16 q, out, new rows */
 } pa_dtype;
 
 typedef struct {
@@ -126,9 +138,10 @@ typedef struct {
 
 /* Bytes of ONE of the K / V pools for `desc`:
  * num_blocks * num_kv_heads * block_size * head_dim * element size, or for
- * PA_DTYPE_I8 num_blocks * num_kv_heads * (block_size * head_dim +
- * 4 * block_size).  Returns 0 for an invalid descriptor (including an I8
- * descriptor whose block_size or head_dim is not a multiple of 16). */
+ * PA_DTYPE_I8 and PA_DTYPE_FP8 num_blocks * num_kv_heads * (block_size *
+ * head_dim + 4 * block_size).  Returns 0 for an invalid descriptor
+ * (including an I8 or FP8 descriptor whose block_size or head_dim is not a
+ * multiple of 16). */
 size_t pa_pool_bytes(const pa_pool_desc* desc);
 
 /* Create a pool over caller-allocated device pools ([KVPool] physical_pool).

@@ -32,6 +32,7 @@ PA_ERR_DEVICE = -5
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PA_DTYPE_I8 = 2
+PA_DTYPE_FP8 = 3
 
 PA_KERNEL_DECODE = 0
 PA_KERNEL_MERGE = 1

@@ -262,12 +262,13 @@ bool desc_ok(const pa_pool_desc* d, std::string* msg) {
     *msg = "head_dim must be at most 512";
     return false;
   }
-  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16 && d->dtype != PA_DTYPE_I8) {
-    *msg = "dtype must be PA_DTYPE_F32, PA_DTYPE_BF16 or PA_DTYPE_I8";
+  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16 && d->dtype != PA_DTYPE_I8 &&
+      d->dtype != PA_DTYPE_FP8) {
+    *msg = "dtype must be PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_I8 or PA_DTYPE_FP8";
     return false;
   }
-  if (d->dtype == PA_DTYPE_I8 && (d->block_size % 16 || d->head_dim % 16)) {
-    *msg = "PA_DTYPE_I8 needs block_size and head_dim to be multiples of 16";
+  if ((d->dtype == PA_DTYPE_I8 || d->dtype == PA_DTYPE_FP8) && (d->block_size % 16 || d->head_dim % 16)) {
+    *msg = "PA_DTYPE_I8 and PA_DTYPE_FP8 need block_size and head_dim to be multiples of 16";
     return false;
   }
   return true;

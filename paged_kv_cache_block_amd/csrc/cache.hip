@@ -80,8 +80,51 @@ __device__ __forceinline__ double q8_scale(float absmax) {
   return s == 0.0 ? 1.0 : s;
 }
 
+// E4M3 codes (bit 7 sign, exponent bias 7, no infinities): the value nearest
+// to x / scale, decided in float64, ties to the even code, magnitudes above
+// the largest value 448 to 448; a zero (of either sign) is code 0x00.
+constexpr double kE4M3Max = 448.0;
+__device__ __forceinline__ uint8_t f8_code(float x, double scale) {
+  const double y = static_cast<double>(x) / scale;
+  const double a = fmin(fabs(y), kE4M3Max);
+  int k;
+  (void)frexp(a, &k);                        // a = f * 2^k, f in [0.5, 1)
+  const int e = max(k - 1, -6);              // exponent of a's binade (subnormals: -6)
+  const double quantum = ldexp(1.0, e - 3);  // 3 mantissa bits
+  const double r = rint(a / quantum) * quantum;
+  if (r == 0.0) return 0;
+  uint32_t mag;
+  if (r < 0.015625) {  // below 2^-6: a subnormal m * 2^-9
+    mag = static_cast<uint32_t>(r * 512.0);
+  } else {
+    int kr;
+    (void)frexp(r, &kr);
+    const int er = kr - 1;
+    mag = (static_cast<uint32_t>(er + 7) << 3) | static_cast<uint32_t>(r / ldexp(1.0, er - 3) - 8.0);
+  }
+  return static_cast<uint8_t>((y < 0.0 ? 0x80u : 0u) | mag);
+}
+
+__device__ __forceinline__ double f8_scale(float absmax) {
+  const double s = static_cast<double>(absmax) / kE4M3Max;
+  return s == 0.0 ? 1.0 : s;
+}
+
+// Code and scale of a row, by code kind (1: int8, 2: E4M3).
+template <int Q8>
+__device__ __forceinline__ uint8_t row_code(float x, double scale) {
+  if constexpr (Q8 == 2) return f8_code(x, scale);
+  else return static_cast<uint8_t>(q8_code(x, scale));
+}
+template <int Q8>
+__device__ __forceinline__ double row_scale(float absmax) {
+  if constexpr (Q8 == 2) return f8_scale(absmax);
+  else return q8_scale(absmax);
+}
+
 // One wave quantises one (row, head): K codes row-major, V codes in operand
 // order, then the two fp32 scales.  D <= 512 (8 values per lane).
+template <int Q8>
 __device__ __forceinline__ void q8_store_row_head(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_row,
                                                   const uint16_t* v_row, int64_t blk, int32_t off,
                                                   int32_t h, int32_t hkv, int32_t bs, int32_t dim, int lane) {
@@ -97,7 +140,7 @@ __device__ __forceinline__ void q8_store_row_head(uint8_t* k_pool, uint8_t* v_po
   }
   kmax = wave_max(kmax);
   vmax = wave_max(vmax);
-  const double ks = q8_scale(kmax), vs = q8_scale(vmax);
+  const double ks = row_scale<Q8>(kmax), vs = row_scale<Q8>(vmax);
   const size_t page_bytes = static_cast<size_t>(bs) * dim + 4 * static_cast<size_t>(bs);
   uint8_t* kp = k_pool + (blk * hkv + h) * page_bytes;
   uint8_t* vp = v_pool + (blk * hkv + h) * page_bytes;
@@ -105,8 +148,8 @@ __device__ __forceinline__ void q8_store_row_head(uint8_t* k_pool, uint8_t* v_po
   for (int k = 0; k < 8; ++k) {
     const int d = lane + 64 * k;
     if (d < dim) {
-      kp[static_cast<size_t>(off) * dim + d] = static_cast<uint8_t>(q8_code(kx[k], ks));
-      vp[q8_v_offset(off, d, dim)] = static_cast<uint8_t>(q8_code(vx[k], vs));
+      kp[static_cast<size_t>(off) * dim + d] = row_code<Q8>(kx[k], ks);
+      vp[q8_v_offset(off, d, dim)] = row_code<Q8>(vx[k], vs);
     }
   }
   if (lane == 0) {
@@ -115,7 +158,8 @@ __device__ __forceinline__ void q8_store_row_head(uint8_t* k_pool, uint8_t* v_po
   }
 }
 
-// reshape_and_cache for int8 pools: one wave per (row i, head h).
+// reshape_and_cache for 8-bit pools: one wave per (row i, head h).
+template <int Q8>
 __global__ __launch_bounds__(256) void reshape_and_cache_q8(
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slots, int64_t n, int32_t hkv,
@@ -128,13 +172,14 @@ __global__ __launch_bounds__(256) void reshape_and_cache_q8(
     const int64_t slot = slots[i];
     if (slot < 0 || slot >= num_slots) continue;
     const int64_t blk = slot / bs;
-    q8_store_row_head(k_pool, v_pool, k_new + rh * dim, v_new + rh * dim, blk,
-                      static_cast<int32_t>(slot - blk * bs), h, hkv, bs, dim, lane);
+    q8_store_row_head<Q8>(k_pool, v_pool, k_new + rh * dim, v_new + rh * dim, blk,
+                          static_cast<int32_t>(slot - blk * bs), h, hkv, bs, dim, lane);
   }
 }
 
-// Decode-step prologue for int8 pools: blocks [0, nu) copy the plan, the
+// Decode-step prologue for 8-bit pools: blocks [0, nu) copy the plan, the
 // others quantise and store the new rows (one wave per (row, head)).
+template <int Q8>
 __global__ __launch_bounds__(256) void step_prep_q8(
     const uint4* __restrict__ plan_src, uint4* __restrict__ plan_dst, int64_t n16, int nu,
     const int64_t* __restrict__ slots, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
@@ -153,8 +198,8 @@ __global__ __launch_bounds__(256) void step_prep_q8(
     const int64_t slot = slots[i];
     if (slot < 0 || slot >= num_slots) continue;
     const int64_t blk = slot / bs;
-    q8_store_row_head(k_pool, v_pool, k_new + rh * dim, v_new + rh * dim, blk,
-                      static_cast<int32_t>(slot - blk * bs), h, hkv, bs, dim, lane);
+    q8_store_row_head<Q8>(k_pool, v_pool, k_new + rh * dim, v_new + rh * dim, blk,
+                          static_cast<int32_t>(slot - blk * bs), h, hkv, bs, dim, lane);
   }
 }
 
@@ -246,11 +291,18 @@ hipError_t launch_step_prep(const PoolGeom& geom, const void* plan_src, void* pl
   const int64_t num_slots = static_cast<int64_t>(geom.num_blocks) * geom.block_size;
   if (geom.q8()) {
     const int nq = grid_for(static_cast<int64_t>(n) * geom.num_kv_heads, 4, 4096);
-    PA_LAUNCH(ev, step_prep_q8, dim3(nu + nq), dim3(256), 0, stream,
-                       static_cast<const uint4*>(plan_src), static_cast<uint4*>(plan_dst), n16, nu, slots,
-                       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
-                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                       static_cast<int64_t>(n), geom.num_kv_heads, geom.block_size, geom.head_dim, num_slots);
+    if (geom.fp8())
+      PA_LAUNCH(ev, step_prep_q8<2>, dim3(nu + nq), dim3(256), 0, stream,
+                static_cast<const uint4*>(plan_src), static_cast<uint4*>(plan_dst), n16, nu, slots,
+                static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                static_cast<int64_t>(n), geom.num_kv_heads, geom.block_size, geom.head_dim, num_slots);
+    else
+      PA_LAUNCH(ev, step_prep_q8<1>, dim3(nu + nq), dim3(256), 0, stream,
+                static_cast<const uint4*>(plan_src), static_cast<uint4*>(plan_dst), n16, nu, slots,
+                static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                static_cast<int64_t>(n), geom.num_kv_heads, geom.block_size, geom.head_dim, num_slots);
     return hipGetLastError();
   }
   const dim3 grid(nu + nc);
@@ -278,10 +330,16 @@ hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_
   const int grid = grid_for(total, 256, 65536);
   if (geom.q8()) {
     const int gq = grid_for(static_cast<int64_t>(n) * geom.num_kv_heads, 4, 65536);
-    PA_LAUNCH(ev, reshape_and_cache_q8, dim3(gq), dim3(256), 0, stream, static_cast<uint8_t*>(k_pool),
-                       static_cast<uint8_t*>(v_pool), static_cast<const uint16_t*>(k_new),
-                       static_cast<const uint16_t*>(v_new), slots, static_cast<int64_t>(n), geom.num_kv_heads,
-                       geom.block_size, geom.head_dim, num_slots);
+    if (geom.fp8())
+      PA_LAUNCH(ev, reshape_and_cache_q8<2>, dim3(gq), dim3(256), 0, stream, static_cast<uint8_t*>(k_pool),
+                static_cast<uint8_t*>(v_pool), static_cast<const uint16_t*>(k_new),
+                static_cast<const uint16_t*>(v_new), slots, static_cast<int64_t>(n), geom.num_kv_heads,
+                geom.block_size, geom.head_dim, num_slots);
+    else
+      PA_LAUNCH(ev, reshape_and_cache_q8<1>, dim3(gq), dim3(256), 0, stream, static_cast<uint8_t*>(k_pool),
+                static_cast<uint8_t*>(v_pool), static_cast<const uint16_t*>(k_new),
+                static_cast<const uint16_t*>(v_new), slots, static_cast<int64_t>(n), geom.num_kv_heads,
+                geom.block_size, geom.head_dim, num_slots);
   } else if (geom.dtype == 1) {
     PA_LAUNCH(ev, reshape_and_cache_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
                        static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),

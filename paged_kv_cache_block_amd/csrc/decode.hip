@@ -70,9 +70,9 @@ struct GenericArgs {
   float scale_log2;
 };
 
-// Q8: int8 pages (codes + fp32 row scales, q / out bf16); T is the q / out
-// element type.
-template <typename T, bool Q8>
+// Q8: pages of 8-bit codes + fp32 row scales (1: int8, 2: E4M3; q / out
+// bf16); T is the q / out element type.
+template <typename T, int Q8>
 __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
   extern __shared__ float smem[];
   float* qs = smem;                                            // [D]
@@ -125,8 +125,8 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
       float dot = 0.f;
       if constexpr (Q8) {
         const uint8_t* kp = static_cast<const uint8_t*>(a.k_pool) + (static_cast<size_t>(blk) * Hkv + g) * q8_page;
-        const int8_t* kr = reinterpret_cast<const int8_t*>(kp) + off * D;
-        for (int d = 0; d < D; ++d) dot += qs[d] * static_cast<float>(kr[d]);
+        const uint8_t* kr = kp + off * D;
+        for (int d = 0; d < D; ++d) dot += qs[d] * code_value<Q8>(kr[d]);
         dot *= reinterpret_cast<const float*>(kp + BS * D)[off];
       } else {
         const T* kr = K + ((static_cast<size_t>(blk) * Hkv + g) * BS + off) * D;
@@ -157,11 +157,11 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
       float x = acc[k] * alpha;
       if (d < D) {
         if constexpr (Q8) {
-          const int8_t* vb = static_cast<const int8_t*>(a.v_pool);
+          const uint8_t* vb = static_cast<const uint8_t*>(a.v_pool);
           for (int jj = 0; jj < nj; ++jj)
             if (blks[jj] >= 0)
-              x += ps[jj] * static_cast<float>(vb[(static_cast<size_t>(blks[jj]) * Hkv + g) * q8_page +
-                                                 q8_v_offset(offs[jj], d, D)]);
+              x += ps[jj] * code_value<Q8>(vb[(static_cast<size_t>(blks[jj]) * Hkv + g) * q8_page +
+                                               q8_v_offset(offs[jj], d, D)]);
         } else {
           for (int jj = 0; jj < nj; ++jj)
             if (blks[jj] >= 0)
@@ -185,19 +185,18 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
 // ------------------------------------------------------------ GQA / MFMA ---
 // One page of one KV head, as one lane holds it.
 //   bf16: k[tt][j] = K[16tt + n][32j + 8grp .. +8], v[nt][tt] = V^T[16nt + n][16tt + 4grp .. +4]
-//   int8: kc[tt][.] = K codes of token 16tt + n, d in [grp * D/4, +D/4) (the QK
+//   codes: kc[tt][.] = K codes of token 16tt + n, d in [grp * D/4, +D/4) (the QK
 //         contraction runs over that permuted d order, Q takes the same),
 //         vc[tt][nt] = V codes of d = 16nt + n, tokens 16tt + 4grp .. +4,
 //         ks / vs = the row scales of tokens 16tt + 4grp .. +4.
-template <int D, int BS, bool Q8> struct PageRegs;
-template <int D, int BS> struct PageRegs<D, BS, false> {
-  bf16x8 k[BS / 16][D / 32];
-  s16x4 v[D / 16][BS / 16];
-};
-template <int D, int BS> struct PageRegs<D, BS, true> {
+template <int D, int BS, int Q8> struct PageRegs {  // 8-bit codes
   uint32_t kc[BS / 16][D / 16];
   uint32_t vc[BS / 16][D / 16];
   f32x4 ks[BS / 16], vs[BS / 16];
+};
+template <int D, int BS> struct PageRegs<D, BS, 0> {
+  bf16x8 k[BS / 16][D / 32];
+  s16x4 v[D / 16][BS / 16];
 };
 
 // Minimum waves per SIMD a decode kernel variant is compiled for (its
@@ -205,7 +204,7 @@ template <int D, int BS> struct PageRegs<D, BS, true> {
 // int8 kernel asks for 3 resident waves to keep enough bytes in flight; the
 // d 128 / 32-slot / 32-column variants hold two 32-token pages for two
 // column tiles and would spill under 2, so they take what they need.
-template <int D, int BS, int CT, bool Q8>
+template <int D, int BS, int CT, int Q8>
 constexpr int decode_waves() {
   if (Q8 && CT == 1 && BS == 16) return PA_DECODE_WAVES_I8;
   if (D == 128 && BS == 32 && CT == 2) return 1;
@@ -218,8 +217,9 @@ constexpr int decode_waves() {
 // What is computed (docs.rs ferrum-kv 0.4.0 src/attention.rs,
 // paged_attention: GQA head g = h / G, scale 1/sqrt(D), query row t of q_len
 // sees keys j <= L - q_len + t), over the page range of one work item; with
-// Q8 over int8 pages whose rows read back as code * scale (vladkulikov.com
-// notebook "Модуль 10", KV-compression experiment):
+// Q8 over pages of 8-bit codes (1: int8, 2: E4M3) whose rows read back as
+// value(code) * scale (vladkulikov.com notebook "Модуль 10", KV-compression
+// experiment; the E4M3 codes extend its integer ones):
 //   s_j = (q . ck_j) * sk_j / sqrt(D),  o = sum_j p_j sv_j cv_j / sum_j p_j
 // with sk folded into the scores and sv into the P operand.
 //
@@ -234,7 +234,7 @@ constexpr int decode_waves() {
 // split into bf16 hi + lo terms (~16 mantissa bits of p); the 4 waves merge
 // in LDS; a range that is the whole sequence writes bf16 output, otherwise
 // fp32 partials (m, l, acc) for the merge kernel.
-template <int D, int BS, int CT, bool Q8>
+template <int D, int BS, int CT, int Q8>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(decode_waves<D, BS, CT, Q8>())))
 void decode_mfma(DecodeArgs a) {
@@ -358,7 +358,7 @@ void decode_mfma(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         if constexpr (Q8)
-          kop[j] = i8x8_to_bf16x8(P.kc[tt][2 * j], P.kc[tt][2 * j + 1]);
+          kop[j] = codes8_to_bf16x8<Q8>(P.kc[tt][2 * j], P.kc[tt][2 * j + 1]);
         else
           kop[j] = P.k[tt][j];
       }
@@ -426,9 +426,10 @@ void decode_mfma(DecodeArgs a) {
         }
       l_run[ct] = l_run[ct] * alpha[ct] + psum;
     }
-    // bf16 pages: past-end slots of the last page have weight 0 and their
-    // values are zeroed too, so 0 * V cannot meet non-finite bits left there.
-    const bool tail = EDGE && pg == nblk - 1;
+    // Past-end slots of the last page have weight 0 and their values are
+    // zeroed too, so 0 * V cannot meet non-finite bits left there (int8
+    // codes are always finite; bf16 and E4M3 bytes may be NaN).
+    const bool tail = EDGE && Q8 != 1 && pg == nblk - 1;
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
 #pragma unroll
@@ -436,16 +437,13 @@ void decode_mfma(DecodeArgs a) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         s16x4 v;
-        if constexpr (Q8) {
-          v = i8x4_to_bf16x4(P.vc[tt][nt]);
-        } else {
-          v = P.v[nt][tt];
-          if (EDGE && tail) {
-            const int live = L - (pg * BS + 16 * tt + 4 * grp);
+        if constexpr (Q8) v = codes4_to_bf16x4<Q8>(P.vc[tt][nt]);
+        else v = P.v[nt][tt];
+        if (tail) {
+          const int live = L - (pg * BS + 16 * tt + 4 * grp);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (i >= live) v[i] = 0;
-          }
+          for (int i = 0; i < 4; ++i)
+            if (i >= live) v[i] = 0;
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -612,13 +610,13 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   }
 }
 
-template <int D, int BS, int CT, bool Q8>
+template <int D, int BS, int CT, int Q8>
 void launch_mfma(const DecodeArgs& a, int groups, hipStream_t stream, const KernelEvents& ev) {
   const size_t shmem = static_cast<size_t>(kDecodeWaves) * min(a.max_cols, 16) * (D + 4) * sizeof(float);
   PA_LAUNCH(ev, (decode_mfma<D, BS, CT, Q8>), dim3(groups), dim3(256), shmem, stream, a);
 }
 
-template <int CT, bool Q8>
+template <int CT, int Q8>
 void launch_mfma_shape(const PoolGeom& geom, const DecodeArgs& a, hipStream_t stream, const KernelEvents& ev) {
   const int groups = a.n_work * a.num_kv_heads;
   const int D = geom.head_dim, BS = geom.block_size;
@@ -631,12 +629,14 @@ void launch_mfma_shape(const PoolGeom& geom, const DecodeArgs& a, hipStream_t st
 void launch_generic(const PoolGeom& geom, const GenericArgs& g, dim3 grid, hipStream_t stream,
                     const KernelEvents& ev) {
   const size_t shmem = (geom.head_dim + 64) * sizeof(float) + 128 * sizeof(int);
-  if (geom.q8())
-    PA_LAUNCH(ev, (attn_generic<uint16_t, true>), grid, dim3(64), shmem, stream, g);
+  if (geom.fp8())
+    PA_LAUNCH(ev, (attn_generic<uint16_t, 2>), grid, dim3(64), shmem, stream, g);
+  else if (geom.q8())
+    PA_LAUNCH(ev, (attn_generic<uint16_t, 1>), grid, dim3(64), shmem, stream, g);
   else if (geom.dtype == 1)
-    PA_LAUNCH(ev, (attn_generic<uint16_t, false>), grid, dim3(64), shmem, stream, g);
+    PA_LAUNCH(ev, (attn_generic<uint16_t, 0>), grid, dim3(64), shmem, stream, g);
   else
-    PA_LAUNCH(ev, (attn_generic<float, false>), grid, dim3(64), shmem, stream, g);
+    PA_LAUNCH(ev, (attn_generic<float, 0>), grid, dim3(64), shmem, stream, g);
 }
 
 }  // namespace
@@ -664,12 +664,17 @@ hipError_t launch_decode_partial(const PoolGeom& geom, const DecodeArgs& a, hipS
   const bool two = a.max_cols > 16;
   switch (k) {
     case DecodeKernel::kGqaMfma:
-      if (two) launch_mfma_shape<2, false>(geom, a, stream, ev);
-      else launch_mfma_shape<1, false>(geom, a, stream, ev);
+      if (two) launch_mfma_shape<2, 0>(geom, a, stream, ev);
+      else launch_mfma_shape<1, 0>(geom, a, stream, ev);
       break;
     case DecodeKernel::kQ8Mfma:
-      if (two) launch_mfma_shape<2, true>(geom, a, stream, ev);
-      else launch_mfma_shape<1, true>(geom, a, stream, ev);
+      if (geom.fp8()) {
+        if (two) launch_mfma_shape<2, 2>(geom, a, stream, ev);
+        else launch_mfma_shape<1, 2>(geom, a, stream, ev);
+      } else {
+        if (two) launch_mfma_shape<2, 1>(geom, a, stream, ev);
+        else launch_mfma_shape<1, 1>(geom, a, stream, ev);
+      }
       break;
     default: {
       GenericArgs g{a.k_pool, a.v_pool, a.q, a.out, a.ctx_len, a.tbl_off, a.tables, nullptr, nullptr,

@@ -15,6 +15,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 bit pattern <-> float.  Widening is exact; narrowing is round to
 // nearest even (NaN stays NaN).
@@ -97,6 +99,45 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, v[i]);
   return r;
+}
+
+// 4 E4M3 codes (one dword; bit 7 sign, exponent bias 7, no infinities) ->
+// 4 bf16, exact (every E4M3 value is a bf16): gfx950's scaled conversion
+// with scale 1, two codes per instruction, each result a packed dword
+// (byte 2i in the low half, byte 2i + 1 in the high half).  The results are
+// moved as whole dwords: extracting their bf16 elements one by one has
+// produced the low half twice.
+__device__ __forceinline__ u32x2 f8x4_to_bf16x4_words(uint32_t w) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  return u32x2{a, b};
+}
+__device__ __forceinline__ s16x4 f8x4_to_bf16x4(uint32_t w) {
+  return __builtin_bit_cast(s16x4, f8x4_to_bf16x4_words(w));
+}
+
+// 8-bit codes of a page, by kind: Q8 = 1 int8 integers, 2 E4M3 floats.
+template <int Q8>
+__device__ __forceinline__ s16x4 codes4_to_bf16x4(uint32_t w) {
+  if constexpr (Q8 == 2) return f8x4_to_bf16x4(w);
+  else return i8x4_to_bf16x4(w);
+}
+template <int Q8>
+__device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  if constexpr (Q8 == 2) {
+    const u32x2 a = f8x4_to_bf16x4_words(lo), b = f8x4_to_bf16x4_words(hi);
+    return __builtin_bit_cast(bf16x8, (u32x4{a[0], a[1], b[0], b[1]}));
+  }
+  const s16x4 a = codes4_to_bf16x4<Q8>(lo), b = codes4_to_bf16x4<Q8>(hi);
+  const short v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, v[i]);
+  return r;
+}
+template <int Q8>
+__device__ __forceinline__ float code_value(uint8_t c) {
+  return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(codes4_to_bf16x4<Q8>(c)[0])) << 16);
 }
 
 // Uniform value in a scalar register (the compiler cannot always prove it).

@@ -7,7 +7,7 @@
 // masks cached decoding).  The one-pass running max / sum per key tile is
 // lecture 19's tiled_attention recurrence.
 //
-// prefill_gqa_mfma<D, BS, CG, NW, S, Q8>  (bf16 or int8 pages, D in {64, 128},
+// prefill_gqa_mfma<D, BS, CG, NW, S, Q8>  (bf16 pages, or Q8 1 int8 / 2 E4M3 codes; D in {64, 128},
 //                                         BS in {16, 32}, G | 16)
 //   One workgroup of NW waves = (sequence, block of query rows, KV head).
 //   The MFMA N dimension packs (query row, head of the group) pairs: column c
@@ -48,12 +48,12 @@
 //   resident (released pages are -1 in the table, staged as zeros and
 //   masked).
 //
-//   int8 pages (the [KVquant] rows: codes plus one fp32 scale per token and
-//   KV head): the ring holds tiles as the pages store them (K codes, V codes
+//   8-bit pages (the [KVquant] rows: int8 or E4M3 codes plus one fp32 scale
+//   per token and KV head): the ring holds tiles as the pages store them (K codes, V codes
 //   in their operand order, the 64 scales; 16-byte chunks permuted so every
 //   LDS access is conflict-free), fetched with the same direct loads; each
 //   step four waves convert the next tile's K operand blocks and four its V
-//   blocks to bf16 (exact: |code| <= 127) into one of two operand-ordered
+//   blocks to bf16 (exact for both code kinds) into one of two operand-ordered
 //   tiles, so the MFMA part is the bf16 one.  The scales stay
 //   in fp32: K's multiply the scores, V's the weights entering P.V (l sums
 //   the weights without them).
@@ -119,7 +119,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
 }
 
-template <int D, int BS, int CG, int NW, int S, bool Q8>
+template <int D, int BS, int CG, int NW, int S, int Q8>
 __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(PrefillArgs a) {
   constexpr int KS = D / 32;         // k-steps of QK per token half
   constexpr int DT = D / 16;         // d tiles of P.V
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
       for (int r = 0; r < kKPW; ++r) {
         const uint2 c = *reinterpret_cast<const uint2*>(src + cv_off[r]);
-        ring[os][wave * kKPW + r][lane] = __builtin_bit_cast(uint4, i8x8_to_bf16x8(c.x, c.y));
+        ring[os][wave * kKPW + r][lane] = __builtin_bit_cast(uint4, codes8_to_bf16x8<Q8>(c.x, c.y));
       }
     } else {
       const uint4 lo = *reinterpret_cast<const uint4*>(src + cv_vlo);
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
       for (int r = 0; r < kVPW; ++r) {
         const int nt = (wave - 4) * kVPW + r;
-        ring[os][KB + nt][lane] = __builtin_bit_cast(uint4, i8x8_to_bf16x8(lw[nt & 3], hw[nt & 3]));
+        ring[os][KB + nt][lane] = __builtin_bit_cast(uint4, codes8_to_bf16x8<Q8>(lw[nt & 3], hw[nt & 3]));
       }
     }
   };
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
       bf16x8 vop = blocks[(KB + nt) * 64 + lane];
-      if constexpr (kTail && !Q8) {  // int8 codes are always finite
+      if constexpr (kTail && Q8 != 1) {  // int8 codes are always finite; bf16 and E4M3 may be NaN
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (e >= live) vop[e] = static_cast<__bf16>(0.f);
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   }
 }
 
-template <int D, int BS, bool Q8>
+template <int D, int BS, int Q8>
 void launch_mfma(const PrefillArgs& a, hipStream_t stream, const KernelEvents& ev) {
   const dim3 grid(a.n_tiles * a.num_kv_heads);
   constexpr int S = Q8 ? kPrefillStagesQ8 : kPrefillStages;
@@ -654,7 +654,7 @@ void launch_mfma(const PrefillArgs& a, hipStream_t stream, const KernelEvents& e
                      dim3(64 * kPrefillWaves), 0, stream, a);
 }
 
-template <bool Q8>
+template <int Q8>
 void launch_mfma_shape(int D, int BS, const PrefillArgs& a, hipStream_t stream, const KernelEvents& ev) {
   if (D == 128 && BS == 16) launch_mfma<128, 16, Q8>(a, stream, ev);
   else if (D == 128 && BS == 32) launch_mfma<128, 32, Q8>(a, stream, ev);
@@ -679,8 +679,9 @@ int32_t prefill_rows_per_tile(const PoolGeom& geom, int32_t group) {
 hipError_t launch_prefill(const PoolGeom& geom, const PrefillArgs& a, hipStream_t stream,
                           const KernelEvents& ev) {
   if (!prefill_uses_mfma(geom, a.group)) return launch_prefill_generic(geom, a, stream, ev);
-  if (geom.q8()) launch_mfma_shape<true>(geom.head_dim, geom.block_size, a, stream, ev);
-  else launch_mfma_shape<false>(geom.head_dim, geom.block_size, a, stream, ev);
+  if (geom.fp8()) launch_mfma_shape<2>(geom.head_dim, geom.block_size, a, stream, ev);
+  else if (geom.q8()) launch_mfma_shape<1>(geom.head_dim, geom.block_size, a, stream, ev);
+  else launch_mfma_shape<0>(geom.head_dim, geom.block_size, a, stream, ev);
   return hipGetLastError();
 }
 

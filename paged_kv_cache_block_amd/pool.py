@@ -12,7 +12,8 @@ import numpy as np
 
 from . import abi
 
-_DTYPES = {"f32": abi.PA_DTYPE_F32, "bf16": abi.PA_DTYPE_BF16, "i8": abi.PA_DTYPE_I8}
+_DTYPES = {"f32": abi.PA_DTYPE_F32, "bf16": abi.PA_DTYPE_BF16, "i8": abi.PA_DTYPE_I8,
+           "fp8": abi.PA_DTYPE_FP8}
 
 
 def _torch():
@@ -23,10 +24,10 @@ def _torch():
 class DevicePool:
     """One pool of ``num_blocks`` blocks; K and V live on ``device``.
 
-    ``dtype`` is "bf16", "f32" or "i8" (int8 codes with one fp32 scale per
-    (token, KV head) row; queries, outputs and new rows are then bf16, and
-    ``k`` / ``v`` are raw byte tensors ``[num_blocks, num_kv_heads,
-    page_bytes]`` in the library's int8 page layout).
+    ``dtype`` is "bf16", "f32", "i8" or "fp8" (int8 or E4M3 codes with one
+    fp32 scale per (token, KV head) row; queries, outputs and new rows are
+    then bf16, and ``k`` / ``v`` are raw byte tensors ``[num_blocks,
+    num_kv_heads, page_bytes]`` in the library's 8-bit page layout).
     With ``metadata_only=True`` no device memory is allocated and only the
     bookkeeping calls work (usable on a machine without a GPU).
     """
@@ -42,7 +43,7 @@ class DevicePool:
         self.handle = None
         if not metadata_only:
             torch = _torch()
-            if dtype == "i8":
+            if dtype in ("i8", "fp8"):
                 page = block_size * head_dim + 4 * block_size
                 shape_k = shape_v = (num_blocks, num_kv_heads, page)
                 tdt = torch.uint8

@@ -119,11 +119,14 @@ def test_int8_pool_descriptor():
     assert per_pool == 10 * 8 * (16 * 128 + 16 * 4)
     n_rows = 10 * 16 * 8
     assert 2 * per_pool == oracle.packed_bytes(n_rows, 128, 8)
+    # The 8-bit float codes share the layout byte for byte.
+    assert abi.pa_pool_bytes(abi.make_desc(10, 16, 8, 128, abi.PA_DTYPE_FP8)) == per_pool
     for bs, d in ((8, 128), (16, 40), (4, 8)):
-        assert abi.pa_pool_bytes(abi.make_desc(10, bs, 8, d, abi.PA_DTYPE_I8)) == 0
-        with pytest.raises(InvalidArgumentError):
-            DevicePool(10, bs, 1, d, dtype="i8", metadata_only=True)
-    assert abi.pa_pool_bytes(abi.make_desc(10, 16, 8, 128, 3)) == 0
+        for dt, name in ((abi.PA_DTYPE_I8, "i8"), (abi.PA_DTYPE_FP8, "fp8")):
+            assert abi.pa_pool_bytes(abi.make_desc(10, bs, 8, d, dt)) == 0
+            with pytest.raises(InvalidArgumentError):
+                DevicePool(10, bs, 1, d, dtype=name, metadata_only=True)
+    assert abi.pa_pool_bytes(abi.make_desc(10, 16, 8, 128, 4)) == 0
     pool = DevicePool(8, 16, 2, 64, dtype="i8", metadata_only=True)
     pool.create(1)
     assert pool.append(1, 20).tolist() == list(range(32))[:20]

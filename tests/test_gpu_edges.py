@@ -44,7 +44,8 @@ def _pool(lengths, hkv, d, bs, kv, seed=1):
     nb = int(sum(-(-n // bs) for n in lengths) + 5)
     order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
     pool = DevicePool(nb, bs, hkv, d, dtype=kv, allocation_order=order)
-    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv == "i8" else None)
+    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv in ("i8", "fp8") else None,
+                     quant_fp8=kv == "fp8")
     rng = np.random.default_rng(seed + 7)
     io = _io(kv)
     for s, n in enumerate(lengths):
@@ -69,6 +70,8 @@ EDGE_CASES = [
     ([1, 40, 1200], 16, 2, 256, 32, "i8"),      # int8 pages, head_dim 256 (generic)
     ([7], 32, 8, 128, 16, "bf16"),              # a batch of one
     ([1, 1, 1], 32, 8, 128, 16, "i8"),          # one-token sequences, int8
+    ([1, 40, 1200], 16, 2, 256, 32, "fp8"),     # E4M3 pages, head_dim 256 (generic)
+    ([1, 1, 1], 32, 8, 128, 16, "fp8"),         # one-token sequences, E4M3
 ]
 
 
@@ -109,8 +112,9 @@ def test_reshape_and_cache_skips_out_of_range_slots():
     pool.write(slots, k, k)
     torch.cuda.synchronize()
     assert torch.equal(pool.k, before[0]) and torch.equal(pool.v, before[1])
-    q8 = DevicePool(4, 16, 2, 64, dtype="i8")
-    before = q8.k.clone()
-    q8.write(slots, k, k)
-    torch.cuda.synchronize()
-    assert torch.equal(q8.k, before)
+    for kind in ("i8", "fp8"):
+        q8 = DevicePool(4, 16, 2, 64, dtype=kind)
+        before = q8.k.clone()
+        q8.write(slots, k, k)
+        torch.cuda.synchronize()
+        assert torch.equal(q8.k, before)

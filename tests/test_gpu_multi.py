@@ -35,7 +35,8 @@ def _setup(lengths, hq, hkv, d, bs, kv, seed=5, fork=True):
     nb = int(sum(-(-n // bs) for n in lengths) * 2 + 64)
     order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
     pool = DevicePool(nb, bs, hkv, d, dtype=kv, allocation_order=order)
-    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv == "i8" else None)
+    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv in ("i8", "fp8") else None,
+                     quant_fp8=kv == "fp8")
     rng = np.random.default_rng(seed + 1)
     for s, n in enumerate(lengths):
         pool.create(s)
@@ -71,6 +72,8 @@ VERIFY_CASES = [
     ([5, 40, 2049], [16, 32, 1, 7], 16, 16, 64, 32, "bf16"),                 # MHA, 32 rows
     ([3, 77, 3000], [4, 8, 1, 2], 32, 8, 128, 16, "i8"),                     # int8 pages
     ([20, 513], [16, 3, 9], 8, 4, 64, 16, "i8"),                             # int8, G2, D64
+    ([3, 77, 3000], [4, 8, 1, 2], 32, 8, 128, 16, "fp8"),                    # E4M3 pages
+    ([20, 513], [16, 3, 9], 8, 4, 64, 16, "fp8"),                            # E4M3, G2, D64
     ([31, 1000], [2, 3, 4], 16, 2, 128, 32, "bf16"),                         # G8, bs 32
 ]
 
@@ -125,7 +128,7 @@ def test_verify_step_rejections_change_nothing():
     assert f32.seq_len(0) == 3
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 def test_short_prefill_chunks_use_split_k(kv):
     """pa_prefill_chunk with every q_len * G <= 32 runs on the decode
     kernels (rows of a split sequence merge by log-sum-exp)."""

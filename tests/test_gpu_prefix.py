@@ -29,13 +29,14 @@ def _gpu():
     abi.load()
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 def test_decode_after_prefix_attach(kv):
     from paged_kv_cache_block_amd import DevicePool
     hq, hkv, d, bs, nb = 32, 8, 128, 16, 64
     order = np.random.default_rng(8).permutation(nb).astype(np.int32)
     pool = DevicePool(nb, bs, hkv, d, dtype=kv, allocation_order=order)
-    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv == "i8" else None)
+    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv in ("i8", "fp8") else None,
+                     quant_fp8=kv == "fp8")
     cache = PrefixCache(ref)
     rng = np.random.default_rng(9)
     prompt = [int(x) for x in rng.integers(0, 50, size=70)]

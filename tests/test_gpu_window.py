@@ -47,7 +47,8 @@ def _build(specs, hq, hkv, d, bs, kv, chunk=64, seed=3):
     nb = int(sum(-(-n // bs) + 2 for n, _ in specs) + 32)
     order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
     pool = DevicePool(nb, bs, hkv, d, dtype=kv, allocation_order=order)
-    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv == "i8" else None)
+    ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv in ("i8", "fp8") else None,
+                     quant_fp8=kv == "fp8")
     rng = np.random.default_rng(seed + 1)
     io = _io(kv)
     for s, (n, win) in enumerate(specs):
@@ -95,8 +96,8 @@ WINDOW_SPECS = [
 
 
 @pytest.mark.parametrize("kv,hq,hkv,d,bs", [("bf16", 32, 8, 128, 16), ("i8", 32, 8, 128, 16),
-                                            ("bf16", 16, 16, 64, 32)],
-                         ids=["bf16-G4", "i8-G4", "bf16-MHA-bs32"])
+                                            ("fp8", 32, 8, 128, 16), ("bf16", 16, 16, 64, 32)],
+                         ids=["bf16-G4", "i8-G4", "fp8-G4", "bf16-MHA-bs32"])
 def test_windowed_decode(kv, hq, hkv, d, bs):
     log(f"windowed decode {kv}")
     pool, ref, rng = _build(WINDOW_SPECS, hq, hkv, d, bs, kv)
@@ -109,7 +110,7 @@ def test_windowed_decode(kv, hq, hkv, d, bs):
         assert_close(got[i], _want(ref, s, q[i:i + 1], "bf16")[0], *BF16_TOL, what=f"seq {s} {WINDOW_SPECS[s]}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 def test_windowed_decode_and_verify_steps_with_rollback(kv):
     hq, hkv, d, bs = 32, 8, 128, 16
     specs = [(1200, (4, 300)), (600, (0, 100)), (2000, None)]
@@ -177,8 +178,10 @@ PREFILL_SPECS = [
 
 
 @pytest.mark.parametrize("kv,hq,hkv,d,bs", [("bf16", 32, 8, 128, 16), ("i8", 32, 8, 128, 16),
-                                            ("bf16", 16, 16, 64, 32), ("i8", 16, 8, 64, 32)],
-                         ids=["bf16-G4-D128", "i8-G4-D128", "bf16-MHA-D64-bs32", "i8-G2-D64-bs32"])
+                                            ("bf16", 16, 16, 64, 32), ("i8", 16, 8, 64, 32),
+                                            ("fp8", 32, 8, 128, 16), ("fp8", 16, 8, 64, 32)],
+                         ids=["bf16-G4-D128", "i8-G4-D128", "bf16-MHA-D64-bs32", "i8-G2-D64-bs32",
+                              "fp8-G4-D128", "fp8-G2-D64-bs32"])
 def test_windowed_prefill_mfma(kv, hq, hkv, d, bs):
     """Chunked prefill over windowed sequences on the MFMA kernel: sink
     tiles, then the tiles of the rows' windows; released pages are masked."""
