@@ -6,7 +6,10 @@ bookkeeping and slot mapping), store the new K/V rows in their slots and
 upload the plan (one kernel), then decode attention (split-K partial kernel,
 log-sum-exp merge).  Workload: 32 sequences with lengths uniform in [1, 8192], 32 query /
 8 KV heads, head_dim 128, bf16 K/V, block_size 16, a 32768-block pool with
-shuffled block tables, Q/K/V ~ N(0, 1) (seeded, synthetic).
+shuffled block tables, Q/K/V ~ N(0, 1) (seeded, synthetic).  Successive steps
+take the pools of ``--layers`` layers (default 8) in turn, as a model's layers
+do, so a step never finds its pages in the 256 MB last-level cache from the
+step before.
 
 Printed: one JSON line.  ``value`` = decode KV GB/s over whole steps
 (algorithmic bytes: every cached K and V row once, plus Q, O and the block
@@ -66,6 +69,32 @@ def build_pool(wl, kv=None):
             _, s, n, k, v = op
             pool.write(pool.append(s, n), to_device(k, wl.dtype), to_device(v, wl.dtype))
     return pool
+
+
+def build_layers(wl, kv, n_layers):
+    """``n_layers`` pools of ``wl`` (one per model layer): the first replays
+    the workload with its rows, the others replay the same bookkeeping (so
+    the same block tables) and copy the first's pages."""
+    from paged_kv_cache_block_amd import DevicePool
+    import torch
+    first = build_pool(wl, kv)
+    pools = [first]
+    for _ in range(n_layers - 1):
+        p = DevicePool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, dtype=kv or wl.dtype,
+                       allocation_order=wl.allocation_order)
+        for op in wl.ops:
+            if op[0] == "create":
+                p.create(op[1])
+            elif op[0] == "share":
+                p.share(*op[1:])
+            else:
+                p.append(op[1], op[2])
+        p.flush()
+        p.k.copy_(first.k)
+        p.v.copy_(first.v)
+        pools.append(p)
+    torch.cuda.synchronize()
+    return pools
 
 
 def decode_alg_bytes(lengths, wl, kv_dtype=None):
@@ -143,17 +172,23 @@ def percentiles_us(samples_ms):
 
 
 def run_decode(args, kv="bf16", window=None, cold_steps=0):
+    """Decode steps of workload 2 over ``args.layers`` layers' pools taken in
+    turn (a step is one layer's pa_decode_step), so no step finds the pages it
+    reads in a cache from an earlier step, as in a model whose layers each
+    read their own cache once per token."""
     import torch
     from paged_kv_cache_block_amd import abi
     from synth import decode_queries, gqa_decode
 
     wl = gqa_decode()
-    log(f"building the decode workload (32 x U[1,8192], 32/8 heads, d 128, {kv} pages, bs 16"
-        + (f", window {window}" if window else "") + ")")
-    pool = build_pool(wl, kv)
+    n_layers = max(1, args.layers)
+    log(f"building the decode workload (32 x U[1,8192], 32/8 heads, d 128, {kv} pages, bs 16, "
+        f"{n_layers} layers" + (f", window {window}" if window else "") + ")")
+    pools = build_layers(wl, kv, n_layers)
     if window:
-        for s in wl.decode_seqs:
-            pool.set_window(s, *window)
+        for pool in pools:
+            for s in wl.decode_seqs:
+                pool.set_window(s, *window)
     seqs = list(wl.decode_seqs)
     B = len(seqs)
     q = to_device(decode_queries(wl), wl.dtype)
@@ -164,23 +199,25 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     n_new = total_steps + extra_steps + cold_steps
     new_k = torch.randn((n_new, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     new_v = torch.randn((n_new, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
-    lengths = np.array([pool.seq_len(s) for s in seqs], dtype=np.int64)
+    # lengths[l]: the sequence lengths of layer l's pool (each grows by 1 per step of that layer)
+    lengths = [np.array([pool.seq_len(s) for s in seqs], dtype=np.int64) for pool in pools]
     # Workspace for the longest batch this run reaches (lengths grow by 1 a step).
-    ws_need = abi.pa_decode_step_workspace_bytes(pool.handle, seqs, wl.num_heads)
+    ws_need = abi.pa_decode_step_workspace_bytes(pools[0].handle, seqs, wl.num_heads)
     ws = torch.empty(2 * ws_need + (1 << 20), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    handle = pool.handle
     alg = []
 
     def step(i):
-        # append 1 token per sequence + store its K/V + decode, one C call
-        abi.pa_decode_step(handle, seqs, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws.numel(),
+        # append 1 token per sequence + store its K/V + decode, one C call, on layer i % n_layers
+        layer = i % n_layers
+        abi.pa_decode_step(pools[layer].handle, seqs, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws.numel(),
                            stream.cuda_stream)
+        lengths[layer] += 1
+        return window_alg_bytes(lengths[layer], wl, *window) if window else decode_alg_bytes(lengths[layer], wl, kv)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
-        lengths += 1
     torch.cuda.synchronize()
     abi.pa_timing_reset()
     # The decode kernel's duration comes from HIP events that its dispatch
@@ -196,12 +233,9 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
         timed = j % SAMPLE_EVERY == 0
         if timed:
             abi.pa_timing_enable(True)
-        step(i)
+        alg.append(step(i))
         if timed:
             abi.pa_timing_enable(False)
-        lengths += 1
-        alg.append(window_alg_bytes(lengths, wl, *window) if window else decode_alg_bytes(lengths, wl, kv))
-        if timed:
             alg_timed.append(alg[-1])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -209,10 +243,8 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     dec_pct = percentiles_us(abi.pa_timing_samples(abi.PA_KERNEL_DECODE))
     abi.pa_timing_select([abi.PA_KERNEL_MERGE, abi.PA_KERNEL_CACHE])
     abi.pa_timing_enable(True)
-    for i in range(extra_steps):
-        abi.pa_decode_step(handle, seqs, wl.num_heads, new_k[total_steps + i], new_v[total_steps + i], q, out, ws,
-                           ws.numel(), stream.cuda_stream)
-        lengths += 1
+    for i in range(total_steps, total_steps + extra_steps):
+        step(i)
     torch.cuda.synchronize()
     abi.pa_timing_enable(False)
     abi.pa_timing_select(None)
@@ -230,12 +262,9 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
         abi.pa_timing_select([abi.PA_KERNEL_DECODE])
         abi.pa_timing_enable(True)
         cold_alg = []
-        for i in range(cold_steps):
-            torch.sum(flush, dim=0, out=sink[i])
-            abi.pa_decode_step(handle, seqs, wl.num_heads, new_k[total_steps + extra_steps + i],
-                               new_v[total_steps + extra_steps + i], q, out, ws, ws.numel(), stream.cuda_stream)
-            lengths += 1
-            cold_alg.append(window_alg_bytes(lengths, wl, *window) if window else decode_alg_bytes(lengths, wl, kv))
+        for c, i in enumerate(range(total_steps + extra_steps, n_new)):
+            torch.sum(flush, dim=0, out=sink[c])
+            cold_alg.append(step(i))
         torch.cuda.synchronize()
         abi.pa_timing_enable(False)
         abi.pa_timing_select(None)
@@ -247,7 +276,8 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
                         f"({len(samples)} steps)",
                 "decode_kernel_us": round(c_ms * 1e3, 2), **percentiles_us(samples),
                 "GBs": round(c_gbs, 1), "frac": round(c_gbs / HBM_PEAK_GBS, 4)}
-    pool.validate()
+    for pool in pools:
+        pool.validate()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     alg_per_step = float(np.mean(alg))
     kernel_ms = dec_ms / max(dec_n, 1)
@@ -262,7 +292,8 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
         "cache_kernel_us": cache_ms / max(cache_n, 1) * 1e3,
         "kernel_launches": {"decode": dec_n, "merge": mrg_n, "cache": cache_n},
         "decode_kernel_us_pct": dec_pct,
-        "sum_len": int(lengths.sum()),
+        "sum_len": int(lengths[0].sum()),
+        "layers": n_layers,
     }
     if cold:
         result["cold_cache"] = cold
@@ -275,7 +306,8 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
                           "traffic_unit": "GB per launch",
                           "kernel": f"decode_mfma<128,16,1,{ {'i8': 'int8', 'fp8': 'e4m3'}.get(kv, 'bf16')}>",
                           "decode_plus_merge_GBs": round(alg_per_step / ((kernel_ms + merge_ms) * 1e-3) / 1e9, 1)}
-    pool.close()
+    for pool in pools:
+        pool.close()
     return wl, result
 
 
@@ -288,8 +320,9 @@ def run_verify(args, q_len=4):
     from synth import gqa_decode
 
     wl = gqa_decode()
-    log(f"building the verify workload ({q_len} rows per sequence and step)")
-    pool = build_pool(wl)
+    n_layers = max(1, args.layers)
+    log(f"building the verify workload ({q_len} rows per sequence and step, {n_layers} layers)")
+    pools = build_layers(wl, "bf16", n_layers)
     seqs = list(wl.decode_seqs)
     B = len(seqs)
     q_lens = [q_len] * B
@@ -300,13 +333,20 @@ def run_verify(args, q_len=4):
     new_v = torch.randn((total_steps, R, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     q = torch.randn((R, wl.num_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     out = torch.empty_like(q)
-    lengths = np.array([pool.seq_len(s) for s in seqs], dtype=np.int64)
-    need = abi.pa_verify_step_workspace_bytes(pool.handle, seqs, q_lens, wl.num_heads)
+    lengths = [np.array([pool.seq_len(s) for s in seqs], dtype=np.int64) for pool in pools]
+    need = abi.pa_verify_step_workspace_bytes(pools[0].handle, seqs, q_lens, wl.num_heads)
     ws = torch.empty(2 * need + (1 << 20), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        layer = i % n_layers
+        abi.pa_verify_step(pools[layer].handle, seqs, q_lens, wl.num_heads, new_k[i], new_v[i], q, out, ws,
+                           ws.numel(), stream)
+        lengths[layer] += q_len
+        return decode_alg_bytes(lengths[layer], wl) + 2 * (R - B) * wl.num_heads * wl.head_dim * wl.elt_bytes
+
     for i in range(args.warmup):
-        abi.pa_verify_step(pool.handle, seqs, q_lens, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws.numel(), stream)
-        lengths += q_len
+        step(i)
     torch.cuda.synchronize()
     abi.pa_timing_reset()
     abi.pa_timing_select([abi.PA_KERNEL_DECODE])
@@ -316,18 +356,17 @@ def run_verify(args, q_len=4):
         timed = j % SAMPLE_EVERY == 0
         if timed:
             abi.pa_timing_enable(True)
-        abi.pa_verify_step(pool.handle, seqs, q_lens, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws.numel(), stream)
+        a = step(i)
         if timed:
             abi.pa_timing_enable(False)
-        lengths += q_len
-        if timed:
-            alg.append(decode_alg_bytes(lengths, wl) + 2 * (R - B) * wl.num_heads * wl.head_dim * wl.elt_bytes)
+            alg.append(a)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     abi.pa_timing_select(None)
     dec_ms, dec_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
-    pool.validate()
-    pool.close()
+    for pool in pools:
+        pool.validate()
+        pool.close()
     ms = (t1 - t0) * 1e3 / args.steps
     kernel_ms = dec_ms / max(dec_n, 1)
     return {"workload": f"gqa_decode with {q_len} query rows per sequence and step (pa_verify_step: "
@@ -510,6 +549,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=8,
+                    help="decode / verify steps take this many layers' pools in turn (one layer per step)")
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
@@ -561,8 +602,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "gqa_decode: 32 seqs, lengths U[1,8192] (seed 1), 32 query / 8 KV heads, "
-                               "head_dim 128, bf16 K/V, block_size 16, 32768-block pool, one layer; "
-                               "step = pa_decode_step: append 1 token/seq + store its K/V + decode",
+                               "head_dim 128, bf16 K/V, block_size 16, 32768-block pool per layer; "
+                               "step = one layer's pa_decode_step (append 1 token/seq + store its K/V + "
+                               f"decode), {args.layers} layers' pools taken in turn so no step re-reads "
+                               "pages an earlier step left in a cache",
                    "global_batch": 32, "seq_len": "U[1,8192]", "parallelism": "single GPU"},
         "tokens_per_s": round(dec["tokens_per_s"], 1),
         "hbm_frac_step": round(dec["value"] / HBM_PEAK_GBS, 4),

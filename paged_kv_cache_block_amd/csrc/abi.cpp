@@ -141,26 +141,37 @@ struct pa_pool {
 
   // Copy `bytes` of host data into the next pinned staging buffer and return
   // its device address; the buffer is reused only after the event recorded
-  // behind its previous use (staged_done) has fired.
+  // behind its previous use (staged_done) has fired.  When a buffer has to
+  // grow, every idle buffer of the ring grows with it, so that pinned
+  // allocations happen on the first calls and not later, one call at a time.
   pa_status stage(const void* src, size_t bytes, const void** dev_copy) {
     Staging& st = ring[next];
     if (st.pending) {
       PA_HIP(hipEventSynchronize(st.ev));
       st.pending = false;
     }
-    if (!st.ev) PA_HIP(hipEventCreateWithFlags(&st.ev, hipEventDisableTiming));
     const size_t padded = pa::align_up(bytes, 16);
     if (st.cap < padded) {
-      if (st.host) PA_HIP(hipHostFree(st.host));
-      st.host = st.dev = nullptr;
-      st.cap = 0;
-      size_t cap = pa::align_up(std::max<size_t>(padded + padded / 2, 1 << 16), 16);
-      PA_HIP(hipHostMalloc(&st.host, cap, hipHostMallocDefault));
-      PA_HIP(hipHostGetDevicePointer(&st.dev, st.host, 0));
-      st.cap = cap;
+      const size_t cap = pa::align_up(std::max<size_t>(padded + padded / 2, 1 << 16), 16);
+      for (Staging& b : ring) {
+        if (&b != &st && (b.pending || b.cap >= padded)) continue;
+        const pa_status r = grow(b, cap);
+        if (r != PA_OK) return r;
+      }
     }
     std::memcpy(st.host, src, bytes);
     *dev_copy = st.dev;
+    return ok();
+  }
+
+  pa_status grow(Staging& b, size_t cap) {
+    if (!b.ev) PA_HIP(hipEventCreateWithFlags(&b.ev, hipEventDisableTiming));
+    if (b.host) PA_HIP(hipHostFree(b.host));
+    b.host = b.dev = nullptr;
+    b.cap = 0;
+    PA_HIP(hipHostMalloc(&b.host, cap, hipHostMallocDefault));
+    PA_HIP(hipHostGetDevicePointer(&b.dev, b.host, 0));
+    b.cap = cap;
     return ok();
   }
 
