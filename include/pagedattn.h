@@ -42,12 +42,19 @@
  *     the last error on the calling thread is returned by pa_last_error().
  *   - A pool is not thread-safe.
  *
- * Device layouts (row-major, element size 4 for PA_DTYPE_F32, 2 for BF16):
- *   K pool  [num_blocks][num_kv_heads][block_size][head_dim]
+ * Device layouts (element size 4 for PA_DTYPE_F32, 2 for BF16):
+ *   K pool  [num_blocks][num_kv_heads][page of block_size * head_dim values]
  *   V pool  [num_blocks][num_kv_heads][head_dim][block_size]
- *   (one (block, KV head) page of K is block_size rows of head_dim values;
- *    the same page of V is stored transposed, head_dim rows of block_size
- *    tokens, so that the P.V contraction over tokens reads contiguous memory.)
+ *   (one (block, KV head) page of V is stored transposed, head_dim rows of
+ *    block_size tokens, so that the P.V contraction over tokens reads
+ *    contiguous memory.)  A K page of PA_DTYPE_F32, or of BF16 with
+ *   block_size % 16 != 0 or head_dim % 32 != 0, is row-major
+ *   [block_size][head_dim].  Other BF16 K pages are in the order of the
+ *   decode kernel's operands: in each 16-token tile, the 8 values
+ *   d = 32 j + 8 grp .. +7 of token t sit at element
+ *     (t / 16) * 16 * head_dim + (j * 64 + grp * 16 + t % 16) * 8 + d % 8,
+ *   so one 64-lane load of 16 bytes per lane reads 1 KB of consecutive
+ *   memory.
  *   Both pools must be 16-byte aligned.  The layout is a physical choice:
  *   the logical K/V row of token p of a sequence is the slot
  *   table[p / block_size] * block_size + p % block_size ([KVPool]
@@ -67,14 +74,21 @@
  * x / scale rounded to nearest, ties to even, clipped to [-127, 127]; the
  * stored scale is that float64 value rounded to fp32.  Requires block_size
  * and head_dim to be multiples of 16.  One page (block, KV head) of either
- * pool is page_bytes = block_size * head_dim + 4 * block_size bytes:
- *   K page  codes [block_size][head_dim] row-major, then scales [block_size]
- *   V page  codes in MFMA operand order, then scales [block_size]: the code
- *           of token t, dim d sits at byte
- *             (t / 16) * 16 * head_dim + ((t % 16) / 4 * 16 + d % 16) *
- *             (head_dim / 4) + (d / 16) * 4 + t % 4
- *           (per 16-token tile: for every group of 4 tokens and every d % 16,
- *           the head_dim / 16 runs of 4 tokens are contiguous).
+ * pool is page_bytes = block_size * head_dim + 4 * block_size bytes, the
+ * codes (block_size * head_dim bytes, in 16-token tiles of 16 * head_dim
+ * bytes) then the block_size fp32 scales:
+ *   K codes  with head_dim % 64 == 0: with span = head_dim / 4, the code of
+ *            token t, dim d (grp = d / span, c = d % span) sits at byte
+ *              (t / 16) * 16 * head_dim + ((c / 16) * 64 + grp * 16 + t % 16)
+ *              * 16 + c % 16;
+ *            other head_dims: row-major [block_size][head_dim].
+ *   V codes  MFMA operand order: in each 16-token tile, row r = (t % 16) / 4
+ *            * 16 + d % 16 holds head_dim / 4 codes, byte c = (d / 16) * 4 +
+ *            t % 4 of the row; with head_dim % 64 == 0 the code sits at
+ *              (t / 16) * 16 * head_dim + ((c / 16) * 64 + r) * 16 + c % 16,
+ *            otherwise at (t / 16) * 16 * head_dim + r * (head_dim / 4) + c.
+ *   Either way one 64-lane load of 16 bytes per lane reads 1 KB of
+ *   consecutive codes in the decode kernel's operand order.
  *   pool bytes = num_blocks * num_kv_heads * page_bytes (each of K, V).
  *
  * PA_DTYPE_FP8 pools hold the same rows and pages with 8-bit float codes

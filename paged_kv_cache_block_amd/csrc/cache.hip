@@ -39,9 +39,17 @@ __global__ __launch_bounds__(256) void copy_blocks_2(uint16_t* __restrict__ k_po
     pool[dst * words_per_block + w] = pool[src * words_per_block + w];
 }
 
-// One thread per (row i, head h, element d).  K rows are contiguous in d; the
-// V page is stored transposed ([head_dim][block_size]), so V writes stride
-// by block_size.
+// Element offset of K (token t of the page, dim d): bf16 pages in the
+// decode kernel's operand order where the shape allows it, fp32 row-major.
+template <typename T>
+__device__ __forceinline__ int64_t k_offset(int t, int d, int dim, int bs) {
+  if constexpr (sizeof(T) == 2) return k16_offset(t, d, dim, bs);
+  else return static_cast<int64_t>(t) * dim + d;
+}
+
+// One thread per (row i, head h, element d).  K elements go to their place
+// in the page order above; the V page is stored transposed ([head_dim]
+// [block_size]), so V writes stride by block_size.
 template <typename T>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     T* __restrict__ k_pool, T* __restrict__ v_pool, const T* __restrict__ k_new,
@@ -58,7 +66,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     if (slot < 0 || slot >= num_slots) continue;
     const int64_t blk = slot / bs, off = slot - blk * bs;
     const int64_t page = (blk * hkv + h) * bs * dim;
-    k_pool[page + off * dim + d] = k_new[e];
+    k_pool[page + k_offset<T>(static_cast<int>(off), static_cast<int>(d), dim, bs)] = k_new[e];
     v_pool[page + d * bs + off] = v_new[e];
   }
 }
@@ -122,8 +130,8 @@ __device__ __forceinline__ double row_scale(float absmax) {
   else return q8_scale(absmax);
 }
 
-// One wave quantises one (row, head): K codes row-major, V codes in operand
-// order, then the two fp32 scales.  D <= 512 (8 values per lane).
+// One wave quantises one (row, head): K and V codes at their places in the
+// page order (k8_offset, q8_v_offset), then the two fp32 scales.  D <= 512 (8 values per lane).
 template <int Q8>
 __device__ __forceinline__ void q8_store_row_head(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_row,
                                                   const uint16_t* v_row, int64_t blk, int32_t off,
@@ -148,7 +156,7 @@ __device__ __forceinline__ void q8_store_row_head(uint8_t* k_pool, uint8_t* v_po
   for (int k = 0; k < 8; ++k) {
     const int d = lane + 64 * k;
     if (d < dim) {
-      kp[static_cast<size_t>(off) * dim + d] = row_code<Q8>(kx[k], ks);
+      kp[k8_offset(off, d, dim)] = row_code<Q8>(kx[k], ks);
       vp[q8_v_offset(off, d, dim)] = row_code<Q8>(vx[k], vs);
     }
   }
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(256) void step_prep_kernel(
     if (slot < 0 || slot >= num_slots) continue;
     const int64_t blk = slot / bs, off = slot - blk * bs;
     const int64_t page = (blk * hkv + h) * bs * dim;
-    k_pool[page + off * dim + d] = k_new[e];
+    k_pool[page + k_offset<T>(static_cast<int>(off), static_cast<int>(d), dim, bs)] = k_new[e];
     v_pool[page + d * bs + off] = v_new[e];
   }
 }

@@ -125,12 +125,15 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
       float dot = 0.f;
       if constexpr (Q8) {
         const uint8_t* kp = static_cast<const uint8_t*>(a.k_pool) + (static_cast<size_t>(blk) * Hkv + g) * q8_page;
-        const uint8_t* kr = kp + off * D;
-        for (int d = 0; d < D; ++d) dot += qs[d] * code_value<Q8>(kr[d]);
+        for (int d = 0; d < D; ++d) dot += qs[d] * code_value<Q8>(kp[k8_offset(off, d, D)]);
         dot *= reinterpret_cast<const float*>(kp + BS * D)[off];
       } else {
-        const T* kr = K + ((static_cast<size_t>(blk) * Hkv + g) * BS + off) * D;
-        for (int d = 0; d < D; ++d) dot += qs[d] * Elt<T>::load(kr + d);
+        const T* kp = K + (static_cast<size_t>(blk) * Hkv + g) * BS * D;
+        if constexpr (sizeof(T) == 2) {
+          for (int d = 0; d < D; ++d) dot += qs[d] * Elt<T>::load(kp + k16_offset(off, d, D, BS));
+        } else {
+          for (int d = 0; d < D; ++d) dot += qs[d] * Elt<T>::load(kp + off * D + d);
+        }
       }
       s = dot * a.scale_log2;
     }
@@ -313,19 +316,27 @@ void decode_mfma(DecodeArgs a) {
   auto load_page_blk = [&](int blk, Page& P) {
     const char* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
     const char* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
+    // Every page byte is read once per launch: all page loads carry the
+    // non-temporal (streaming) hint.  K pages (and 8-bit V pages) are in the
+    // page order of k16_offset / k8_offset / q8_v_offset, so each load
+    // instruction reads 1 KB of consecutive bytes (lane l: bytes 16l ..
+    // 16l + 15 of a 1 KB run), already in operand order.
     if constexpr (Q8) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const uint4* ks = reinterpret_cast<const uint4*>(kp + (16 * tt + n) * D + (D / 4) * grp);
-        const uint4* vs = reinterpret_cast<const uint4*>(vp + 16 * tt * D + (16 * grp + n) * (D / 4));
+        const u32x4* ks = reinterpret_cast<const u32x4*>(kp + 16 * tt * D) + lane;
+        const u32x4* vs = reinterpret_cast<const u32x4*>(vp + 16 * tt * D) + lane;
 #pragma unroll
         for (int w = 0; w < DT / 4; ++w) {
-          const uint4 x = ks[w], y = vs[w];
-          P.kc[tt][4 * w] = x.x; P.kc[tt][4 * w + 1] = x.y; P.kc[tt][4 * w + 2] = x.z; P.kc[tt][4 * w + 3] = x.w;
-          P.vc[tt][4 * w] = y.x; P.vc[tt][4 * w + 1] = y.y; P.vc[tt][4 * w + 2] = y.z; P.vc[tt][4 * w + 3] = y.w;
+          const u32x4 x = __builtin_nontemporal_load(ks + 64 * w), y = __builtin_nontemporal_load(vs + 64 * w);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            P.kc[tt][4 * w + i] = x[i];
+            P.vc[tt][4 * w + i] = y[i];
+          }
         }
-        P.ks[tt] = *reinterpret_cast<const f32x4*>(kp + BS * D + 4 * (16 * tt + 4 * grp));
-        P.vs[tt] = *reinterpret_cast<const f32x4*>(vp + BS * D + 4 * (16 * tt + 4 * grp));
+        P.ks[tt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kp + BS * D + 4 * (16 * tt + 4 * grp)));
+        P.vs[tt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vp + BS * D + 4 * (16 * tt + 4 * grp)));
       }
     } else {
       const uint16_t* k16 = reinterpret_cast<const uint16_t*>(kp);
@@ -334,11 +345,8 @@ void decode_mfma(DecodeArgs a) {
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int j = 0; j < KS; ++j)
-          P.k[tt][j] = *reinterpret_cast<const bf16x8*>(k16 + (16 * tt + n) * D + 32 * j + 8 * grp);
-      // V pages are loaded with the non-temporal (streaming) hint and K
-      // pages without: measured on bf16 pages, the mix streams 7-22% faster
-      // than either policy for both (6.5 vs 5.4 TB/s at 540 MB per launch).
-      // On 8-bit pages the hint is slower and is not used.
+          P.k[tt][j] = __builtin_nontemporal_load(
+              reinterpret_cast<const bf16x8*>(k16 + 16 * tt * D + (64 * j + lane) * 8));
 #pragma unroll
       for (int nt = 0; nt < DT; ++nt)
 #pragma unroll

@@ -75,11 +75,44 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Byte offset of the code of token t (within its block), dim d, inside an
-// int8 V page of head_dim D: each 16-token tile of a page is stored in the
-// operand order of the P.V MFMA, so that one lane's codes are contiguous.
+// Page layouts (offsets inside one (block, KV head) page; t = token within
+// the block).  Each 16-token tile of a page is stored so that one wave load
+// instruction of the decode kernel (64 lanes x 16 bytes) reads 1 KB of
+// consecutive bytes, already in the MFMA operand order:
+//
+// bf16 K pages (block_size % 16 == 0, head_dim % 32 == 0): the 8 values
+//   d = 32j + 8grp .. +7 of token t sit at element
+//   (t / 16) * 16 D + ((j * 64 + grp * 16 + t % 16) * 8); other shapes are
+//   row-major [block_size][head_dim].
+__device__ __forceinline__ int k16_offset(int t, int d, int D, int BS) {
+  if ((BS & 15) == 0 && (D & 31) == 0)
+    return (t >> 4) * 16 * D + ((((d >> 5) * 64 + ((d & 31) >> 3) * 16 + (t & 15)) << 3) | (d & 7));
+  return t * D + d;
+}
+
+// 8-bit K pages (head_dim % 64 == 0): lane grp of the QK contraction owns
+//   d in [grp * D/4, +D/4); its 16-byte chunk w (d = grp * D/4 + 16w .. +15)
+//   of token t sits at byte (t / 16) * 16 D + (w * 64 + grp * 16 + t % 16) * 16.
+//   Other head_dims: row-major [block_size][head_dim].
+__device__ __forceinline__ int k8_offset(int t, int d, int D) {
+  if ((D & 63) == 0) {
+    const int span = D >> 2;
+    const int grp = d / span, c = d - grp * span;
+    return (t >> 4) * 16 * D + ((((c >> 4) * 64 + grp * 16 + (t & 15)) << 4) | (c & 15));
+  }
+  return t * D + d;
+}
+
+// 8-bit V pages: the operand order of the P.V MFMA.  Within a 16-token tile,
+//   row r = (t % 16) / 4 * 16 + d % 16 holds D/4 codes, byte c = (d / 16) * 4 +
+//   t % 4 of the row; with head_dim % 64 == 0 chunk w = c / 16 of every row
+//   sits at (w * 64 + r) * 16 + c % 16, otherwise rows are consecutive
+//   (r * D/4 + c).
 __device__ __forceinline__ int q8_v_offset(int t, int d, int D) {
-  return (t >> 4) * 16 * D + (((t & 15) >> 2) * 16 + (d & 15)) * (D >> 2) + (d >> 4) * 4 + (t & 3);
+  const int r = ((t & 15) >> 2) * 16 + (d & 15);
+  const int c = (d >> 4) * 4 + (t & 3);
+  if ((D & 63) == 0) return (t >> 4) * 16 * D + ((((c >> 4) * 64 + r) << 4) | (c & 15));
+  return (t >> 4) * 16 * D + r * (D >> 2) + c;
 }
 
 // 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       const int tt = blkid / KS, j = blkid - tt * KS;
       const int tok = 8 * (n >> 2) + 4 * tt + (n & 3);
       blk_pgi[r] = tok / BS;
-      blk_off[r] = (tok % BS) * D + 32 * j + 8 * grp;
+      blk_off[r] = k16_offset(tok % BS, 32 * j + 8 * grp, D, BS);
     } else {
       const int nt = blkid - KB;
       const int tok = 8 * grp;
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
         const int pgi = tok / BS;
         const int blk = pgi ? ent[PAGES - 1] : ent[0];
         if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L && blk >= 0)
-          src = kpool + (static_cast<size_t>(blk) * Hkv + g) * page + (tok % BS) * D + 32 * j + 8 * grp;
+          src = kpool + (static_cast<size_t>(blk) * Hkv + g) * page + k16_offset(tok % BS, 32 * j + 8 * grp, D, BS);
       } else {
         const int nt = blkid - KB;
         const int tok = 8 * grp;
@@ -317,19 +317,24 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       const bool isv = wave >= kHalf;
       const int o0 = (isv ? wave - kHalf : wave) * 1024;  // wave's first byte in the region
       const int P = o0 / 16 + lane;                        // 16-byte chunk this lane fills
-      int tok0, within;  // first token of the chunk's page row / subtile, byte in it
+      // The chunk's token (K) or first token of its 16-token subtile (V),
+      // and its byte offset in the page (page order: k8_offset,
+      // q8_v_offset; a 16-byte chunk is 16 consecutive codes of one K row
+      // or of one V operand row).
+      int tok0, at;
       if (!isv) {
         tok0 = P / kRowChunks;
-        within = 16 * ((P % kRowChunks) ^ q8_k_swizzle(tok0));
+        at = k8_offset(tok0 % BS, 16 * ((P % kRowChunks) ^ q8_k_swizzle(tok0)), D);
       } else {
         tok0 = 16 * (P / D);
-        within = 16 * q8_v_swizzle(P % D);
+        const int q = q8_v_swizzle(P % D);  // chunk q of the subtile: row q / (D/64), part q % (D/64)
+        at = (tok0 % BS) * D + 16 * ((q % kRowChunksV) * 64 + q / kRowChunksV);
       }
       const int pgi = tok0 / BS;
       const int blk = pgi ? ent[PAGES - 1] : ent[0];
       const void* src = a.zeros;
       if (blk >= 0)
-        src = (isv ? vq : kq) + (static_cast<size_t>(blk) * Hkv + g) * q8_page + (tok0 % BS) * D + within;
+        src = (isv ? vq : kq) + (static_cast<size_t>(blk) * Hkv + g) * q8_page + at;
       __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(dst + (isv ? kTile * D : 0) + o0), 16, 0, 0);
     }
     if (wave == 0 && lane < 16) {

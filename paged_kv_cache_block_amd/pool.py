@@ -27,7 +27,11 @@ class DevicePool:
     ``dtype`` is "bf16", "f32", "i8" or "fp8" (int8 or E4M3 codes with one
     fp32 scale per (token, KV head) row; queries, outputs and new rows are
     then bf16, and ``k`` / ``v`` are raw byte tensors ``[num_blocks,
-    num_kv_heads, page_bytes]`` in the library's 8-bit page layout).
+    num_kv_heads, page_bytes]`` in the library's 8-bit page layout).  bf16
+    ``k`` is ``[num_blocks, num_kv_heads, block_size * head_dim]`` in the
+    library's K page order, fp32 ``k`` ``[num_blocks, num_kv_heads,
+    block_size, head_dim]``; ``v`` of both is ``[num_blocks, num_kv_heads,
+    head_dim, block_size]``.
     With ``metadata_only=True`` no device memory is allocated and only the
     bookkeeping calls work (usable on a machine without a GPU).
     """
@@ -49,7 +53,8 @@ class DevicePool:
                 tdt = torch.uint8
             else:
                 tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-                shape_k = (num_blocks, num_kv_heads, block_size, head_dim)
+                shape_k = ((num_blocks, num_kv_heads, block_size * head_dim) if dtype == "bf16"
+                           else (num_blocks, num_kv_heads, block_size, head_dim))
                 shape_v = (num_blocks, num_kv_heads, head_dim, block_size)
             self.k = torch.zeros(shape_k, dtype=tdt, device=device)
             self.v = torch.zeros(shape_v, dtype=tdt, device=device)

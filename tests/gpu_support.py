@@ -18,6 +18,50 @@ def log(msg):
     sys.stdout.flush()
 
 
+# ------------------------------------------------------------ page layouts
+# The byte / element places of a page's values as the C header documents
+# them, written out here from that text (the tests read device pages
+# through these, independently of the library's own index code).
+def k16_index(bs, d):
+    """[bs, d] element offsets of a bf16 K page: with bs % 16 == 0 and
+    d % 32 == 0, values d' = 32j + 8grp .. +7 of token t sit at
+    (t // 16) * 16 d + (j * 64 + grp * 16 + t % 16) * 8 (+ d' % 8); other
+    shapes are row-major."""
+    t = np.arange(bs)[:, None]
+    j = np.arange(d)[None, :]
+    if bs % 16 or d % 32:
+        return t * d + j
+    return (t // 16) * 16 * d + ((j // 32) * 64 + (j % 32) // 8 * 16 + t % 16) * 8 + j % 8
+
+
+def k8_index(bs, d):
+    """[bs, d] byte offsets of the K codes of an 8-bit page: with d % 64 ==
+    0, lane span s = d / 4, grp = d' // s, c = d' % s, chunk w = c // 16:
+    (t // 16) * 16 d + (w * 64 + grp * 16 + t % 16) * 16 + c % 16;
+    otherwise row-major."""
+    t = np.arange(bs)[:, None]
+    j = np.arange(d)[None, :]
+    if d % 64:
+        return t * d + j
+    span = d // 4
+    grp, c = j // span, j % span
+    return (t // 16) * 16 * d + ((c // 16) * 64 + grp * 16 + t % 16) * 16 + c % 16
+
+
+def v8_index(bs, d):
+    """[bs, d] byte offsets of the V codes of an 8-bit page: row r = (t % 16)
+    // 4 * 16 + d' % 16, byte c = (d' // 16) * 4 + t % 4 of the row; with
+    d % 64 == 0 at (t // 16) * 16 d + ((c // 16) * 64 + r) * 16 + c % 16,
+    otherwise at (t // 16) * 16 d + r * d / 4 + c."""
+    t = np.arange(bs)[:, None]
+    j = np.arange(d)[None, :]
+    r = (t % 16) // 4 * 16 + j % 16
+    c = (j // 16) * 4 + t % 4
+    if d % 64:
+        return (t // 16) * 16 * d + r * (d // 4) + c
+    return (t // 16) * 16 * d + ((c // 16) * 64 + r) * 16 + c % 16
+
+
 def to_device(arr, dtype):
     import torch
     if dtype == "bf16":

@@ -18,7 +18,7 @@ from synth import (append_stream, decode_queries, gqa_decode, heavy_tail, logica
 from synth.workloads import Workload, bf16_round, to_f64
 
 from gpu_support import (BF16_TOL, F32_TOL, assert_close, build_device_pool, expected_decode, log,
-                         to_device, to_host_f64, tol)
+                         to_device, to_host_f64, tol, k16_index)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,12 +35,14 @@ def _gpu():
 
 def _gather_pool_rows(pool, seq, length):
     """Live K/V rows of ``seq`` read back from the device pools through the
-    documented layout (K [N][Hkv][bs][D], V [N][Hkv][D][bs])."""
+    documented layout (K pages: fp32 row-major [bs][D], bf16 in the page
+    order of ``k16_index``; V pages [D][bs])."""
     table = pool.block_table(seq)
-    k = pool.k.float().cpu().numpy()
+    bs, d = pool.block_size, pool.head_dim
+    k = pool.k.float().cpu().numpy().reshape(pool.num_blocks, pool.num_kv_heads, bs * d)
     v = pool.v.float().cpu().numpy()
-    bs = pool.block_size
-    K = np.stack([k[table[p // bs], :, p % bs, :] for p in range(length)])
+    kidx = k16_index(bs, d) if pool.dtype == "bf16" else np.arange(bs * d).reshape(bs, d)
+    K = np.stack([k[table[p // bs]][:, kidx[p % bs]] for p in range(length)])
     V = np.stack([v[table[p // bs], :, :, p % bs] for p in range(length)])
     return K, V
 
@@ -438,3 +440,28 @@ def test_prefix_prefill_full_size_sampled_rows():
             vis = L - 512 + t + 1
             exp = oracle.attention(to_f64(qp[r:r + 1], wl.dtype), K[:vis], V[:vis])[0]
             assert_close(out[r], exp, *BF16_TOL, what=f"seq {s} row {t}")
+
+
+@pytest.mark.parametrize("bs,d", [(16, 128), (32, 64), (16, 64), (8, 128), (16, 48), (128, 128)])
+def test_bf16_pages_hold_rows_at_documented_places(bs, d):
+    """pa_reshape_and_cache and the step prologue put every K value where the
+    header's page order says (reordered tiles for bs % 16 == 0 and d % 32 ==
+    0, row-major otherwise) and every V value at [d][slot]."""
+    from paged_kv_cache_block_amd import DevicePool
+    hkv, nb = 2, 12
+    pool = DevicePool(nb, bs, hkv, d, dtype="bf16", allocation_order=np.random.default_rng(bs + d).permutation(nb))
+    gen = torch.Generator(device="cuda").manual_seed(bs * d)
+    n0 = 3 * bs + 5
+    k = torch.randn(n0, hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(n0, hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    pool.create(0)
+    pool.write(pool.append(0, n0), k, v)
+    # One decode step appends and stores a row through the fused prologue.
+    kn = torch.randn(1, hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(1, hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    q = torch.randn(1, 2 * hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    pool.decode_step([0], kn, vn, q)
+    torch.cuda.synchronize()
+    K, V = _gather_pool_rows(pool, 0, n0 + 1)
+    np.testing.assert_array_equal(K, torch.cat([k, kn]).float().cpu().numpy())
+    np.testing.assert_array_equal(V, torch.cat([v, vn]).float().cpu().numpy())

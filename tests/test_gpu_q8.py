@@ -20,7 +20,7 @@ import oracle
 from synth import append_stream, decode_queries, gqa_decode, logical_kv, prefill_queries, prefix_prefill
 from synth.workloads import Workload, bf16_round, to_f64
 
-from gpu_support import BF16_TOL, assert_close, log, to_device, to_host_f64
+from gpu_support import BF16_TOL, assert_close, k8_index, log, to_device, to_host_f64, v8_index
 
 pytestmark = pytest.mark.gpu
 
@@ -39,14 +39,6 @@ KINDS = ["i8", "fp8"]
 
 
 # ------------------------------------------------------------ helpers
-def _v_index(bs, d):
-    """Byte of the code of (token t, dim j) in an int8 V page, as the header
-    documents it: (t/16)*16*D + ((t%16)/4*16 + j%16)*(D/4) + (j/16)*4 + t%4."""
-    t = np.arange(bs)[:, None]
-    j = np.arange(d)[None, :]
-    return (t // 16) * 16 * d + ((t % 16) // 4 * 16 + j % 16) * (d // 4) + (j // 16) * 4 + t % 4
-
-
 def _device_codes(pool):
     """(K codes, K scales, V codes, V scales) of the whole device pool, in the
     oracle's [block][slot][head][dim] order (views where possible); int8
@@ -61,8 +53,8 @@ def _device_codes(pool):
 
     kcodes, kscales = split(pool.k.cpu().numpy())
     vcodes, vscales = split(pool.v.cpu().numpy())
-    kc = kcodes.reshape(kcodes.shape[0], kcodes.shape[1], bs, d).transpose(0, 2, 1, 3)
-    vc = vcodes[..., _v_index(bs, d)].transpose(0, 2, 1, 3)
+    kc = kcodes[..., k8_index(bs, d)].transpose(0, 2, 1, 3)
+    vc = vcodes[..., v8_index(bs, d)].transpose(0, 2, 1, 3)
     return kc, kscales, vc, vscales
 
 
@@ -237,11 +229,11 @@ def test_q8_unused_slots_hold_garbage(kind):
         blk = ref.tables[s][-1]
         for raw in (pool.k, pool.v):
             raw[blk, :, bs * d:].view(torch.float32)[:, n % bs:] = float("nan")
-        pool.k[blk, :, (n % bs) * d:bs * d] = 0x7F
+        # K codes of the past-end slots (for E4M3 not-a-number), and for
+        # E4M3 the V codes too, at their documented bytes.
+        pool.k[blk, :, torch.as_tensor(k8_index(bs, d)[n % bs:].ravel(), device="cuda")] = 0x7F
         if kind == "fp8":
-            # V codes of the past-end slots, at the operand-order bytes.
-            idx = torch.as_tensor(_v_index(bs, d)[n % bs:].ravel(), device="cuda")
-            pool.v[blk, :, idx] = 0xFF
+            pool.v[blk, :, torch.as_tensor(v8_index(bs, d)[n % bs:].ravel(), device="cuda")] = 0xFF
     got = to_host_f64(pool.decode([0, 1, 2], to_device(q_bits, "bf16")))
     for i in range(3):
         assert_close(got[i], want[i], *BF16_TOL, what=f"decode seq {i}")
