@@ -206,14 +206,21 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     ws = torch.empty(2 * ws_need + (1 << 20), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     alg = []
+    seq_arr = np.asarray(seqs, dtype=np.int64)
+    handles = [pool.handle for pool in pools]
+    ws_n = ws.numel()
 
     def step(i):
-        # append 1 token per sequence + store its K/V + decode, one C call, on layer i % n_layers
+        # append 1 token per sequence + store its K/V + decode, one C call, on layer i % n_layers;
+        # returns the lengths the call decoded over (its bytes are counted after the timed loop)
         layer = i % n_layers
-        abi.pa_decode_step(pools[layer].handle, seqs, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws.numel(),
+        abi.pa_decode_step(handles[layer], seq_arr, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws_n,
                            stream.cuda_stream)
         lengths[layer] += 1
-        return window_alg_bytes(lengths[layer], wl, *window) if window else decode_alg_bytes(lengths[layer], wl, kv)
+        return lengths[layer].copy()
+
+    def step_bytes(lens):
+        return window_alg_bytes(lens, wl, *window) if window else decode_alg_bytes(lens, wl, kv)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -229,16 +236,21 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     alg_timed = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    host_ms = []  # host time of each timed call (the call returns before its kernels finish)
     for j, i in enumerate(range(args.warmup, total_steps)):
         timed = j % SAMPLE_EVERY == 0
         if timed:
             abi.pa_timing_enable(True)
+        h0 = time.perf_counter()
         alg.append(step(i))
+        host_ms.append((time.perf_counter() - h0) * 1e3)
         if timed:
             abi.pa_timing_enable(False)
             alg_timed.append(alg[-1])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    alg = [step_bytes(x) for x in alg]
+    alg_timed = [step_bytes(x) for x in alg_timed]
     dec_ms, dec_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
     dec_pct = percentiles_us(abi.pa_timing_samples(abi.PA_KERNEL_DECODE))
     abi.pa_timing_select([abi.PA_KERNEL_MERGE, abi.PA_KERNEL_CACHE])
@@ -264,7 +276,7 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
         cold_alg = []
         for c, i in enumerate(range(total_steps + extra_steps, n_new)):
             torch.sum(flush, dim=0, out=sink[c])
-            cold_alg.append(step(i))
+            cold_alg.append(step_bytes(step(i)))
         torch.cuda.synchronize()
         abi.pa_timing_enable(False)
         abi.pa_timing_select(None)
@@ -294,6 +306,8 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
         "decode_kernel_us_pct": dec_pct,
         "sum_len": int(lengths[0].sum()),
         "layers": n_layers,
+        "host_call_ms": {"p50": round(float(np.median(host_ms)), 4), "max": round(float(np.max(host_ms)), 3),
+                         "max_at_step": int(np.argmax(host_ms))},
     }
     if cold:
         result["cold_cache"] = cold
@@ -338,12 +352,20 @@ def run_verify(args, q_len=4):
     ws = torch.empty(2 * need + (1 << 20), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
 
+    seq_arr = np.asarray(seqs, dtype=np.int64)
+    ql_arr = np.asarray(q_lens, dtype=np.int32)
+    handles = [pool.handle for pool in pools]
+    ws_n = ws.numel()
+
     def step(i):
         layer = i % n_layers
-        abi.pa_verify_step(pools[layer].handle, seqs, q_lens, wl.num_heads, new_k[i], new_v[i], q, out, ws,
-                           ws.numel(), stream)
+        abi.pa_verify_step(handles[layer], seq_arr, ql_arr, wl.num_heads, new_k[i], new_v[i], q, out, ws, ws_n,
+                           stream)
         lengths[layer] += q_len
-        return decode_alg_bytes(lengths[layer], wl) + 2 * (R - B) * wl.num_heads * wl.head_dim * wl.elt_bytes
+        return lengths[layer].copy()
+
+    def step_bytes(lens):
+        return decode_alg_bytes(lens, wl) + 2 * (R - B) * wl.num_heads * wl.head_dim * wl.elt_bytes
 
     for i in range(args.warmup):
         step(i)
@@ -373,7 +395,7 @@ def run_verify(args, q_len=4):
                         f"append {q_len} tokens + store their K/V + causal attention)",
             "ms_per_step": round(ms, 5), "rows_per_s": round(R / (ms * 1e-3), 1),
             "decode_kernel_us": round(kernel_ms * 1e3, 2),
-            "kernel_GBs": round(float(np.mean(alg)) / (kernel_ms * 1e-3) / 1e9, 1)}
+            "kernel_GBs": round(float(np.mean([step_bytes(x) for x in alg])) / (kernel_ms * 1e-3) / 1e9, 1)}
 
 
 def run_decode_only(args, name):
@@ -611,7 +633,7 @@ def main():
         "hbm_frac_step": round(dec["value"] / HBM_PEAK_GBS, 4),
         "decode": {k: dec[k] for k in ("decode_kernel_us", "decode_kernel_us_pct", "merge_kernel_us",
                                         "cache_kernel_us", "alg_bytes_per_step", "kernel_launches", "sum_len",
-                                        "cold_cache") if k in dec},
+                                        "host_call_ms", "cold_cache") if k in dec},
         "roofline": dec["roofline"],
         "device_copy_GBs": device_copy_gbs(),
     }
@@ -628,7 +650,7 @@ def main():
             "kv_GBs_step": round(q8["value"], 2),
             "decode": {k: q8[k] for k in ("decode_kernel_us", "decode_kernel_us_pct", "merge_kernel_us",
                                            "cache_kernel_us", "alg_bytes_per_step", "kernel_launches",
-                                           "sum_len")},
+                                           "sum_len", "host_call_ms")},
             "roofline": q8["roofline"],
         }
     if "verify" in legs:
@@ -647,6 +669,9 @@ def main():
             "decode_kernel_us": round(wdec["decode_kernel_us"], 2),
             "kernel_GBs": wdec["roofline"]["achieved"],
             "kv_GBs_step": round(wdec["value"], 2),
+            "merge_kernel_us": round(wdec["merge_kernel_us"], 2),
+            "cache_kernel_us": round(wdec["cache_kernel_us"], 2),
+            "host_call_ms": wdec["host_call_ms"],
         }
     if not args.no_prefill:
         line["prefill"] = run_prefill(args)
