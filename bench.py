@@ -669,7 +669,6 @@ def main():
             "decode_kernel_us": round(wdec["decode_kernel_us"], 2),
             "kernel_GBs": wdec["roofline"]["achieved"],
             "kv_GBs_step": round(wdec["value"], 2),
-            "merge_kernel_us": round(wdec["merge_kernel_us"], 2),
             "cache_kernel_us": round(wdec["cache_kernel_us"], 2),
             "host_call_ms": wdec["host_call_ms"],
         }
