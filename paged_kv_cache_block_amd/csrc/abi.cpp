@@ -123,6 +123,7 @@ void drain_timing_locked() {
 struct pa_pool {
   pa::BlockPool meta;
   pa::PrefixCache prefix;  // complete-block prefix keys -> pinned blocks
+  pa::DecodePlan plan;     // the last decode plan; its buffer is reused by the next call
   pa::PoolGeom geom{};
   void* k = nullptr;
   void* v = nullptr;
@@ -577,14 +578,15 @@ pa_status step_impl(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
   std::string msg;
   // Size and validate against the lengths after the append, before anything changes.
   std::vector<int32_t> extra = step_extra_tokens(seqs, n_tokens, B);
-  pa::DecodePlan plan;
+  pa::DecodePlan sizing;
   pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
                                        pool->geom.head_dim, decode_tokens_per_part(), extra.data(),
-                                       n_tokens, static_cast<int32_t>(rows), &plan, &msg);
+                                       n_tokens, static_cast<int32_t>(rows), &sizing, &msg);
   if (s != pa::kOk) return fail(s, msg);
-  if (ws_bytes < plan.total_bytes)
-    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(plan.total_bytes) +
+  if (ws_bytes < sizing.total_bytes)
+    return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(sizing.total_bytes) +
                                         " bytes, got " + std::to_string(ws_bytes));
+  pa::DecodePlan& plan = pool->plan;
   std::vector<int32_t> ones;
   if (!n_tokens) ones.assign(B, 1);
   std::vector<int64_t> slots(rows);
@@ -637,7 +639,7 @@ pa_status pa_decode(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_h
                     void* out, void* ws, size_t ws_bytes, void* stream) {
   pa_status r = check_decode_args(pool, num_heads, q, out, ws);
   if (r != PA_OK) return r;
-  pa::DecodePlan plan;
+  pa::DecodePlan& plan = pool->plan;
   std::string msg;
   pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
                                        pool->geom.head_dim, decode_tokens_per_part(), nullptr, nullptr,

@@ -134,7 +134,11 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
 
   std::vector<int32_t> n_parts_of(B);
   struct Item { int32_t b, c, pages; };
-  std::vector<Item> items;
+  // Longest page ranges first so short tails fill in at the end: the full
+  // ranges in sequence order, then the shorter last ranges (at most one per
+  // sequence) by decreasing length, ties in sequence order.
+  std::vector<Item> items, tails;
+  items.reserve(static_cast<size_t>(total_pages / ppp) + B);
   std::vector<int32_t> part_base(B, -1), merge;
   int32_t n_parts = 0;
   int64_t row_heads = 0;
@@ -142,7 +146,10 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     int32_t nb = static_cast<int32_t>(nvis[b]);
     int32_t np = static_cast<int32_t>(ceil_div(nb, ppp));
     n_parts_of[b] = np;
-    for (int32_t c = 0; c < np; ++c) items.push_back({b, c, std::min(ppp, nb - c * ppp)});
+    for (int32_t c = 0; c < np; ++c) {
+      const int32_t pages = std::min(ppp, nb - c * ppp);
+      (pages == ppp ? items : tails).push_back({b, c, pages});
+    }
     if (np > 1) {
       if (row_heads + static_cast<int64_t>(np) * qlen[b] * num_heads > INT32_MAX) {
         *msg = "too many split-K partial rows";
@@ -157,9 +164,9 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
       }
     }
   }
-  // Longest page ranges first so short tails fill in at the end.
-  std::stable_sort(items.begin(), items.end(),
+  std::stable_sort(tails.begin(), tails.end(),
                    [](const Item& x, const Item& y) { return x.pages > y.pages; });
+  items.insert(items.end(), tails.begin(), tails.end());
 
   DecodePlan p;
   p.batch = B;
@@ -170,17 +177,38 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.n_rows = static_cast<int32_t>(n_rows);
   p.max_q_len = max_q;
   p.total_pages = total_pages;
+  // Section offsets (4-word aligned), then one allocation for all of them.
+  size_t words = 0;
+  auto place = [&](size_t n) {
+    const size_t at = align_up(words, 4);
+    words = at + n;
+    return at * sizeof(int32_t);
+  };
+  p.ctx_off = place(B);
+  p.tbl_off_off = place(B);
+  p.qstart_off = place(B + 1);
+  p.base_off = place(B);
+  p.nparts_off = place(B);
+  p.win_off = place(4 * static_cast<size_t>(B));
+  p.work_off = place(kWorkInts * items.size());
+  p.merge_off = place(std::max<size_t>(2, merge.size()));
+  p.tables_off = place(static_cast<size_t>(total_pages));
+  p.slots_off = place(2 * static_cast<size_t>(std::max(slot_count, 0)));
+  const size_t rows_hq = static_cast<size_t>(row_heads);
+  p.meta_bytes = align_up(words * sizeof(int32_t), kWsAlign);
+  p.part_m_off = p.meta_bytes;
+  p.part_l_off = p.part_m_off + align_up(rows_hq * sizeof(float), kWsAlign);
+  p.part_acc_off = p.part_l_off + align_up(rows_hq * sizeof(float), kWsAlign);
+  p.total_bytes = p.part_acc_off + align_up(rows_hq * head_dim * sizeof(float), kWsAlign);
+  if (extra_tokens) {  // sizing only: the sections are not filled
+    *plan = std::move(p);
+    return kOk;
+  }
+  // The caller's previous plan buffer is reused (no allocation once it is
+  // large enough).
   std::vector<int32_t>& meta = p.meta;
-  p.ctx_off = reserve(meta, B);
-  p.tbl_off_off = reserve(meta, B);
-  p.qstart_off = reserve(meta, B + 1);
-  p.base_off = reserve(meta, B);
-  p.nparts_off = reserve(meta, B);
-  p.win_off = reserve(meta, 4 * static_cast<size_t>(B));
-  p.work_off = reserve(meta, kWorkInts * items.size());
-  p.merge_off = reserve(meta, std::max<size_t>(2, merge.size()));
-  p.tables_off = reserve(meta, static_cast<size_t>(total_pages));
-  p.slots_off = reserve(meta, 2 * static_cast<size_t>(std::max(slot_count, 0)));
+  meta = std::move(plan->meta);
+  meta.assign(words, 0);
   int32_t* ctx = at_bytes(meta, p.ctx_off);
   int32_t* toff = at_bytes(meta, p.tbl_off_off);
   int32_t* base = at_bytes(meta, p.base_off);
@@ -231,13 +259,6 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   qs[B] = row;
   std::copy(merge.begin(), merge.end(), mrg);
   std::copy(win.begin(), win.end(), at_bytes(meta, p.win_off));
-
-  p.meta_bytes = align_up(meta.size() * sizeof(int32_t), kWsAlign);
-  size_t rows_hq = static_cast<size_t>(row_heads);
-  p.part_m_off = p.meta_bytes;
-  p.part_l_off = p.part_m_off + align_up(rows_hq * sizeof(float), kWsAlign);
-  p.part_acc_off = p.part_l_off + align_up(rows_hq * sizeof(float), kWsAlign);
-  p.total_bytes = p.part_acc_off + align_up(rows_hq * head_dim * sizeof(float), kWsAlign);
   *plan = std::move(p);
   return kOk;
 }

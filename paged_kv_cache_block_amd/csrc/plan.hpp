@@ -95,8 +95,8 @@ struct DecodePlan {
 // kInvalidArg with msg.
 // `tokens_per_part` = 0 chooses the partition size automatically.
 // `extra_tokens` (nullable, [B]) sizes the plan as if row b had that many
-// more tokens (page ids of not-yet-allocated pages are left 0: such a plan
-// is for sizing only).  `q_lens` (nullable = all 1) gives the query rows of
+// more tokens: such a plan is for sizing only (its offsets and sizes are
+// set, its `meta` is left empty).  `q_lens` (nullable = all 1) gives the query rows of
 // each sequence.  `slot_count` reserves an int64 slot array (slots_off) for
 // the caller to fill.
 Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, int32_t num_heads,
