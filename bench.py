@@ -121,17 +121,31 @@ def causal_flops(wl):
 def recorded_traffic(name):
     """HBM bytes per launch from the committed counter summary of a kernel,
     or None when the kernel's source has changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", name + ".counters.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    csrc = os.path.join(ROOT, "paged_kv_cache_block_amd", "csrc")
-    digest = hashlib.sha256(open(os.path.join(csrc, "decode.hip"), "rb").read() +
-                            open(os.path.join(csrc, "device.hpp"), "rb").read()).hexdigest()
-    if digest != rec.get("kernel_source_sha256"):
+    if decode_source_digest() != rec.get("kernel_code_sha256"):
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
+def decode_source_digest(texts=None):
+    """sha256 of the decode kernel's code (decode.hip then device.hpp) with
+    line comments, trailing blanks and empty lines removed, so that an edit of
+    comments alone keeps the recorded counters."""
+    import hashlib
+    import re
+    if texts is None:
+        csrc = os.path.join(ROOT, "paged_kv_cache_block_amd", "csrc")
+        texts = [open(os.path.join(csrc, f), encoding="utf-8").read() for f in ("decode.hip", "device.hpp")]
+    lines = []
+    for text in texts:
+        for line in text.splitlines():
+            code = re.sub(r"//.*$", "", line).rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def window_alg_bytes(lengths, wl, sinks, recent):

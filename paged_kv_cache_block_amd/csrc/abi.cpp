@@ -572,7 +572,7 @@ pa_status step_impl(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
     const int32_t group = num_heads / pool->geom.num_kv_heads;
     if (!pa::decode_handles_rows(pool->geom, group, max_q))
       return fail(PA_ERR_INVALID_ARG,
-                  "verify step needs an MFMA decode shape (bf16 or int8 pages, head_dim 64/128, "
+                  "verify step needs an MFMA decode shape (bf16 or 8-bit pages, head_dim 64/128, "
                   "block_size 16/32) and q_len * group <= 32");
   }
   std::string msg;

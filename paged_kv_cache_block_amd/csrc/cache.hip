@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
-// ---------------------------------------------------------- int8 pages ---
+// --------------------------------------------------------- 8-bit pages ---
 // Per-row absmax quantisation (vladkulikov.com notebook "Модуль 10", the
 // KV-compression experiment): scale = max|x| / 127 (1 for a zero row), code =
 // x / scale rounded to nearest even and clipped to [-127, 127], decided in

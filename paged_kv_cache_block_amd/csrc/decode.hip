@@ -9,13 +9,13 @@
 // through the block table.
 //
 // Kernels
-//   decode_mfma      bf16 or int8 pages, D in {64, 128}, block_size in
+//   decode_mfma      bf16 or 8-bit pages, D in {64, 128}, block_size in
 //       {16, 32}, G <= 16, q_len * G <= 32 query columns per sequence.
 //       One workgroup = (work item = (sequence, page range), KV head); its 4
 //       waves stride over the pages of the range.  The query rows x heads of
 //       the KV head form the N dimension of two MFMA contractions per page
 //       (S^T = K . Q^T, then O^T += V^T . P^T, P kept in registers); the
-//       transposed (bf16) or operand-ordered (int8) V page makes every V
+//       transposed (bf16) or operand-ordered (8-bit) V page makes every V
 //       operand a contiguous load.  Online softmax per page (exp2 with
 //       log2(e) folded into the scale); the 4 waves merge in LDS; a range
 //       that is the whole sequence writes bf16 output, otherwise fp32
@@ -203,8 +203,8 @@ template <int D, int BS> struct PageRegs<D, BS, 0> {
 };
 
 // Minimum waves per SIMD a decode kernel variant is compiled for (its
-// register budget).  int8 pages move fewer bytes per load, so the 16-column
-// int8 kernel asks for 3 resident waves to keep enough bytes in flight; the
+// register budget).  8-bit pages move fewer bytes per load, so the 16-column
+// 8-bit kernels ask for 3 resident waves to keep enough bytes in flight; the
 // d 128 / 32-slot / 32-column variants hold two 32-token pages for two
 // column tiles and would spill under 2, so they take what they need.
 template <int D, int BS, int CT, int Q8>

@@ -21,17 +21,17 @@ constexpr int kWorkInts = 16;    // ints per decode work item
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Geometry of a pool.  dtype: 0 = fp32, 1 = bf16, 2 = int8 codes with one
-// fp32 scale per (token, KV head) row (q / out / new rows are then bf16).
+// Geometry of a pool.  dtype: 0 = fp32, 1 = bf16, 2 = int8 codes, 3 = E4M3
+// codes; 8-bit codes come with one fp32 scale per (token, KV head) row (q /
+// out / new rows are then bf16).
 struct PoolGeom {
   int32_t num_blocks, block_size, num_kv_heads, head_dim, dtype;
   bool q8() const { return dtype == 2 || dtype == 3; }  // 8-bit codes + fp32 row scales
   bool fp8() const { return dtype == 3; }               // the codes are E4M3 floats
-  int code_kind() const { return dtype == 3 ? 2 : dtype == 2 ? 1 : 0; }  // kernels' Q8 parameter
   // Element size of q, out, k_new and v_new.
   int32_t io_elt() const { return dtype == 0 ? 4 : 2; }
   size_t page_elems() const { return static_cast<size_t>(block_size) * head_dim; }
-  // Bytes of one (block, KV head) page: codes then scales for int8 pools.
+  // Bytes of one (block, KV head) page: codes then scales for 8-bit pools.
   size_t page_bytes() const {
     if (q8()) return page_elems() + 4 * static_cast<size_t>(block_size);
     return page_elems() * (dtype == 1 ? 2 : 4);

@@ -98,7 +98,7 @@ typedef __attribute__((address_space(1))) void global_void;
 constexpr int kPrefillCG = PA_PREFILL_CG;          // 16-column groups per wave
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;    // waves per workgroup
 constexpr int kPrefillStages = PA_PREFILL_STAGES;  // key tiles in the LDS ring
-constexpr int kPrefillStagesQ8 = PA_PREFILL_STAGES_Q8;  // raw int8 tiles in the LDS ring
+constexpr int kPrefillStagesQ8 = PA_PREFILL_STAGES_Q8;  // raw 8-bit tiles in the LDS ring
 constexpr int kTile = 32;                          // key tokens per step
 constexpr float kSlackLog2 = 8.f;                  // largest softmax weight, log2
 
@@ -127,16 +127,16 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   constexpr int NB = KB + DT;        // operand blocks per key tile
   constexpr int PAGES = kTile / BS;  // pages per key tile
   static_assert(NB % NW == 0, "each wave stages the same number of blocks");
-  constexpr int BPW = NB / NW;       // blocks staged (bf16) or converted (int8) by each wave per tile
+  constexpr int BPW = NB / NW;       // blocks staged (bf16) or converted (8-bit) by each wave per tile
   static_assert((S - 2) * BPW < 64, "vmcnt range");
-  // int8 pages: a tile as the pages hold it (K codes, V codes, K scales, V
+  // 8-bit pages: a tile as the pages hold it (K codes, V codes, K scales, V
   // scales of its 32 tokens), moved by kCodeLoads 1 KB wave loads of codes
   // plus one 256-byte load of scales.
   constexpr int kRawBytes = 2 * kTile * D + 2 * kTile * 4;
   constexpr int kCodeLoads = 2 * kTile * D / 1024;
   constexpr int kRowChunks = D / 16;      // 16-byte chunks per K row
   constexpr int kRowChunksV = D / 64;     // 16-byte chunks per V operand-order row (D / 4 bytes)
-  // Chunk permutations of the raw int8 tile in LDS (each an involution on
+  // Chunk permutations of the raw 8-bit tile in LDS (each an involution on
   // its range).  K: chunk c of token t's row sits at c ^ q8_k_swizzle(t), so
   // the 32 lanes of an 8-byte conversion read (16 tokens x 2 halves of a
   // chunk) cover all 64 banks.  V (d 128, two chunks per row): chunk q of a
@@ -151,8 +151,8 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     if constexpr (D == 128) return q ^ ((q >> 4) & 1);
     else return q;
   };
-  static_assert(!Q8 || (S >= 4 && kCodeLoads <= NW && kCodeLoads % 2 == 0), "int8 ring");
-  // bf16: an S-stage ring of operand-ordered tiles.  int8: an S-stage ring of
+  static_assert(!Q8 || (S >= 4 && kCodeLoads <= NW && kCodeLoads % 2 == 0), "8-bit ring");
+  // bf16: an S-stage ring of operand-ordered tiles.  8-bit: an S-stage ring of
   // raw tiles and two operand-ordered bf16 tiles converted from them.
   __shared__ uint4 ring[Q8 ? 2 : S][NB][64];
   __shared__ uint4 raw[Q8 ? S : 1][Q8 ? kRawBytes / 16 : 1];
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   const size_t page = static_cast<size_t>(BS) * D;  // bf16 elements per page
   const uint8_t* kq = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vq = static_cast<const uint8_t*>(a.v_pool);
-  const size_t q8_page = static_cast<size_t>(BS) * D + 4 * BS;  // bytes per int8 page (codes, scales)
+  const size_t q8_page = static_cast<size_t>(BS) * D + 4 * BS;  // bytes per 8-bit page (codes, scales)
 
   // Rows of the workgroup and of this wave.
   const int wg_rows = NW * CG * 16 / G;
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     }
   };
 
-  // int8: stage raw tile T into raw slot st.  Wave w < kCodeLoads moves 1 KB
+  // 8-bit: stage raw tile T into raw slot st.  Wave w < kCodeLoads moves 1 KB
   // of codes (the first half of the loads K codes, the second V codes) in
   // 16-byte chunks: token t's K codes fill row t (D bytes) with the chunks
   // permuted by q8_k_swizzle(t); each 16-token subtile of V codes keeps the
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(dst + 2 * kTile * D), 16, 0, 0);
     }
   };
-  // Loads a wave issues per int8 tile, and waits that leave at most `tiles`
+  // Loads a wave issues per 8-bit tile, and waits that leave at most `tiles`
   // later tiles' loads outstanding (a wave-uniform count).
   const int q8_loads = (wave < kCodeLoads ? 1 : 0) + (wave == 0 ? 1 : 0);
   auto q8_wait = [&](auto tiles_c) {
@@ -360,13 +360,13 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   };
-  // int8: convert raw slot rs into bf16 operand tile os (the operand order
+  // 8-bit: convert raw slot rs into bf16 operand tile os (the operand order
   // of the bf16 ring; codes are exact in bf16, the scales stay apart in
   // fp32).  Waves 0-3 convert the K blocks (8 codes per lane, one 8-byte
   // read), waves 4-7 the V blocks: a lane reads the 16-byte chunks of its
   // two V rows (tokens 8grp .. +3 and +4 .. +7 of d = 16nt + n) once for all
   // the blocks it converts.
-  static_assert(!Q8 || (NW == 8 && KB % 4 == 0 && DT % 4 == 0), "int8 conversion split");
+  static_assert(!Q8 || (NW == 8 && KB % 4 == 0 && DT % 4 == 0), "8-bit conversion split");
   constexpr int kKPW = KB / 4, kVPW = DT / 4;  // blocks per K / V converting wave
   int cv_off[kKPW > 0 ? kKPW : 1];
   int cv_vlo = 0, cv_vhi = 0;
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
           s[k][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[k][j], s[k][tt], 0, 0, 0);
       }
     // s[k][tt][i] is the score of token T*32 + 8*grp + 4*tt + i for column n.
-    // int8: the row scales of this lane's 8 tokens; K's scales the scores,
+    // 8-bit: the row scales of this lane's 8 tokens; K's scales the scores,
     // V's the weights that enter P.V (not l).
     float sk[8], sv[8];
     if constexpr (Q8) {
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
       }
     }
   } else {
-    // int8 step i: this wave's loads of the raw tile of iteration i+1 have
+    // 8-bit step i: this wave's loads of the raw tile of iteration i+1 have
     // landed once at most those of iteration i+2 are outstanding; the barrier
     // publishes that raw tile and the bf16 tile of iteration i (converted in
     // step i-1) and guarantees every wave has left step i-1, the last reader
