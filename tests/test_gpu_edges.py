@@ -1,8 +1,8 @@
 """GPU parity at the edges of the supported shapes: the largest head_dim
 (512), large and tiny blocks, a single slot per block, group 16 and a
-single query head per KV head, int8 pages on the generic kernel (head_dim
-256), one-token sequences, a batch of one, and chunks whose rows reach the
-first position of the sequence.
+single query head per KV head, 8-bit pages on the generic kernel (head_dim
+256), one-token sequences, a batch of one, chunks whose rows reach the
+first position of the sequence, and pools larger than 4 GiB.
 
 Source: docs.rs ferrum-kv 0.4.0 src/attention.rs, paged_attention (decode and
 q_tokens > 1); int8 rows as in the vladkulikov.com notebook "Модуль 10"
@@ -118,3 +118,61 @@ def test_reshape_and_cache_skips_out_of_range_slots():
         q8.write(slots, k, k)
         torch.cuda.synchronize()
         assert torch.equal(q8.k, before)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_pools_beyond_4_gib(kv):
+    """Each pool larger than 4 GiB, its highest blocks handed out first, so
+    every page address needs more than 32 bits: cache writes, a decode step,
+    decode and prefill read the rows back within tolerance of the oracle
+    (attention over the rows as written, or as read back for int8)."""
+    from paged_kv_cache_block_amd import DevicePool, abi
+    hq, hkv, d, bs = 32, 8, 128, 16
+    page = bs * d * 2 if kv == "bf16" else bs * d + 4 * bs
+    nb = (4 << 30) // (hkv * page) + 4096
+    assert abi.pa_pool_bytes(abi.make_desc(nb, bs, hkv, d, abi.PA_DTYPE_BF16 if kv == "bf16" else abi.PA_DTYPE_I8)) > 4 << 30
+    order = np.arange(nb - 1, -1, -1, dtype=np.int32)      # highest block first
+    log(f"pool beyond 4 GiB ({kv}): {nb} blocks")
+    pool = DevicePool(nb, bs, hkv, d, dtype=kv, allocation_order=order)
+    rng = np.random.default_rng(44)
+    lengths = [37, 300, 1000]
+    rows = []
+    for s, n in enumerate(lengths):
+        pool.create(s)
+        k, v = bf16_round(rng.standard_normal((n, hkv, d)).astype(np.float32)), \
+            bf16_round(rng.standard_normal((n, hkv, d)).astype(np.float32))
+        slots = pool.append(s, n)
+        assert int(slots.min()) >= (nb - 100) * bs
+        pool.write(slots, to_device(k, "bf16"), to_device(v, "bf16"))
+        rows.append([to_f64(k, "bf16"), to_f64(v, "bf16")])
+    kn = bf16_round(rng.standard_normal((3, hkv, d)).astype(np.float32))
+    vn = bf16_round(rng.standard_normal((3, hkv, d)).astype(np.float32))
+    q = bf16_round(rng.standard_normal((3, hq, d)).astype(np.float32))
+    out, _ = pool.decode_step([0, 1, 2], to_device(kn, "bf16"), to_device(vn, "bf16"), to_device(q, "bf16"))
+    for s in range(3):
+        rows[s][0] = np.concatenate([rows[s][0], to_f64(kn[s:s + 1], "bf16")])
+        rows[s][1] = np.concatenate([rows[s][1], to_f64(vn[s:s + 1], "bf16")])
+
+    def kv_of(s):
+        K, V = rows[s]
+        if kv == "i8":
+            return oracle.fake_quantize_rows(K, 8), oracle.fake_quantize_rows(V, 8)
+        return K, V
+
+    got = to_host_f64(out)
+    for s in range(3):
+        K, V = kv_of(s)
+        assert_close(got[s], oracle.attention(to_f64(q[s:s + 1], "bf16"), K, V)[0], *BF16_TOL,
+                     what=f"decode step seq {s}")
+    q_lens = [37, 64, 200]
+    qp = bf16_round(rng.standard_normal((sum(q_lens), hq, d)).astype(np.float32))
+    outp = to_host_f64(pool.prefill([0, 1, 2], q_lens, to_device(qp, "bf16")))
+    r0 = 0
+    for s, n in enumerate(q_lens):
+        K, V = kv_of(s)
+        assert_close(outp[r0:r0 + n], oracle.attention(to_f64(qp[r0:r0 + n], "bf16"), K, V), *BF16_TOL,
+                     what=f"prefill seq {s}")
+        r0 += n
+    pool.close()
+    del pool
+    torch.cuda.empty_cache()
