@@ -430,15 +430,33 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     f32x4 s[CG][2];
 #pragma unroll
     for (int k = 0; k < CG; ++k) s[k][0] = s[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // bf16 pages: every K operand of the tile is read from LDS before the
+    // first QK^T MFMA and every V operand right after the last, and the
+    // scheduler may not move them (sched_barrier): the MFMAs then issue back
+    // to back instead of waiting on an LDS read each two (3-4% faster
+    // prefill).  The 8-bit path, which converts the next tile meanwhile, is
+    // slower so and keeps the reads next to their MFMAs.
+    bf16x8 kops[2 * KS];
+    if constexpr (!Q8) {
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) kops[i] = blocks[i * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        const bf16x8 kop = blocks[(tt * KS + j) * 64 + lane];
+        const bf16x8 kop = Q8 ? blocks[(tt * KS + j) * 64 + lane] : kops[tt * KS + j];
 #pragma unroll
         for (int k = 0; k < CG; ++k)
           s[k][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[k][j], s[k][tt], 0, 0, 0);
       }
+    bf16x8 vops[DT];
+    if constexpr (!Q8) {
+#pragma unroll
+      for (int nt = 0; nt < DT; ++nt) vops[nt] = blocks[(KB + nt) * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // s[k][tt][i] is the score of token T*32 + 8*grp + 4*tt + i for column n.
     // 8-bit: the row scales of this lane's 8 tokens; K's scales the scores,
     // V's the weights that enter P.V (not l).
@@ -529,7 +547,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     const int live = kTail ? L - (T * kTile + 8 * grp) : kTile;  // tokens of this lane's 8 inside the sequence
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
-      bf16x8 vop = blocks[(KB + nt) * 64 + lane];
+      bf16x8 vop = Q8 ? blocks[(KB + nt) * 64 + lane] : vops[nt];
       if constexpr (kTail && Q8 != 1) {  // int8 codes are always finite; bf16 and E4M3 may be NaN
 #pragma unroll
         for (int e = 0; e < 8; ++e)
