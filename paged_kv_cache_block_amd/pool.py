@@ -151,15 +151,40 @@ class DevicePool:
     def flush(self, stream=None):
         abi.pa_flush_copies(self.handle, self._stream(stream))
 
+    def _rows(self, t, rows, heads, name):
+        """``t`` must be a contiguous device tensor [rows, heads, head_dim] of
+        the pool's input dtype: the kernels read and write exactly that many
+        bytes through its pointer."""
+        torch = _torch()
+        if self.k is None:  # metadata-only pool: the library rejects the call itself
+            return
+        ok = (torch.is_tensor(t) and t.device == self.k.device and t.dtype == self.io_dtype
+              and t.is_contiguous() and tuple(t.shape) == (rows, heads, self.head_dim))
+        if not ok:
+            got = (tuple(t.shape), t.dtype, str(t.device), t.is_contiguous()) if torch.is_tensor(t) else type(t)
+            raise ValueError(f"{name} must be a contiguous {self.io_dtype} tensor of shape "
+                             f"{(rows, heads, self.head_dim)} on {self.k.device}; got {got}")
+
+    def _queries(self, q, out, rows):
+        if not _torch().is_tensor(q) or q.dim() != 3:
+            raise ValueError("q must be a [rows, num_heads, head_dim] tensor")
+        heads = int(q.shape[1])
+        self._rows(q, rows, heads, "q")
+        if out is None:
+            out = _torch().empty_like(q)
+        self._rows(out, rows, heads, "out")
+        return heads, out
+
     def write(self, slots, k_new, v_new, stream=None):
         """Store rows ``k_new[i], v_new[i]`` ([n, Hkv, D] device tensors) at ``slots``."""
         torch = _torch()
         if not torch.is_tensor(slots) or slots.device.type != "cuda":
             slots = torch.as_tensor(np.asarray(slots, dtype=np.int64)).to(self.k.device, non_blocking=False)
+        if slots.dtype != torch.int64 or not slots.is_contiguous():
+            raise ValueError("slots must be a contiguous int64 tensor")
         n = int(slots.numel())
-        assert k_new.shape == (n, self.num_kv_heads, self.head_dim) and k_new.dtype == self.io_dtype
-        assert v_new.shape == k_new.shape and v_new.dtype == k_new.dtype
-        assert k_new.is_contiguous() and v_new.is_contiguous() and slots.dtype == torch.int64
+        self._rows(k_new, n, self.num_kv_heads, "k_new")
+        self._rows(v_new, n, self.num_kv_heads, "v_new")
         abi.pa_reshape_and_cache(self.handle, k_new, v_new, slots, n, self._stream(stream))
         return slots
 
@@ -172,9 +197,7 @@ class DevicePool:
 
     def decode(self, seqs, q, out=None, stream=None, ws=None):
         """One query row per sequence: ``q`` [B, Hq, D] -> ``out`` [B, Hq, D]."""
-        num_heads = q.shape[1]
-        if out is None:
-            out = _torch().empty_like(q)
+        num_heads, out = self._queries(q, out, len(seqs))
         need = abi.pa_decode_workspace_bytes(self.handle, seqs, num_heads)
         if need == 0:
             # Invalid batch: let the call itself report why.
@@ -188,9 +211,9 @@ class DevicePool:
         """Append one token per sequence, store its K/V, decode over the caches.
 
         Returns ``(out, slots)``."""
-        num_heads = q.shape[1]
-        if out is None:
-            out = _torch().empty_like(q)
+        num_heads, out = self._queries(q, out, len(seqs))
+        self._rows(k_new, len(seqs), self.num_kv_heads, "k_new")
+        self._rows(v_new, len(seqs), self.num_kv_heads, "v_new")
         need = abi.pa_decode_step_workspace_bytes(self.handle, seqs, num_heads) or 256
         if ws is None:
             ws = self.workspace(need)
@@ -202,9 +225,10 @@ class DevicePool:
         """Append ``q_lens[b]`` tokens per sequence, store their K/V rows
         ([sum q_lens, Hkv, D]) and attend causally for those rows (``q``
         [sum q_lens, Hq, D]).  Returns ``(out, slots)``."""
-        num_heads = q.shape[1]
-        if out is None:
-            out = _torch().empty_like(q)
+        rows = int(np.sum(np.asarray(q_lens, dtype=np.int64)))
+        num_heads, out = self._queries(q, out, rows)
+        self._rows(k_new, rows, self.num_kv_heads, "k_new")
+        self._rows(v_new, rows, self.num_kv_heads, "v_new")
         need = abi.pa_verify_step_workspace_bytes(self.handle, seqs, q_lens, num_heads) or 256
         if ws is None:
             ws = self.workspace(need)
@@ -214,9 +238,8 @@ class DevicePool:
 
     def prefill(self, seqs, q_lens, q, out=None, stream=None, ws=None):
         """Last ``q_lens[b]`` positions of each sequence: ``q`` [sum q_lens, Hq, D]."""
-        num_heads = q.shape[1]
-        if out is None:
-            out = _torch().empty_like(q)
+        rows = int(np.sum(np.asarray(q_lens, dtype=np.int64)))
+        num_heads, out = self._queries(q, out, rows)
         need = abi.pa_prefill_workspace_bytes(self.handle, seqs, q_lens, num_heads) or 256
         if ws is None:
             ws = self.workspace(need)

@@ -176,3 +176,43 @@ def test_pools_beyond_4_gib(kv):
     pool.close()
     del pool
     torch.cuda.empty_cache()
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python binding checks every tensor it hands to the library (the
+    kernels trust the pointers): wrong row counts, head_dim, dtype, device or
+    layout raise ValueError before any call, and the pool is unchanged."""
+    from paged_kv_cache_block_amd import DevicePool
+    pool = DevicePool(16, 16, 2, 64, dtype="bf16")
+    pool.create(0)
+    pool.create(1)
+    k = torch.zeros(10, 2, 64, dtype=torch.bfloat16, device="cuda")
+    pool.write(pool.append(0, 10), k, k)
+    pool.write(pool.append(1, 10), k, k)
+    torch.cuda.synchronize()
+    q = torch.zeros(2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    kn = torch.zeros(2, 2, 64, dtype=torch.bfloat16, device="cuda")
+    bad_q = [torch.zeros(3, 8, 64, dtype=torch.bfloat16, device="cuda"),       # rows
+             torch.zeros(2, 8, 32, dtype=torch.bfloat16, device="cuda"),       # head_dim
+             torch.zeros(2, 8, 64, dtype=torch.float32, device="cuda"),        # dtype
+             torch.zeros(2, 8, 64, dtype=torch.bfloat16),                      # host memory
+             torch.zeros(2, 64, 8, dtype=torch.bfloat16, device="cuda").transpose(1, 2)]  # layout
+    for bq in bad_q:
+        with pytest.raises(ValueError):
+            pool.decode([0, 1], bq)
+        with pytest.raises(ValueError):
+            pool.decode_step([0, 1], kn, kn, bq)
+    with pytest.raises(ValueError):
+        pool.decode([0, 1], q, out=torch.zeros(1, 8, 64, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        pool.decode_step([0, 1], kn[:1], kn, q)
+    with pytest.raises(ValueError):
+        pool.verify_step([0, 1], [2, 1], kn, kn, q)           # 3 rows, tensors of 2
+    with pytest.raises(ValueError):
+        pool.prefill([0, 1], [2, 2], q)                       # 4 rows, q of 2
+    with pytest.raises(ValueError):
+        pool.write(np.zeros(0, dtype=np.int64), kn, kn)       # 0 slots, 2 rows
+    assert pool.seq_len(0) == 10 and pool.seq_len(1) == 10
+    out = pool.decode([0, 1], q)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()

@@ -364,9 +364,9 @@ def test_prefill_rejects_bad_rows():
     pool, _ = build_device_pool(wl)
     q = torch.zeros(21, 8, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(InvalidArgumentError):
-        pool.prefill([0], [11], q)
+        pool.prefill([0], [11], q[:11])         # 11 rows of a 10-token sequence
     with pytest.raises(InvalidArgumentError):
-        pool.prefill([0, 1], [0, 5], q)
+        pool.prefill([0, 1], [0, 5], q[:5])     # an empty chunk
 
 
 # ------------------------------------------------------------ full size
