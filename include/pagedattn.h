@@ -304,11 +304,12 @@ pa_status pa_flush_copies(pa_pool* pool, void* stream);
 
 /* Write new K/V rows into their slots ([KVPool] append stores the row at
  * (table[p / block_size], p % block_size); ferrum's write_kv):
- *   Kpool[slot / bs][h][slot % bs][:] = k_new[i][h][:]
- *   Vpool[slot / bs][h][:][slot % bs] = v_new[i][h][:]   for i < n, every h.
+ *   K page (slot / bs, h), token slot % bs   <- k_new[i][h][:]
+ *   Vpool[slot / bs][h][:][slot % bs]        <- v_new[i][h][:]   for i < n, every h,
+ * each K value at its place in the K page order of the header comment.
  * k_new, v_new: device [n][num_kv_heads][head_dim]; slots: device int64 [n].
- * An I8 pool stores each row's codes and scale instead ([KVquant]; the
- * layout and rounding are in the header comment).
+ * An I8 or FP8 pool stores each row's codes and scale instead ([KVquant];
+ * the layout and rounding are in the header comment).
  * A slot outside [0, num_blocks * block_size) is skipped.  Two rows naming
  * one slot race.  Pending copies are flushed first on `stream`.
  * Errors: PA_ERR_INVALID_ARG (NULL pointers with n > 0, n < 0,
@@ -335,7 +336,7 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, const int64_t* seqs, int32
  * Long sequences are split into page ranges whose partial (max, sum, acc)
  * are merged by log-sum-exp ([lecture19] online_softmax_stats applied
  * across ranges).
- * On an I8 pool K_j and V_j are the rows read back (code * scale).
+ * On an I8 or FP8 pool K_j and V_j are the rows read back (value(code) * scale).
  * seqs: host [B] live ids (duplicates allowed); q, out: device
  *   [B][num_heads][head_dim] in the pool dtype; ws: device, at least
  *   pa_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by the
@@ -388,7 +389,7 @@ size_t pa_verify_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, 
  * [R][num_heads][head_dim] (rows sequence-major, as pa_prefill_chunk);
  * ws: at least pa_verify_step_workspace_bytes(...) bytes, 256-byte aligned;
  * slots_out: host [R] or NULL.
- * Needs bf16 or int8 pages, head_dim 64 or 128, block_size 16 or 32 and
+ * Needs bf16, int8 or E4M3 pages, head_dim 64 or 128, block_size 16 or 32 and
  * q_lens[b] * (num_heads / num_kv_heads) <= 32.
  * Errors: as pa_decode_step; PA_ERR_INVALID_ARG for a repeated sequence, a
  *   q_len < 1 or a shape the kernels do not cover, before anything changes. */
