@@ -199,6 +199,31 @@ Status BlockPool::append_batch(const int64_t* seqs, const int32_t* n, int32_t co
     *msg = "count must be >= 0 with non-NULL seqs and n_tokens";
     return kInvalidArg;
   }
+  // Fast path: distinct, known sequences whose appends together need no more
+  // blocks than are free (each need taken on the state before the batch; an
+  // earlier append can only lower a later one's need, by dropping a shared
+  // tail's reference or releasing pages behind a window) cannot fail, so
+  // they run without an undo log.
+  if (count > 0) {
+    std::vector<int64_t> ids(seqs, seqs + count);
+    std::sort(ids.begin(), ids.end());
+    bool fast = std::adjacent_find(ids.begin(), ids.end()) == ids.end();
+    int64_t need = 0;
+    for (int32_t i = 0; fast && i < count; ++i) {
+      auto it = seqs_.find(seqs[i]);
+      fast = it != seqs_.end() && n[i] >= 0 && (n[i] == 0 || slots_out);
+      if (fast) need += blocks_needed(it->second, n[i]);
+    }
+    if (fast && need <= free_count()) {
+      int64_t offset = 0;
+      for (int32_t i = 0; i < count; ++i) {
+        const Status st = append(seqs[i], n[i], slots_out ? slots_out + offset : nullptr, msg);
+        if (st != kOk) return st;  // unreachable: checked above
+        offset += n[i];
+      }
+      return kOk;
+    }
+  }
   // Undo log: the first-seen state of every touched sequence and of every
   // block whose refcount or free flag the batch changed (allocations,
   // copy-on-write drops, window releases), and the pending-copy list
