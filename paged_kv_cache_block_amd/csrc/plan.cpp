@@ -137,18 +137,24 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   // Longest page ranges first so short tails fill in at the end: the full
   // ranges in sequence order, then the shorter last ranges (at most one per
   // sequence) by decreasing length, ties in sequence order.
+  // A sizing-only plan (extra_tokens) counts the items and merge rows
+  // without listing them.
+  const bool sizing = extra_tokens != nullptr;
   std::vector<Item> items, tails;
-  items.reserve(static_cast<size_t>(total_pages / ppp) + B);
+  if (!sizing) items.reserve(static_cast<size_t>(total_pages / ppp) + B);
   std::vector<int32_t> part_base(B, -1), merge;
   int32_t n_parts = 0;
-  int64_t row_heads = 0;
+  int64_t row_heads = 0, n_work = 0, n_merge = 0;
   for (int32_t b = 0; b < B; ++b) {
     int32_t nb = static_cast<int32_t>(nvis[b]);
     int32_t np = static_cast<int32_t>(ceil_div(nb, ppp));
     n_parts_of[b] = np;
-    for (int32_t c = 0; c < np; ++c) {
-      const int32_t pages = std::min(ppp, nb - c * ppp);
-      (pages == ppp ? items : tails).push_back({b, c, pages});
+    n_work += np;
+    if (!sizing) {
+      for (int32_t c = 0; c < np; ++c) {
+        const int32_t pages = std::min(ppp, nb - c * ppp);
+        (pages == ppp ? items : tails).push_back({b, c, pages});
+      }
     }
     if (np > 1) {
       if (row_heads + static_cast<int64_t>(np) * qlen[b] * num_heads > INT32_MAX) {
@@ -158,9 +164,12 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
       part_base[b] = static_cast<int32_t>(row_heads);
       row_heads += static_cast<int64_t>(np) * qlen[b] * num_heads;
       n_parts += np;
-      for (int32_t t = 0; t < qlen[b]; ++t) {
-        merge.push_back(b);
-        merge.push_back(t);
+      n_merge += qlen[b];
+      if (!sizing) {
+        for (int32_t t = 0; t < qlen[b]; ++t) {
+          merge.push_back(b);
+          merge.push_back(t);
+        }
       }
     }
   }
@@ -171,8 +180,8 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   DecodePlan p;
   p.batch = B;
   p.pages_per_part = ppp;
-  p.n_work = static_cast<int32_t>(items.size());
-  p.n_merge = static_cast<int32_t>(merge.size() / 2);
+  p.n_work = static_cast<int32_t>(n_work);
+  p.n_merge = static_cast<int32_t>(n_merge);
   p.n_parts = n_parts;
   p.n_rows = static_cast<int32_t>(n_rows);
   p.max_q_len = max_q;
@@ -190,8 +199,8 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.base_off = place(B);
   p.nparts_off = place(B);
   p.win_off = place(4 * static_cast<size_t>(B));
-  p.work_off = place(kWorkInts * items.size());
-  p.merge_off = place(std::max<size_t>(2, merge.size()));
+  p.work_off = place(kWorkInts * static_cast<size_t>(n_work));
+  p.merge_off = place(std::max<size_t>(2, 2 * static_cast<size_t>(n_merge)));
   p.tables_off = place(static_cast<size_t>(total_pages));
   p.slots_off = place(2 * static_cast<size_t>(std::max(slot_count, 0)));
   const size_t rows_hq = static_cast<size_t>(row_heads);
@@ -200,7 +209,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.part_l_off = p.part_m_off + align_up(rows_hq * sizeof(float), kWsAlign);
   p.part_acc_off = p.part_l_off + align_up(rows_hq * sizeof(float), kWsAlign);
   p.total_bytes = p.part_acc_off + align_up(rows_hq * head_dim * sizeof(float), kWsAlign);
-  if (extra_tokens) {  // sizing only: the sections are not filled
+  if (sizing) {  // sizing only: the sections are not filled
     *plan = std::move(p);
     return kOk;
   }
