@@ -24,6 +24,7 @@ the float64 oracle on a bounded sample of the same decode workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -157,6 +158,20 @@ def window_alg_bytes(lengths, wl, sinks, recent):
     return kv + qo + sum(-(-n // wl.block_size) for n in seen) * 4
 
 
+def settle():
+    """Before a timed loop: collect garbage (earlier legs' pools and tensors)
+    and wait for the device, then keep the collector off until ``unsettle``,
+    so no collection or deferred free lands inside the timed steps."""
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    gc.disable()
+
+
+def unsettle():
+    gc.enable()
+
+
 SAMPLE_EVERY = 5  # timed steps that carry kernel timing events: one in this many
 
 
@@ -249,6 +264,7 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     log(f"timing {args.steps} steps")
     alg_timed = []
     torch.cuda.synchronize()
+    settle()
     t0 = time.perf_counter()
     host_ms = []  # host time of each timed call (the call returns before its kernels finish)
     for j, i in enumerate(range(args.warmup, total_steps)):
@@ -263,6 +279,7 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
             alg_timed.append(alg[-1])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    unsettle()
     alg = [step_bytes(x) for x in alg]
     alg_timed = [step_bytes(x) for x in alg_timed]
     dec_ms, dec_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
@@ -387,6 +404,7 @@ def run_verify(args, q_len=4):
     abi.pa_timing_reset()
     abi.pa_timing_select([abi.PA_KERNEL_DECODE])
     alg = []
+    settle()
     t0 = time.perf_counter()
     for j, i in enumerate(range(args.warmup, total_steps)):
         timed = j % SAMPLE_EVERY == 0
@@ -398,6 +416,7 @@ def run_verify(args, q_len=4):
             alg.append(a)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    unsettle()
     abi.pa_timing_select(None)
     dec_ms, dec_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
     for pool in pools:
@@ -439,11 +458,13 @@ def run_decode_only(args, name):
     abi.pa_timing_reset()
     abi.pa_timing_select([abi.PA_KERNEL_DECODE, abi.PA_KERNEL_MERGE])
     abi.pa_timing_enable(True)
+    settle()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         abi.pa_decode(pool.handle, seqs, wl.num_heads, q, out, ws, ws.numel(), stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    unsettle()
     abi.pa_timing_enable(False)
     abi.pa_timing_select(None)
     d_ms, d_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
@@ -484,11 +505,13 @@ def run_prefill(args, kv=None):
     torch.cuda.synchronize()
     abi.pa_timing_reset()
     abi.pa_timing_enable(True)
+    settle()
     t0 = time.perf_counter()
     for _ in range(args.prefill_iters):
         abi.pa_prefill_chunk(pool.handle, seqs, q_lens, wl.num_heads, q, out, ws, ws.numel(), stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    unsettle()
     abi.pa_timing_enable(False)
     k_ms, k_n = abi.pa_timing_read(abi.PA_KERNEL_PREFILL)
     k_pct = percentiles_us(abi.pa_timing_samples(abi.PA_KERNEL_PREFILL))
@@ -522,6 +545,7 @@ def run_prefix_cache(reps=20):
     reqs = [r[2] for r in prefix_trace_requests()]
     pool = DevicePool(1024, 16, 8, 128, metadata_only=True)
     hits = cached = 0
+    settle()
     t0 = time.perf_counter()
     for rep in range(reps):
         hits = cached = 0
@@ -534,6 +558,7 @@ def run_prefix_cache(reps=20):
             cached += hit
         pool.prefix_clear()
     dt = time.perf_counter() - t0
+    unsettle()
     pool.close()
     n = reps * len(reqs)
     return {"workload": "notebook prefix trace: 500 requests x 48 tokens, block 16, shared scope, "
@@ -563,6 +588,7 @@ def run_cpu_baseline(wl, seconds):
             pool.create(op[1])
             pool.write(pool.append(op[1], op[2]), to_f64(op[3], wl.dtype), to_f64(op[4], wl.dtype))
     q = to_f64(decode_queries(wl, sample), wl.dtype)
+    settle()
     t0 = time.perf_counter()
     reps = 0
     while True:
@@ -572,6 +598,7 @@ def run_cpu_baseline(wl, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    unsettle()
     sample_lengths = [lengths[s] for s in sample]
     alg = decode_alg_bytes(sample_lengths, wl) * reps
     return {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
