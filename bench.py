@@ -159,12 +159,11 @@ def window_alg_bytes(lengths, wl, sinks, recent):
 
 
 def settle():
-    """Before a timed loop: collect garbage (earlier legs' pools and tensors)
-    and wait for the device, then keep the collector off until ``unsettle``,
-    so no collection or deferred free lands inside the timed steps."""
-    import torch
+    """Before the warmup of a timed loop: collect garbage (earlier legs'
+    pools and tensors), then keep the collector off until ``unsettle``, so no
+    collection lands inside the timed steps (the warmup re-warms what the
+    collection evicted)."""
     gc.collect()
-    torch.cuda.synchronize()
     gc.disable()
 
 
@@ -251,6 +250,7 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     def step_bytes(lens):
         return window_alg_bytes(lens, wl, *window) if window else decode_alg_bytes(lens, wl, kv)
 
+    settle()
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
@@ -264,7 +264,6 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     log(f"timing {args.steps} steps")
     alg_timed = []
     torch.cuda.synchronize()
-    settle()
     t0 = time.perf_counter()
     host_ms = []  # host time of each timed call (the call returns before its kernels finish)
     for j, i in enumerate(range(args.warmup, total_steps)):
@@ -398,13 +397,13 @@ def run_verify(args, q_len=4):
     def step_bytes(lens):
         return decode_alg_bytes(lens, wl) + 2 * (R - B) * wl.num_heads * wl.head_dim * wl.elt_bytes
 
+    settle()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     abi.pa_timing_reset()
     abi.pa_timing_select([abi.PA_KERNEL_DECODE])
     alg = []
-    settle()
     t0 = time.perf_counter()
     for j, i in enumerate(range(args.warmup, total_steps)):
         timed = j % SAMPLE_EVERY == 0
@@ -452,13 +451,13 @@ def run_decode_only(args, name):
     stream = torch.cuda.current_stream().cuda_stream
     lengths = np.array([pool.seq_len(s) for s in seqs], dtype=np.int64)
     alg = decode_alg_bytes(lengths, wl)
+    settle()
     for _ in range(args.warmup):
         abi.pa_decode(pool.handle, seqs, wl.num_heads, q, out, ws, ws.numel(), stream)
     torch.cuda.synchronize()
     abi.pa_timing_reset()
     abi.pa_timing_select([abi.PA_KERNEL_DECODE, abi.PA_KERNEL_MERGE])
     abi.pa_timing_enable(True)
-    settle()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         abi.pa_decode(pool.handle, seqs, wl.num_heads, q, out, ws, ws.numel(), stream)
@@ -500,12 +499,12 @@ def run_prefill(args, kv=None):
     need = abi.pa_prefill_workspace_bytes(pool.handle, seqs, q_lens, wl.num_heads)
     ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
+    settle()
     for _ in range(max(1, args.prefill_warmup)):
         abi.pa_prefill_chunk(pool.handle, seqs, q_lens, wl.num_heads, q, out, ws, ws.numel(), stream)
     torch.cuda.synchronize()
     abi.pa_timing_reset()
     abi.pa_timing_enable(True)
-    settle()
     t0 = time.perf_counter()
     for _ in range(args.prefill_iters):
         abi.pa_prefill_chunk(pool.handle, seqs, q_lens, wl.num_heads, q, out, ws, ws.numel(), stream)
