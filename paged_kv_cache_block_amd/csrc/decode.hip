@@ -299,6 +299,20 @@ void decode_mfma(DecodeArgs a) {
         qv[ct][j] = bf16x8{};
     }
   }
+  // The 32-column variants read their Q operands from LDS on every page
+  // (written once by wave 0: the four waves share the columns), leaving the
+  // registers to the page ring and the accumulators.
+  constexpr bool kQInLds = CT == 2;
+  __shared__ bf16x8 s_q[kQInLds ? CT * KS : 1][64];
+  if constexpr (kQInLds) {
+    if (wave == 0) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int j = 0; j < KS; ++j) s_q[ct * KS + j][lane] = qv[ct][j];
+    }
+    __syncthreads();
+  }
 
   float m_run[CT], l_run[CT];
   f32x4 acc[CT][DT];
@@ -380,7 +394,8 @@ void decode_mfma(DecodeArgs a) {
         s[ct][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < KS; ++j)
-          s[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j], qv[ct][j], s[ct][tt], 0, 0, 0);
+          s[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j], kQInLds ? s_q[ct * KS + j][lane] : qv[ct][j],
+                                                              s[ct][tt], 0, 0, 0);
       }
     }
     s16x4 p_hi[CT][TT], p_lo[CT][TT];
