@@ -17,8 +17,8 @@ Sources (the pages, cited by title and section):
   -- ``PagedKVPool`` (preflighted multi-token append, share_prefix, release,
   fill accounting, ``validate``) and its embedded reference contract; its
   KV-compression experiment (per-row absmax codes, ``fake_quantize_rows``);
-  its prefix-caching cell (``prefix_key``, ``run_prefix_trace``); its
-  eviction cell (``streaming_keep_indices``) and explicit window caches.
+  its prefix-caching cell (block keys, ``run_prefix_trace``); its
+  eviction cell (the streaming keep rule) and explicit window caches.
 * docs.rs ferrum-kv 0.4.0 ``src/attention.rs`` -- ``paged_attention``
   (GQA head grouping, 1/sqrt(head_dim) scale, bottom-right causal mask).
 * CMU 11-667 lecture 19 ``infer_world.py``, section 3 "online softmax and
@@ -36,8 +36,8 @@ Modules:
   definition); a ``Pool(quant_fp8=True)`` stores through it.
 * :mod:`oracle.prefix` -- prefix-hash block reuse: complete-block keys
   (scope, revision, all preceding tokens) mapped to pinned pool blocks.
-* :mod:`oracle.window` -- sliding-window attention with sinks
-  (``streaming_keep_indices``) over the resident rows of a windowed pool
+* :mod:`oracle.window` -- sliding-window attention with sinks (the keep
+  rule as ``window_keep``) over the resident rows of a windowed pool
   sequence.
 * :mod:`oracle.attention` -- the attention definition, its online-softmax
   restatement, the log-sum-exp merge of partial results and a pure-Python
@@ -66,11 +66,12 @@ from .fp8 import (
     dequantize_rows_fp8,
     fake_quantize_rows_fp8,
 )
-from .prefix import PrefixCache, prefix_key, run_prefix_trace
-from .window import streaming_keep_indices, windowed_attention
+from .prefix import BlockKey, PrefixCache, block_key, run_prefix_trace
+from .window import window_keep, windowed_attention
 from .attention import (
     attention,
     paged_attention,
+    combine_stats,
     online_softmax_stats,
     tiled_attention,
     brute_force_attention,
@@ -85,6 +86,7 @@ __all__ = [
     "SequenceExists",
     "attention",
     "paged_attention",
+    "combine_stats",
     "online_softmax_stats",
     "tiled_attention",
     "brute_force_attention",
@@ -104,8 +106,9 @@ __all__ = [
     "dequantize_rows_fp8",
     "fake_quantize_rows_fp8",
     "PrefixCache",
-    "prefix_key",
+    "BlockKey",
+    "block_key",
     "run_prefix_trace",
-    "streaming_keep_indices",
+    "window_keep",
     "windowed_attention",
 ]

@@ -35,6 +35,7 @@ Readings where the pages are silent or differ: an empty cache
 
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -91,15 +92,30 @@ def paged_attention(pool, seq, q):
     return attention(q, K, V)
 
 
+def _score_stats(block):
+    """(max, sum of exp(s - max)) of one block of scores; (-inf, 0) when
+    the block is empty or wholly masked."""
+    x = np.asarray(block, dtype=np.float64).ravel()
+    top = float(x.max()) if x.size else -math.inf
+    if top == -math.inf:
+        return -math.inf, 0.0
+    return top, float(np.exp(x - top).sum())
+
+
+def combine_stats(a, b):
+    """Statistics of the union of two score sets from theirs: the larger
+    maximum, and each normaliser moved onto it by exp(m - max)."""
+    top = max(a[0], b[0])
+    if top == -math.inf:
+        return -math.inf, 0.0
+    return top, sum(l * math.exp(m - top) for m, l in (a, b) if m != -math.inf)
+
+
 def online_softmax_stats(score_blocks):
-    """Running (max, normaliser) over a stream of score blocks."""
-    m, l = -math.inf, 0.0
-    for block in score_blocks:
-        block = np.asarray(block, dtype=np.float64)
-        m_new = max(m, float(block.max()))
-        l = l * math.exp(m - m_new) + float(np.exp(block - m_new).sum())
-        m = m_new
-    return m, l
+    """Running (max, normaliser) over a stream of score blocks, folded one
+    block at a time with :func:`combine_stats`; softmax(x)_i is then
+    exp(x_i - max) / normaliser."""
+    return functools.reduce(combine_stats, map(_score_stats, score_blocks), (-math.inf, 0.0))
 
 
 def tiled_attention(q, K, V, block):

@@ -250,8 +250,7 @@ class Pool:
     # ------------------------------------------------------------ windows
     def set_window(self, seq, sinks, recent):
         """Give ``seq`` a (sinks, recent) window: its queries see the
-        positions oracle.window.streaming_keep_indices keeps with budget
-        ``sinks + recent``, and appends release the pages no later query of
+        positions oracle.window.window_keep keeps, and appends release the pages no later query of
         the appended rows can see."""
         self._existing(seq)
         sinks = _non_negative_int(sinks, "sinks")

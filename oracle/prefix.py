@@ -3,7 +3,7 @@
 Test infrastructure only (see the package docstring).
 
 Source: vladkulikov.com notebook "Модуль 10. KV-кэши и эффективный
-инференс", the prefix-caching cell (``prefix_key`` and ``run_prefix_trace``)
+инференс", the prefix-caching cell (its block keys and ``run_prefix_trace``)
 and the context / model-revision identity checks after it.
 
 * A cache key exists only at a complete block boundary ``end`` (a multiple of
@@ -30,12 +30,28 @@ Readings taken here (the notebook's cache is a set of keys with no pool):
 
 from __future__ import annotations
 
+from typing import NamedTuple
+
 from .pool import HOLE
 
 
-def prefix_key(tokens, end, scope, revision):
-    """The key of the complete block ending at ``end``."""
-    return (scope, revision, tuple(tokens[:end]))
+class BlockKey(NamedTuple):
+    """Identity of the complete block ending at token index ``end`` of a
+    request: its scope and model revision, and the ids of every token before
+    ``end`` (so the same block content after another context is another
+    key)."""
+
+    scope: str
+    revision: str
+    context: tuple
+
+
+def block_key(scope, revision, tokens, end):
+    """:class:`BlockKey` of the complete block ending at ``end`` (a multiple
+    of the block size, at most ``len(tokens)``)."""
+    if not 0 < end <= len(tokens):
+        raise ValueError("a block key ends inside the request")
+    return BlockKey(scope, revision, tuple(int(t) for t in tokens[:end]))
 
 
 class PrefixCache:
@@ -50,7 +66,7 @@ class PrefixCache:
         bs = self.pool.block_size
         hit = 0
         for end in range(bs, len(tokens) + 1, bs):
-            if prefix_key(tokens, end, scope, revision) not in self.entries:
+            if block_key(scope, revision, tokens, end) not in self.entries:
                 break
             hit = end
         return hit
@@ -59,7 +75,7 @@ class PrefixCache:
         """New sequence holding the cached blocks of its hit; returns the hit."""
         bs = self.pool.block_size
         hit = self.lookup(tokens, scope, revision)
-        blocks = [self.entries[prefix_key(tokens, end, scope, revision)]
+        blocks = [self.entries[block_key(scope, revision, tokens, end)]
                   for end in range(bs, hit + 1, bs)]
         self.pool.adopt(seq, blocks, hit)
         return hit
@@ -76,7 +92,7 @@ class PrefixCache:
         for end in range(bs, len(tokens) + 1, bs):
             if table[end // bs - 1] == HOLE:
                 break  # keys stop at the first page a window released
-            key = prefix_key(tokens, end, scope, revision)
+            key = block_key(scope, revision, tokens, end)
             if key in self.entries:
                 continue
             block = table[end // bs - 1]

@@ -5,11 +5,9 @@ Test infrastructure only (see the package docstring).
 Sources: vladkulikov.com notebook "Модуль 10. KV-кэши и эффективный
 инференс":
 
-* the eviction cell, ``streaming_keep_indices(length, budget, sink_tokens)``:
-  with ``n = length`` tokens and ``budget`` kept, a sequence no longer than
-  the budget keeps everything; otherwise the first ``min(sinks, n)`` tokens
-  (the sinks) and the most recent ``budget - sinks`` tokens; ``sinks`` may
-  not exceed the budget;
+* the eviction cell's streaming rule: a sequence keeps its first ``sinks``
+  tokens and its latest tokens up to a fixed budget, everything when it is
+  no longer than the budget; the sinks may not exceed the budget;
 * the explicit window caches (``NumpyKVCacheExplicit`` with ``window``): a
   query attends over the cache it sees, and a rollback (``truncate``) cannot
   bring back evicted tokens.
@@ -18,9 +16,9 @@ Readings taken here:
 
 * query row t of a sequence whose K/V rows cover positions ``[0, L)`` and
   whose last ``q_len`` positions are being queried is itself position
-  ``L - q_len + t``; it sees the positions ``streaming_keep_indices(L -
-  q_len + t + 1, sinks + recent, sinks)`` (its causal prefix, then the
-  window rule);
+  ``L - q_len + t``; it sees the positions ``window_keep(L - q_len + t + 1,
+  sinks, recent)`` (its causal prefix, then the window rule with budget
+  ``sinks + recent``);
 * positions whose rows were evicted are gone: a row sees the kept positions
   that are still resident (the explicit caches attend over what they hold).
 """
@@ -32,20 +30,20 @@ import numpy as np
 from .attention import attention
 
 
-def streaming_keep_indices(length, budget, sink_tokens):
-    """Kept positions of a ``length``-token sequence under ``budget``."""
-    for name, value, low in (("length", length, 0), ("budget", budget, 1), ("sink_tokens", sink_tokens, 0)):
-        if isinstance(value, bool) or not isinstance(value, (int, np.integer)) or value < low:
-            raise ValueError(f"{name} must be an integer >= {low}")
-    n, keep, sinks = int(length), int(budget), int(sink_tokens)
-    if sinks > keep:
-        raise ValueError("sink_tokens cannot exceed budget")
-    if n <= keep:
-        return tuple(range(n))
-    sink_count = min(sinks, n)
-    recent_count = keep - sink_count
-    recent_start = max(sink_count, n - recent_count)
-    return tuple(range(sink_count)) + tuple(range(recent_start, n))
+def window_keep(length, sinks, recent):
+    """Positions of a ``length``-token prefix that a window of ``sinks``
+    leading tokens and ``recent`` latest tokens keeps (the streaming rule
+    with budget ``sinks + recent``): position p stays when it is a sink, p <
+    sinks, or one of the latest, p >= length - recent.  A prefix no longer
+    than the budget keeps every position, since then length - recent <=
+    sinks."""
+    for name, value in (("length", length), ("sinks", sinks), ("recent", recent)):
+        if isinstance(value, bool) or not isinstance(value, (int, np.integer)) or value < 0:
+            raise ValueError(f"{name} must be a non-negative integer")
+    if sinks + recent < 1:
+        raise ValueError("the window must keep at least one position")
+    first_recent = int(length) - int(recent)
+    return tuple(p for p in range(int(length)) if p < sinks or p >= first_recent)
 
 
 def windowed_attention(q, keys, values, positions, length, sinks, recent):
@@ -54,7 +52,7 @@ def windowed_attention(q, keys, values, positions, length, sinks, recent):
 
     ``keys`` / ``values`` ``[n, Hkv, D]`` are the resident rows, at
     ``positions`` (ascending).  Row t uses the resident positions among
-    ``streaming_keep_indices(length - q_len + t + 1, sinks + recent, sinks)``.
+    ``window_keep(length - q_len + t + 1, sinks, recent)``.
     """
     q = np.asarray(q, dtype=np.float64)
     positions = list(positions)
@@ -62,7 +60,7 @@ def windowed_attention(q, keys, values, positions, length, sinks, recent):
     q_len = q.shape[0]
     out = np.empty_like(q)
     for t in range(q_len):
-        kept = streaming_keep_indices(length - q_len + t + 1, sinks + recent, sinks)
+        kept = window_keep(length - q_len + t + 1, sinks, recent)
         rows = [index[p] for p in kept if p in index]
         if not rows:
             raise ValueError(f"row {t} sees no resident key")

@@ -24,7 +24,7 @@ import numpy as np
 import pytest
 
 from oracle import (Pool, attention, brute_force_attention, merge_partials,
-                    online_softmax_stats, paged_attention, partial_attention,
+                    combine_stats, online_softmax_stats, paged_attention, partial_attention,
                     tiled_attention)
 from synth import logical_kv, append_stream, prefix_prefill, gqa_decode, tiny_fp32
 
@@ -118,6 +118,24 @@ def test_online_softmax_stats_is_max_and_normaliser():
     m, l = online_softmax_stats(blocks)
     assert m == x.max()
     np.testing.assert_allclose(l, np.exp(x - x.max()).sum(), rtol=1e-14)
+
+
+def test_online_stats_in_any_block_order_and_with_masked_blocks():
+    """The fold does not depend on how the scores are cut into blocks or in
+    which order the blocks come, and an empty or wholly masked block (all
+    -inf) contributes nothing."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal(40) * 5
+    want = (x.max(), np.exp(x - x.max()).sum())
+    cuts = [x[:7], np.array([]), x[7:30], np.full(3, -np.inf), x[30:]]
+    for blocks in (cuts, cuts[::-1], [x[i:i + 1] for i in range(40)]):
+        m, l = online_softmax_stats(blocks)
+        assert m == want[0]
+        np.testing.assert_allclose(l, want[1], rtol=1e-13)
+    assert online_softmax_stats([np.full(2, -np.inf)]) == (-np.inf, 0.0)
+    assert combine_stats((1.5, 2.0), (-np.inf, 0.0)) == (1.5, 2.0)
+    # Two equal maxima add their normalisers.
+    assert combine_stats((0.0, 1.0), (0.0, 3.0)) == (0.0, 4.0)
 
 
 def test_partials_merge_to_attention():

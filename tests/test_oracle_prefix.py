@@ -26,7 +26,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import Pool, PrefixCache, prefix_key, run_prefix_trace
+from oracle import Pool, PrefixCache, block_key, run_prefix_trace
 from synth import prefix_trace_requests
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "p2_prefix_trace.json")
@@ -63,8 +63,8 @@ def test_notebook_key_identity():
     b = a.copy()
     b[0] = 999
     assert a[16:32] == b[16:32]
-    assert prefix_key(a, 32, "scope", "r1") != prefix_key(b, 32, "scope", "r1")
-    assert prefix_key(a, 32, "scope", "r1") != prefix_key(a, 32, "scope", "r2")
+    assert block_key("scope", "r1", a, 32) != block_key("scope", "r1", b, 32)
+    assert block_key("scope", "r1", a, 32) != block_key("scope", "r2", a, 32)
     # ... and through a cache: the second block of b is not found after a.
     pool = Pool(16, 16, store_values=False)
     cache = PrefixCache(pool)
@@ -143,7 +143,7 @@ def _mutant_no_stop_lookup(cache, tokens, scope, rev):
     bs = cache.pool.block_size
     hit = 0
     for end in range(bs, len(tokens) + 1, bs):
-        if prefix_key(tokens, end, scope, rev) in cache.entries:
+        if block_key(scope, rev, tokens, end) in cache.entries:
             hit = end
     return hit
 
@@ -154,7 +154,7 @@ def test_pins_reject_planted_mistakes():
     b = a.copy()
     b[0] = 999
     assert _mutant_block_only_key(a, 32, "scope", "r1") == _mutant_block_only_key(b, 32, "scope", "r1")
-    assert prefix_key(a, 32, "scope", "r1") != prefix_key(b, 32, "scope", "r1")
+    assert block_key("scope", "r1", a, 32) != block_key("scope", "r1", b, 32)
     # A walk that does not stop at the first miss: the brute-force pin fails.
     pool = Pool(16, 16, store_values=False)
     cache = PrefixCache(pool)
@@ -162,6 +162,6 @@ def test_pins_reject_planted_mistakes():
     pool.append(0, 48)
     toks = list(range(48))
     cache.register(0, toks, "s", "r")
-    del cache.entries[prefix_key(toks, 16, "s", "r")]
+    del cache.entries[block_key("s", "r", toks, 16)]
     assert _mutant_no_stop_lookup(cache, toks, "s", "r") == 48
     assert cache.lookup(toks, "s", "r") == 0 == _brute_hit([], toks, 16)

@@ -27,7 +27,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import Pool, attention, brute_force_attention, streaming_keep_indices, windowed_attention
+from oracle import Pool, attention, brute_force_attention, window_keep, windowed_attention
 from oracle.pool import HOLE
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "p2_eviction.json")
@@ -36,16 +36,23 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "p2_eviction.json")
 def test_notebook_streaming_keep_set():
     g = json.load(open(GOLDEN))
     n = len(g["attention_mass"])
-    keep = streaming_keep_indices(n, g["budget"], g["sink_tokens"])
+    sinks = g["sink_tokens"]
+    keep = window_keep(n, sinks, g["budget"] - sinks)
     assert list(keep) == g["streaming"]
     assert sorted(set(g["heavy_hitters"]) - set(keep)) == g["lost_heavy_hitters"]
-    assert streaming_keep_indices(5, 8, 4) == (0, 1, 2, 3, 4)
-    assert streaming_keep_indices(9, 8, 0) == tuple(range(1, 9))
-    assert streaming_keep_indices(9, 8, 8) == tuple(range(8))
+    assert window_keep(5, 4, 4) == (0, 1, 2, 3, 4)
+    assert window_keep(9, 0, 8) == tuple(range(1, 9))
+    assert window_keep(9, 8, 0) == tuple(range(8))
+    # The budget always holds exactly min(length, budget) positions.
+    for length in range(12):
+        for s in range(5):
+            for r in range(5):
+                if s + r:
+                    assert len(window_keep(length, s, r)) == min(length, s + r)
+    with pytest.raises(ValueError):  # sinks above the budget: a negative recent part
+        window_keep(9, 5, -1)
     with pytest.raises(ValueError):
-        streaming_keep_indices(9, 4, 5)
-    with pytest.raises(ValueError):
-        streaming_keep_indices(9, 0, 0)
+        window_keep(9, 0, 0)
 
 
 def _window_pool(bs, recent, sinks=0, nb=64, d=2):
@@ -152,17 +159,16 @@ def test_recent_zero_keeps_the_appended_pages():
         pool.append(0, 1)
         pool.validate()
         assert pool.tables[0][-1] != HOLE
-    assert streaming_keep_indices(9, 2, 2) == (0, 1)
+    assert window_keep(9, 2, 0) == (0, 1)
 
 
 # ------------------------------------------------------------ planted mistakes
 def _mutant_wide(length, budget, sinks):
-    keep = streaming_keep_indices(length, budget + 1, sinks) if length > budget else tuple(range(length))
-    return keep
+    return window_keep(length, sinks, budget - sinks + 1) if length > budget else tuple(range(length))
 
 
 def _mutant_no_sinks(length, budget, sinks):
-    return streaming_keep_indices(length, budget, 0)
+    return window_keep(length, 0, budget)
 
 
 def test_pins_reject_planted_mistakes():
