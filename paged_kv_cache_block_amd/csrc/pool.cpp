@@ -411,68 +411,61 @@ PoolStats BlockPool::stats() const {
   return st;
 }
 
+// The invariants the [PagedPool] validate method states, recomputed from the
+// tables: (1) a table holds ceil(length / block_size) pages, no block twice,
+// and never a released partial tail; (2) a block's refcount is the number of
+// tables that list it plus its pins; (3) a block is free exactly when its
+// refcount is 0, and every free block can be drawn from the free heap; (4) a
+// block's fill is 0 unless a table lists it, then 1..block_size; (5) the
+// logical tokens are at least the physical payload.
 Status BlockPool::validate(std::string* msg) const {
-  std::vector<int32_t> expected(num_blocks_, 0);
+  auto broken = [msg](const std::string& what, int64_t at) {
+    *msg = "pool invariant broken: " + what + " (at " + std::to_string(at) + ")";
+    return kInvalidArg;
+  };
+  std::vector<int32_t> listed_by(num_blocks_, 0);
+  std::vector<int64_t> stamp(num_blocks_, -1);  // last table (by visit number) that listed the block
+  int64_t visit = 0;
   for (const auto& kv : seqs_) {
     const Sequence& s = kv.second;
-    if (s.length < 0) { *msg = "negative sequence length"; return kInvalidArg; }
-    if (static_cast<int64_t>(s.table.size()) != ceil_div(s.length, block_size_)) {
-      *msg = "page-table length does not match sequence length";
-      return kInvalidArg;
+    if (s.length < 0 || static_cast<int64_t>(s.table.size()) != ceil_div(s.length, block_size_))
+      return broken("table size is not ceil(length / block_size) for sequence", kv.first);
+    const size_t n = s.table.size();
+    for (size_t i = 0; i < n; ++i) {
+      const int32_t b = s.table[i];
+      if (b == kHole) {
+        if (i + 1 == n && s.length % block_size_)
+          return broken("the partially filled last page is released in sequence", kv.first);
+        continue;
+      }
+      if (b < 0 || b >= num_blocks_) return broken("block id outside the pool in sequence", kv.first);
+      if (stamp[b] == visit) return broken("a block appears twice in the table of sequence", kv.first);
+      stamp[b] = visit;
+      ++listed_by[b];
     }
-    std::vector<int32_t> sorted;
-    for (int32_t b : s.table)
-      if (b != kHole) sorted.push_back(b);
-    std::sort(sorted.begin(), sorted.end());
-    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) {
-      *msg = "one sequence references a physical block twice";
-      return kInvalidArg;
-    }
-    if (!s.table.empty() && s.length % block_size_ && s.table.back() == kHole) {
-      *msg = "a partially filled tail page was released";
-      return kInvalidArg;
-    }
-    for (int32_t b : sorted) {
-      if (b < 0 || b >= num_blocks_) { *msg = "page table contains an invalid block id"; return kInvalidArg; }
-      ++expected[b];
-    }
+    ++visit;
   }
-  // Free set = the free flags; every free block has an entry in the heap.
-  const std::vector<char>& is_free = is_free_;
-  std::vector<char> in_heap(num_blocks_, 0);
-  auto heap = free_heap_;
-  while (!heap.empty()) {
-    int32_t r = heap.top();
-    heap.pop();
-    if (r < 0 || r >= num_blocks_) { *msg = "free list contains an invalid block id"; return kInvalidArg; }
-    in_heap[order_[r]] = 1;
+  std::vector<char> drawable(num_blocks_, 0);
+  for (auto heap = free_heap_; !heap.empty(); heap.pop()) {
+    const int32_t r = heap.top();
+    if (r < 0 || r >= num_blocks_) return broken("free-heap rank outside the pool", r);
+    drawable[order_[r]] = 1;
   }
-  int64_t n_free = 0;
+  const std::vector<int32_t> fill = fills();
+  int64_t free_blocks = 0;
   for (int32_t b = 0; b < num_blocks_; ++b) {
-    if (is_free[b] && !in_heap[b]) { *msg = "free block missing from the free list"; return kInvalidArg; }
-    n_free += is_free[b];
+    if (refs_[b] != listed_by[b] + pins_[b]) return broken("refcount != table references + pins of block", b);
+    const bool is_free = is_free_[b] != 0;
+    if (is_free != (refs_[b] == 0)) return broken("free flag disagrees with the refcount of block", b);
+    if (is_free && !drawable[b]) return broken("free block missing from the free heap", b);
+    free_blocks += is_free;
+    const int32_t lo = listed_by[b] ? 1 : 0, hi = listed_by[b] ? block_size_ : 0;
+    if (fill[b] < lo || fill[b] > hi) return broken("fill outside its range for block", b);
   }
-  if (n_free != n_free_) { *msg = "free count does not match the free flags"; return kInvalidArg; }
-  std::vector<int32_t> fill = fills();
-  for (int32_t b = 0; b < num_blocks_; ++b) {
-    if (refs_[b] != expected[b] + pins_[b]) {
-      *msg = "physical ref_count does not match page tables plus pins";
-      return kInvalidArg;
-    }
-    if (refs_[b] == 0) {
-      if (!is_free[b] || fill[b] != 0) { *msg = "unreferenced block is not clean and free"; return kInvalidArg; }
-    } else if (expected[b] == 0) {
-      if (is_free[b]) { *msg = "pinned block appears in free list"; return kInvalidArg; }
-    } else {
-      if (is_free[b]) { *msg = "referenced block appears in free list"; return kInvalidArg; }
-      if (fill[b] < 1 || fill[b] > block_size_) { *msg = "referenced block has invalid fill"; return kInvalidArg; }
-    }
-  }
-  PoolStats st = stats();
-  if (st.logical_tokens < st.physical_payload_tokens) {
-    *msg = "physical payload exceeds logical payload";
-    return kInvalidArg;
-  }
+  if (free_blocks != n_free_) return broken("free-block counter differs from the free flags", n_free_);
+  const PoolStats st = stats();
+  if (st.logical_tokens < st.physical_payload_tokens)
+    return broken("physical payload tokens exceed logical tokens", st.physical_payload_tokens);
   return kOk;
 }
 
