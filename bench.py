@@ -199,6 +199,32 @@ def percentiles_us(samples_ms):
     return {"p10": round(float(p10), 2), "p50": round(float(p50), 2), "p90": round(float(p90), 2)}
 
 
+def step_spread(step, indices):
+    """Spread of the step time: the steps ``indices`` run back to back with
+    one event recorded on the stream before each and one after the last;
+    the interval between consecutive events is one step on the GPU's clock
+    (the events add a few microseconds each, so the mean here sits above
+    the event-free timed loop's)."""
+    import torch
+    indices = list(indices)
+    if not indices:
+        return {}
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(indices) + 1)]
+    torch.cuda.synchronize()
+    settle()
+    for e, i in zip(evs, indices):
+        e.record()
+        step(i)
+    evs[-1].record()
+    evs[-1].synchronize()
+    unsettle()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(evs[:-1], evs[1:])])
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"what": f"{len(us)} more steps, an event before each (adds its own few us)",
+            "mean": round(float(us.mean()), 2), "p10": round(float(p10), 2), "p50": round(float(p50), 2),
+            "p90": round(float(p90), 2), "max": round(float(us.max()), 2)}
+
+
 def run_decode(args, kv="bf16", window=None, cold_steps=0):
     """Decode steps of workload 2 over ``args.layers`` layers' pools taken in
     turn (a step is one layer's pa_decode_step), so no step finds the pages it
@@ -221,10 +247,14 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     B = len(seqs)
     q = to_device(decode_queries(wl), wl.dtype)
     out = torch.empty_like(q)
-    total_steps = args.warmup + args.steps
+    # Every layer's pool takes at least one untimed step before the timed
+    # loop, whatever --warmup is.
+    warm = max(args.warmup, n_layers)
+    total_steps = warm + args.steps
     extra_steps = 10  # after the timed region: merge / prologue kernel timing
+    spread_steps = args.steps  # then the per-step spread, one event between steps
     gen = torch.Generator(device="cuda").manual_seed(1234)
-    n_new = total_steps + extra_steps + cold_steps
+    n_new = total_steps + extra_steps + spread_steps + cold_steps
     new_k = torch.randn((n_new, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     new_v = torch.randn((n_new, B, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     # lengths[l]: the sequence lengths of layer l's pool (each grows by 1 per step of that layer)
@@ -251,8 +281,8 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
         return window_alg_bytes(lens, wl, *window) if window else decode_alg_bytes(lens, wl, kv)
 
     settle()
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
+    log(f"warmup {warm} steps")
+    for i in range(warm):
         step(i)
     torch.cuda.synchronize()
     abi.pa_timing_reset()
@@ -266,7 +296,7 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     host_ms = []  # host time of each timed call (the call returns before its kernels finish)
-    for j, i in enumerate(range(args.warmup, total_steps)):
+    for j, i in enumerate(range(warm, total_steps)):
         timed = j % SAMPLE_EVERY == 0
         if timed:
             abi.pa_timing_enable(True)
@@ -292,6 +322,8 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
     abi.pa_timing_select(None)
     mrg_ms, mrg_n = abi.pa_timing_read(abi.PA_KERNEL_MERGE)
     cache_ms, cache_n = abi.pa_timing_read(abi.PA_KERNEL_CACHE)
+    first_spread = total_steps + extra_steps
+    spread = step_spread(step, range(first_spread, first_spread + spread_steps))
     cold = None
     if cold_steps:
         # Cold caches: before each step a read of 1 GiB (outside the events)
@@ -304,7 +336,7 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
         abi.pa_timing_select([abi.PA_KERNEL_DECODE])
         abi.pa_timing_enable(True)
         cold_alg = []
-        for c, i in enumerate(range(total_steps + extra_steps, n_new)):
+        for c, i in enumerate(range(first_spread + spread_steps, n_new)):
             torch.sum(flush, dim=0, out=sink[c])
             cold_alg.append(step_bytes(step(i)))
         torch.cuda.synchronize()
@@ -338,6 +370,8 @@ def run_decode(args, kv="bf16", window=None, cold_steps=0):
         "layers": n_layers,
         "host_call_ms": {"p50": round(float(np.median(host_ms)), 4), "max": round(float(np.max(host_ms)), 3),
                          "max_at_step": int(np.argmax(host_ms))},
+        "step_us_pct": spread,
+        "warmup_steps_run": warm,
     }
     if cold:
         result["cold_cache"] = cold
@@ -371,10 +405,12 @@ def run_verify(args, q_len=4):
     B = len(seqs)
     q_lens = [q_len] * B
     R = B * q_len
-    total_steps = args.warmup + args.steps
+    warm = max(args.warmup, n_layers)  # every layer's pool takes an untimed step first
+    total_steps = warm + args.steps
+    n_new = total_steps + args.steps  # then the per-step spread
     gen = torch.Generator(device="cuda").manual_seed(4321)
-    new_k = torch.randn((total_steps, R, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
-    new_v = torch.randn((total_steps, R, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    new_k = torch.randn((n_new, R, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    new_v = torch.randn((n_new, R, wl.num_kv_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     q = torch.randn((R, wl.num_heads, wl.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
     out = torch.empty_like(q)
     lengths = [np.array([pool.seq_len(s) for s in seqs], dtype=np.int64) for pool in pools]
@@ -398,14 +434,14 @@ def run_verify(args, q_len=4):
         return decode_alg_bytes(lens, wl) + 2 * (R - B) * wl.num_heads * wl.head_dim * wl.elt_bytes
 
     settle()
-    for i in range(args.warmup):
+    for i in range(warm):
         step(i)
     torch.cuda.synchronize()
     abi.pa_timing_reset()
     abi.pa_timing_select([abi.PA_KERNEL_DECODE])
     alg = []
     t0 = time.perf_counter()
-    for j, i in enumerate(range(args.warmup, total_steps)):
+    for j, i in enumerate(range(warm, total_steps)):
         timed = j % SAMPLE_EVERY == 0
         if timed:
             abi.pa_timing_enable(True)
@@ -418,6 +454,7 @@ def run_verify(args, q_len=4):
     unsettle()
     abi.pa_timing_select(None)
     dec_ms, dec_n = abi.pa_timing_read(abi.PA_KERNEL_DECODE)
+    spread = step_spread(step, range(total_steps, n_new))
     for pool in pools:
         pool.validate()
         pool.close()
@@ -425,7 +462,7 @@ def run_verify(args, q_len=4):
     kernel_ms = dec_ms / max(dec_n, 1)
     return {"workload": f"gqa_decode with {q_len} query rows per sequence and step (pa_verify_step: "
                         f"append {q_len} tokens + store their K/V + causal attention)",
-            "ms_per_step": round(ms, 5), "rows_per_s": round(R / (ms * 1e-3), 1),
+            "ms_per_step": round(ms, 5), "step_us_pct": spread, "rows_per_s": round(R / (ms * 1e-3), 1),
             "decode_kernel_us": round(kernel_ms * 1e3, 2),
             "kernel_GBs": round(float(np.mean([step_bytes(x) for x in alg])) / (kernel_ms * 1e-3) / 1e9, 1)}
 
@@ -671,9 +708,10 @@ def main():
                    "global_batch": 32, "seq_len": "U[1,8192]", "parallelism": "single GPU"},
         "tokens_per_s": round(dec["tokens_per_s"], 1),
         "hbm_frac_step": round(dec["value"] / HBM_PEAK_GBS, 4),
+        "step_us_pct": dec["step_us_pct"],
         "decode": {k: dec[k] for k in ("decode_kernel_us", "decode_kernel_us_pct", "merge_kernel_us",
                                         "cache_kernel_us", "alg_bytes_per_step", "kernel_launches", "sum_len",
-                                        "host_call_ms", "cold_cache") if k in dec},
+                                        "host_call_ms", "warmup_steps_run", "cold_cache") if k in dec},
         "roofline": dec["roofline"],
         "device_copy_GBs": device_copy_gbs(),
     }
@@ -686,6 +724,7 @@ def main():
             "workload": f"the same decode steps over {what} K/V pages (one fp32 scale per token and "
                         "KV head row; bf16 q, out and new rows)",
             "ms_per_step": round(q8["ms_per_step"], 5),
+            "step_us_pct": q8["step_us_pct"],
             "tokens_per_s": round(q8["tokens_per_s"], 1),
             "kv_GBs_step": round(q8["value"], 2),
             "decode": {k: q8[k] for k in ("decode_kernel_us", "decode_kernel_us_pct", "merge_kernel_us",
@@ -705,6 +744,7 @@ def main():
             "workload": "the same decode steps with a window on every sequence: 4 sink tokens + the "
                         "1024 most recent (pages outside released by the appends)",
             "ms_per_step": round(wdec["ms_per_step"], 5),
+            "step_us_pct": wdec["step_us_pct"],
             "tokens_per_s": round(wdec["tokens_per_s"], 1),
             "decode_kernel_us": round(wdec["decode_kernel_us"], 2),
             "kernel_GBs": wdec["roofline"]["achieved"],

@@ -167,10 +167,26 @@ size_t pa_pool_bytes(const pa_pool_desc* desc);
  *   on it fails with PA_ERR_INVALID_ARG).  The caller keeps ownership and
  *   must keep them alive until pa_pool_destroy.
  * out: receives the new pool.
+ * A pool with device memory also reserves its ring of 4 pinned host staging
+ *   buffers here (through which plans cross to the device), each of
+ *   min(8 * num_blocks + 256 KiB, 8 MiB) bytes, so the attention calls
+ *   allocate nothing while their plans fit (pa_pool_reserve_staging).
  * Errors: PA_ERR_INVALID_ARG for a bad descriptor, a non-permutation order,
- *   exactly one NULL pool pointer, misaligned pools or a NULL `out`. */
+ *   exactly one NULL pool pointer, misaligned pools or a NULL `out`;
+ *   PA_ERR_DEVICE if the staging buffers cannot be allocated. */
 pa_status pa_pool_create(const pa_pool_desc* desc, const int32_t* allocation_order,
                          void* k_pool, void* v_pool, pa_pool** out);
+
+/* Grow each of the pool's 4 pinned staging buffers to at least plan_bytes
+ * (buffers still in use by enqueued work are waited for first; none
+ * shrinks).  A call whose plan exceeds the reserved size grows the ring
+ * inside that call (pinned allocation).  A plan is at most the metadata part of the
+ * workspace the *_workspace_bytes calls return, so reserving that much is
+ * always enough.  reserved: host, may be NULL; receives the size now
+ * reserved per buffer.  Host-side; allocates pinned host memory.
+ * Errors: PA_ERR_INVALID_ARG (NULL or metadata-only pool, plan_bytes above
+ *   4 GiB), PA_ERR_DEVICE. */
+pa_status pa_pool_reserve_staging(pa_pool* pool, size_t plan_bytes, size_t* reserved);
 
 /* Free the pool's host metadata and staging buffers (waits for the pool's
  * own pending uploads).  NULL is ignored. */
@@ -193,7 +209,12 @@ pa_status pa_seq_create(pa_pool* pool, int64_t seq);
  *   slot of each new position p = old_len .. old_len+n_tokens-1, i.e.
  *   table[p / block_size] * block_size + p % block_size.  Pass them (on the
  *   device) to pa_reshape_and_cache.
- * This call is host-only: it launches nothing.
+ * This call is host-only: it launches nothing.  Hazard of the deferred
+ *   copy: until the next device call on this pool (or pa_flush_copies) has
+ *   been enqueued, the new tail block does not hold the old tail's rows yet,
+ *   and the old block must still hold them.  So the caller must not write
+ *   the pool's device memory by other means (a torch copy into the pools,
+ *   another library) before that call: flush first, on the same stream.
  * Errors: PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG (n_tokens < 0, NULL
  *   slots_out with n_tokens > 0), PA_ERR_OUT_OF_BLOCKS. */
 pa_status pa_append(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slots_out);
@@ -310,12 +331,28 @@ pa_status pa_flush_copies(pa_pool* pool, void* stream);
  * k_new, v_new: device [n][num_kv_heads][head_dim]; slots: device int64 [n].
  * An I8 or FP8 pool stores each row's codes and scale instead ([KVquant];
  * the layout and rounding are in the header comment).
- * A slot outside [0, num_blocks * block_size) is skipped.  Two rows naming
- * one slot race.  Pending copies are flushed first on `stream`.
+ * Without slot checks (the default) a slot outside [0, num_blocks *
+ * block_size) is skipped and two rows naming one slot race; with them
+ * (pa_pool_set_slot_checks) the call is rejected first.  Pending copies are
+ * flushed first on `stream`.
  * Errors: PA_ERR_INVALID_ARG (NULL pointers with n > 0, n < 0,
- *   metadata-only pool), PA_ERR_DEVICE. */
+ *   metadata-only pool; with slot checks on, a bad slot), PA_ERR_DEVICE. */
 pa_status pa_reshape_and_cache(pa_pool* pool, const void* k_new, const void* v_new,
                                const int64_t* slots, int32_t n, void* stream);
+
+/* Debug checks of this pool's pa_reshape_and_cache calls, off by default
+ * (validate before mutate, as [PagedPool]'s negative tests ask of every
+ * operation).  When on, each call first checks on the device, before it
+ * writes anything, that every slot lies in [0, num_blocks * block_size) and
+ * that no two rows of the call name one slot; it waits for that check
+ * (synchronizing `stream`) and on failure returns PA_ERR_INVALID_ARG naming
+ * an offending row and its slot, with the pool's memory and pending copies
+ * untouched.  Turning the checks on allocates 4 bytes of device memory per
+ * slot, zeroed on `stream`; turning them off (or pa_pool_destroy) frees it
+ * after waiting for the device.  The fused steps compute their slots
+ * themselves and are not checked.
+ * Errors: PA_ERR_INVALID_ARG (NULL or metadata-only pool), PA_ERR_DEVICE. */
+pa_status pa_pool_set_slot_checks(pa_pool* pool, int on, void* stream);
 
 /* ------------------------------------------------------------ attention --- */
 

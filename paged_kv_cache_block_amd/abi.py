@@ -99,6 +99,7 @@ SIGNATURES = {
     "pa_pool_create": (_i32, [ctypes.POINTER(pa_pool_desc), _i32p, _c_void_p, _c_void_p,
                               ctypes.POINTER(_c_void_p)]),
     "pa_pool_destroy": (None, [_c_void_p]),
+    "pa_pool_reserve_staging": (_i32, [_c_void_p, _size, ctypes.POINTER(_size)]),
     "pa_seq_create": (_i32, [_c_void_p, _i64]),
     "pa_append": (_i32, [_c_void_p, _i64, _i32, _i64p]),
     "pa_append_batch": (_i32, [_c_void_p, _i64p, _i32p, _i32, _i64p]),
@@ -115,6 +116,7 @@ SIGNATURES = {
     "pa_pending_copies": (_i32, [_c_void_p, _i32p, _i32, _i32p]),
     "pa_flush_copies": (_i32, [_c_void_p, _c_void_p]),
     "pa_reshape_and_cache": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p]),
+    "pa_pool_set_slot_checks": (_i32, [_c_void_p, ctypes.c_int, _c_void_p]),
     "pa_decode_workspace_bytes": (_size, [_c_void_p, _i64p, _i32, _i32]),
     "pa_decode": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _size,
                          _c_void_p]),
@@ -216,6 +218,13 @@ def pa_pool_create(desc, allocation_order=None, k_pool=None, v_pool=None):
 
 def pa_pool_destroy(pool):
     load().pa_pool_destroy(pool)
+
+
+def pa_pool_reserve_staging(pool, plan_bytes):
+    """Grow the pool's pinned staging buffers to ``plan_bytes``; returns the size reserved."""
+    reserved = _size()
+    _check(load().pa_pool_reserve_staging(pool, plan_bytes, ctypes.byref(reserved)))
+    return reserved.value
 
 
 def pa_seq_create(pool, seq):
@@ -320,6 +329,10 @@ def pa_flush_copies(pool, stream=None):
 def pa_reshape_and_cache(pool, k_new, v_new, slots, n, stream=None):
     _check(load().pa_reshape_and_cache(pool, _addr(k_new), _addr(v_new), _addr(slots), n,
                                        _stream(stream)))
+
+
+def pa_pool_set_slot_checks(pool, on, stream=None):
+    _check(load().pa_pool_set_slot_checks(pool, 1 if on else 0, _stream(stream)))
 
 
 # ---------------------------------------------------------------- attention

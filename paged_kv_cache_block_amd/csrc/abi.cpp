@@ -16,6 +16,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "abi_internal.hpp"
 #include "kernels.hpp"
 #include "pagedattn.h"
 #include "plan.hpp"
@@ -137,21 +138,31 @@ struct pa_pool {
   static constexpr int kRing = 4;
   Staging ring[kRing];
   int next = 0;
+  // Debug slot checks of pa_reshape_and_cache (pa_pool_set_slot_checks):
+  // per-slot stamps and the check's result, device memory of the library.
+  uint32_t* slot_marks = nullptr;
+  int32_t* check_result = nullptr;
+  uint32_t check_stamp = 0;
 
   bool has_device() const { return k != nullptr; }
 
   // Copy `bytes` of host data into the next pinned staging buffer and return
   // its device address; the buffer is reused only after the event recorded
-  // behind its previous use (staged_done) has fired.  When a buffer has to
-  // grow, every idle buffer of the ring grows with it, so that pinned
-  // allocations happen on the first calls and not later, one call at a time.
-  pa_status stage(const void* src, size_t bytes, const void** dev_copy) {
+  // behind its previous use (staged_done) has fired.  The ring is reserved
+  // when the pool is created (reserve_staging); a plan larger than that
+  // grows every idle buffer of the ring at once when `may_grow`, and is an
+  // error otherwise (the entry point that allocates nothing).
+  pa_status stage(const void* src, size_t bytes, const void** dev_copy, bool may_grow = true) {
     Staging& st = ring[next];
+    const size_t padded = pa::align_up(bytes, 16);
+    if (st.cap < padded && !may_grow)
+      return fail(PA_ERR_INVALID_ARG, "plan of " + std::to_string(padded) +
+                                          " bytes exceeds the pool's reserved staging buffers (" +
+                                          std::to_string(st.cap) + " bytes; see pa_pool_reserve_staging)");
     if (st.pending) {
       PA_HIP(hipEventSynchronize(st.ev));
       st.pending = false;
     }
-    const size_t padded = pa::align_up(bytes, 16);
     if (st.cap < padded) {
       const size_t cap = pa::align_up(std::max<size_t>(padded + padded / 2, 1 << 16), 16);
       for (Staging& b : ring) {
@@ -163,6 +174,28 @@ struct pa_pool {
     std::memcpy(st.host, src, bytes);
     *dev_copy = st.dev;
     return ok();
+  }
+
+  // Grow every buffer of the ring to at least `bytes` (waiting for buffers
+  // still in use); buffers already that large are kept.
+  pa_status reserve_staging(size_t bytes) {
+    const size_t cap = pa::align_up(std::max<size_t>(bytes, 16), 16);
+    for (Staging& b : ring) {
+      if (b.cap >= cap) continue;
+      if (b.pending) {
+        PA_HIP(hipEventSynchronize(b.ev));
+        b.pending = false;
+      }
+      const pa_status r = grow(b, cap);
+      if (r != PA_OK) return r;
+    }
+    return ok();
+  }
+
+  size_t staging_capacity() const {
+    size_t cap = ring[0].cap;
+    for (const Staging& b : ring) cap = std::min(cap, b.cap);
+    return cap;
   }
 
   pa_status grow(Staging& b, size_t cap) {
@@ -250,7 +283,65 @@ struct pa_pool {
     return ok();
   }
 
+  // Turn the slot checks on (allocating their device memory, zeroed on
+  // `stream`) or off (freeing it once the device is idle).
+  pa_status set_slot_checks(bool on, hipStream_t stream) {
+    if (on == (slot_marks != nullptr)) return ok();
+    if (!on) {
+      PA_HIP(hipDeviceSynchronize());
+      PA_HIP(hipFree(slot_marks));
+      PA_HIP(hipFree(check_result));
+      slot_marks = nullptr;
+      check_result = nullptr;
+      return ok();
+    }
+    const int64_t n = static_cast<int64_t>(geom.num_blocks) * geom.block_size;
+    uint32_t* marks = nullptr;
+    int32_t* result = nullptr;
+    hipError_t e = hipMalloc(&marks, sizeof(uint32_t) * n);
+    if (e == hipSuccess) e = hipMalloc(&result, 2 * sizeof(int32_t));
+    if (e == hipSuccess) e = pa::launch_zero_u32(marks, n, stream);
+    if (e != hipSuccess) {
+      if (marks) (void)hipFree(marks);
+      if (result) (void)hipFree(result);
+      return hip_fail(e, "slot checks");
+    }
+    slot_marks = marks;
+    check_result = result;
+    check_stamp = 0;
+    return ok();
+  }
+
+  // The debug check of n caller slots before a cache write: waits for it on
+  // `stream` and fails naming the first offending row.
+  pa_status check_slots(const int64_t* slots, int32_t n, hipStream_t stream) {
+    if (++check_stamp == 0) {  // stamps wrapped: every mark is stale again
+      PA_HIP(pa::launch_zero_u32(slot_marks, static_cast<int64_t>(geom.num_blocks) * geom.block_size, stream));
+      check_stamp = 1;
+    }
+    PA_HIP(pa::launch_check_slots(geom, slots, n, slot_marks, check_stamp, check_result, stream));
+    int32_t bad[2] = {-1, -1};
+    PA_HIP(hipMemcpyAsync(bad, check_result, sizeof(bad), hipMemcpyDeviceToHost, stream));
+    PA_HIP(hipStreamSynchronize(stream));
+    for (int kind = 0; kind < 2; ++kind) {
+      if (bad[kind] < 0) continue;
+      int64_t slot = 0;
+      PA_HIP(hipMemcpy(&slot, slots + bad[kind], sizeof(slot), hipMemcpyDeviceToHost));
+      const int64_t limit = static_cast<int64_t>(geom.num_blocks) * geom.block_size;
+      return fail(PA_ERR_INVALID_ARG,
+                  "row " + std::to_string(bad[kind]) + " names slot " + std::to_string(slot) +
+                      (kind == 0 ? ", outside [0, " + std::to_string(limit) + ")"
+                                 : ", which another row of the same call also names"));
+    }
+    return ok();
+  }
+
   ~pa_pool() {
+    if (slot_marks) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(slot_marks);
+      (void)hipFree(check_result);
+    }
     for (auto& st : ring) {
       if (st.pending) (void)hipEventSynchronize(st.ev);
       if (st.ev) (void)hipEventDestroy(st.ev);
@@ -314,6 +405,20 @@ size_t pa_pool_bytes(const pa_pool_desc* desc) {
   return static_cast<size_t>(desc->num_blocks) * geom.block_bytes();
 }
 
+namespace {
+
+// Pinned staging bytes reserved per ring buffer when a pool with device
+// memory is created: 8 bytes per pool block (a plan holds one 4-byte table
+// entry per page of the batch, plus 64-byte work items per page range) and
+// 256 KiB for per-sequence data, at most 8 MiB.  A decode plan of a batch
+// whose tables reference each block about once fits.
+size_t default_staging_bytes(const pa::PoolGeom& g) {
+  const size_t bytes = 8 * static_cast<size_t>(g.num_blocks) + (size_t{256} << 10);
+  return std::min(bytes, size_t{8} << 20);
+}
+
+}  // namespace
+
 pa_status pa_pool_create(const pa_pool_desc* desc, const int32_t* allocation_order, void* k_pool,
                          void* v_pool, pa_pool** out) {
   std::string msg;
@@ -331,11 +436,35 @@ pa_status pa_pool_create(const pa_pool_desc* desc, const int32_t* allocation_ord
   p->geom = {desc->num_blocks, desc->block_size, desc->num_kv_heads, desc->head_dim, desc->dtype};
   p->k = k_pool;
   p->v = v_pool;
+  if (p->has_device()) {
+    const pa_status r = p->reserve_staging(default_staging_bytes(p->geom));
+    if (r != PA_OK) {
+      const std::string why = g_err;
+      delete p;
+      return fail(r, why);
+    }
+  }
   *out = p;
   return ok();
 }
 
+pa_status pa_pool_reserve_staging(pa_pool* pool, size_t plan_bytes, size_t* reserved) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  if (!pool->has_device()) return fail(PA_ERR_INVALID_ARG, "metadata-only pool has no device memory");
+  if (plan_bytes > (size_t{1} << 32)) return fail(PA_ERR_INVALID_ARG, "plan_bytes above 4 GiB");
+  const pa_status r = pool->reserve_staging(plan_bytes);
+  if (r != PA_OK) return r;
+  if (reserved) *reserved = pool->staging_capacity();
+  return ok();
+}
+
 void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+pa_status pa_pool_set_slot_checks(pa_pool* pool, int on, void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
+  if (!pool->has_device()) return fail(PA_ERR_INVALID_ARG, "metadata-only pool has no device memory");
+  return pool->set_slot_checks(on != 0, as_stream(stream));
+}
 
 pa_status pa_seq_create(pa_pool* pool, int64_t seq) {
   if (!pool) return fail(PA_ERR_INVALID_ARG, "NULL pool");
@@ -450,6 +579,10 @@ pa_status pa_reshape_and_cache(pa_pool* pool, const void* k_new, const void* v_n
   if (n < 0 || (n > 0 && (!k_new || !v_new || !slots)))
     return fail(PA_ERR_INVALID_ARG, "n must be >= 0 with non-NULL k_new, v_new, slots");
   hipStream_t s = as_stream(stream);
+  if (pool->slot_marks && n > 0) {
+    const pa_status c = pool->check_slots(slots, n, s);
+    if (c != PA_OK) return c;
+  }
   pa_status st = pool->flush(s);
   if (st != PA_OK) return st;
   if (n == 0) return ok();  // nothing to launch (and nothing to time)
@@ -547,12 +680,17 @@ std::vector<int32_t> step_extra_tokens(const int64_t* seqs, const int32_t* n_tok
   return extra;
 }
 
-// Append n_tokens[b] (1 each when NULL) tokens to every sequence, store
-// their K/V rows and run attention for those rows: the fused decode step
-// (n_tokens NULL) and the multi-token verify step.
-pa_status step_impl(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens, int32_t B,
-                    int32_t num_heads, const void* k_new, const void* v_new, const void* q, void* out,
-                    void* ws, size_t ws_bytes, int64_t* slots_out, void* stream) {
+}  // namespace
+
+namespace pa {
+
+pa_status fail_status(pa_status status, const std::string& msg) { return fail(status, msg); }
+
+pa_status fused_step(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens, int32_t B,
+                     int32_t num_heads, const void* k_new, const void* v_new, const void* q, void* out,
+                     const StepWorkspace& wsp, int64_t* slots_out, void* stream) {
+  void* ws = wsp.ptr;
+  const size_t ws_bytes = wsp.bytes;
   pa_status r = check_decode_args(pool, num_heads, q, out, ws);
   if (r != PA_OK) return r;
   if (!k_new || !v_new) return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
@@ -583,9 +721,19 @@ pa_status step_impl(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
                                        pool->geom.head_dim, decode_tokens_per_part(), extra.data(),
                                        n_tokens, static_cast<int32_t>(rows), &sizing, &msg);
   if (s != pa::kOk) return fail(s, msg);
-  if (ws_bytes < sizing.total_bytes)
+  if (ws_bytes < sizing.total_bytes) {
+    if (wsp.static_scratch)
+      return fail(PA_ERR_INVALID_ARG, "the step needs " + std::to_string(sizing.total_bytes) +
+                                          " bytes of workspace, more than the " + std::to_string(ws_bytes) +
+                                          " bytes of the static scratch");
     return fail(PA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(sizing.total_bytes) +
                                         " bytes, got " + std::to_string(ws_bytes));
+  }
+  if (wsp.static_scratch && sizing.meta_bytes > pool->staging_capacity())
+    return fail(PA_ERR_INVALID_ARG, "the step's plan of " + std::to_string(sizing.meta_bytes) +
+                                        " bytes exceeds the pool's reserved staging buffers (" +
+                                        std::to_string(pool->staging_capacity()) +
+                                        " bytes; see pa_pool_reserve_staging)");
   pa::DecodePlan& plan = pool->plan;
   std::vector<int32_t> ones;
   if (!n_tokens) ones.assign(B, 1);
@@ -605,7 +753,7 @@ pa_status step_impl(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
   if (r != PA_OK) return r;
   const void* staged = nullptr;
   const size_t bytes = plan.meta.size() * sizeof(int32_t);
-  r = pool->stage(plan.meta.data(), bytes, &staged);
+  r = pool->stage(plan.meta.data(), bytes, &staged, !wsp.static_scratch);
   if (r != PA_OK) return r;
   {
     TimedLaunch t(PA_KERNEL_CACHE);
@@ -621,6 +769,10 @@ pa_status step_impl(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
   use.stream = st;
   return launch_decode_plan(pool, plan, B, num_heads, q, out, ws, st);
 }
+
+}  // namespace pa
+
+namespace {
 
 // Whether a prefill chunk goes through the split-K decode kernels (every
 // q_len small enough for one workgroup's query columns).
@@ -673,8 +825,8 @@ size_t pa_decode_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, 
 pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                          const void* k_new, const void* v_new, const void* q, void* out, void* ws,
                          size_t ws_bytes, int64_t* slots_out, void* stream) {
-  return step_impl(pool, seqs, nullptr, B, num_heads, k_new, v_new, q, out, ws, ws_bytes, slots_out,
-                   stream);
+  return pa::fused_step(pool, seqs, nullptr, B, num_heads, k_new, v_new, q, out, {ws, ws_bytes, false},
+                        slots_out, stream);
 }
 
 size_t pa_verify_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,
@@ -700,8 +852,8 @@ pa_status pa_verify_step(pa_pool* pool, const int64_t* seqs, const int32_t* q_le
                          int32_t num_heads, const void* k_new, const void* v_new, const void* q, void* out,
                          void* ws, size_t ws_bytes, int64_t* slots_out, void* stream) {
   if (!q_lens) return fail(PA_ERR_INVALID_ARG, "q_lens must be non-NULL");
-  return step_impl(pool, seqs, q_lens, B, num_heads, k_new, v_new, q, out, ws, ws_bytes, slots_out,
-                   stream);
+  return pa::fused_step(pool, seqs, q_lens, B, num_heads, k_new, v_new, q, out, {ws, ws_bytes, false},
+                        slots_out, stream);
 }
 
 size_t pa_prefill_workspace_bytes(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens,

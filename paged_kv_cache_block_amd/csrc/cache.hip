@@ -247,6 +247,34 @@ __global__ __launch_bounds__(256) void step_prep_kernel(
   }
 }
 
+// Slot check of one reshape_and_cache call, before it writes anything
+// (validate before mutate, as the [PagedPool] negative tests require of the
+// bookkeeping): one workgroup walks the rows; a slot outside [0, num_slots)
+// marks its row, and marks[slot] takes the call's stamp, so a row that finds
+// the stamp already there names a slot another row of the same call names.
+// result[0] / result[1] = the smallest row with a slot out of range / that
+// found its slot taken, or -1.
+__global__ __launch_bounds__(1024) void check_slots_kernel(const int64_t* __restrict__ slots, int32_t n,
+                                                           int64_t num_slots, uint32_t* __restrict__ marks,
+                                                           uint32_t stamp, int32_t* __restrict__ result) {
+  __shared__ int32_t first_bad[2];
+  if (threadIdx.x < 2) first_bad[threadIdx.x] = INT32_MAX;
+  __syncthreads();
+  for (int32_t i = threadIdx.x; i < n; i += 1024) {
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots)
+      atomicMin(&first_bad[0], i);
+    else if (atomicExch(&marks[slot], stamp) == stamp)
+      atomicMin(&first_bad[1], i);
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) result[threadIdx.x] = first_bad[threadIdx.x] == INT32_MAX ? -1 : first_bad[threadIdx.x];
+}
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += gridDim.x * 256ll) p[i] = 0u;
+}
+
 int grid_for(int64_t work, int64_t per_block, int64_t cap) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -361,6 +389,20 @@ hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_
                        static_cast<int64_t>(n), geom.num_kv_heads, geom.block_size, geom.head_dim,
                        num_slots);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_check_slots(const PoolGeom& geom, const int64_t* slots, int32_t n, uint32_t* marks,
+                              uint32_t stamp, int32_t* result, hipStream_t stream) {
+  const int64_t num_slots = static_cast<int64_t>(geom.num_blocks) * geom.block_size;
+  hipLaunchKernelGGL(check_slots_kernel, dim3(1), dim3(1024), 0, stream, slots, n, num_slots, marks, stamp,
+                     result);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(grid_for(n, 256, 4096)), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 

@@ -40,6 +40,16 @@ hipError_t launch_reshape_and_cache(const PoolGeom& geom, void* k_pool, void* v_
                                     int32_t n, hipStream_t stream,
                                     const KernelEvents& ev = KernelEvents{});
 
+// Debug slot check of n rows' slots (device int64 [n]): result (device
+// int32 [2]) receives the smallest row whose slot is outside the pool and the
+// smallest row that found its slot already taken by another row of the call
+// (-1 = none; which row of a repeated pair reports it depends on timing).
+// marks (device uint32 [num_blocks * block_size]) keeps per slot the stamp of
+// the last check that saw it; stamps must differ between calls.
+hipError_t launch_check_slots(const PoolGeom& geom, const int64_t* slots, int32_t n, uint32_t* marks,
+                              uint32_t stamp, int32_t* result, hipStream_t stream);
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
+
 // Which decode kernel serves a geometry (for timing labels and tests).
 enum class DecodeKernel { kGqaMfma, kQ8Mfma, kGeneric };
 DecodeKernel pick_decode_kernel(const PoolGeom& geom, int32_t group);

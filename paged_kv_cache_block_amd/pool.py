@@ -188,6 +188,11 @@ class DevicePool:
         abi.pa_reshape_and_cache(self.handle, k_new, v_new, slots, n, self._stream(stream))
         return slots
 
+    def set_slot_checks(self, on, stream=None):
+        """Debug checks of ``write`` (pa_pool_set_slot_checks): bad or
+        repeated slots are rejected before anything is written."""
+        abi.pa_pool_set_slot_checks(self.handle, on, self._stream(stream))
+
     def workspace(self, nbytes):
         torch = _torch()
         if self._ws is None or self._ws.numel() < nbytes:

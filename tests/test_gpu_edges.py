@@ -2,7 +2,8 @@
 (512), large and tiny blocks, a single slot per block, group 16 and a
 single query head per KV head, 8-bit pages on the generic kernel (head_dim
 256), one-token sequences, a batch of one, chunks whose rows reach the
-first position of the sequence, and pools larger than 4 GiB.
+first position of the sequence, pools larger than 4 GiB, and the debug slot
+checks of the cache writes.
 
 Source: docs.rs ferrum-kv 0.4.0 src/attention.rs, paged_attention (decode and
 q_tokens > 1); int8 rows as in the vladkulikov.com notebook "Модуль 10"
@@ -118,6 +119,48 @@ def test_reshape_and_cache_skips_out_of_range_slots():
         q8.write(slots, k, k)
         torch.cuda.synchronize()
         assert torch.equal(q8.k, before)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_slot_checks_reject_bad_slots_before_writing(kv):
+    """With slot checks on, a slot outside the pool or a slot two rows of one
+    call name is rejected with PA_ERR_INVALID_ARG and nothing is written
+    (the [PagedPool] negative tests' rule: validate before mutate); valid
+    rows are then stored as usual, pending copy-on-write copies included, and
+    a second valid call with the same slots passes (stamps differ per call)."""
+    from paged_kv_cache_block_amd import DevicePool
+    from paged_kv_cache_block_amd.abi import InvalidArgumentError
+    pool = DevicePool(8, 16, 2, 64, dtype=kv)
+    pool.set_slot_checks(True)
+    pool.create(0)
+    pool.append(0, 20)
+    pool.fork(0, 1)
+    slots = pool.append(1, 3)  # copy-on-write of the shared partial tail, left pending
+    assert pool.pending_copies()
+    torch.cuda.synchronize()
+    before = pool.k.clone(), pool.v.clone()
+    rows = torch.ones(3, 2, 64, dtype=torch.bfloat16, device="cuda")
+    log(f"slot checks ({kv}): out of range")
+    for bad in ([int(slots[0]), 8 * 16, int(slots[2])], [-1, int(slots[1]), int(slots[2])]):
+        with pytest.raises(InvalidArgumentError, match="outside"):
+            pool.write(torch.tensor(bad, dtype=torch.int64, device="cuda"), rows, rows)
+    log(f"slot checks ({kv}): repeated slot")
+    with pytest.raises(InvalidArgumentError, match="also names"):
+        pool.write(torch.tensor([int(slots[0]), int(slots[1]), int(slots[0])], dtype=torch.int64,
+                                device="cuda"), rows, rows)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k, before[0]) and torch.equal(pool.v, before[1])
+    assert pool.pending_copies(), "a rejected call must not flush the pending copies"
+    log(f"slot checks ({kv}): valid rows, twice")
+    good = torch.as_tensor(slots, dtype=torch.int64).cuda()
+    pool.write(good, rows, rows)
+    pool.write(good, rows, rows)
+    torch.cuda.synchronize()
+    assert not pool.pending_copies()
+    assert not torch.equal(pool.k, before[0])
+    pool.set_slot_checks(False)
+    pool.validate()
+    pool.close()
 
 
 @pytest.mark.parametrize("kv", ["bf16", "i8"])
