@@ -180,7 +180,8 @@ pa_status pa_pool_create(const pa_pool_desc* desc, const int32_t* allocation_ord
 /* Grow each of the pool's 4 pinned staging buffers to at least plan_bytes
  * (buffers still in use by enqueued work are waited for first; none
  * shrinks).  A call whose plan exceeds the reserved size grows the ring
- * inside that call (pinned allocation).  A plan is at most the metadata part of the
+ * inside that call (pinned allocation), except pa_decode_step_noalloc,
+ * which fails instead.  A plan is at most the metadata part of the
  * workspace the *_workspace_bytes calls return, so reserving that much is
  * always enough.  reserved: host, may be NULL; receives the size now
  * reserved per buffer.  Host-side; allocates pinned host memory.
@@ -408,6 +409,31 @@ size_t pa_decode_step_workspace_bytes(const pa_pool* pool, const int64_t* seqs, 
 pa_status pa_decode_step(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
                          const void* k_new, const void* v_new, const void* q, void* out, void* ws,
                          size_t ws_bytes, int64_t* slots_out, void* stream);
+
+/* pa_decode_step for callers that cannot allocate memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, semantics, kernels and results as pa_decode_step, but the
+ * workspace is a static device array of the library, PA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) per GPU, which each GPU the library runs on holds until the
+ * process ends; the plan crosses to the device through the pool's reserved
+ * staging buffers.  The call makes no device or pinned-host allocation
+ * (hipMalloc, hipHostMalloc, hipFree or a library routine that allocates);
+ * host bookkeeping uses ordinary heap memory, and timing (pa_timing_enable)
+ * creates its events when on.  The array used is that of the device
+ * `stream` belongs to (the current device for NULL).
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * there: calls that may overlap on one GPU (different streams, or other
+ * threads) race and must be ordered by the caller; successive calls on one
+ * stream are ordered by the stream.
+ * Errors: as pa_decode_step, checked before anything changes;
+ *   PA_ERR_INVALID_ARG also when the step's workspace (pa_decode_step_
+ *   workspace_bytes) exceeds PA_NOALLOC_SCRATCH_BYTES or its plan exceeds
+ *   the pool's reserved staging buffers; PA_ERR_DEVICE if the array's
+ *   address cannot be obtained. */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+pa_status pa_decode_step_noalloc(pa_pool* pool, const int64_t* seqs, int32_t B, int32_t num_heads,
+                                 const void* k_new, const void* v_new, const void* q, void* out,
+                                 int64_t* slots_out, void* stream);
 
 /* Workspace bytes pa_verify_step needs for this batch (sized for the lengths
  * after its appends).  0 if the arguments are invalid. */

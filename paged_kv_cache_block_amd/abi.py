@@ -123,6 +123,8 @@ SIGNATURES = {
     "pa_decode_step_workspace_bytes": (_size, [_c_void_p, _i64p, _i32, _i32]),
     "pa_decode_step": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _size, _i64p, _c_void_p]),
+    "pa_decode_step_noalloc": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                      _c_void_p, _i64p, _c_void_p]),
     "pa_verify_step_workspace_bytes": (_size, [_c_void_p, _i64p, _i32p, _i32, _i32]),
     "pa_verify_step": (_i32, [_c_void_p, _i64p, _i32p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _size, _i64p, _c_void_p]),
@@ -365,6 +367,24 @@ def pa_decode_step(pool, seqs, num_heads, k_new, v_new, q, out, ws, ws_bytes, st
     _check(load().pa_decode_step(pool, ptr, len(arr), num_heads, _addr(k_new), _addr(v_new), _addr(q),
                                  _addr(out), _addr(ws), ws_bytes, sp, _stream(stream)))
     return slots_out
+
+
+def pa_decode_step_noalloc(pool, seqs, num_heads, k_new, v_new, q, out, stream=None, slots_out=None):
+    """pa_decode_step with the library's static scratch as its workspace;
+    returns the new slots when ``slots_out`` is given or True."""
+    arr, ptr = _i64_array(seqs)
+    sp = None
+    if slots_out is True:
+        slots_out = np.empty(len(arr), dtype=np.int64)
+    if slots_out is not None:
+        assert slots_out.dtype == np.int64 and slots_out.size >= len(arr)
+        sp = slots_out.ctypes.data_as(_i64p)
+    _check(load().pa_decode_step_noalloc(pool, ptr, len(arr), num_heads, _addr(k_new), _addr(v_new),
+                                         _addr(q), _addr(out), sp, _stream(stream)))
+    return slots_out
+
+
+PA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def pa_verify_step_workspace_bytes(pool, seqs, q_lens, num_heads):

@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libpagedattn.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["cache.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["cache.hip", "decode.hip", "prefill.hip", "noalloc.hip"]
 CXX_SOURCES = ["abi.cpp", "pool.cpp", "plan.cpp", "prefix.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -226,6 +226,19 @@ class DevicePool:
                                    self._stream(stream), slots_out=True)
         return out, slots
 
+    def decode_step_noalloc(self, seqs, k_new, v_new, q, out, stream=None):
+        """decode_step with the library's static scratch as its workspace
+        (pa_decode_step_noalloc: no device or pinned allocation in the call;
+        ``out`` must be given).  Returns ``(out, slots)``."""
+        if out is None:
+            raise ValueError("decode_step_noalloc needs a caller-allocated out")
+        num_heads, out = self._queries(q, out, len(seqs))
+        self._rows(k_new, len(seqs), self.num_kv_heads, "k_new")
+        self._rows(v_new, len(seqs), self.num_kv_heads, "v_new")
+        slots = abi.pa_decode_step_noalloc(self.handle, seqs, num_heads, k_new, v_new, q, out,
+                                           self._stream(stream), slots_out=True)
+        return out, slots
+
     def verify_step(self, seqs, q_lens, k_new, v_new, q, out=None, stream=None, ws=None):
         """Append ``q_lens[b]`` tokens per sequence, store their K/V rows
         ([sum q_lens, Hkv, D]) and attend causally for those rows (``q``
