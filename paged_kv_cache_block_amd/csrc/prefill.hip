@@ -7,8 +7,13 @@
 // masks cached decoding).  The one-pass running max / sum per key tile is
 // lecture 19's tiled_attention recurrence.
 //
-// prefill_gqa_mfma<D, BS, CG, NW, S, Q8>  (bf16 pages, or Q8 1 int8 / 2 E4M3 codes; D in {64, 128},
-//                                         BS in {16, 32}, G | 16)
+// Two kernels share the plan (tiles of query rows) and the key-tile walk:
+// prefill_bf16_mfma32 (bf16 pages, 32x32x16 MFMA tiles, further below) and
+// prefill_q8_mfma (8-bit pages, 16x16x32 tiles over bf16 operands converted
+// in LDS).
+//
+// prefill_q8_mfma<D, BS, CG, NW, S, Q8>  (Q8 1 int8 / 2 E4M3 codes; D in {64, 128},
+//                                        BS in {16, 32}, G | 16)
 //   One workgroup of NW waves = (sequence, block of query rows, KV head).
 //   The MFMA N dimension packs (query row, head of the group) pairs: column c
 //   of the workgroup is row t0 + c / G, head g*G + c % G, so each key tile
@@ -26,6 +31,9 @@
 //   page row.  Every K and V operand of a tile is therefore one 16-byte
 //   chunk per lane, and the tile is NB blocks of 64 such chunks.
 //
+//   (The ring, staging, masks and windows below are described for bf16
+//   operand tiles; prefill_bf16_mfma32 stages exactly so, and this kernel
+//   stages raw 8-bit tiles and converts them, see the last paragraph.)
 //   The workgroup keeps an S-stage ring of tiles in LDS.  Each block is
 //   fetched with one direct global->LDS load (global_load_lds_dwordx4; lane l
 //   writes bytes 16l..16l+15 of the block), already in operand order, so the
@@ -70,11 +78,17 @@
 #ifndef PA_PREFILL_WAVES
 #define PA_PREFILL_WAVES 8
 #endif
-#ifndef PA_PREFILL_STAGES
-#define PA_PREFILL_STAGES 3
-#endif
 #ifndef PA_PREFILL_STAGES_Q8
 #define PA_PREFILL_STAGES_Q8 4
+#endif
+#ifndef PA_PREFILL32_WAVES
+#define PA_PREFILL32_WAVES 4
+#endif
+#ifndef PA_PREFILL32_STAGES
+#define PA_PREFILL32_STAGES 3
+#endif
+#ifndef PA_PREFILL32_Q_LDS
+#define PA_PREFILL32_Q_LDS 0
 #endif
 #ifndef PA_PREFILL_WAVES_PER_EU
 #define PA_PREFILL_WAVES_PER_EU 0  // occupancy hint (0 = none)
@@ -97,8 +111,9 @@ typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int kPrefillCG = PA_PREFILL_CG;          // 16-column groups per wave
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;    // waves per workgroup
-constexpr int kPrefillStages = PA_PREFILL_STAGES;  // key tiles in the LDS ring
 constexpr int kPrefillStagesQ8 = PA_PREFILL_STAGES_Q8;  // raw 8-bit tiles in the LDS ring
+constexpr int kPrefill32Waves = PA_PREFILL32_WAVES;     // waves per 32x32-tile workgroup
+constexpr int kPrefill32Stages = PA_PREFILL32_STAGES;   // key tiles in its LDS ring
 constexpr int kTile = 32;                          // key tokens per step
 constexpr float kSlackLog2 = 8.f;                  // largest softmax weight, log2
 
@@ -120,7 +135,8 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 }
 
 template <int D, int BS, int CG, int NW, int S, int Q8>
-__global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(PrefillArgs a) {
+__global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_q8_mfma(PrefillArgs a) {
+  static_assert(Q8 == 1 || Q8 == 2, "bf16 pages take prefill_bf16_mfma32");
   constexpr int KS = D / 32;         // k-steps of QK per token half
   constexpr int DT = D / 16;         // d tiles of P.V
   constexpr int KB = 2 * KS;         // K operand blocks per key tile
@@ -154,8 +170,8 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   static_assert(!Q8 || (S >= 4 && kCodeLoads <= NW && kCodeLoads % 2 == 0), "8-bit ring");
   // bf16: an S-stage ring of operand-ordered tiles.  8-bit: an S-stage ring of
   // raw tiles and two operand-ordered bf16 tiles converted from them.
-  __shared__ uint4 ring[Q8 ? 2 : S][NB][64];
-  __shared__ uint4 raw[Q8 ? S : 1][Q8 ? kRawBytes / 16 : 1];
+  __shared__ uint4 ring[2][NB][64];
+  __shared__ uint4 raw[S][kRawBytes / 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -221,79 +237,6 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) acc[k][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  // Stage tile T into ring slot st: this wave's BPW blocks, one direct
-  // global->LDS load each.  Tiles past the last (issued to keep every wave's
-  // vmcnt accounting uniform), slots past the sequence end and pages a
-  // window released read zeros.
-  // Per-lane element offsets of this wave's blocks inside their page (and
-  // which page of the tile each comes from): loop-invariant, so a tile
-  // wholly inside the sequence is staged with one multiply-add per block.
-  int blk_off[BPW], blk_pgi[BPW];
-#pragma unroll
-  for (int r = 0; r < BPW; ++r) {
-    const int blkid = wave * BPW + r;
-    if (blkid < KB) {
-      const int tt = blkid / KS, j = blkid - tt * KS;
-      const int tok = 8 * (n >> 2) + 4 * tt + (n & 3);
-      blk_pgi[r] = tok / BS;
-      blk_off[r] = k16_offset(tok % BS, 32 * j + 8 * grp, D, BS);
-    } else {
-      const int nt = blkid - KB;
-      const int tok = 8 * grp;
-      blk_pgi[r] = tok / BS;
-      blk_off[r] = (16 * nt + n) * BS + tok % BS;
-    }
-  }
-
-  auto stage = [&](int T, int st) {
-    if (T < n_tiles && T * kTile + kTile <= L) {
-      int ent[PAGES];
-#pragma unroll
-      for (int p = 0; p < PAGES; ++p) ent[p] = scalar_load(table, T * PAGES + p);
-      if (ent[0] >= 0 && ent[PAGES - 1] >= 0) {  // no page released by a window
-#pragma unroll
-        for (int r = 0; r < BPW; ++r) {
-          const int blkid = wave * BPW + r;
-          // The tile's page bases are wave-uniform (scalar arithmetic); a
-          // lane only picks one and adds its offset.
-          const uint16_t* pool = blkid < KB ? kpool : vpool;
-          const uint16_t* base0 = uniform_ptr(pool + (static_cast<size_t>(ent[0]) * Hkv + g) * page);
-          const uint16_t* base1 = uniform_ptr(pool + (static_cast<size_t>(ent[PAGES - 1]) * Hkv + g) * page);
-          const uint16_t* src = (blk_pgi[r] ? base1 : base0) + blk_off[r];
-          __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
-        }
-        return;
-      }
-    }
-    int ent[PAGES];
-#pragma unroll
-    for (int p = 0; p < PAGES; ++p) {
-      const int pg = T * PAGES + p;
-      ent[p] = (T < n_tiles && pg < nblk) ? scalar_load(table, pg) : 0;
-    }
-#pragma unroll
-    for (int r = 0; r < BPW; ++r) {
-      const int blkid = wave * BPW + r;
-      const void* src = a.zeros;
-      if (blkid < KB) {
-        const int tt = blkid / KS, j = blkid - tt * KS;
-        const int tok = 8 * (n >> 2) + 4 * tt + (n & 3);
-        const int pgi = tok / BS;
-        const int blk = pgi ? ent[PAGES - 1] : ent[0];
-        if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L && blk >= 0)
-          src = kpool + (static_cast<size_t>(blk) * Hkv + g) * page + k16_offset(tok % BS, 32 * j + 8 * grp, D, BS);
-      } else {
-        const int nt = blkid - KB;
-        const int tok = 8 * grp;
-        const int pgi = tok / BS;
-        const int blk = pgi ? ent[PAGES - 1] : ent[0];
-        if (T < n_tiles && T * PAGES + pgi < nblk && T * kTile + tok < L && blk >= 0)
-          src = vpool + (static_cast<size_t>(blk) * Hkv + g) * page + (16 * nt + n) * BS + tok % BS;
-      }
-      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
-    }
-  };
 
   // 8-bit: stage raw tile T into raw slot st.  Wave w < kCodeLoads moves 1 KB
   // of codes (the first half of the loads K codes, the second V codes) in
@@ -430,38 +373,22 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     f32x4 s[CG][2];
 #pragma unroll
     for (int k = 0; k < CG; ++k) s[k][0] = s[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // bf16 pages: every K operand of the tile is read from LDS before the
-    // first QK^T MFMA and every V operand right after the last, and the
-    // scheduler may not move them (sched_barrier): the MFMAs then issue back
-    // to back instead of waiting on an LDS read each two (3-4% faster
-    // prefill).  The 8-bit path, which converts the next tile meanwhile, is
-    // slower so and keeps the reads next to their MFMAs.
-    bf16x8 kops[2 * KS];
-    if constexpr (!Q8) {
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) kops[i] = blocks[i * 64 + lane];
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // The operands are read next to their MFMAs (this path converts the
+    // next tile meanwhile; reading them all ahead was slower).
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        const bf16x8 kop = Q8 ? blocks[(tt * KS + j) * 64 + lane] : kops[tt * KS + j];
+        const bf16x8 kop = blocks[(tt * KS + j) * 64 + lane];
 #pragma unroll
         for (int k = 0; k < CG; ++k)
           s[k][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qv[k][j], s[k][tt], 0, 0, 0);
       }
-    bf16x8 vops[DT];
-    if constexpr (!Q8) {
-#pragma unroll
-      for (int nt = 0; nt < DT; ++nt) vops[nt] = blocks[(KB + nt) * 64 + lane];
-      __builtin_amdgcn_sched_barrier(0);
-    }
     // s[k][tt][i] is the score of token T*32 + 8*grp + 4*tt + i for column n.
-    // 8-bit: the row scales of this lane's 8 tokens; K's scales the scores,
-    // V's the weights that enter P.V (not l).
+    // The row scales of this lane's 8 tokens: K's scale the scores, V's the
+    // weights that enter P.V (not l).
     float sk[8], sv[8];
-    if constexpr (Q8) {
+    {
       const float4* sc = reinterpret_cast<const float4*>(
           reinterpret_cast<const uint8_t*>(&raw[rs][0]) + 2 * kTile * D + 32 * grp);
       const float4 k0 = sc[0], k1 = sc[1], v0 = sc[kTile / 4], v1 = sc[kTile / 4 + 1];
@@ -490,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = s[k][tt][i];
-          if constexpr (Q8) x *= sk[4 * tt + i];
+          x *= sk[4 * tt + i];
           if (kMasked && !visible(4 * tt + i)) x = -INFINITY;
           s[k][tt][i] = x;
           mloc = fmaxf(mloc, x);
@@ -526,13 +453,10 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
         for (int h = 0; h < 2; ++h) {
           const int idx = 2 * w + h;
           const float w8 = exp2_flush(fmaf(s[k][idx / 4][idx % 4], a.scale_log2, -ms));
-          e[h] = w8;
-          if constexpr (Q8) {
-            // A slot past the sequence end may hold any scale bits: its
-            // weight is exactly 0 and must stay so.
-            e[h] = w8 * sv[idx];
-            if (kMasked && !visible(idx)) e[h] = 0.f;
-          }
+          // A slot past the sequence end may hold any scale bits: its
+          // weight is exactly 0 and must stay so.
+          e[h] = w8 * sv[idx];
+          if (kMasked && !visible(idx)) e[h] = 0.f;
           // hi = e with the low 16 bits cleared (a bf16 value); e - hi is exact
           // and enters P.V as a second bf16 term.
           const float lo = e[h] - __uint_as_float(__float_as_uint(e[h]) & 0xffff0000u);
@@ -547,8 +471,8 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
     const int live = kTail ? L - (T * kTile + 8 * grp) : kTile;  // tokens of this lane's 8 inside the sequence
 #pragma unroll
     for (int nt = 0; nt < DT; ++nt) {
-      bf16x8 vop = Q8 ? blocks[(KB + nt) * 64 + lane] : vops[nt];
-      if constexpr (kTail && Q8 != 1) {  // int8 codes are always finite; bf16 and E4M3 may be NaN
+      bf16x8 vop = blocks[(KB + nt) * 64 + lane];
+      if constexpr (kTail && Q8 != 1) {  // int8 codes are always finite; E4M3 bytes may be NaN
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (e >= live) vop[e] = static_cast<__bf16>(0.f);
@@ -574,39 +498,7 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   };
   using F = std::false_type;
   using Tr = std::true_type;
-  if constexpr (!Q8) {
-    // One pipeline step: the blocks of iteration i's tile from this wave have
-    // landed once at most those of the S-2 later iterations are outstanding;
-    // the barrier then publishes the whole tile and guarantees every wave has
-    // finished reading the slot that the next stage() overwrites (read in
-    // iteration i-1).
-    auto step = [&](int i) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * BPW, 0));
-      __builtin_amdgcn_s_barrier();
-      stage(tile_of(i + S - 1), (i + S - 1) % S);
-    };
-#pragma unroll
-    for (int i = 0; i < S - 1; ++i) stage(tile_of(i), i);
-    int i = 0;
-    if (!wave_live) {
-      for (; i < n_iter; ++i) step(i);
-    } else if (!windowed) {
-      for (; i < t_split; ++i) {
-        step(i);
-        compute_tile(i, i % S, 0, F{}, F{}, F{});
-      }
-      for (; i < n_tiles; ++i) {
-        step(i);
-        if (i * kTile <= wave_keys) compute_tile(i, i % S, 0, Tr{}, Tr{}, F{});
-      }
-    } else {
-      for (; i < n_iter; ++i) {
-        step(i);
-        const int T = tile_of(i);
-        if (wave_sees(T)) compute_tile(T, i % S, 0, Tr{}, Tr{}, Tr{});
-      }
-    }
-  } else {
+  {
     // 8-bit step i: this wave's loads of the raw tile of iteration i+1 have
     // landed once at most those of iteration i+2 are outstanding; the barrier
     // publishes that raw tile and the bf16 tile of iteration i (converted in
@@ -669,12 +561,338 @@ __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_gqa_mfma(Prefi
   }
 }
 
+// prefill_bf16_mfma32<D, BS, NW, S>  (bf16 pages; D in {64, 128}, BS in {16, 32}, G | 16)
+//   The same computation on v_mfma_f32_32x32x16_bf16 tiles: one workgroup of
+//   NW waves = (sequence, block of query rows, KV head); each wave owns 32
+//   columns (query row, head) and each lane exactly one of them (column
+//   lane % 32; lanes l and l ^ 32 share it).  Per 32-token key tile:
+//     S^T[32 tok x 32 col] = K_tile . Q^T      (D/16 k-steps)
+//     O^T[32 d x 32 col] += V^T_tile . P^T     (2 token k-steps x D/32 d blocks, P as hi + lo)
+//   Each 1 KB operand read from LDS feeds a 32x32x16 MFMA (twice the flops
+//   of a 16x16x32 one), and the per-tile softmax bookkeeping is shared by
+//   32 columns.  Row m of the QK tile is token 16*(m/16) + 8*((m/4)%2) +
+//   4*((m/8)%2) + m%4, so accumulator element j of lane l is token 16*(j/8) +
+//   8*(l/32) + j%8: the lane's P^T operand of token k-step s is its own
+//   elements 8s .. 8s+7, and the matching V^T operand (d = 32db + l%32,
+//   tokens 16s + 8*(l/32) .. +7) is 16 contiguous bytes of a V page row.
+//   Staging, windows, masks and the exponent reference follow
+//   prefill_q8_mfma above (with bf16 operand tiles staged directly).  Each
+//   workgroup uses a 48 KB ring and 168 registers per lane, so a CU holds
+//   three of them (three waves per SIMD).  The staging step fetches the
+//   block-table entries of the next tile one step ahead, so their scalar
+//   loads are never waited for on a tile's path.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int D, int BS, int NW, int S>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void prefill_bf16_mfma32(PrefillArgs a) {
+  constexpr int KS = D / 16;         // QK k-steps (16 d each) per key tile
+  constexpr int DB = D / 32;         // 32-row d blocks of P.V
+  constexpr int KB = KS;             // K operand blocks per key tile
+  constexpr int NB = KB + 2 * DB;    // operand blocks per key tile (V: token k-step s, d block db)
+  constexpr int PAGES = kTile / BS;  // pages per key tile
+  static_assert(NB % NW == 0, "each wave stages the same number of blocks");
+  constexpr int BPW = NB / NW;
+  static_assert((S - 2) * BPW < 64, "vmcnt range");
+  // Optionally the Q^T operands live in LDS (each wave reads only its own)
+  // instead of 8 registers per k-step.
+  constexpr bool kQInLds = PA_PREFILL32_Q_LDS != 0;
+  __shared__ uint4 ring[S][NB][64];
+  __shared__ uint4 qlds[kQInLds ? NW : 1][kQInLds ? KS : 1][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int cl = lane & 31, hf = lane >> 5;  // column of the lane in the wave, half of the wave
+  const int Hkv = a.num_kv_heads, Hq = a.num_heads, G = a.group;
+  const int tile = blockIdx.x / Hkv, g = blockIdx.x - tile * Hkv;
+  const int b = a.tiles[2 * tile], t0 = a.tiles[2 * tile + 1];
+  const int q0 = a.q_start[b];
+  const int q_len = a.q_start[b + 1] - q0;
+  const int L = a.ctx_len[b];
+  const int off = L - q_len;  // row t sees keys 0 .. off + t
+  const int nblk = (L + BS - 1) / BS;
+  const int32_t* table = a.tables + a.tbl_off[b];
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+  const size_t page = static_cast<size_t>(BS) * D;
+
+  const int wg_rows = NW * 32 / G;
+  const int wg_last = min(q_len - 1, t0 + wg_rows - 1);
+  const int n_tiles = (off + wg_last) / kTile + 1;
+  const int wave_c0 = wave * 32;
+  const int t_first = t0 + wave_c0 / G;
+  const bool wave_live = t_first < q_len;
+  const int t_last = min(q_len - 1, t0 + (wave_c0 + 31) / G);
+  const int wave_keys = off + t_last;
+  const float slack = kSlackLog2 / a.scale_log2;
+  const int win_sinks = a.seq_win[4 * b], win_recent = a.seq_win[4 * b + 1];
+  const bool windowed = win_recent < kNoWindowRecent;
+  const int t_win = windowed ? max(0, off + t0 + 1 - win_recent) / kTile : 0;
+  const int n_sink = windowed ? min(t_win, (win_sinks + kTile - 1) / kTile) : 0;
+  const int n_iter = n_sink + n_tiles - t_win;
+  const int lo_wave = off + t_first + 1 - win_recent;
+
+  const int c = wave_c0 + cl;
+  const int row = t0 + c / G, head = g * G + c % G;
+  const int lim = off + min(row, q_len - 1);  // columns past the last row use its limit, not stored
+  bf16x8 qv[kQInLds ? 1 : KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<size_t>(q0 + min(row, q_len - 1)) * Hq + head) * D + 8 * hf;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * j);
+      if constexpr (kQInLds) qlds[wave][j][lane] = __builtin_bit_cast(uint4, v);
+      else qv[j] = v;
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
+
+  // Per-lane offsets of this wave's blocks inside their page and the page of
+  // the tile each comes from.
+  int blk_off[BPW], blk_pgi[BPW];
+#pragma unroll
+  for (int r = 0; r < BPW; ++r) {
+    const int blkid = wave * BPW + r;
+    if (blkid < KB) {
+      const int m = cl;
+      const int tok = 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+      blk_pgi[r] = tok / BS;
+      blk_off[r] = k16_offset(tok % BS, 16 * blkid + 8 * hf, D, BS);
+    } else {
+      const int v = blkid - KB, ks = v / DB, db = v - ks * DB;
+      const int tok = 16 * ks + 8 * hf;
+      blk_pgi[r] = tok / BS;
+      blk_off[r] = (32 * db + cl) * BS + tok % BS;
+    }
+  }
+
+  // Table entries of tile T's pages (-1: released by a window; -2: past the
+  // sequence or past the last tile), fetched one staging step before they
+  // are used so the scalar loads are not waited for on the tile's path.
+  auto load_ent = [&](int T, int* ent) {
+#pragma unroll
+    for (int p = 0; p < PAGES; ++p) {
+      const int pg = T * PAGES + p;
+      ent[p] = (T < n_tiles && pg < nblk) ? scalar_load(table, pg) : -2;
+    }
+  };
+  auto stage = [&](int T, int st, const int* ent) {
+    if (T < n_tiles && T * kTile + kTile <= L && ent[0] >= 0 && ent[PAGES - 1] >= 0) {
+#pragma unroll
+      for (int r = 0; r < BPW; ++r) {
+        const int blkid = wave * BPW + r;
+        const uint16_t* pool = blkid < KB ? kpool : vpool;
+        const uint16_t* base0 = uniform_ptr(pool + (static_cast<size_t>(ent[0]) * Hkv + g) * page);
+        const uint16_t* base1 = uniform_ptr(pool + (static_cast<size_t>(ent[PAGES - 1]) * Hkv + g) * page);
+        const uint16_t* src = (blk_pgi[r] ? base1 : base0) + blk_off[r];
+        __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
+      }
+      return;
+    }
+    // Slow path: the tile reaches past the sequence end, a page was
+    // released, or the tile is past the last one (kept for uniform vmcnt).
+#pragma unroll
+    for (int r = 0; r < BPW; ++r) {
+      const int blkid = wave * BPW + r;
+      int tok;
+      if (blkid < KB) {
+        const int m = cl;
+        tok = 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+      } else {
+        const int v = blkid - KB, ks = v / DB;
+        tok = 16 * ks + 8 * hf;
+      }
+      const int pgi = tok / BS;
+      const int blk = pgi ? ent[PAGES - 1] : ent[0];
+      const void* src = a.zeros;
+      if (T * kTile + tok < L && blk >= 0)
+        src = (blkid < KB ? kpool : vpool) + (static_cast<size_t>(blk) * Hkv + g) * page + blk_off[r];
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)&ring[st][blkid][0], 16, 0, 0);
+    }
+  };
+
+  // S^T of the tile in ring slot st: D/16 MFMAs over K operands read from
+  // LDS ahead of the first one.
+  auto qk = [&](int st) {
+    const bf16x8* blocks = reinterpret_cast<const bf16x8*>(&ring[st][0][0]);
+    bf16x8 kops[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) kops[i] = blocks[i * 64 + lane];
+    f32x16 sc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      bf16x8 qop;
+      if constexpr (kQInLds) qop = __builtin_bit_cast(bf16x8, qlds[wave][j][lane]);
+      else qop = qv[j];
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kops[j], qop, sc, 0, 0, 0);
+    }
+    return sc;
+  };
+
+  // Softmax of tile T's scores `sc` (masks per kMasked / kWin, see above)
+  // and its P.V step over the V operands of ring slot st.
+  auto soft_pv = [&](int T, int st, f32x16 sc, auto masked_c, auto tail_c, auto win_c) {
+    constexpr bool kMasked = decltype(masked_c)::value;
+    constexpr bool kTail = decltype(tail_c)::value;
+    constexpr bool kWin = decltype(win_c)::value;
+    static_assert(kMasked || !kWin, "windowed tiles are masked");
+    // Released pages under a window: token k-step s of this lane lies in
+    // page T*PAGES + 16s/BS.
+    bool hole[2] = {false, false};
+    if constexpr (kWin) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int pg = T * PAGES + (16 * s2) / BS;
+        hole[s2] = pg < nblk && scalar_load(table, pg) < 0;
+      }
+    }
+    const bf16x8* blocks = reinterpret_cast<const bf16x8*>(&ring[st][0][0]);
+    // sc[j] is the score of key T*32 + 16*(j/8) + 8*hf + j%8 for this column.
+    const int base = T * kTile + 8 * hf;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float x = sc[j];
+      if constexpr (kMasked) {
+        const int key = base + 16 * (j >> 3) + (j & 7);
+        bool vis = key <= lim;
+        if constexpr (kWin) vis = vis && !hole[j >> 3] && (key < win_sinks || key > lim - win_recent);
+        if (!vis) x = -INFINITY;
+      }
+      sc[j] = x;
+      mloc = fmaxf(mloc, x);
+    }
+    // Lazy exponent reference (as above): moves only when a score passes it
+    // by more than `slack`; the column's two lanes agree on it.
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + slack)) {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+      const float mcol = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      if (mcol > m_run + slack) {
+        const float alpha = exp2_flush((m_run - mcol) * a.scale_log2);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        m_run = mcol;
+      }
+    }
+    const float ms = (kMasked && m_run == -INFINITY) ? 0.f : m_run * a.scale_log2;
+    float psum = 0.f;
+    bf16x8 p_hi[2], p_lo[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      uint32_t hw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float e[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int j = 8 * s2 + 2 * w + h2;
+          e[h2] = exp2_flush(fmaf(sc[j], a.scale_log2, -ms));
+          const float lo = e[h2] - __uint_as_float(__float_as_uint(e[h2]) & 0xffff0000u);
+          p_lo[s2][2 * w + h2] = static_cast<__bf16>(lo);
+          psum += e[h2];
+        }
+        hw[w] = __builtin_amdgcn_perm(__float_as_uint(e[1]), __float_as_uint(e[0]), 0x07060302u);
+      }
+      p_hi[s2] = __builtin_bit_cast(bf16x8, (uint4{hw[0], hw[1], hw[2], hw[3]}));
+    }
+    l_run += psum;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int live = kTail ? L - (base + 16 * s2) : 8;  // keys of the lane's 8 inside the sequence
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        bf16x8 vop = blocks[(KB + s2 * DB + db) * 64 + lane];
+        if constexpr (kTail) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= live) vop[e] = static_cast<__bf16>(0.f);
+        }
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, p_hi[s2], acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, p_lo[s2], acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  const int t_split = min(n_tiles, (off + t0 + 1) / kTile);
+  auto tile_of = [&](int i) { return i < n_sink ? i : t_win + i - n_sink; };
+  auto wave_sees = [&](int T) {
+    return T * kTile <= wave_keys && (T * kTile < win_sinks || T * kTile + kTile - 1 >= lo_wave);
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  int ent_next[PAGES];
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) {
+    load_ent(tile_of(i), ent_next);
+    stage(tile_of(i), i, ent_next);
+  }
+  load_ent(tile_of(S - 1), ent_next);
+  auto step = [&](int i) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((S - 2) * BPW, 0));
+    __builtin_amdgcn_s_barrier();
+    stage(tile_of(i + S - 1), (i + S - 1) % S, ent_next);
+    load_ent(tile_of(i + S), ent_next);
+  };
+  int i = 0;
+  if (!wave_live) {
+    for (; i < n_iter; ++i) step(i);
+  } else if (!windowed) {
+    for (; i < t_split; ++i) {
+      step(i);
+      soft_pv(i, i % S, qk(i % S), F{}, F{}, F{});
+    }
+    for (; i < n_tiles; ++i) {
+      step(i);
+      if (i * kTile <= wave_keys) soft_pv(i, i % S, qk(i % S), Tr{}, Tr{}, F{});
+    }
+  } else {
+    for (; i < n_iter; ++i) {
+      step(i);
+      const int T = tile_of(i);
+      if (wave_sees(T)) soft_pv(T, i % S, qk(i % S), Tr{}, Tr{}, Tr{});
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+  if (!wave_live) return;
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  if (row >= q_len) return;
+  const float inv = 1.f / l;
+  uint16_t* o = static_cast<uint16_t*>(a.out) + (static_cast<size_t>(q0 + row) * Hq + head) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // acc[db][4 q4 + r] is d = 32 db + 8 q4 + 4 hf + r.
+      uint2 packed;
+      packed.x = static_cast<uint32_t>(f32_to_bf16(acc[db][4 * q4 + 0] * inv)) |
+                 (static_cast<uint32_t>(f32_to_bf16(acc[db][4 * q4 + 1] * inv)) << 16);
+      packed.y = static_cast<uint32_t>(f32_to_bf16(acc[db][4 * q4 + 2] * inv)) |
+                 (static_cast<uint32_t>(f32_to_bf16(acc[db][4 * q4 + 3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(o + 32 * db + 8 * q4 + 4 * hf) = packed;
+    }
+}
+
 template <int D, int BS, int Q8>
 void launch_mfma(const PrefillArgs& a, hipStream_t stream, const KernelEvents& ev) {
   const dim3 grid(a.n_tiles * a.num_kv_heads);
-  constexpr int S = Q8 ? kPrefillStagesQ8 : kPrefillStages;
-  PA_LAUNCH(ev, (prefill_gqa_mfma<D, BS, kPrefillCG, kPrefillWaves, S, Q8>), grid,
-                     dim3(64 * kPrefillWaves), 0, stream, a);
+  if constexpr (Q8 == 0) {
+    PA_LAUNCH(ev, (prefill_bf16_mfma32<D, BS, kPrefill32Waves, kPrefill32Stages>), grid,
+              dim3(64 * kPrefill32Waves), 0, stream, a);
+  } else {
+    PA_LAUNCH(ev, (prefill_q8_mfma<D, BS, kPrefillCG, kPrefillWaves, kPrefillStagesQ8, Q8>), grid,
+              dim3(64 * kPrefillWaves), 0, stream, a);
+  }
 }
 
 template <int Q8>
@@ -696,6 +914,7 @@ bool prefill_uses_mfma(const PoolGeom& geom, int32_t group) {
 
 int32_t prefill_rows_per_tile(const PoolGeom& geom, int32_t group) {
   if (!prefill_uses_mfma(geom, group)) return 64;
+  if (!geom.q8()) return kPrefill32Waves * 32 / group;
   return kPrefillWaves * kPrefillCG * 16 / group;
 }
 
