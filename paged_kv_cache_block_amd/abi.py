@@ -96,47 +96,41 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 # name: (restype, argtypes)
 SIGNATURES = {
     "pa_pool_bytes": (_size, [ctypes.POINTER(pa_pool_desc)]),
-    "pa_pool_create": (_i32, [ctypes.POINTER(pa_pool_desc), _i32p, _c_void_p, _c_void_p,
-                              ctypes.POINTER(_c_void_p)]),
+    "pa_pool_create": (_i32, [ctypes.POINTER(pa_pool_desc), _c_void_p, _c_void_p, _c_void_p, ctypes.POINTER(_c_void_p)]),
     "pa_pool_destroy": (None, [_c_void_p]),
     "pa_pool_reserve_staging": (_i32, [_c_void_p, _size, ctypes.POINTER(_size)]),
     "pa_seq_create": (_i32, [_c_void_p, _i64]),
-    "pa_append": (_i32, [_c_void_p, _i64, _i32, _i64p]),
-    "pa_append_batch": (_i32, [_c_void_p, _i64p, _i32p, _i32, _i64p]),
+    "pa_append": (_i32, [_c_void_p, _i64, _i32, _c_void_p]),
+    "pa_append_batch": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p]),
     "pa_share": (_i32, [_c_void_p, _i64, _i64, _i32]),
     "pa_fork": (_i32, [_c_void_p, _i64, _i64]),
     "pa_release": (_i32, [_c_void_p, _i64]),
     "pa_seq_set_window": (_i32, [_c_void_p, _i64, _i32, _i32]),
     "pa_truncate": (_i32, [_c_void_p, _i64, _i32]),
-    "pa_prefix_lookup": (_i32, [_c_void_p, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
-    "pa_prefix_attach": (_i32, [_c_void_p, _i64, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
-    "pa_prefix_register": (_i32, [_c_void_p, _i64, ctypes.c_char_p, ctypes.c_char_p, _i32p, _i32, _i32p]),
+    "pa_prefix_lookup": (_i32, [_c_void_p, ctypes.c_char_p, ctypes.c_char_p, _c_void_p, _i32, _i32p]),
+    "pa_prefix_attach": (_i32, [_c_void_p, _i64, ctypes.c_char_p, ctypes.c_char_p, _c_void_p, _i32, _i32p]),
+    "pa_prefix_register": (_i32, [_c_void_p, _i64, ctypes.c_char_p, ctypes.c_char_p, _c_void_p, _i32, _i32p]),
     "pa_prefix_clear": (_i32, [_c_void_p, _i32p]),
     "pa_prefix_entries": (_i32, [_c_void_p, _i64p]),
-    "pa_pending_copies": (_i32, [_c_void_p, _i32p, _i32, _i32p]),
+    "pa_pending_copies": (_i32, [_c_void_p, _c_void_p, _i32, _i32p]),
     "pa_flush_copies": (_i32, [_c_void_p, _c_void_p]),
     "pa_reshape_and_cache": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p]),
     "pa_pool_set_slot_checks": (_i32, [_c_void_p, ctypes.c_int, _c_void_p]),
-    "pa_decode_workspace_bytes": (_size, [_c_void_p, _i64p, _i32, _i32]),
-    "pa_decode": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _size,
-                         _c_void_p]),
-    "pa_decode_step_workspace_bytes": (_size, [_c_void_p, _i64p, _i32, _i32]),
-    "pa_decode_step": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
-                              _c_void_p, _c_void_p, _size, _i64p, _c_void_p]),
-    "pa_decode_step_noalloc": (_i32, [_c_void_p, _i64p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
-                                      _c_void_p, _i64p, _c_void_p]),
-    "pa_verify_step_workspace_bytes": (_size, [_c_void_p, _i64p, _i32p, _i32, _i32]),
-    "pa_verify_step": (_i32, [_c_void_p, _i64p, _i32p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
-                              _c_void_p, _c_void_p, _size, _i64p, _c_void_p]),
-    "pa_prefill_workspace_bytes": (_size, [_c_void_p, _i64p, _i32p, _i32, _i32]),
-    "pa_prefill_chunk": (_i32, [_c_void_p, _i64p, _i32p, _i32, _i32, _c_void_p, _c_void_p,
-                                _c_void_p, _size, _c_void_p]),
+    "pa_decode_workspace_bytes": (_size, [_c_void_p, _c_void_p, _i32, _i32]),
+    "pa_decode": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "pa_decode_step_workspace_bytes": (_size, [_c_void_p, _c_void_p, _i32, _i32]),
+    "pa_decode_step": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p, _c_void_p]),
+    "pa_decode_step_noalloc": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "pa_verify_step_workspace_bytes": (_size, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32]),
+    "pa_verify_step": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p, _c_void_p]),
+    "pa_prefill_workspace_bytes": (_size, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32]),
+    "pa_prefill_chunk": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
     "pa_seq_len": (_i32, [_c_void_p, _i64, _i32p]),
-    "pa_block_table": (_i32, [_c_void_p, _i64, _i32p, _i32, _i32p]),
+    "pa_block_table": (_i32, [_c_void_p, _i64, _c_void_p, _i32, _i32p]),
     "pa_refcount": (_i32, [_c_void_p, _i32, _i32p]),
     "pa_stats": (_i32, [_c_void_p, ctypes.POINTER(pa_pool_stats)]),
     "pa_validate": (_i32, [_c_void_p]),
-    "pa_sequences": (_i32, [_c_void_p, _i64p, _i32, _i32p]),
+    "pa_sequences": (_i32, [_c_void_p, _c_void_p, _i32, _i32p]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_timing_enable": (_i32, [ctypes.c_int]),
     "pa_timing_reset": (_i32, []),
@@ -189,14 +183,24 @@ def _stream(s):
     return int(s)
 
 
+def _ptr(arr):
+    """Address of a contiguous numpy array's data, passed as a void pointer
+    (cheaper than building a typed ctypes pointer on every call)."""
+    return arr.__array_interface__["data"][0]
+
+
 def _i64_array(values):
-    arr = np.ascontiguousarray(np.asarray(values, dtype=np.int64))
-    return arr, arr.ctypes.data_as(_i64p)
+    arr = values
+    if not (isinstance(arr, np.ndarray) and arr.dtype == np.int64 and arr.flags.c_contiguous):
+        arr = np.ascontiguousarray(np.asarray(values, dtype=np.int64))
+    return arr, _ptr(arr)
 
 
 def _i32_array(values):
-    arr = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
-    return arr, arr.ctypes.data_as(_i32p)
+    arr = values
+    if not (isinstance(arr, np.ndarray) and arr.dtype == np.int32 and arr.flags.c_contiguous):
+        arr = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    return arr, _ptr(arr)
 
 
 # --------------------------------------------------------------------- pool
@@ -235,7 +239,7 @@ def pa_seq_create(pool, seq):
 
 def pa_append(pool, seq, n_tokens):
     slots = np.empty(max(n_tokens, 0), dtype=np.int64)
-    _check(load().pa_append(pool, seq, n_tokens, slots.ctypes.data_as(_i64p) if n_tokens > 0 else None))
+    _check(load().pa_append(pool, seq, n_tokens, _ptr(slots) if n_tokens > 0 else None))
     return slots
 
 
@@ -248,7 +252,7 @@ def pa_append_batch(pool, seqs, n_tokens, slots_out=None):
         slots_out = np.empty(total, dtype=np.int64)
     assert slots_out.dtype == np.int64 and slots_out.flags.c_contiguous and slots_out.size >= total
     _check(load().pa_append_batch(pool, ptr, nptr, len(arr),
-                                  slots_out.ctypes.data_as(_i64p) if total else None))
+                                  _ptr(slots_out) if total else None))
     return slots_out[:total]
 
 
@@ -320,7 +324,7 @@ def pa_pending_copies(pool):
     _check(load().pa_pending_copies(pool, None, 0, ctypes.byref(n)))
     pairs = np.empty((n.value, 2), dtype=np.int32)
     if n.value:
-        _check(load().pa_pending_copies(pool, pairs.ctypes.data_as(_i32p), n.value, ctypes.byref(n)))
+        _check(load().pa_pending_copies(pool, _ptr(pairs), n.value, ctypes.byref(n)))
     return [tuple(map(int, p)) for p in pairs]
 
 
@@ -363,7 +367,7 @@ def pa_decode_step(pool, seqs, num_heads, k_new, v_new, q, out, ws, ws_bytes, st
         slots_out = np.empty(len(arr), dtype=np.int64)
     if slots_out is not None:
         assert slots_out.dtype == np.int64 and slots_out.size >= len(arr)
-        sp = slots_out.ctypes.data_as(_i64p)
+        sp = _ptr(slots_out)
     _check(load().pa_decode_step(pool, ptr, len(arr), num_heads, _addr(k_new), _addr(v_new), _addr(q),
                                  _addr(out), _addr(ws), ws_bytes, sp, _stream(stream)))
     return slots_out
@@ -378,7 +382,7 @@ def pa_decode_step_noalloc(pool, seqs, num_heads, k_new, v_new, q, out, stream=N
         slots_out = np.empty(len(arr), dtype=np.int64)
     if slots_out is not None:
         assert slots_out.dtype == np.int64 and slots_out.size >= len(arr)
-        sp = slots_out.ctypes.data_as(_i64p)
+        sp = _ptr(slots_out)
     _check(load().pa_decode_step_noalloc(pool, ptr, len(arr), num_heads, _addr(k_new), _addr(v_new),
                                          _addr(q), _addr(out), sp, _stream(stream)))
     return slots_out
@@ -404,7 +408,7 @@ def pa_verify_step(pool, seqs, q_lens, num_heads, k_new, v_new, q, out, ws, ws_b
         slots_out = np.empty(int(ql.sum()), dtype=np.int64)
     if slots_out is not None:
         assert slots_out.dtype == np.int64 and slots_out.size >= int(ql.sum())
-        sp = slots_out.ctypes.data_as(_i64p)
+        sp = _ptr(slots_out)
     _check(load().pa_verify_step(pool, ptr, qptr, len(arr), num_heads, _addr(k_new), _addr(v_new),
                                  _addr(q), _addr(out), _addr(ws), ws_bytes, sp, _stream(stream)))
     return slots_out
@@ -435,7 +439,7 @@ def pa_block_table(pool, seq):
     _check(load().pa_block_table(pool, seq, None, 0, ctypes.byref(n)))
     out = np.empty(n.value, dtype=np.int32)
     if n.value:
-        _check(load().pa_block_table(pool, seq, out.ctypes.data_as(_i32p), n.value, ctypes.byref(n)))
+        _check(load().pa_block_table(pool, seq, _ptr(out), n.value, ctypes.byref(n)))
     return out
 
 
@@ -460,7 +464,7 @@ def pa_sequences(pool):
     _check(load().pa_sequences(pool, None, 0, ctypes.byref(n)))
     out = np.empty(n.value, dtype=np.int64)
     if n.value:
-        _check(load().pa_sequences(pool, out.ctypes.data_as(_i64p), n.value, ctypes.byref(n)))
+        _check(load().pa_sequences(pool, _ptr(out), n.value, ctypes.byref(n)))
     return out
 
 

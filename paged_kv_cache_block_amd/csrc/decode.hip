@@ -117,8 +117,17 @@ __global__ __launch_bounds__(64) void attn_generic(GenericArgs a) {
     int blk = 0, off = 0;
     bool keep = j < visible && (j < sinks || j >= win_lo);
     if (keep) {
-      blk = table[j / BS];
-      keep = blk >= 0;
+      // Decode plans list the visited pages only: page pg is entry pg below
+      // the sink pages, then entry pg - gap; the gap's pages hold no key any
+      // row sees (prefill plans have no gap).
+      const int pg = j / BS;
+      const int sp = a.seq_win ? a.seq_win[4 * b + 2] : 0, gp = a.seq_win ? a.seq_win[4 * b + 3] : 0;
+      if (pg >= sp && pg < sp + gp) {
+        keep = false;
+      } else {
+        blk = table[pg < sp ? pg : pg - gp];
+        keep = blk >= 0;
+      }
     }
     if (keep) {
       off = j - (j / BS) * BS;
@@ -326,7 +335,7 @@ void decode_mfma(DecodeArgs a) {
 
   using Page = PageRegs<D, BS, Q8>;
   auto page_of = [&](int ci) { return ci < sink_pages ? ci : ci + gap; };
-  auto block_of = [&](int ci) { return uniform(table[page_of(ci)]); };
+  auto block_of = [&](int ci) { return uniform(table[ci]); };  // tables list the visited pages
   auto load_page_blk = [&](int blk, Page& P) {
     const char* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
     const char* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
@@ -590,11 +599,17 @@ void decode_mfma(DecodeArgs a) {
 // page ranges).  A range with no visible key has m = -inf and weight 0.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
+  // One workgroup per (split query row, head).  Thread (r, v) owns float4 v
+  // of the partial rows c = r, r + R, ...: it loads kBatch of them at once
+  // (their m, l and acc chunk, all issued before any is used) and folds them
+  // into a running (max, numerator, denominator) with the log-sum-exp rule;
+  // a split of up to R * kBatch partial rows thus costs one memory round
+  // trip.  The R running triples then combine through LDS.
   constexpr int V4 = D / 4;      // float4 lanes per partial row
   constexpr int R = 256 / V4;    // partial rows in flight
-  __shared__ float s_red[4];
+  constexpr int kBatch = 4;      // partial rows per thread per round trip
+  __shared__ float s_m[R], s_den[R];
   __shared__ f32x4 s_num[R][V4];
-  __shared__ float s_den[R];
   const int tid = threadIdx.x;
   const int Hq = a.num_heads;
   const int mi = blockIdx.x / Hq, h = blockIdx.x - mi * Hq;
@@ -602,34 +617,59 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int row0 = a.q_start[b], qlen = a.q_start[b + 1] - row0;
   const int base = a.part_base[b], np = a.n_parts_of[b];
   auto prow = [&](int c) { return static_cast<size_t>(base) + (static_cast<size_t>(c) * qlen + t) * Hq + h; };
-
-  float M = -INFINITY;
-  for (int c = tid; c < np; c += 256) M = fmaxf(M, a.part_m[prow(c)]);
-  M = wave_max(M);
-  if ((tid & 63) == 0) s_red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
   const int r = tid / V4, v = tid - r * V4;
+
+  float m_t = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int c = r; c < np; c += R) {
-    const size_t row = prow(c);
-    const float mc = a.part_m[row];
-    const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
-    num += w * reinterpret_cast<const f32x4*>(a.part_acc + row * D)[v];
-    den += w * a.part_l[row];
+  for (int c0 = r; c0 < np; c0 += R * kBatch) {
+    float mc[kBatch], lc[kBatch];
+    f32x4 xc[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = c0 + k * R;
+      if (c < np) {
+        const size_t row = prow(c);
+        mc[k] = a.part_m[row];
+        lc[k] = a.part_l[row];
+        xc[k] = reinterpret_cast<const f32x4*>(a.part_acc + row * D)[v];
+      } else {
+        mc[k] = -INFINITY;
+        lc[k] = 0.f;
+        xc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float mm = m_t;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mm = fmaxf(mm, mc[k]);
+    if (mm == -INFINITY) continue;  // nothing visible yet (window ranges)
+    const float keep = m_t == -INFINITY ? 0.f : exp2f(m_t - mm);
+    num *= keep;
+    den *= keep;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = mc[k] == -INFINITY ? 0.f : exp2f(mc[k] - mm);
+      num += w * xc[k];
+      den += w * lc[k];
+    }
+    m_t = mm;
   }
   s_num[r][v] = num;
-  if (v == 0) s_den[r] = den;
+  if (v == 0) {
+    s_m[r] = m_t;
+    s_den[r] = den;
+  }
   __syncthreads();
   if (tid < V4) {
-    f32x4 tot = s_num[0][tid];
-    float dtot = s_den[0];
+    float M = s_m[0];
 #pragma unroll
-    for (int k = 1; k < R; ++k) {
-      tot += s_num[k][tid];
-      dtot += s_den[k];
+    for (int k = 1; k < R; ++k) M = fmaxf(M, s_m[k]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float dtot = 0.f;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const float w = s_m[k] == -INFINITY ? 0.f : exp2f(s_m[k] - M);
+      tot += w * s_num[k][tid];
+      dtot += w * s_den[k];
     }
     const float inv = 1.f / dtot;
     T* o = static_cast<T*>(a.out) + (static_cast<size_t>(row0 + t) * Hq + h) * D + 4 * tid;

@@ -201,7 +201,12 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.win_off = place(4 * static_cast<size_t>(B));
   p.work_off = place(kWorkInts * static_cast<size_t>(n_work));
   p.merge_off = place(std::max<size_t>(2, 2 * static_cast<size_t>(n_merge)));
-  p.tables_off = place(static_cast<size_t>(total_pages));
+  // Tables hold the visited pages only (a windowed sequence: its sink pages,
+  // then its pages from the first row's window on), indexed by the compact
+  // page index the kernels walk.
+  int64_t visited_pages = 0;
+  for (int32_t b = 0; b < B; ++b) visited_pages += nvis[b];
+  p.tables_off = place(static_cast<size_t>(visited_pages));
   p.slots_off = place(2 * static_cast<size_t>(std::max(slot_count, 0)));
   const size_t rows_hq = static_cast<size_t>(row_heads);
   p.meta_bytes = align_up(words * sizeof(int32_t), kWsAlign);
@@ -235,10 +240,11 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     toff[b] = static_cast<int32_t>(cursor);
     base[b] = part_base[b];
     npo[b] = n_parts_of[b];
-    // With extra tokens (sizing only) the pages not allocated yet stay 0.
-    const size_t have = std::min<size_t>(rows[b]->table.size(), static_cast<size_t>(nblk[b]));
-    std::copy(rows[b]->table.begin(), rows[b]->table.begin() + have, tables + cursor);
-    cursor += nblk[b];
+    const int32_t* w8 = &win[4 * static_cast<size_t>(b)];
+    const std::vector<int32_t>& tb = rows[b]->table;  // nblk[b] entries (not a sizing plan)
+    std::copy(tb.begin(), tb.begin() + w8[2], tables + cursor);
+    std::copy(tb.begin() + w8[2] + w8[3], tb.begin() + nblk[b], tables + cursor + w8[2]);
+    cursor += nvis[b];
   }
   for (size_t i = 0; i < items.size(); ++i) {
     const int32_t b = items[i].b, c = items[i].c;

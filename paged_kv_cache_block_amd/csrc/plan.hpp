@@ -52,7 +52,8 @@ struct DecodeArgs {
   void* out;                // [R][Hq][D]
   const int32_t* ctx_len;   // [B] tokens per sequence
   const int32_t* tbl_off;   // [B] offset of the sequence's table in `tables`
-  const int32_t* tables;    // concatenated block tables
+  const int32_t* tables;    // concatenated block tables of the visited pages, by compact
+                            // page index (see seq_win)
   const int32_t* q_start;   // [B+1] first query row of b
   const int32_t* work;      // [n_work][kWorkInts]: b, partition c, L, row0, q_len, sinks,
                             // recent, sink pages, gap, table offset, part_base, 0, then the

@@ -77,18 +77,18 @@ void BlockPool::evict(Sequence& s, int64_t first_new) {
   const int64_t sink_pages = ceil_div(s.sinks, block_size_);
   const int64_t lo = first_new + 1 - s.recent;
   const int64_t end = std::min(std::max<int64_t>(lo, 0) / block_size_, first_new / block_size_);
-  for (int64_t j = sink_pages; j < end; ++j) {
+  // Pages below scan_from are released already: each page is visited once
+  // over the sequence's appends instead of on every append.
+  for (int64_t j = std::max(sink_pages, s.scan_from); j < end; ++j) {
     if (s.table[j] == kHole) continue;
     drop_ref(s.table[j]);
     s.table[j] = kHole;
+    s.hole_end = std::max(s.hole_end, j + 1);
   }
+  s.scan_from = std::max(s.scan_from, end);
 }
 
-int64_t BlockPool::evicted_end(const Sequence& s) const {
-  for (int64_t j = static_cast<int64_t>(s.table.size()) - 1; j >= 0; --j)
-    if (s.table[j] == kHole) return (j + 1) * block_size_;
-  return 0;
-}
+int64_t BlockPool::evicted_end(const Sequence& s) const { return s.hole_end * block_size_; }
 
 Status BlockPool::set_window(int64_t seq, int32_t sinks, int32_t recent, std::string* msg) {
   auto it = seqs_.find(seq);
@@ -103,6 +103,7 @@ Status BlockPool::set_window(int64_t seq, int32_t sinks, int32_t recent, std::st
   }
   it->second.sinks = sinks;
   it->second.recent = recent;
+  it->second.scan_from = 0;  // other sink pages: the next release scans from them
   ++version_;
   return kOk;
 }
@@ -127,6 +128,7 @@ Status BlockPool::truncate(int64_t seq, int64_t new_length, std::string* msg) {
     if (s.table[j] != kHole) drop_ref(s.table[j]);
   s.table.resize(keep);
   s.length = new_length;
+  s.scan_from = std::min<int64_t>(s.scan_from, static_cast<int64_t>(keep));
   ++version_;
   return kOk;
 }
@@ -292,6 +294,8 @@ Status BlockPool::share(int64_t src, int64_t dst, int32_t prefix, std::string* m
                      it->second.table.begin() + ceil_div(prefix, block_size_));
   child.sinks = it->second.sinks;
   child.recent = it->second.recent;
+  child.hole_end = it->second.hole_end;  // <= the copied pages: prefix >= evicted_end(src)
+  child.scan_from = std::min<int64_t>(it->second.scan_from, static_cast<int64_t>(child.table.size()));
   for (int32_t b : child.table)
     if (b != kHole) ++refs_[b];
   seqs_.emplace(dst, std::move(child));
@@ -431,17 +435,26 @@ Status BlockPool::validate(std::string* msg) const {
     if (s.length < 0 || static_cast<int64_t>(s.table.size()) != ceil_div(s.length, block_size_))
       return broken("table size is not ceil(length / block_size) for sequence", kv.first);
     const size_t n = s.table.size();
+    int64_t last_hole = 0;
     for (size_t i = 0; i < n; ++i) {
       const int32_t b = s.table[i];
       if (b == kHole) {
         if (i + 1 == n && s.length % block_size_)
           return broken("the partially filled last page is released in sequence", kv.first);
+        last_hole = static_cast<int64_t>(i) + 1;
         continue;
       }
       if (b < 0 || b >= num_blocks_) return broken("block id outside the pool in sequence", kv.first);
       if (stamp[b] == visit) return broken("a block appears twice in the table of sequence", kv.first);
       stamp[b] = visit;
       ++listed_by[b];
+    }
+    if (last_hole != s.hole_end)
+      return broken("recorded end of the released pages is stale in sequence", kv.first);
+    if (s.windowed()) {
+      const int64_t sink_pages = ceil_div(s.sinks, block_size_);
+      for (int64_t j = sink_pages; j < std::min<int64_t>(s.scan_from, static_cast<int64_t>(n)); ++j)
+        if (s.table[j] != kHole) return broken("a page below the release cursor is resident in sequence", kv.first);
     }
     ++visit;
   }

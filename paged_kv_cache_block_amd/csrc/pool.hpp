@@ -38,6 +38,11 @@ struct Sequence {
   // with budget sinks + recent); sinks < 0: no window.
   int32_t sinks = -1, recent = 0;
   bool windowed() const { return sinks >= 0; }
+  // Incremental window bookkeeping: the pages from the sink pages up to
+  // scan_from are all released (the next release resumes there), and
+  // hole_end is one past the last released page (0 if none).
+  int64_t scan_from = 0;
+  int64_t hole_end = 0;
 };
 
 struct PoolStats {
