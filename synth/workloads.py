@@ -50,11 +50,18 @@ import numpy as np
 
 # --------------------------------------------------------------- dtype helpers
 def bf16_round(x):
-    """float32 array -> uint16 bfloat16 bit patterns, round-to-nearest-even."""
+    """float32 array -> uint16 bfloat16 bit patterns, round-to-nearest-even:
+    the high half of the bits plus the carry out of low half + 0x7FFF + the
+    high half's lowest bit (all in uint32, no widening)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    hi = u >> 16
+    carry = u & 0xFFFF
+    carry += 0x7FFF
+    carry += hi & 1
+    carry >>= 16
+    hi += carry
+    return hi.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits):

@@ -102,6 +102,38 @@ def build_device_pool(wl, check_against_oracle_pool=False):
     return pool, ref
 
 
+def build_device_pool_keeping_rows(wl):
+    """``build_device_pool`` that also returns every sequence's K/V rows in
+    logical order (``{seq: (K, V)}`` in the input dtype, as
+    ``synth.logical_kv`` gives them), from the same single draw."""
+    import torch
+    from paged_kv_cache_block_amd import DevicePool
+    pool = DevicePool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, dtype=wl.dtype,
+                      allocation_order=wl.allocation_order)
+    parts = {}
+    for op in append_stream(wl):
+        if op[0] == "create":
+            pool.create(op[1])
+            parts[op[1]] = []
+        elif op[0] == "share":
+            _, src, dst, prefix = op
+            pool.share(src, dst, prefix)
+            taken, need = [], prefix
+            for k, v in parts[src]:
+                if need <= 0:
+                    break
+                taken.append((k[:need], v[:need]))
+                need -= len(k)
+            parts[dst] = taken
+        else:
+            _, s, n, k, v = op
+            pool.write(pool.append(s, n), to_device(k, wl.dtype), to_device(v, wl.dtype))
+            parts[s].append((k, v))
+    torch.cuda.synchronize()
+    rows = {s: (np.concatenate([k for k, _ in p]), np.concatenate([v for _, v in p])) for s, p in parts.items() if p}
+    return pool, rows
+
+
 def expected_decode(wl, seqs, q_bits):
     """Oracle output for one query row per sequence (float64)."""
     rows = logical_kv(wl, sorted(set(seqs)))

@@ -17,7 +17,7 @@ from synth import (append_stream, decode_queries, gqa_decode, heavy_tail, logica
                    long_decode, prefill_queries, prefix_prefill, tiny_fp32)
 from synth.workloads import Workload, bf16_round, to_f64
 
-from gpu_support import (BF16_TOL, F32_TOL, assert_close, build_device_pool, expected_decode, log,
+from gpu_support import (build_device_pool_keeping_rows, BF16_TOL, F32_TOL, assert_close, build_device_pool, expected_decode, log,
                          to_device, to_host_f64, tol, k16_index)
 
 pytestmark = pytest.mark.gpu
@@ -385,41 +385,57 @@ def test_gqa_decode_full_size():
         assert_close(got[i], want[i], *BF16_TOL, what=f"seq {i}")
 
 
-def test_long_decode_full_size_sampled():
+def _expected_each(wl, seqs, q_bits, rows):
+    """Oracle decode rows of ``seqs``, one sequence at a time (its rows
+    widened to float64 and released before the next)."""
+    for i, s in enumerate(seqs):
+        K, V = rows[s]
+        yield i, s, oracle.attention(to_f64(q_bits[i:i + 1], wl.dtype), to_f64(K, wl.dtype),
+                                     to_f64(V, wl.dtype))[0]
+
+
+def test_long_decode_full_size():
+    """Every output of workload 3 (4 x 131,072 tokens, 64 / 8 heads): split-K
+    over 32 page ranges per sequence and the log-sum-exp merge, in the launch
+    configuration the bench times."""
     wl = long_decode()
     log("long_decode full: build")
-    pool, _ = build_device_pool(wl)
+    pool, rows = build_device_pool_keeping_rows(wl)
     assert pool.stats()["free_blocks"] == 0
     seqs = wl.decode_seqs
     q_bits, got = _decode(pool, wl, seqs)
-    log("long_decode full: oracle on sequences 0 and 3")
-    sample = [0, 3]
-    want = expected_decode(wl, sample, q_bits[sample])
-    for j, i in enumerate(sample):
-        assert_close(got[i], want[j], *BF16_TOL, what=f"seq {i}")
+    pool.close()
+    for i, s, want in _expected_each(wl, seqs, q_bits, rows):
+        log(f"long_decode full: oracle on sequence {s}")
+        assert_close(got[i], want, *BF16_TOL, what=f"seq {s}")
 
 
-def test_heavy_tail_full_size_sampled():
+def test_heavy_tail_full_size():
+    """Every output of workload 5: 256 sequences of 17 .. 32,373 tokens, MHA
+    d 64, bs 32, 1% of K/V rows x8 (the softmax maximum's stress case)."""
     wl = heavy_tail()
     log("heavy_tail full: build")
-    pool, _ = build_device_pool(wl)
+    pool, rows = build_device_pool_keeping_rows(wl)
     st = pool.stats()
     assert st["allocated_blocks"] == 42982 and st["logical_tokens"] == 1371446
     seqs = wl.decode_seqs
     q_bits, got = _decode(pool, wl, seqs)
+    pool.close()
     lengths = wl.final_lengths()
-    order = sorted(seqs, key=lambda s: lengths[s])
-    sample = sorted(set(order[:6] + order[-6:] + list(np.random.default_rng(0).choice(seqs, 12, replace=False))))
-    log(f"heavy_tail full: oracle on {len(sample)} sequences")
-    want = expected_decode(wl, sample, q_bits[sample])
-    for j, i in enumerate(sample):
-        assert_close(got[i], want[j], *BF16_TOL, what=f"seq {i} (L={lengths[i]})")
+    log(f"heavy_tail full: oracle on all {len(seqs)} sequences")
+    for i, s, want in _expected_each(wl, seqs, q_bits, rows):
+        assert_close(got[i], want, *BF16_TOL, what=f"seq {s} (L={lengths[s]})")
+        if i % 64 == 63:
+            log(f"heavy_tail full: {i + 1} sequences compared")
 
 
-def test_prefix_prefill_full_size_sampled_rows():
+def test_prefix_prefill_full_size():
+    """Every output row x head of workload 4: 16 x 512 causal rows over a
+    4096-token prefix shared by all 16 sequences (refcount 16) plus their own
+    512 tokens."""
     wl = prefix_prefill()
     log("prefix_prefill full: build")
-    pool, _ = build_device_pool(wl)
+    pool, rows = build_device_pool_keeping_rows(wl)
     st = pool.stats()
     assert st["allocated_blocks"] == 768 and pool.refcount(pool.block_table(0)[0]) == 16
     qp = prefill_queries(wl)
@@ -428,18 +444,14 @@ def test_prefix_prefill_full_size_sampled_rows():
     log("prefix_prefill full: prefill")
     out = to_host_f64(pool.prefill(seqs, q_lens, to_device(qp, wl.dtype)))
     torch.cuda.synchronize()
-    sample_seqs = [0, 7, 15]
-    rows = logical_kv(wl, sample_seqs)
-    rng = np.random.default_rng(1)
-    log("prefix_prefill full: oracle on sampled rows")
-    for s in sample_seqs:
+    pool.close()
+    r0 = 0
+    for s, n in wl.prefill:
         K, V = (to_f64(x, wl.dtype) for x in rows[s])
-        L = K.shape[0]
-        for t in sorted(set([0, 1, 15, 16, 255, 511] + list(rng.integers(0, 512, 6)))):
-            r = s * 512 + t
-            vis = L - 512 + t + 1
-            exp = oracle.attention(to_f64(qp[r:r + 1], wl.dtype), K[:vis], V[:vis])[0]
-            assert_close(out[r], exp, *BF16_TOL, what=f"seq {s} row {t}")
+        want = oracle.attention(to_f64(qp[r0:r0 + n], wl.dtype), K, V)
+        assert_close(out[r0:r0 + n], want, *BF16_TOL, what=f"prefill seq {s}")
+        r0 += n
+    log(f"prefix_prefill full: {r0} rows x {wl.num_heads} heads compared")
 
 
 @pytest.mark.parametrize("bs,d", [(16, 128), (32, 64), (16, 64), (8, 128), (16, 48), (128, 128)])
