@@ -335,7 +335,9 @@ void decode_mfma(DecodeArgs a) {
 
   using Page = PageRegs<D, BS, Q8>;
   auto page_of = [&](int ci) { return ci < sink_pages ? ci : ci + gap; };
-  auto block_of = [&](int ci) { return uniform(table[ci]); };  // tables list the visited pages
+  // Tables list the visited pages.  A scalar load (counted by lgkmcnt), so
+  // waiting for a block id never waits behind the wave's page loads.
+  auto block_of = [&](int ci) { return scalar_load(table, uniform(ci)); };
   auto load_page_blk = [&](int blk, Page& P) {
     const char* kp = kpool + (static_cast<size_t>(blk) * Hkv + g) * PB;
     const char* vp = vpool + (static_cast<size_t>(blk) * Hkv + g) * PB;

@@ -173,6 +173,17 @@ __device__ __forceinline__ float code_value(uint8_t c) {
   return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(codes4_to_bf16x4<Q8>(c)[0])) << 16);
 }
 
+// Address spaces of the direct global-to-LDS load builtin.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// and `lgkm` LDS/scalar operations of this wave are outstanding (lgkm 15:
+// LDS and scalar loads are not waited for).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
+}
+
 // Uniform value in a scalar register (the compiler cannot always prove it).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -25,6 +25,22 @@ int32_t* at_bytes(std::vector<int32_t>& meta, size_t byte_off) {
 // 256 CUs x 8 groups.
 constexpr int64_t kTargetGroups = 2048;
 
+struct Item { int32_t b, c, pages; };
+
+// Per-thread scratch of build_decode_plan, reused across calls so that a
+// steady stream of decode steps allocates nothing on the host.
+struct DecodeScratch {
+  std::vector<const Sequence*> rows;
+  std::vector<int64_t> len, nblk, nvis;
+  std::vector<int32_t> qlen, win, n_parts_of, part_base, merge;
+  std::vector<Item> items, tails;
+};
+
+DecodeScratch& decode_scratch() {
+  thread_local DecodeScratch scratch;
+  return scratch;
+}
+
 }  // namespace
 
 Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, int32_t num_heads,
@@ -40,8 +56,13 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     return kInvalidArg;
   }
   const int32_t bs = pool.block_size();
-  std::vector<const Sequence*> rows(B);
-  std::vector<int64_t> len(B), nblk(B), nvis(B);
+  DecodeScratch& scr = decode_scratch();
+  std::vector<const Sequence*>& rows = scr.rows;
+  std::vector<int64_t>&len = scr.len, &nblk = scr.nblk, &nvis = scr.nvis;
+  rows.assign(B, nullptr);
+  len.assign(B, 0);
+  nblk.assign(B, 0);
+  nvis.assign(B, 0);
   int64_t total_pages = 0;
   for (int32_t b = 0; b < B; ++b) {
     rows[b] = pool.find(seqs[b]);
@@ -61,8 +82,10 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     }
     total_pages += nblk[b];
   }
-  std::vector<int32_t> qlen(B, 1);
-  std::vector<int32_t> win(4 * static_cast<size_t>(B));
+  std::vector<int32_t>& qlen = scr.qlen;
+  std::vector<int32_t>& win = scr.win;
+  qlen.assign(B, 1);
+  win.assign(4 * static_cast<size_t>(B), 0);
   int64_t n_rows = B;
   int32_t max_q = 1;
   if (q_lens) {
@@ -132,17 +155,20 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     }
   }
 
-  std::vector<int32_t> n_parts_of(B);
-  struct Item { int32_t b, c, pages; };
+  std::vector<int32_t>& n_parts_of = scr.n_parts_of;
+  n_parts_of.assign(B, 0);
   // Longest page ranges first so short tails fill in at the end: the full
   // ranges in sequence order, then the shorter last ranges (at most one per
   // sequence) by decreasing length, ties in sequence order.
   // A sizing-only plan (extra_tokens) counts the items and merge rows
   // without listing them.
   const bool sizing = extra_tokens != nullptr;
-  std::vector<Item> items, tails;
-  if (!sizing) items.reserve(static_cast<size_t>(total_pages / ppp) + B);
-  std::vector<int32_t> part_base(B, -1), merge;
+  std::vector<Item>&items = scr.items, &tails = scr.tails;
+  items.clear();
+  tails.clear();
+  std::vector<int32_t>&part_base = scr.part_base, &merge = scr.merge;
+  part_base.assign(B, -1);
+  merge.clear();
   int32_t n_parts = 0;
   int64_t row_heads = 0, n_work = 0, n_merge = 0;
   for (int32_t b = 0; b < B; ++b) {
@@ -219,10 +245,11 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
     return kOk;
   }
   // The caller's previous plan buffer is reused (no allocation once it is
-  // large enough).
+  // large enough).  Every section is written below; the alignment padding
+  // between sections is never read, so the buffer is not cleared.
   std::vector<int32_t>& meta = p.meta;
   meta = std::move(plan->meta);
-  meta.assign(words, 0);
+  meta.resize(words);
   int32_t* ctx = at_bytes(meta, p.ctx_off);
   int32_t* toff = at_bytes(meta, p.tbl_off_off);
   int32_t* base = at_bytes(meta, p.base_off);

@@ -106,8 +106,6 @@ hipError_t launch_prefill_generic(const PoolGeom& geom, const PrefillArgs& a, hi
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int kPrefillCG = PA_PREFILL_CG;          // 16-column groups per wave
 constexpr int kPrefillWaves = PA_PREFILL_WAVES;    // waves per workgroup
@@ -128,11 +126,6 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return reinterpret_cast<const T*>(lo | (hi << 32));
 }
 
-// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
-// and `lgkm` LDS/scalar operations of this wave are outstanding.
-constexpr int waitcnt_imm(int vm, int lgkm) {
-  return (vm & 0xF) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
-}
 
 template <int D, int BS, int CG, int NW, int S, int Q8>
 __global__ __launch_bounds__(NW * 64) PA_PREFILL_OCC void prefill_q8_mfma(PrefillArgs a) {
