@@ -132,14 +132,16 @@ def recorded_traffic(name):
 
 
 def decode_source_digest(texts=None):
-    """sha256 of the decode kernel's code (decode.hip then device.hpp) with
-    line comments, trailing blanks and empty lines removed, so that an edit of
-    comments alone keeps the recorded counters."""
+    """sha256 of the decode kernel's code and of the plan builder that sizes
+    its launch (decode.hip, device.hpp, plan.cpp) with line comments,
+    trailing blanks and empty lines removed, so that an edit of comments
+    alone keeps the recorded counters."""
     import hashlib
     import re
     if texts is None:
         csrc = os.path.join(ROOT, "paged_kv_cache_block_amd", "csrc")
-        texts = [open(os.path.join(csrc, f), encoding="utf-8").read() for f in ("decode.hip", "device.hpp")]
+        texts = [open(os.path.join(csrc, f), encoding="utf-8").read()
+                 for f in ("decode.hip", "device.hpp", "plan.cpp")]
     lines = []
     for text in texts:
         for line in text.splitlines():
@@ -651,7 +653,9 @@ def main():
     ap.add_argument("--layers", type=int, default=8,
                     help="decode / verify steps take this many layers' pools in turn (one layer per step)")
     ap.add_argument("--prefill-iters", type=int, default=20)
-    ap.add_argument("--prefill-warmup", type=int, default=2)
+    ap.add_argument("--prefill-warmup", type=int, default=10,
+                    help="untimed prefill calls before the timed ones (the clock settles over the "
+                         "first ~10 calls after the memory-bound decode legs)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--legs", default="int8,fp8,verify,window,long,heavy,prefix",
                     help="comma list of the legs after the headline decode leg: int8, fp8 (decode and "

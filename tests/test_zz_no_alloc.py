@@ -111,27 +111,38 @@ def test_noalloc_step_matches_decode_step(case):
         p.close()
 
 
-def test_noalloc_step_rejects_workspace_above_the_scratch():
-    """16 sequences of 16384 tokens at 16 query heads over 1 KV head split
-    into ~2064 page ranges: the partial results alone exceed 16 MiB.  The
-    call fails before anything changes (no rows are written, so none are
-    needed)."""
+def _pool_above_the_scratch():
+    """A pool and batch whose decode step needs more workspace than the
+    static scratch: 32 query heads over 1 KV head (the split-K partial rows
+    hold 32 x 130 floats per page range), with the batch grown until the
+    page ranges the plan picks add up to more than 16 MiB of partials."""
     from paged_kv_cache_block_amd import DevicePool, abi
+    hq = 32
+    for B, L in ((16, 16384), (127, 16383), (255, 16383)):
+        pool = DevicePool(B * (L // 16 + 2) + 16, 16, 1, 128, dtype="bf16")
+        seqs = list(range(B))
+        for s in seqs:
+            pool.create(s)
+            pool.append(s, L)
+        need = abi.pa_decode_step_workspace_bytes(pool.handle, seqs, hq)
+        if need > abi.PA_NOALLOC_SCRATCH_BYTES:
+            return pool, seqs, hq, need
+        pool.close()
+    pytest.fail("no batch of the list needs more workspace than the static scratch")
+
+
+def test_noalloc_step_rejects_workspace_above_the_scratch():
+    """A step whose workspace exceeds the static scratch fails before
+    anything changes (no rows are written, so none are needed)."""
     from paged_kv_cache_block_amd.abi import InvalidArgumentError
-    nb = 16 * 1025 + 16
-    pool = DevicePool(nb, 16, 1, 128, dtype="bf16")
-    seqs = list(range(16))
-    for s in seqs:
-        pool.create(s)
-        pool.append(s, 16384)
-    need = abi.pa_decode_step_workspace_bytes(pool.handle, seqs, 16)
-    assert need > abi.PA_NOALLOC_SCRATCH_BYTES, need
+    pool, seqs, hq, need = _pool_above_the_scratch()
+    B = len(seqs)
     before = [pool.seq_len(s) for s in seqs]
     stats = pool.stats()
-    new = torch.zeros((16, 1, 128), dtype=torch.bfloat16, device="cuda")
-    q = torch.zeros((16, 16, 128), dtype=torch.bfloat16, device="cuda")
+    new = torch.zeros((B, 1, 128), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((B, hq, 128), dtype=torch.bfloat16, device="cuda")
     out = torch.empty_like(q)
-    log("noalloc rejection: workspace above the static scratch")
+    log(f"noalloc rejection: {B} sequences, workspace {need} bytes above the static scratch")
     with pytest.raises(InvalidArgumentError, match="static scratch"):
         pool.decode_step_noalloc(seqs, new, new, q, out)
     assert [pool.seq_len(s) for s in seqs] == before
