@@ -6,8 +6,12 @@ sequences with log-uniform lengths, and a sliding window (sinks + recent)
 on some of them; then, against the float64 oracle on the same rows:
 decode of every sequence, a verify step with random row counts (the
 MFMA page dtypes), and a prefill chunk of random length appended to every
-sequence.  The fixed cases of the other GPU tests pin known shapes; this
-one walks shapes nobody picked by hand.
+sequence.  A child sharing a random prefix of one sequence (then growing
+past it) and a fork of that sequence join the batch first, and two fused
+decode steps run before the verify step, so copy-on-write of shared
+partial tails happens inside the device calls.  The fixed cases of the
+other GPU tests pin known shapes; this one walks shapes nobody picked by
+hand.
 
 Sources: docs.rs ferrum-kv 0.4.0 src/attention.rs, paged_attention (GQA,
 scale, bottom-right causal mask for multi-token queries); vladkulikov.com
@@ -29,7 +33,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-SEEDS = list(range(24))
+SEEDS = list(range(32))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -91,7 +95,7 @@ def test_random_shapes_match_oracle(seed):
     group = hq // hkv
     log(f"fuzz seed {seed}: {kv} d {d} bs {bs} heads {hq}/{hkv} lengths {lengths} windows {windows}")
     grow = 300 + 32  # prefill chunk and verify rows appended later, per sequence
-    nb = int(sum(-(-(n + grow) // bs) + 2 for n in lengths) + 16)
+    nb = int(sum(-(-(n + grow) // bs) + 2 for n in lengths) + 2 * (-(-(64 + grow) // bs) + 2) + 16)
     order = rng.permutation(nb).astype(np.int32)
     pool = DevicePool(nb, bs, hkv, d, dtype=kv, allocation_order=order)
     ref = oracle.Pool(nb, bs, hkv, d, allocation_order=order, quant_bits=8 if kv in ("i8", "fp8") else None,
@@ -109,11 +113,38 @@ def test_random_shapes_match_oracle(seed):
             _append_rows(pool, ref, rng, s, m, hkv, d, io)
             done += m
 
+    # A child sharing a random prefix of the first sequence without a window,
+    # grown past it, and a fork of the same sequence.
+    plain = [s for s, w in zip(seqs, windows) if w is None]
+    if plain:
+        src, child, fork = plain[0], len(lengths), len(lengths) + 1
+        prefix = int(rng.integers(1, ref.lengths[src] + 1))
+        pool.share(src, child, prefix)
+        ref.share(src, child, prefix)
+        _append_rows(pool, ref, rng, child, int(rng.integers(1, 64)), hkv, d, io)
+        pool.fork(src, fork)
+        ref.fork(src, fork)
+        seqs += [child, fork]
+
     # Decode: one query row per sequence over its whole (or windowed) cache.
     q = _draw(rng, (len(seqs), hq, d), io)
     got = to_host_f64(pool.decode(seqs, to_device(q, io)))
     want = np.concatenate([_want(ref, s, q[b:b + 1], io) for b, s in enumerate(seqs)])
     assert_close(got, want, *tol, what=f"seed {seed} decode")
+
+    # Two fused decode steps: append one token to every sequence, store its
+    # K/V row and decode, in one call.
+    for step in range(2):
+        k, v = _draw(rng, (len(seqs), hkv, d), io), _draw(rng, (len(seqs), hkv, d), io)
+        q = _draw(rng, (len(seqs), hq, d), io)
+        out, slots = pool.decode_step(seqs, to_device(k, io), to_device(v, io), to_device(q, io))
+        want_slots = []
+        for s in seqs:
+            want_slots += ref.append(s, 1)
+        assert slots.tolist() == want_slots
+        ref.write(want_slots, to_f64(k, io), to_f64(v, io))
+        want = np.concatenate([_want(ref, s, q[b:b + 1], io) for b, s in enumerate(seqs)])
+        assert_close(to_host_f64(out), want, *tol, what=f"seed {seed} decode step {step}")
 
     # Verify step: append + store + causal attention of 1..32/G rows.
     if kv != "f32":
