@@ -499,6 +499,28 @@ pa_status pa_validate(const pa_pool* pool);
 /* Number of live sequences; ids_out (host [cap], may be NULL) receives them
  * in ascending order. */
 pa_status pa_sequences(const pa_pool* pool, int64_t* ids_out, int32_t cap, int32_t* n);
+
+/* The split-K work list a decode call (pa_decode, or with q_lens the verify
+ * step and short prefill chunks) builds for this batch, in launch order;
+ * host only, for tests and debugging (no page defines the partition: it is
+ * this library's split of [ferrum] paged_attention's key loop, merged by
+ * [lecture19] online_softmax_stats).  q_lens NULL = one row per sequence.
+ * *pages_per_range: the pages of one range; items: host [cap_items][16]
+ * ints per work item: batch row b, range c (compact pages [c * pages_per_range,
+ * min(visited, (c + 1) * pages_per_range)) of the sequence's visited pages),
+ * length L, first query row, q_len, sinks, recent (2^29 without a window),
+ * sink pages, gap, table offset, first split-K partial row-head (-1: the
+ * sequence is one range), 0, then the block of compact page
+ * c * pages_per_range + w for waves w < 4 (0 past the range); tables: host
+ * [cap_tables], the visited pages of every row from its table offset:
+ * compact page i is page i for i < sink pages, else page i + gap.
+ * *n_items / *n_tables receive the counts; only what fits is written.
+ * Errors: as the plan of pa_decode (PA_ERR_UNKNOWN_SEQ, PA_ERR_INVALID_ARG
+ * for an empty sequence, q_lens[b] outside 1..length, a head mismatch or
+ * NULL outputs). */
+pa_status pa_decode_work_items(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens, int32_t B,
+                               int32_t num_heads, int32_t* pages_per_range, int32_t* items, int32_t cap_items,
+                               int32_t* n_items, int32_t* tables, int64_t cap_tables, int64_t* n_tables);
 /* Message of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);
 

@@ -131,6 +131,8 @@ SIGNATURES = {
     "pa_stats": (_i32, [_c_void_p, ctypes.POINTER(pa_pool_stats)]),
     "pa_validate": (_i32, [_c_void_p]),
     "pa_sequences": (_i32, [_c_void_p, _c_void_p, _i32, _i32p]),
+    "pa_decode_work_items": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32p, _c_void_p, _i32, _i32p,
+                                    _c_void_p, _i64, _i64p]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_timing_enable": (_i32, [ctypes.c_int]),
     "pa_timing_reset": (_i32, []),
@@ -441,6 +443,21 @@ def pa_block_table(pool, seq):
     if n.value:
         _check(load().pa_block_table(pool, seq, _ptr(out), n.value, ctypes.byref(n)))
     return out
+
+
+def pa_decode_work_items(pool, seqs, num_heads, q_lens=None):
+    """(pages_per_range, items [n][16] int32, tables int32) of the decode work
+    list for this batch (see the header)."""
+    seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+    ql = None if q_lens is None else np.ascontiguousarray(q_lens, dtype=np.int32)
+    ppr, n_items, n_tables = _i32(), _i32(), ctypes.c_int64()
+    args = (pool, _ptr(seqs), None if ql is None else _ptr(ql), len(seqs), num_heads, ctypes.byref(ppr))
+    _check(load().pa_decode_work_items(*args, None, 0, ctypes.byref(n_items), None, 0, ctypes.byref(n_tables)))
+    items = np.zeros((n_items.value, 16), dtype=np.int32)
+    tables = np.zeros(n_tables.value, dtype=np.int32)
+    _check(load().pa_decode_work_items(*args, _ptr(items), n_items.value, ctypes.byref(n_items),
+                                       _ptr(tables), n_tables.value, ctypes.byref(n_tables)))
+    return ppr.value, items, tables
 
 
 def pa_refcount(pool, block):

@@ -993,6 +993,38 @@ pa_status pa_validate(const pa_pool* pool) {
   return from(pool->meta.validate(&msg), msg);
 }
 
+pa_status pa_decode_work_items(const pa_pool* pool, const int64_t* seqs, const int32_t* q_lens, int32_t B,
+                               int32_t num_heads, int32_t* pages_per_range, int32_t* items, int32_t cap_items,
+                               int32_t* n_items, int32_t* tables, int64_t cap_tables, int64_t* n_tables) {
+  if (!pool || !pages_per_range || !n_items || !n_tables || cap_items < 0 || cap_tables < 0 ||
+      (cap_items > 0 && !items) || (cap_tables > 0 && !tables))
+    return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  pa::DecodePlan plan;
+  std::string msg;
+  const pa::Status s = pa::build_decode_plan(pool->meta, seqs, B, num_heads, pool->geom.num_kv_heads,
+                                             pool->geom.head_dim, decode_tokens_per_part(), nullptr, q_lens, 0,
+                                             &plan, &msg);
+  if (s != pa::kOk) return fail(s, msg);
+  const int32_t* meta = plan.meta.data();
+  *pages_per_range = plan.pages_per_part;
+  *n_items = plan.n_work;
+  const int32_t* work = meta + plan.work_off / sizeof(int32_t);
+  std::copy(work, work + pa::kWorkInts * static_cast<size_t>(std::min(cap_items, plan.n_work)), items);
+  // The tables section runs to the slots section (4-word padding aside).
+  const int32_t* toff = meta + plan.tbl_off_off / sizeof(int32_t);
+  const int32_t* ctx = meta + plan.ctx_off / sizeof(int32_t);
+  const int32_t* win = meta + plan.win_off / sizeof(int32_t);
+  int64_t visited = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t nblk = (ctx[b] + pool->geom.block_size - 1) / pool->geom.block_size;
+    visited = std::max<int64_t>(visited, toff[b] + nblk - win[4 * static_cast<size_t>(b) + 3]);
+  }
+  *n_tables = visited;
+  const int32_t* tab = meta + plan.tables_off / sizeof(int32_t);
+  std::copy(tab, tab + std::min(cap_tables, visited), tables);
+  return ok();
+}
+
 pa_status pa_sequences(const pa_pool* pool, int64_t* ids_out, int32_t cap, int32_t* n) {
   if (!pool || !n || cap < 0 || (cap > 0 && !ids_out)) return fail(PA_ERR_INVALID_ARG, "bad arguments");
   std::vector<int64_t> ids = pool->meta.sequence_ids();

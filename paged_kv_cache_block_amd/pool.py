@@ -129,6 +129,11 @@ class DevicePool:
     def block_table(self, seq):
         return abi.pa_block_table(self.handle, seq)
 
+    def decode_work_items(self, seqs, num_heads, q_lens=None):
+        """(pages per range, work items [n][16], visited-page tables) of the
+        decode work list for this batch (pa_decode_work_items)."""
+        return abi.pa_decode_work_items(self.handle, seqs, num_heads, q_lens)
+
     def refcount(self, block):
         return abi.pa_refcount(self.handle, block)
 

@@ -3,8 +3,8 @@
 C ABI layer) are built with both sanitizers, and the differential fuzzers of
 the pool against the oracle -- [KVPool] append_or_allocate, copy_on_write,
 release_sequence and the [PagedPool] validate invariants after every
-operation, the window / rollback fuzz and the prefix-cache trace -- run
-against that build in a child process.  Any sanitizer report aborts the
+operation, the window / rollback fuzz, the prefix-cache trace and the
+decode work-list checks -- run against that build in a child process.  Any sanitizer report aborts the
 child and fails the test.
 """
 
@@ -15,7 +15,7 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-FUZZERS = ["tests/test_abi_host.py", "tests/test_abi_window.py", "tests/test_abi_prefix.py"]
+FUZZERS = ["tests/test_abi_host.py", "tests/test_abi_window.py", "tests/test_abi_prefix.py", "tests/test_plan_host.py"]
 
 
 def test_fuzzers_under_address_and_undefined_sanitizers():
