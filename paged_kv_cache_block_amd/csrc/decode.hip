@@ -615,10 +615,10 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int Hq = a.num_heads;
   const int mi = blockIdx.x / Hq, h = blockIdx.x - mi * Hq;
-  const int b = a.merge_rows[2 * mi], t = a.merge_rows[2 * mi + 1];
-  const int row0 = a.q_start[b], qlen = a.q_start[b + 1] - row0;
-  const int base = a.part_base[b], np = a.n_parts_of[b];
-  auto prow = [&](int c) { return static_cast<size_t>(base) + (static_cast<size_t>(c) * qlen + t) * Hq + h; };
+  // The merge entry carries everything (one scalar load, no second hop).
+  const int32_t* entry = a.merge_rows + 4 * mi;
+  const int out_row = entry[0], first = entry[1], stride = entry[2], np = entry[3];
+  auto prow = [&](int c) { return static_cast<size_t>(first) + h + static_cast<size_t>(c) * stride; };
   const int r = tid / V4, v = tid - r * V4;
 
   float m_t = -INFINITY, den = 0.f;
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
       dtot += w * s_den[k];
     }
     const float inv = 1.f / dtot;
-    T* o = static_cast<T*>(a.out) + (static_cast<size_t>(row0 + t) * Hq + h) * D + 4 * tid;
+    T* o = static_cast<T*>(a.out) + (static_cast<size_t>(out_row) * Hq + h) * D + 4 * tid;
 #pragma unroll
     for (int i = 0; i < 4; ++i) Elt<T>::store(o + i, tot[i] * inv);
   }

@@ -190,7 +190,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   part_base.assign(B, -1);
   merge.clear();
   int32_t n_parts = 0;
-  int64_t row_heads = 0, n_work = 0, n_merge = 0;
+  int64_t row_heads = 0, n_work = 0, n_merge = 0, row_start = 0;
   for (int32_t b = 0; b < B; ++b) {
     int32_t nb = static_cast<int32_t>(nvis[b]);
     int32_t np = static_cast<int32_t>(ceil_div(nb, ppp));
@@ -213,11 +213,14 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
       n_merge += qlen[b];
       if (!sizing) {
         for (int32_t t = 0; t < qlen[b]; ++t) {
-          merge.push_back(b);
-          merge.push_back(t);
+          merge.push_back(static_cast<int32_t>(row_start + t));
+          merge.push_back(part_base[b] + t * num_heads);
+          merge.push_back(qlen[b] * num_heads);
+          merge.push_back(np);
         }
       }
     }
+    row_start += qlen[b];
   }
   std::stable_sort(tails.begin(), tails.end(),
                    [](const Item& x, const Item& y) { return x.pages > y.pages; });
@@ -246,7 +249,7 @@ Status build_decode_plan(const BlockPool& pool, const int64_t* seqs, int32_t B, 
   p.nparts_off = place(B);
   p.win_off = place(4 * static_cast<size_t>(B));
   p.work_off = place(kWorkInts * static_cast<size_t>(n_work));
-  p.merge_off = place(std::max<size_t>(2, 2 * static_cast<size_t>(n_merge)));
+  p.merge_off = place(std::max<size_t>(4, 4 * static_cast<size_t>(n_merge)));
   // Tables hold the visited pages only (a windowed sequence: its sink pages,
   // then its pages from the first row's window on), indexed by the compact
   // page index the kernels walk.

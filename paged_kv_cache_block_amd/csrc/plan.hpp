@@ -66,7 +66,9 @@ struct DecodeArgs {
   float* part_m;            // [row-heads]
   float* part_l;            // [row-heads]
   float* part_acc;          // [row-heads][D]
-  const int32_t* merge_rows;// [n_merge][2] = (b, t) query rows of split sequences
+  const int32_t* merge_rows;// [n_merge][4] per query row of a split sequence: its output
+                            // row, the partial row-head of its head 0 in partition 0,
+                            // the row-head stride between partitions, the partitions
   const int32_t* seq_win;   // [B][4] = (sinks, recent, sink pages, gap): the pages
                             // visited are the compact indices i < n_visit = nblk - gap,
                             // page i for i < sink pages, else page i + gap; a key p is
