@@ -164,6 +164,35 @@ def test_windowed_prefill_long_chunk_and_fp32_generic():
         assert_close(got[s], _want(ref32, s, q32[s:s + 1], "f32")[0], *F32_TOL, what=f"fp32 seq {s}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_balanced_windowed_batch_runs_unsplit(kv):
+    """32 windowed rows of equal visited length over 8 KV heads (256
+    workgroups): the work list leaves every row whole (one range, no split-K
+    partials, no merge launch), and the outputs still match the oracle."""
+    log(f"balanced windowed batch {kv}")
+    specs = [(1100 + 3 * i, (4, 1024)) for i in range(32)]
+    pool, ref, rng = _build(specs, 32, 8, 128, 16, kv, chunk=256)
+    seqs = list(range(len(specs)))
+    _, items, _ = pool.decode_work_items(seqs, 32)
+    assert len(items) == len(seqs) and (items[:, 10] == -1).all()
+    q = _draw(rng, (len(seqs), 32, 128), "bf16")
+    got = to_host_f64(pool.decode(seqs, to_device(q, "bf16")))
+    for i, s in enumerate(seqs):
+        assert_close(got[i], _want(ref, s, q[i:i + 1], "bf16")[0], *BF16_TOL, what=f"seq {s}")
+    k, v = _draw(rng, (len(seqs), 8, 128), "bf16"), _draw(rng, (len(seqs), 8, 128), "bf16")
+    q = _draw(rng, (len(seqs), 32, 128), "bf16")
+    out, slots = pool.decode_step(seqs, to_device(k, "bf16"), to_device(v, "bf16"), to_device(q, "bf16"))
+    want_slots = []
+    for s in seqs:
+        want_slots += ref.append(s, 1)
+    assert slots.tolist() == want_slots
+    ref.write(want_slots, to_f64(k, "bf16"), to_f64(v, "bf16"))
+    got = to_host_f64(out)
+    for i, s in enumerate(seqs):
+        assert_close(got[i], _want(ref, s, q[i:i + 1], "bf16")[0], *BF16_TOL, what=f"step seq {s}")
+    _check_tables(pool, ref, seqs)
+
+
 PREFILL_SPECS = [
     # (length, window, wanted rows): the rows are capped at the positions
     # still resident, so early rows of a long chunk may find pages of their

@@ -162,3 +162,20 @@ def test_work_list_errors():
         pool.decode_work_items([0], 4, [41])      # more rows than tokens
     ppr, items, tables = pool.decode_work_items([0, 0], 4)
     assert len(items) == 2 and tables.tolist() == pool.block_table(0).tolist() * 2
+
+
+def test_balanced_batch_that_fills_the_gpu_is_not_split():
+    """Rows of about equal visited length whose count times the KV heads
+    reaches 256 keep one range each (no split-K partials); a batch just short
+    of 256 workgroups, or with one row much longer than the mean, is split."""
+    pool = DevicePool(8192, 16, 8, 64, metadata_only=True)
+    for s in range(40):
+        pool.create(s)
+        pool.append(s, 2000 + 7 * s if s < 39 else 2000)
+    ppr, items, _ = pool.decode_work_items(list(range(32)), 32)
+    assert len(items) == 32 and (items[:, 10] == -1).all() and ppr >= -(-2217 // 16)
+    _, items, _ = pool.decode_work_items(list(range(31)), 32)       # 248 workgroups
+    assert (items[:, 10] >= 0).any()
+    pool.append(39, 6000)                                           # one row 4x the others
+    _, items, _ = pool.decode_work_items(list(range(31)) + [39], 32)
+    assert (items[:, 10] >= 0).any()
